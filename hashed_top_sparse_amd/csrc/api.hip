@@ -1,0 +1,233 @@
+// api.hip -- the C ABI of libdkv: argument validation, workspace plan and
+// the launch sequence of one decode step.  Every entry point validates on
+// the host and returns a status before any launch; nothing is allocated.
+#include <string.h>
+
+#include "internal.h"
+
+namespace dkv {
+namespace {
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool valid_config(const dkv_config *cfg, dkv_status *why) {
+  if (cfg == nullptr) {
+    *why = DKV_ERR_INVALID_ARG;
+    return false;
+  }
+  if (cfg->num_q_heads <= 0 || cfg->num_kv_heads <= 0 || cfg->top_k < 0 ||
+      cfg->window < 0 || cfg->sinks < 0 ||
+      cfg->num_q_heads % cfg->num_kv_heads != 0) {
+    *why = DKV_ERR_INVALID_ARG;
+    return false;
+  }
+  const int G = cfg->num_q_heads / cfg->num_kv_heads;
+  const int64_t sel = (int64_t)cfg->top_k + cfg->window + cfg->sinks;
+  if (cfg->head_dim != kHeadDim || cfg->page_size != kPage ||
+      !(cfg->code_bits == 64 || cfg->code_bits == 128 ||
+        cfg->code_bits == 256) ||
+      !(G == 1 || G == 2 || G == 4 || G == 8) || sel > DKV_MAX_SELECT ||
+      cfg->num_kv_heads > 4096) {
+    *why = DKV_ERR_UNSUPPORTED;
+    return false;
+  }
+  return true;
+}
+
+bool make_dims(const dkv_config *cfg, int32_t batch, int32_t max_seq_len,
+               int32_t max_blocks, int64_t num_blocks, DecodeDims *d,
+               dkv_status *why) {
+  if (!valid_config(cfg, why)) return false;
+  if (batch <= 0 || batch > 65535 || max_seq_len < 0 || max_blocks < 0 ||
+      num_blocks < 0) {
+    *why = DKV_ERR_INVALID_ARG;
+    return false;
+  }
+  if (max_seq_len > DKV_MAX_SEQ_LEN) {
+    *why = DKV_ERR_UNSUPPORTED;
+    return false;
+  }
+  d->B = batch;
+  d->Hq = cfg->num_q_heads;
+  d->Hkv = cfg->num_kv_heads;
+  d->G = d->Hq / d->Hkv;
+  d->b = cfg->code_bits;
+  d->W = d->b / 32;
+  d->k = cfg->top_k;
+  d->w = cfg->window;
+  d->sigma = cfg->sinks;
+  d->cap = d->k + d->w + d->sigma;
+  d->max_seq_len = max_seq_len;
+  const int64_t by_blocks = (int64_t)kPage * max_blocks;
+  d->n_max = (int)(by_blocks < max_seq_len ? by_blocks : max_seq_len);
+  d->max_blocks = max_blocks;
+  d->num_blocks = num_blocks;
+  const int cap = d->cap > 0 ? d->cap : 1;
+  d->nsplit = (cap + kAttnRows - 1) / kAttnRows;
+  if ((int64_t)d->B * d->Hkv > 65535 * 64) {
+    *why = DKV_ERR_UNSUPPORTED;
+    return false;
+  }
+  return true;
+}
+
+dkv_status decode_impl(const dkv_config *cfg, const void *q,
+                       const void *k_pool, const void *v_pool,
+                       const uint32_t *codes, const uint8_t *radii,
+                       int64_t num_blocks, const int32_t *block_table,
+                       int32_t max_blocks_per_seq, const int32_t *seq_lens,
+                       int32_t batch, int32_t max_seq_len, const void *proj,
+                       float *out, int32_t *sel_idx, int32_t *sel_cnt,
+                       void *workspace, size_t workspace_bytes, int8_t *q8_out,
+                       int32_t *scores_out, hipStream_t stream) {
+  DecodeDims d;
+  dkv_status why = DKV_OK;
+  if (!make_dims(cfg, batch, max_seq_len, max_blocks_per_seq, num_blocks, &d,
+                 &why))
+    return why;
+  if (q == nullptr || k_pool == nullptr || v_pool == nullptr ||
+      codes == nullptr || radii == nullptr || block_table == nullptr ||
+      seq_lens == nullptr || proj == nullptr || out == nullptr ||
+      max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return DKV_ERR_INVALID_ARG;
+  const WorkspacePlan plan = plan_workspace(d);
+  if (workspace == nullptr || workspace_bytes < plan.total ||
+      ((uintptr_t)workspace & 255) != 0)
+    return DKV_ERR_WORKSPACE;
+
+  char *ws = static_cast<char *>(workspace);
+  int8_t *q8 = q8_out ? q8_out : reinterpret_cast<int8_t *>(ws + plan.q8);
+  int32_t *scores =
+      scores_out ? scores_out : reinterpret_cast<int32_t *>(ws + plan.scores);
+  int32_t *sel = reinterpret_cast<int32_t *>(ws + plan.sel);
+  int32_t *cnt = reinterpret_cast<int32_t *>(ws + plan.cnt);
+  float *part = reinterpret_cast<float *>(ws + plan.part);
+  const uint16_t *q16 = static_cast<const uint16_t *>(q);
+  const uint16_t *k16 = static_cast<const uint16_t *>(k_pool);
+  const uint16_t *v16 = static_cast<const uint16_t *>(v_pool);
+  const uint16_t *p16 = static_cast<const uint16_t *>(proj);
+
+  if (launch_qprep(d, q16, p16, q8, stream) != hipSuccess)
+    return DKV_ERR_LAUNCH;
+  if (launch_score(d, codes, radii, block_table, seq_lens, q8, scores,
+                   stream) != hipSuccess)
+    return DKV_ERR_LAUNCH;
+  if (launch_select(d, scores, seq_lens, sel, cnt, sel_idx, sel_cnt, stream) !=
+      hipSuccess)
+    return DKV_ERR_LAUNCH;
+  if (launch_attend(d, q16, k16, v16, block_table, sel, cnt, part, out,
+                    stream) != hipSuccess)
+    return DKV_ERR_LAUNCH;
+  return DKV_OK;
+}
+
+} // namespace
+
+WorkspacePlan plan_workspace(const DecodeDims &d) {
+  WorkspacePlan p;
+  size_t off = 0;
+  p.q8 = off;
+  off += align256((size_t)d.B * d.Hq * d.b);
+  p.scores = off;
+  off += align256((size_t)d.B * d.Hkv * (size_t)d.max_seq_len * 4);
+  p.sel = off;
+  off += align256((size_t)d.B * d.Hkv * (size_t)d.cap * 4);
+  p.cnt = off;
+  off += align256((size_t)d.B * d.Hkv * 4);
+  p.part = off;
+  off += align256((size_t)d.B * d.Hkv * d.nsplit * d.G * (kHeadDim + 2) * 4);
+  p.total = off;
+  return p;
+}
+
+} // namespace dkv
+
+using namespace dkv;
+
+extern "C" {
+
+__attribute__((visibility("default"))) dkv_status
+dkv_encode(const dkv_config *cfg, const void *k_pool, int64_t num_blocks,
+           const int32_t *block_table, int32_t max_blocks_per_seq,
+           int32_t batch, const int32_t *enc_start, const int32_t *enc_end,
+           int32_t max_encode_len, const void *proj, uint32_t *codes,
+           uint8_t *radii, dkv_stream_t stream) {
+  dkv_status why = DKV_OK;
+  if (!valid_config(cfg, &why)) return why;
+  if (k_pool == nullptr || block_table == nullptr || enc_start == nullptr ||
+      enc_end == nullptr || proj == nullptr || codes == nullptr ||
+      radii == nullptr || num_blocks <= 0 || max_blocks_per_seq <= 0 ||
+      batch <= 0 || batch > 65535 || max_encode_len < 0)
+    return DKV_ERR_INVALID_ARG;
+  if (max_encode_len > DKV_MAX_SEQ_LEN) return DKV_ERR_UNSUPPORTED;
+  hipError_t e = launch_encode(
+      static_cast<const uint16_t *>(k_pool), num_blocks, block_table,
+      max_blocks_per_seq, batch, enc_start, enc_end, max_encode_len,
+      static_cast<const uint16_t *>(proj), cfg->num_kv_heads, cfg->code_bits,
+      codes, radii, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DKV_OK : DKV_ERR_LAUNCH;
+}
+
+__attribute__((visibility("default"))) size_t
+dkv_decode_workspace_size(const dkv_config *cfg, int32_t batch,
+                          int32_t max_seq_len) {
+  DecodeDims d;
+  dkv_status why;
+  const int32_t max_blocks = (max_seq_len + kPage - 1) / kPage;
+  if (!make_dims(cfg, batch, max_seq_len, max_blocks, 1, &d, &why)) return 0;
+  return plan_workspace(d).total;
+}
+
+__attribute__((visibility("default"))) dkv_status
+dkv_decode(const dkv_config *cfg, const void *q, const void *k_pool,
+           const void *v_pool, const uint32_t *codes, const uint8_t *radii,
+           int64_t num_blocks, const int32_t *block_table,
+           int32_t max_blocks_per_seq, const int32_t *seq_lens, int32_t batch,
+           int32_t max_seq_len, const void *proj, float *out, int32_t *sel_idx,
+           int32_t *sel_cnt, void *workspace, size_t workspace_bytes,
+           dkv_stream_t stream) {
+  return decode_impl(cfg, q, k_pool, v_pool, codes, radii, num_blocks,
+                     block_table, max_blocks_per_seq, seq_lens, batch,
+                     max_seq_len, proj, out, sel_idx, sel_cnt, workspace,
+                     workspace_bytes, nullptr, nullptr,
+                     reinterpret_cast<hipStream_t>(stream));
+}
+
+__attribute__((visibility("default"))) dkv_status dkv_decode_debug(
+    const dkv_config *cfg, const void *q, const void *k_pool,
+    const void *v_pool, const uint32_t *codes, const uint8_t *radii,
+    int64_t num_blocks, const int32_t *block_table, int32_t max_blocks_per_seq,
+    const int32_t *seq_lens, int32_t batch, int32_t max_seq_len,
+    const void *proj, float *out, int32_t *sel_idx, int32_t *sel_cnt,
+    void *workspace, size_t workspace_bytes, int8_t *q8_out,
+    int32_t *scores_out, dkv_stream_t stream) {
+  return decode_impl(cfg, q, k_pool, v_pool, codes, radii, num_blocks,
+                     block_table, max_blocks_per_seq, seq_lens, batch,
+                     max_seq_len, proj, out, sel_idx, sel_cnt, workspace,
+                     workspace_bytes, q8_out, scores_out,
+                     reinterpret_cast<hipStream_t>(stream));
+}
+
+__attribute__((visibility("default"))) const char *
+dkv_status_string(dkv_status status) {
+  switch (status) {
+  case DKV_OK:
+    return "DKV_OK";
+  case DKV_ERR_INVALID_ARG:
+    return "DKV_ERR_INVALID_ARG: null pointer or invalid size/shape";
+  case DKV_ERR_UNSUPPORTED:
+    return "DKV_ERR_UNSUPPORTED: head_dim, code_bits, page_size, group size "
+           "or a size limit is not supported";
+  case DKV_ERR_WORKSPACE:
+    return "DKV_ERR_WORKSPACE: workspace missing, misaligned or too small";
+  case DKV_ERR_LAUNCH:
+    return "DKV_ERR_LAUNCH: a kernel launch failed";
+  }
+  return "unknown dkv_status";
+}
+
+__attribute__((visibility("default"))) int32_t dkv_abi_version(void) {
+  return DKV_ABI_VERSION;
+}
+
+} // extern "C"

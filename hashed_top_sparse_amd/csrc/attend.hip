@@ -1,0 +1,215 @@
+// attend.hip -- exact attention over the selected keys, split over the
+// selection list, and the merge of the splits.
+//
+// [DySCO review, item 1]: attention is softmax(q k^T / sqrt(d)) v.
+// [DeepSeek DSA]: the real attention only reads the selected history.
+// Each split keeps an online-softmax state (m, l, acc[d]) per query head in
+// fp32 (logits are pre-multiplied by log2(e)/sqrt(d) so exp2 is used); the
+// combine kernel merges the split states:
+//   m* = max m_p,  l* = sum l_p 2^(m_p - m*),  o = sum acc_p 2^(m_p - m*) / l*.
+//
+// Work mapping of the split kernel: 256 threads = 16 row groups of 16 lanes;
+// a row group reads one selected key row and value row (256 B each: 16 B
+// per lane), so a workgroup gathers 16 rows per step through the block
+// table.  All G query heads of the KV group share the gathered rows.
+#include "internal.h"
+
+namespace dkv {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kLanesPerRow = 16;
+constexpr int kRowGroups = kThreads / kLanesPerRow;
+constexpr int kPartStride = kHeadDim + 2; // m, l, acc[128]
+
+__device__ __forceinline__ void unpack8(const uint4 &v, float (&f)[8]) {
+  f[0] = __uint_as_float(v.x << 16);
+  f[1] = __uint_as_float(v.x & 0xFFFF0000u);
+  f[2] = __uint_as_float(v.y << 16);
+  f[3] = __uint_as_float(v.y & 0xFFFF0000u);
+  f[4] = __uint_as_float(v.z << 16);
+  f[5] = __uint_as_float(v.z & 0xFFFF0000u);
+  f[6] = __uint_as_float(v.w << 16);
+  f[7] = __uint_as_float(v.w & 0xFFFF0000u);
+}
+
+// Merge online-softmax state (m2, l2, a2) into (m1, l1, a1).
+__device__ __forceinline__ void merge_state(float &m1, float &l1, float *a1,
+                                            float m2, float l2, const float *a2,
+                                            int n) {
+  const float m = fmaxf(m1, m2);
+  const float c1 = (m1 == -INFINITY) ? 0.f : exp2f(m1 - m);
+  const float c2 = (m2 == -INFINITY) ? 0.f : exp2f(m2 - m);
+  l1 = l1 * c1 + l2 * c2;
+  for (int i = 0; i < n; ++i) a1[i] = a1[i] * c1 + a2[i] * c2;
+  m1 = m;
+}
+
+template <int G>
+__global__ __launch_bounds__(kThreads) void attend_split_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_pool,
+    const uint16_t *__restrict__ v_pool, int64_t num_blocks,
+    const int32_t *__restrict__ block_table, int max_blocks,
+    const int32_t *__restrict__ sel, const int32_t *__restrict__ cnt, int cap,
+    float *__restrict__ part, int Hq, int Hkv, int nsplit, float qscale) {
+  const int split = blockIdx.x;
+  const int unit = blockIdx.y;
+  const int s = unit / Hkv, g = unit % Hkv;
+  const int lane = threadIdx.x % kLanesPerRow;
+  const int rg = threadIdx.x / kLanesPerRow;
+  const int n = cnt[unit];
+  const int r0 = split * kAttnRows;
+  const int r1 = (r0 + kAttnRows < n) ? r0 + kAttnRows : n;
+
+  float qv[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const uint4 raw = *reinterpret_cast<const uint4 *>(
+        q + ((int64_t)s * Hq + (int64_t)g * G + h) * kHeadDim + lane * 8);
+    unpack8(raw, qv[h]);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) qv[h][c] *= qscale;
+  }
+  float m[G], l[G], acc[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[h][c] = 0.f;
+  }
+
+  const int32_t *L = sel + (int64_t)unit * cap;
+  for (int r = r0 + rg; r < r1; r += kRowGroups) {
+    const int pos = L[r];
+    if (pos < 0) continue;
+    const int blk = block_table[(int64_t)s * max_blocks + pos / kPage];
+    if (blk < 0 || blk >= num_blocks) continue;
+    const int64_t off =
+        (((int64_t)blk * kPage + pos % kPage) * Hkv + g) * kHeadDim + lane * 8;
+    const uint4 kraw = *reinterpret_cast<const uint4 *>(k_pool + off);
+    const uint4 vraw = *reinterpret_cast<const uint4 *>(v_pool + off);
+    float kf[8], vf[8];
+    unpack8(kraw, kf);
+    unpack8(vraw, vf);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float dot = 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) dot = fmaf(qv[h][c], kf[c], dot);
+#pragma unroll
+      for (int off2 = kLanesPerRow / 2; off2 > 0; off2 >>= 1)
+        dot += __shfl_xor(dot, off2, kLanesPerRow);
+      const float mn = fmaxf(m[h], dot);
+      const float corr = exp2f(m[h] - mn); // m = -inf gives 0
+      const float p = exp2f(dot - mn);
+      l[h] = l[h] * corr + p;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[h][c] = fmaf(p, vf[c], acc[h][c] * corr);
+      m[h] = mn;
+    }
+  }
+
+  // Merge the 16 row groups: first the 4 groups of a wave (lanes l, l+16,
+  // l+32, l+48 hold the same dims), then the 4 waves through LDS.
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+#pragma unroll
+    for (int off2 = 16; off2 < 64; off2 <<= 1) {
+      const float m2 = __shfl_xor(m[h], off2);
+      const float l2 = __shfl_xor(l[h], off2);
+      float a2[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) a2[c] = __shfl_xor(acc[h][c], off2);
+      merge_state(m[h], l[h], acc[h], m2, l2, a2, 8);
+    }
+  }
+  __shared__ float sm[4][G][kPartStride];
+  const int wave = threadIdx.x / 64;
+  if ((threadIdx.x & 63) < kLanesPerRow) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      if (lane == 0) {
+        sm[wave][h][0] = m[h];
+        sm[wave][h][1] = l[h];
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) sm[wave][h][2 + lane * 8 + c] = acc[h][c];
+    }
+  }
+  __syncthreads();
+  // thread t < G*128 finalises (head t/128, dim t%128)
+  for (int t = threadIdx.x; t < G * kHeadDim; t += kThreads) {
+    const int h = t / kHeadDim, dim = t % kHeadDim;
+    float mm = sm[0][h][0], ll = sm[0][h][1], aa = sm[0][h][2 + dim];
+    for (int wv = 1; wv < 4; ++wv)
+      merge_state(mm, ll, &aa, sm[wv][h][0], sm[wv][h][1], &sm[wv][h][2 + dim], 1);
+    float *dst = part + (((int64_t)unit * nsplit + split) * G + h) * kPartStride;
+    if (dim == 0) {
+      dst[0] = mm;
+      dst[1] = ll;
+    }
+    dst[2 + dim] = aa;
+  }
+}
+
+// One workgroup of 128 threads per (sequence, query head).
+__global__ __launch_bounds__(kHeadDim) void attend_combine_kernel(
+    const float *__restrict__ part, float *__restrict__ out, int Hq, int Hkv,
+    int G, int nsplit) {
+  const int sh = blockIdx.x;
+  const int s = sh / Hq, hq = sh % Hq;
+  const int g = hq / G, h = hq % G;
+  const int unit = s * Hkv + g;
+  const int dim = threadIdx.x;
+  float mm = -INFINITY;
+  for (int p = 0; p < nsplit; ++p)
+    mm = fmaxf(mm, part[(((int64_t)unit * nsplit + p) * G + h) * kPartStride]);
+  float ll = 0.f, aa = 0.f;
+  if (mm != -INFINITY) {
+    for (int p = 0; p < nsplit; ++p) {
+      const float *src = part + (((int64_t)unit * nsplit + p) * G + h) * kPartStride;
+      const float mp = src[0];
+      if (mp == -INFINITY) continue;
+      const float c = exp2f(mp - mm);
+      ll = fmaf(src[1], c, ll);
+      aa = fmaf(src[2 + dim], c, aa);
+    }
+  }
+  out[(int64_t)sh * kHeadDim + dim] = (ll > 0.f) ? aa / ll : 0.f;
+}
+
+} // namespace
+
+hipError_t launch_attend(const DecodeDims &d, const uint16_t *q,
+                         const uint16_t *k_pool, const uint16_t *v_pool,
+                         const int32_t *block_table, const int32_t *sel,
+                         const int32_t *cnt, float *part, float *out,
+                         hipStream_t stream) {
+  // log2(e) / sqrt(128)
+  const float qscale = 1.4426950408889634f * 0.08838834764831845f;
+  dim3 grid(d.nsplit, d.B * d.Hkv);
+#define DKV_ATTEND_CASE(GG)                                                    \
+  case GG:                                                                     \
+    hipLaunchKernelGGL(attend_split_kernel<GG>, grid, dim3(kThreads), 0,       \
+                       stream, q, k_pool, v_pool, d.num_blocks, block_table,   \
+                       d.max_blocks, sel, cnt, d.cap, part, d.Hq, d.Hkv,       \
+                       d.nsplit, qscale);                                      \
+    break;
+  switch (d.G) {
+    DKV_ATTEND_CASE(1)
+    DKV_ATTEND_CASE(2)
+    DKV_ATTEND_CASE(4)
+    DKV_ATTEND_CASE(8)
+  default:
+    return hipErrorInvalidValue;
+  }
+#undef DKV_ATTEND_CASE
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attend_combine_kernel, dim3(d.B * d.Hq), dim3(kHeadDim),
+                     0, stream, part, out, d.Hq, d.Hkv, d.G, d.nsplit);
+  return hipGetLastError();
+}
+
+} // namespace dkv

@@ -1,0 +1,213 @@
+/*
+ * dkv.h -- C ABI of libdkv: score-then-select sparse decode attention over a
+ * paged, GQA-shaped KV cache on AMD Instinct MI355X (gfx950).
+ *
+ * The method (sources are web pages, cited by title and section):
+ *  - "SPHERICAL KV: Angle-Domain Attention and Rate-Distortion Retention for
+ *    Efficient Long-Context Inference", technical summary §2.1 (keys stored
+ *    as a quantised radius plus a packed angle code; logits computed from
+ *    the codes without rebuilding dense keys) and §2.3 (paged, ragged KV
+ *    substrate; dense keys are mapped to codes when written).
+ *  - "DASH-KV: asymmetric hashing accelerates long-context LLM inference",
+ *    sections on asymmetric deep hashing (queries and keys get different
+ *    encoders; key codes are cached and reused) and on the quadratic-to-
+ *    linear argument (a light pre-filter keeps only the Top-K keys for
+ *    exact attention).
+ *  - "DeepSeek: why 1M context cannot be bought with memory -- from DSA to
+ *    CSA/HCA", section "starting from DSA" (a light indexer scores all
+ *    history, then real attention runs on the top-k only) and the CSA
+ *    section (a sliding window keeps the most recent tokens).
+ *  - DySCO review page, item 1 of the mathematical model (attention is
+ *    softmax(QK^T/sqrt(d))) and FAQ 3 (a few initial tokens act as
+ *    attention sinks).
+ *
+ * The concrete code (the pages leave the encoders open):
+ *   key code    b sign bits of p = k.P (P: seeded Gaussian d x b, bf16);
+ *               bit j = [p_j > 0], p_j accumulated in double precision in
+ *               index order; bits packed LSB-first into uint32 words.
+ *   key radius  r8 = largest m in 1..255 with |k|^2 >= 2^((m-64)/8), else 0
+ *               (|k|^2 summed in double precision in index order).
+ *   query code  q8 = round_half_even(p*127/M), p = q.P in double precision,
+ *               M = max |p| over the KV group's G query heads and b columns.
+ *   score       S = r8 * max_{h in group} sum_j q8_hj * (bit_j ? +1 : -1).
+ *   selection   per (sequence, KV head): sinks [0, sigma), window
+ *               [N-w, N), plus the top k of [sigma, N-w) by (S descending,
+ *               position ascending).
+ *   attention   exact softmax(q.k/sqrt(d)) . V over the selection, fp32
+ *               accumulation, for each query head of the group.
+ *
+ * Memory layouts (all device memory, row-major, little-endian):
+ *   bf16 tensors are passed as 16-bit bit patterns.
+ *   k_pool, v_pool  [num_blocks][16][Hkv][d]   bf16  (16-token pages)
+ *   codes           [num_blocks][Hkv][b/32][16] uint32 (word-major per page:
+ *                   word w of the key in slot t of the page is at index
+ *                   ((blk*Hkv + h)*(b/32) + w)*16 + t)
+ *   radii           [num_blocks][Hkv][16]      uint8
+ *   block_table     [batch][max_blocks_per_seq] int32 physical page ids
+ *                   (the same id indexes k_pool, v_pool, codes and radii)
+ *   proj            [d][b]                     bf16
+ *   q               [batch][Hq][d]             bf16  (head h is in KV group
+ *                                                      h / G)
+ *   out             [batch][Hq][d]             fp32
+ *
+ * Ownership and execution: the caller owns every buffer; the library
+ * allocates no device or host memory and keeps no mutable global state, so
+ * calls on different streams may run concurrently when their output and
+ * workspace buffers differ.  Every call only validates its arguments on the
+ * host and enqueues kernels on `stream` (a hipStream_t; NULL means the null
+ * stream); it returns before the GPU work finishes.  Device-side values
+ * (seq_lens, enc_start/enc_end, block ids) cannot be checked on the host:
+ * kernels clamp lengths to [0, min(max_seq_len, 16*max_blocks_per_seq)] and
+ * skip page ids outside [0, num_blocks); results for such inputs are
+ * unspecified but no memory outside the buffers is touched.
+ *
+ * Errors: a non-OK status is returned before any launch when an argument is
+ * invalid; DKV_ERR_LAUNCH reports a failed kernel launch.  Faults inside
+ * kernels surface at the caller's next synchronisation.
+ */
+#ifndef DKV_H_
+#define DKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as hipStream_t. */
+typedef struct ihipStream_t *dkv_stream_t;
+
+typedef enum {
+  DKV_OK = 0,
+  DKV_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad shape     */
+  DKV_ERR_UNSUPPORTED = 2, /* d != 128, b not in {64,128,256}, page != 16,
+                              group size not in {1,2,4,8}, size limits    */
+  DKV_ERR_WORKSPACE = 3,   /* workspace missing or too small             */
+  DKV_ERR_LAUNCH = 4       /* hipLaunchKernel / hipGetLastError failure  */
+} dkv_status;
+
+typedef struct {
+  int32_t head_dim;     /* d; must be 128                                 */
+  int32_t num_q_heads;  /* Hq                                             */
+  int32_t num_kv_heads; /* Hkv; Hq % Hkv == 0 and G = Hq/Hkv in {1,2,4,8} */
+  int32_t code_bits;    /* b; 64, 128 or 256                              */
+  int32_t page_size;    /* tokens per page; must be 16                    */
+  int32_t top_k;        /* k >= 0                                         */
+  int32_t window;       /* w >= 0: most recent tokens always kept         */
+  int32_t sinks;        /* sigma >= 0: first tokens always kept           */
+} dkv_config;
+
+/* Limits checked by every entry point (DKV_ERR_UNSUPPORTED beyond them). */
+#define DKV_MAX_SEQ_LEN (1 << 24)
+#define DKV_MAX_SELECT (1 << 20) /* top_k + window + sinks */
+
+/*
+ * dkv_encode -- build key codes and radii when keys are written to the
+ * cache ([SKV §2.3]: dense keys are turned into codes at write time;
+ * [DASH]: key codes are computed once and reused by every later query).
+ *
+ * For every sequence s and every token position t in
+ * [enc_start[s], enc_end[s]) and every KV head h, reads the key row
+ * k_pool[block_table[s][t/16]][t%16][h][:] and writes its code words and
+ * radius into the page's slot in `codes` / `radii`.  Other slots are not
+ * touched.
+ *   k_pool       device, bf16 [num_blocks][16][Hkv][d]
+ *   num_blocks   number of pages in every pool (> 0)
+ *   block_table  device, int32 [batch][max_blocks_per_seq]
+ *   enc_start, enc_end  device, int32 [batch]; positions are clamped to
+ *                [0, 16*max_blocks_per_seq]; empty ranges do nothing
+ *   max_encode_len  host bound on enc_end[s]-enc_start[s] for every s (sizes
+ *                the grid; tokens beyond it are not encoded)
+ *   proj         device, bf16 [d][b]
+ *   codes        device, uint32 [num_blocks][Hkv][b/32][16] (output)
+ *   radii        device, uint8  [num_blocks][Hkv][16]       (output)
+ * Bits are bit-exact with the definition above: the projection runs on bf16
+ * matrix cores in fp32 and every sign the fp32 error bound cannot certify
+ * is recomputed in double precision in index order.
+ */
+dkv_status dkv_encode(const dkv_config *cfg, const void *k_pool,
+                      int64_t num_blocks, const int32_t *block_table,
+                      int32_t max_blocks_per_seq, int32_t batch,
+                      const int32_t *enc_start, const int32_t *enc_end,
+                      int32_t max_encode_len, const void *proj,
+                      uint32_t *codes, uint8_t *radii, dkv_stream_t stream);
+
+/*
+ * dkv_decode_workspace_size -- bytes of device workspace dkv_decode needs
+ * for `batch` sequences of at most `max_seq_len` tokens (0 on invalid
+ * arguments).  The workspace needs no initialisation and may be reused by
+ * later calls on the same stream.
+ */
+size_t dkv_decode_workspace_size(const dkv_config *cfg, int32_t batch,
+                                 int32_t max_seq_len);
+
+/*
+ * dkv_decode -- one decode step: query codes, code-domain scores of every
+ * cached key, selection (sinks + window + top-k), exact attention over the
+ * selection ([DSA]: indexer then attention over the top-k; [SKV §2.1]:
+ * logits straight from the codes; [DYS]: softmax(QK^T/sqrt(d))).
+ *
+ *   q            device, bf16 [batch][Hq][d] (the step's queries)
+ *   k_pool, v_pool  device, bf16 [num_blocks][16][Hkv][d]
+ *   codes, radii device, as written by dkv_encode for every cached token
+ *   num_blocks   pages in every pool
+ *   block_table  device, int32 [batch][max_blocks_per_seq]
+ *   seq_lens     device, int32 [batch]: tokens cached per sequence,
+ *                the current token included (it falls in the window)
+ *   max_seq_len  host bound on seq_lens (sizes grids and the workspace)
+ *   proj         device, bf16 [d][b] (the projection the codes were built
+ *                with)
+ *   out          device, fp32 [batch][Hq][d] (output; 0 for an empty
+ *                sequence)
+ *   sel_idx      optional (may be NULL) device, int32
+ *                [batch][Hkv][top_k+window+sinks]: selected logical
+ *                positions, order within a list unspecified, -1 past the
+ *                count
+ *   sel_cnt      optional (may be NULL) device, int32 [batch][Hkv]:
+ *                min(N, sinks+window+top_k)
+ *   workspace    device, at least dkv_decode_workspace_size(cfg, batch,
+ *                max_seq_len) bytes, 256-byte aligned
+ * The selection is bit-exact with the definition above (ties in S go to
+ * the lowest position); `out` is within |err| <= 2e-3 + 1e-2*|exact|.
+ */
+dkv_status dkv_decode(const dkv_config *cfg, const void *q,
+                      const void *k_pool, const void *v_pool,
+                      const uint32_t *codes, const uint8_t *radii,
+                      int64_t num_blocks, const int32_t *block_table,
+                      int32_t max_blocks_per_seq, const int32_t *seq_lens,
+                      int32_t batch, int32_t max_seq_len, const void *proj,
+                      float *out, int32_t *sel_idx, int32_t *sel_cnt,
+                      void *workspace, size_t workspace_bytes,
+                      dkv_stream_t stream);
+
+/*
+ * dkv_decode_debug -- dkv_decode plus two inspection outputs, for parity
+ * tests (it moves more bytes than dkv_decode; do not time it):
+ *   q8_out      optional device, int8 [batch][Hq][b]: the query codes
+ *   scores_out  optional device, int32 [batch][Hkv][max_seq_len]: S of every
+ *               cached key (entries at positions >= N are not written)
+ */
+dkv_status dkv_decode_debug(const dkv_config *cfg, const void *q,
+                            const void *k_pool, const void *v_pool,
+                            const uint32_t *codes, const uint8_t *radii,
+                            int64_t num_blocks, const int32_t *block_table,
+                            int32_t max_blocks_per_seq,
+                            const int32_t *seq_lens, int32_t batch,
+                            int32_t max_seq_len, const void *proj, float *out,
+                            int32_t *sel_idx, int32_t *sel_cnt, void *workspace,
+                            size_t workspace_bytes, int8_t *q8_out,
+                            int32_t *scores_out, dkv_stream_t stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *dkv_status_string(dkv_status status);
+
+/* ABI version of this header (bumped on any signature or layout change). */
+#define DKV_ABI_VERSION 1
+int32_t dkv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DKV_H_ */

@@ -1,0 +1,117 @@
+"""GPU-vs-oracle parity driver shared by the GPU tests and the smoke check.
+
+Inputs come from ``workloads`` (drawn on the GPU); the GPU path runs through
+the C ABI (``hashed_top_sparse_amd``); the oracle gets host copies of the
+very same input bytes for the (sequence, KV head) units under test and
+computes its own codes, radii, query codes, scores, selection and output.
+Nothing the GPU computed is ever fed to the oracle.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import hashed_top_sparse_amd as dkv
+import oracle
+import workloads
+from helpers import (PAGE, logical_codes, logical_radii, logical_rows,
+                     tensor_bits)
+
+ATOL, RTOL = 2e-3, 1e-2
+
+
+def config_of(wl: workloads.Workload, **over) -> dkv.Config:
+    kw = dict(num_q_heads=wl.num_q_heads, num_kv_heads=wl.num_kv_heads,
+              code_bits=wl.code_bits, top_k=wl.top_k, window=wl.window,
+              sinks=wl.sinks)
+    kw.update(over)
+    return dkv.Config(**kw)
+
+
+def gpu_encode_all(cfg: dkv.Config, inp: dict):
+    """Encode every cached token of every sequence with dkv_encode."""
+    dev = inp["k_pool"].device
+    nb = inp["k_pool"].shape[0]
+    codes = torch.zeros((nb, cfg.num_kv_heads, cfg.code_bits // 32, PAGE),
+                        dtype=torch.int32, device=dev)
+    radii = torch.zeros((nb, cfg.num_kv_heads, PAGE), dtype=torch.uint8, device=dev)
+    B = inp["block_table"].shape[0]
+    start = torch.zeros(B, dtype=torch.int32, device=dev)
+    dkv.encode(cfg, inp["k_pool"], inp["block_table"], start, inp["seq_lens"],
+               inp["max_seq_len"], inp["proj"], codes, radii)
+    return codes, radii
+
+
+def gpu_decode(cfg: dkv.Config, inp: dict, codes, radii, debug: bool = True,
+               seq_lens=None, max_seq_len=None):
+    dev = inp["k_pool"].device
+    B = inp["block_table"].shape[0]
+    seq_lens = inp["seq_lens"] if seq_lens is None else seq_lens
+    max_seq_len = inp["max_seq_len"] if max_seq_len is None else max_seq_len
+    ws = torch.empty(dkv.decode_workspace_size(cfg, B, max_seq_len),
+                     dtype=torch.uint8, device=dev)
+    out = torch.full((B, cfg.num_q_heads, cfg.head_dim), float("nan"), device=dev)
+    sel = torch.full((B, cfg.num_kv_heads, cfg.select_cap), -7, dtype=torch.int32,
+                     device=dev)
+    cnt = torch.full((B, cfg.num_kv_heads), -7, dtype=torch.int32, device=dev)
+    res = {"out": out, "sel": sel, "cnt": cnt}
+    if debug:
+        q8 = torch.zeros((B, cfg.num_q_heads, cfg.code_bits), dtype=torch.int8, device=dev)
+        sc = torch.zeros((B, cfg.num_kv_heads, max(1, max_seq_len)), dtype=torch.int32,
+                         device=dev)
+        if max_seq_len == 0:
+            sc = None
+        dkv.decode_debug(cfg, inp["q"], inp["k_pool"], inp["v_pool"], codes, radii,
+                         inp["block_table"], seq_lens, max_seq_len, inp["proj"], out,
+                         ws, sel, cnt, q8, sc)
+        res.update(q8=q8, scores=sc)
+    else:
+        dkv.decode(cfg, inp["q"], inp["k_pool"], inp["v_pool"], codes, radii,
+                   inp["block_table"], seq_lens, max_seq_len, inp["proj"], out, ws,
+                   sel, cnt)
+    torch.cuda.synchronize()
+    return res
+
+
+def check_unit(cfg: dkv.Config, inp: dict, gpu: dict, codes, radii, s: int, g: int,
+               check_codes: bool = True, needles=None) -> dict:
+    """Compares one (sequence s, KV head g) unit with the oracle."""
+    bt = inp["block_table"].cpu().numpy()
+    N = int(inp["seq_lens"][s].item())
+    G = cfg.group
+    P = tensor_bits(inp["proj"])
+    q = tensor_bits(inp["q"][s, g * G:(g + 1) * G])
+    K = logical_rows(inp["k_pool"], bt, s, N, g)
+    V = logical_rows(inp["v_pool"], bt, s, N, g)
+    o_codes, o_radii = oracle.encode_keys(K, P)
+    if check_codes:
+        g_codes = logical_codes(codes, bt, s, N, g)
+        g_radii = logical_radii(radii, bt, s, N, g)
+        bad = np.nonzero((g_codes != o_codes).any(axis=1))[0]
+        assert len(bad) == 0, f"codes differ at {len(bad)} keys, first {bad[:5]}"
+        assert np.array_equal(g_radii, o_radii), "radii differ"
+    r = oracle.decode_unit(q, P, o_codes, o_radii, K, V, cfg.top_k, cfg.window,
+                           cfg.sinks)
+    if "q8" in gpu:
+        g_q8 = gpu["q8"][s, g * G:(g + 1) * G].cpu().numpy()
+        assert np.array_equal(g_q8, r["q8"]), "query codes differ"
+    if gpu.get("scores") is not None:
+        g_sc = gpu["scores"][s, g, :N].cpu().numpy()
+        bad = np.nonzero(g_sc != r["scores"])[0]
+        assert len(bad) == 0, f"scores differ at {len(bad)} keys, first {bad[:5]}"
+    cnt = int(gpu["cnt"][s, g].item())
+    assert cnt == len(r["sel"]), (cnt, len(r["sel"]))
+    g_sel = gpu["sel"][s, g].cpu().numpy()
+    assert np.array_equal(np.sort(g_sel[:cnt]), np.sort(r["sel"])), "selection differs"
+    assert (g_sel[cnt:] == -1).all(), "selection list not -1 past the count"
+    g_out = gpu["out"][s, g * G:(g + 1) * G].double().cpu().numpy()
+    err = np.abs(g_out - r["out"])
+    ok = err <= ATOL + RTOL * np.abs(r["out"])
+    assert ok.all(), f"out: max abs err {err.max():.3g}"
+    rec = None
+    if needles is not None and len(needles):
+        rec = float(np.isin(needles, g_sel[:cnt]).mean())
+    big = np.abs(r["out"]) >= 0.2
+    return {"max_abs": float(err.max()) if err.size else 0.0,
+            "max_rel": float((err[big] / np.abs(r["out"][big])).max()) if big.any() else 0.0,
+            "recall": rec}

@@ -1,0 +1,118 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before any launch (no GPU needed: every call below
+fails validation, so no kernel is ever enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import hashed_top_sparse_amd as dkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dkv.h")
+FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dkv_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = dkv.load_library()
+    names = declared_functions()
+    assert set(names) == set(dkv.EXPORTED_SYMBOLS)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.dkv_abi_version() == dkv.ABI_VERSION
+
+
+def test_status_strings():
+    lib = dkv.load_library()
+    for code, name in dkv.STATUS.items():
+        assert lib.dkv_status_string(code).decode().startswith(name)
+    assert b"unknown" in lib.dkv_status_string(99)
+
+
+def _cfg(**over):
+    kw = dict(head_dim=128, num_q_heads=32, num_kv_heads=8, code_bits=128,
+              page_size=16, top_k=64, window=16, sinks=4)
+    kw.update(over)
+    return dkv._CConfig(*[kw[f] for f, _ in dkv._CConfig._fields_])
+
+
+def _decode(cfg, ws_bytes=1 << 30, workspace=FAKE, q=FAKE, batch=2, max_seq_len=1000,
+            num_blocks=200, max_blocks=64):
+    lib = dkv.load_library()
+    c = cfg
+    return lib.dkv_decode(ctypes.byref(c) if c is not None else None, q, FAKE, FAKE,
+                          FAKE, FAKE, num_blocks, FAKE, max_blocks, FAKE, batch,
+                          max_seq_len, FAKE, FAKE, None, None, workspace, ws_bytes, None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(head_dim=64), 2), (dict(code_bits=96), 2), (dict(code_bits=512), 2),
+    (dict(page_size=32), 2), (dict(num_q_heads=24, num_kv_heads=8), 2),  # G = 3
+    (dict(num_q_heads=30, num_kv_heads=8), 1), (dict(top_k=-1), 1),
+    (dict(window=-5), 1), (dict(sinks=-1), 1), (dict(num_kv_heads=0), 1),
+    (dict(top_k=1 << 20), 2),
+])
+def test_decode_rejects_bad_config(over, status):
+    assert _decode(_cfg(**over)) == status
+
+
+def test_decode_rejects_bad_arguments():
+    assert _decode(None) == 1
+    assert _decode(_cfg(), q=None) == 1
+    assert _decode(_cfg(), batch=0) == 1
+    assert _decode(_cfg(), max_seq_len=-1) == 1
+    assert _decode(_cfg(), num_blocks=0) == 1
+    assert _decode(_cfg(), max_blocks=0) == 1
+    assert _decode(_cfg(), max_seq_len=(1 << 24) + 1) == 2
+    assert _decode(_cfg(), workspace=None) == 3
+    assert _decode(_cfg(), ws_bytes=16) == 3
+    assert _decode(_cfg(), workspace=ctypes.c_void_p(0x10004)) == 3   # misaligned
+
+
+def test_workspace_size():
+    lib = dkv.load_library()
+    c = _cfg()
+    a = lib.dkv_decode_workspace_size(ctypes.byref(c), 4, 4096)
+    b = lib.dkv_decode_workspace_size(ctypes.byref(c), 4, 8192)
+    assert 0 < a < b and a % 256 == 0
+    bad = _cfg(code_bits=7)
+    assert lib.dkv_decode_workspace_size(ctypes.byref(bad), 4, 4096) == 0
+    assert lib.dkv_decode_workspace_size(ctypes.byref(c), 0, 4096) == 0
+
+
+def test_encode_rejects_bad_arguments():
+    lib = dkv.load_library()
+    c = _cfg()
+    args = [FAKE, 100, FAKE, 8, 2, FAKE, FAKE, 128, FAKE, FAKE, FAKE, None]
+    assert lib.dkv_encode(None, *args) == 1
+    bad = _cfg(code_bits=100)
+    assert lib.dkv_encode(ctypes.byref(bad), *args) == 2
+    a2 = list(args)
+    a2[1] = 0          # num_blocks
+    assert lib.dkv_encode(ctypes.byref(c), *a2) == 1
+    a3 = list(args)
+    a3[7] = -1         # max_encode_len
+    assert lib.dkv_encode(ctypes.byref(c), *a3) == 1
+    a4 = list(args)
+    a4[0] = None       # k_pool
+    assert lib.dkv_encode(ctypes.byref(c), *a4) == 1
+
+
+def test_python_binding_refuses_host_tensors():
+    import torch
+    cfg = dkv.Config(num_q_heads=1, num_kv_heads=1, code_bits=64, top_k=4,
+                     window=4, sinks=1)
+    kp = torch.zeros((2, 16, 1, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        dkv.encode(cfg, kp, torch.zeros((1, 2), dtype=torch.int32),
+                   torch.zeros(1, dtype=torch.int32), torch.ones(1, dtype=torch.int32),
+                   1, torch.zeros((128, 64), dtype=torch.bfloat16),
+                   torch.zeros((2, 1, 2, 16), dtype=torch.int32),
+                   torch.zeros((2, 1, 16), dtype=torch.uint8), stream=0)

@@ -1,0 +1,122 @@
+"""GPU parity: libdkv (through the C ABI) against the CPU oracle.
+
+Bit-exact: key codes, radii, query codes, scores, selected index sets and
+counts.  Within |err| <= 2e-3 + 1e-2*|ref|: attention outputs (fp32
+accumulation on the GPU, fp64 in the oracle).
+
+Small workloads compare every (sequence, KV head) unit; the five full-size
+workloads run at their real shapes in the same launch configuration the
+benchmark times and compare sampled units.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from parity import check_unit, config_of, gpu_decode, gpu_encode_all
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _run(wl, units=None, **cfg_over):
+    print(f"[case] {wl.name} {cfg_over}", flush=True)
+    cfg = config_of(wl, **cfg_over)
+    inp = workloads.make_inputs(wl, DEV)
+    codes, radii = gpu_encode_all(cfg, inp)
+    gpu = gpu_decode(cfg, inp, codes, radii, debug=True)
+    if units is None:
+        units = [(s, g) for s in range(wl.batch) for g in range(wl.num_kv_heads)]
+    stats = []
+    for s, g in units:
+        nd = inp["needles"][s][g] if "top_k" not in cfg_over else None
+        stats.append(check_unit(cfg, inp, gpu, codes, radii, s, g, needles=nd))
+    return stats
+
+
+@pytest.mark.parametrize("name", sorted(workloads.SMALL))
+def test_small_workloads_every_unit(name):
+    stats = _run(workloads.get(name))
+    recalls = [st["recall"] for st in stats if st["recall"] is not None]
+    assert all(r == 1.0 for r in recalls)
+
+
+@pytest.mark.parametrize("over", [
+    dict(top_k=5000, window=16, sinks=4),      # dense: selection = everything
+    dict(top_k=0, window=64, sinks=4),         # window + sinks only
+    dict(top_k=64, window=0, sinks=0),         # top-k only
+    dict(top_k=1, window=1, sinks=1),
+])
+def test_small_selection_edge_configs(over):
+    _run(workloads.get("small_gqa_b128"), **over)
+
+
+def test_short_and_empty_sequences():
+    """N = 0, 1, <= sinks, <= sinks + window, and a one-page tail."""
+    wl = workloads.get("small_gqa_b128")
+    cfg = config_of(wl)
+    inp = workloads.make_inputs(wl, DEV)
+    codes, radii = gpu_encode_all(cfg, inp)
+    for lens in ([0, 1], [3, 4], [5, 68], [69, 17]):
+        sl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+        sub = dict(inp, seq_lens=sl, max_seq_len=int(max(lens)))
+        print(f"[case] lens={lens}", flush=True)
+        gpu = gpu_decode(cfg, sub, codes, radii, debug=True,
+                         seq_lens=sl, max_seq_len=int(max(lens)))
+        for s in range(2):
+            for g in range(wl.num_kv_heads):
+                if lens[s] == 0:
+                    assert int(gpu["cnt"][s, g]) == 0
+                    assert (gpu["out"][s, g * cfg.group:(g + 1) * cfg.group] == 0).all()
+                    continue
+                check_unit(cfg, sub, gpu, codes, radii, s, g)
+
+
+def test_forced_ties_go_to_lowest_positions():
+    """Identical keys everywhere: every score ties, the lowest positions win."""
+    wl = workloads.get("small_gqa_b128")
+    cfg = config_of(wl)
+    inp = workloads.make_inputs(wl, DEV)
+    inp["k_pool"][:] = inp["k_pool"][0, 0]
+    codes, radii = gpu_encode_all(cfg, inp)
+    gpu = gpu_decode(cfg, inp, codes, radii, debug=True)
+    for s in range(wl.batch):
+        for g in range(wl.num_kv_heads):
+            check_unit(cfg, inp, gpu, codes, radii, s, g)
+            sel = np.sort(gpu["sel"][s, g, :int(gpu["cnt"][s, g])].cpu().numpy())
+            top = sel[(sel >= wl.sinks) & (sel < int(inp["seq_lens"][s]) - wl.window)]
+            assert np.array_equal(top, np.arange(wl.sinks, wl.sinks + wl.top_k))
+
+
+def test_decode_is_deterministic():
+    wl = workloads.get("small_ragged_b128")
+    cfg = config_of(wl)
+    inp = workloads.make_inputs(wl, DEV)
+    codes, radii = gpu_encode_all(cfg, inp)
+    a = gpu_decode(cfg, inp, codes, radii, debug=False)
+    b = gpu_decode(cfg, inp, codes, radii, debug=False)
+    assert torch.equal(a["out"], b["out"])
+    for x, y in ((a["sel"], b["sel"]), (a["cnt"], b["cnt"])):
+        assert torch.equal(torch.sort(x, dim=-1).values, torch.sort(y, dim=-1).values)
+
+
+# ---------------------------------------------------------------- full size
+FULL_UNITS = {
+    "mha1_n4k_b64": None,                                   # every unit
+    "gqa32x8_bs1_n32k_b128": None,
+    "gqa32x8_bs16_n128k_b128": [(0, 0), (7, 3), (15, 7)],
+    "gqa32x8_ragged64_4k-128k_b128": [(0, 0), (17, 5), (40, 2), (63, 7)],
+    "gqa32x8_bs4_n256k_b256_lognormal": [(0, 0), (3, 7)],
+}
+
+
+@pytest.mark.parametrize("name", list(FULL_UNITS))
+def test_full_size_workloads(name):
+    wl = workloads.get(name)
+    stats = _run(wl, FULL_UNITS[name])
+    recalls = [st["recall"] for st in stats if st["recall"] is not None]
+    if wl.needles:
+        assert recalls and all(r == 1.0 for r in recalls)
+    print(name, "max abs err", max(st["max_abs"] for st in stats))
+    torch.cuda.empty_cache()
