@@ -86,8 +86,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
   const int base = ns + nwin;
 
   __shared__ uint32_t hist[256];
-  __shared__ uint32_t sh_prefix, sh_kneed, sh_slot;
+  __shared__ uint32_t sh_prefix, sh_kneed;
   __shared__ uint32_t tie_count[kSelThreads];
+  __shared__ uint32_t gt_count[kSelThreads];
 
   if (keff > 0 && keff == nc) {
     for (int i = tid; i < nc; i += kSelThreads) L[base + i] = c0 + i;
@@ -114,7 +115,6 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         }
         sh_prefix = prefix;
         sh_kneed = kneed;
-        sh_slot = 0;
       }
       __syncthreads();
       prefix = sh_prefix;
@@ -123,33 +123,45 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       __syncthreads();
     }
     const uint32_t T = prefix;
-    const int n_gt = keff - (int)kneed;
-    // ties at T are ranked in position order: contiguous ranges per thread
+    // Candidates above T and the first kneed ties at T are written in
+    // position order (deterministic list): contiguous ranges per thread,
+    // exclusive scans of the per-thread counts.
     const int chunk = (nc + kSelThreads - 1) / kSelThreads;
     const int i0 = tid * chunk;
     const int i1 = (i0 + chunk < nc) ? i0 + chunk : nc;
-    uint32_t ties = 0;
-    for (int i = i0; i < i1; ++i)
-      ties += ((uint32_t)S[i] + kScoreBias) == T;
+    uint32_t gt = 0, ties = 0;
+    for (int i = i0; i < i1; ++i) {
+      const uint32_t u = (uint32_t)S[i] + kScoreBias;
+      gt += u > T;
+      ties += u == T;
+    }
+    gt_count[tid] = gt;
     tie_count[tid] = ties;
     __syncthreads();
     if (tid == 0) {
-      uint32_t run = 0;
+      uint32_t run_gt = 0, run_tie = 0;
       for (int t = 0; t < kSelThreads; ++t) {
-        const uint32_t c = tie_count[t];
-        tie_count[t] = run;
-        run += c;
+        const uint32_t a = gt_count[t], c = tie_count[t];
+        gt_count[t] = run_gt;
+        tie_count[t] = run_tie;
+        run_gt += a;
+        run_tie += c;
       }
     }
     __syncthreads();
     uint32_t rank = tie_count[tid];
+    uint32_t above = gt_count[tid];
+    // merged order: a tie of rank r (< kneed) precedes every candidate above
+    // T that comes after it, so the output position is (#above before it) +
+    // (#taken ties before it).
     for (int i = i0; i < i1; ++i) {
       const uint32_t u = (uint32_t)S[i] + kScoreBias;
       if (u > T) {
-        const uint32_t slot = atomicAdd(&sh_slot, 1u);
-        L[base + slot] = c0 + i;
+        const uint32_t taken = rank < kneed ? rank : kneed;
+        L[base + above + taken] = c0 + i;
+        ++above;
       } else if (u == T) {
-        if (rank < kneed) L[base + n_gt + rank] = c0 + i;
+        if (rank < kneed) L[base + above + rank] = c0 + i;
         ++rank;
       }
     }
