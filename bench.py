@@ -1,0 +1,291 @@
+#!/usr/bin/env python
+"""Decode-step benchmark of score-then-select sparse attention on one MI355X.
+
+One step = the whole hot path for one batch: encode the current token of
+every sequence (dkv_encode on B x Hkv keys: sign code + radius) and one
+dkv_decode (query codes, score of every cached key, selection of sinks +
+window + top-k, attention over the selection, split merge).  The prefix codes
+are built once before timing.  Inputs are seeded synthetic tensors resident
+in HBM (see workloads/).
+
+Prints ONE JSON line: scored keys per second (every (key, KV head) pair of
+every sequence is scored once per step), the step latency, per-stage times
+from HIP events recorded on the launch stream inside the timed region, the
+roofline of the dominant kernel (the score stage: it streams every key's
+code and radius), and the CPU oracle timed on a bounded sample of the same
+workload on this host's cores.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("scored keys/s and decode-step latency at 128K ctx; "
+          "achieved HBM GB/s vs peak")
+DEFAULT_WORKLOAD = "gqa32x8_bs16_n128k_b128"
+HBM_PEAK_GBS = 8000.0
+PAGE = 16
+
+
+class HipEvents:
+    """hipEvent_t handles through ctypes (timing on the launch stream)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            if self.lib.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(h.value)
+        return out
+
+    def record(self, ev, stream_handle):
+        if self.lib.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream_handle)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a),
+                                        ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def destroy(self, evs):
+        for e in evs:
+            self.lib.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def algorithmic_bytes(wl, lens, cfg) -> dict:
+    """Bytes the method itself must move per step (not the dense K/V)."""
+    Hkv, Hq, d, b = wl.num_kv_heads, wl.num_q_heads, wl.head_dim, wl.code_bits
+    keys = int(sum(int(n) for n in lens)) * Hkv          # scored (key, KV head)
+    sel_rows = sum(min(int(n), cfg.select_cap) for n in lens) * Hkv
+    pages = sum((int(n) + PAGE - 1) // PAGE for n in lens)
+    score = keys * (b // 8 + 1)
+    attend = sel_rows * 4 * d                            # K + V bf16 rows
+    io = len(lens) * Hq * (2 * d + 4 * d) + 4 * pages    # q in, out, table
+    encode = len(lens) * Hkv * (2 * d + b // 8 + 1)      # current token
+    return {"keys": keys, "score": score, "attend": attend, "io": io,
+            "encode": encode, "total": score + attend + io + encode}
+
+
+def source_digest(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(kernel_src_digest: str, workload: str):
+    """HBM bytes per launch of the score kernel from committed rocprofv3 PMC
+    counters (profiles/score_traffic.json), or None when absent or taken for a
+    different kernel source."""
+    path = os.path.join(ROOT, "profiles", "score_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_digest") != kernel_src_digest or rec.get("workload") != workload:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, inp, units: int, reps: int) -> dict:
+    """The CPU oracle (as it stands) on a bounded sample of the workload."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import numpy as np
+
+    import oracle
+    from helpers import logical_rows, tensor_bits
+
+    bt = inp["block_table"].cpu().numpy()
+    lens = inp["seq_lens"].cpu().numpy()
+    P = tensor_bits(inp["proj"])
+    G, d, b = wl.group, wl.head_dim, wl.code_bits
+    picks = [(s, g) for s in range(wl.batch) for g in range(wl.num_kv_heads)][:units]
+    Nmax = max(int(lens[s]) for s, _ in picks)
+    U = len(picks)
+    q = np.zeros((U, G, d), np.uint16)
+    K = np.zeros((U, Nmax, d), np.uint16)
+    V = np.zeros((U, Nmax, d), np.uint16)
+    codes = np.zeros((U, Nmax, b // 32), np.uint32)
+    radii = np.zeros((U, Nmax), np.uint8)
+    N = np.zeros(U, np.int32)
+    qall = tensor_bits(inp["q"])
+    for i, (s, g) in enumerate(picks):
+        n = int(lens[s])
+        N[i] = n
+        q[i] = qall[s, g * G:(g + 1) * G]
+        K[i, :n] = logical_rows(inp["k_pool"], bt, s, n, g)
+        V[i, :n] = logical_rows(inp["v_pool"], bt, s, n, g)
+        codes[i, :n], radii[i, :n] = oracle.encode_keys(K[i, :n], P)   # untimed
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        oracle.decode_units(q, P, codes, radii, K, V, N, wl.top_k, wl.window,
+                            wl.sinks, want_scores=False)
+    dt = time.perf_counter() - t0
+    keys = float(N.sum()) * reps
+    return {"value": keys / dt, "unit": "scored keys/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": (f"{U} of {wl.batch * wl.num_kv_heads} (sequence, KV head) units "
+                       f"of {wl.name} at full length, decode step (query codes, "
+                       f"scores, select, attention) x{reps}; codes pre-encoded "
+                       f"by the oracle, untimed"),
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-units", type=int, default=16)
+    ap.add_argument("--cpu-reps", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (for "
+                         "scaling PMC byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not "
+              "supported (the path shards by KV head / sequence with no exchange; "
+              "see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import hashed_top_sparse_amd as dkv
+    import workloads
+
+    torch.cuda.set_device(0)
+    wl = workloads.get(args.workload)
+    cfg = dkv.Config(num_q_heads=wl.num_q_heads, num_kv_heads=wl.num_kv_heads,
+                     code_bits=wl.code_bits, top_k=wl.top_k, window=wl.window,
+                     sinks=wl.sinks)
+    print(f"[bench] drawing {wl.name}", file=sys.stderr, flush=True)
+    inp = workloads.make_inputs(wl, "cuda")
+    B, Hkv = wl.batch, wl.num_kv_heads
+    nb = inp["k_pool"].shape[0]
+    dev = inp["k_pool"].device
+    codes = torch.zeros((nb, Hkv, wl.code_bits // 32, PAGE), dtype=torch.int32, device=dev)
+    radii = torch.zeros((nb, Hkv, PAGE), dtype=torch.uint8, device=dev)
+    zeros = torch.zeros(B, dtype=torch.int32, device=dev)
+    dkv.encode(cfg, inp["k_pool"], inp["block_table"], zeros, inp["seq_lens"],
+               inp["max_seq_len"], inp["proj"], codes, radii)
+    cur_start = (inp["seq_lens"] - 1).contiguous()
+    max_len = inp["max_seq_len"]
+    ws = torch.empty(dkv.decode_workspace_size(cfg, B, max_len), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty((B, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    print("[bench] prefix encoded", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    hip = HipEvents()
+    names = ["encode_current"] + dkv.decode_stage_names()
+    n_ev = len(names) + 1
+
+    def step(evs):
+        hip.record(evs[0], sh)
+        dkv.encode(cfg, inp["k_pool"], inp["block_table"], cur_start,
+                   inp["seq_lens"], 1, inp["proj"], codes, radii, stream=stream)
+        dkv.decode_profiled(cfg, inp["q"], inp["k_pool"], inp["v_pool"], codes, radii,
+                            inp["block_table"], inp["seq_lens"], max_len, inp["proj"],
+                            out, ws, evs[1:], stream=stream)
+
+    warm_ev = hip.create(n_ev)
+    for _ in range(args.warmup):
+        step(warm_ev)
+    torch.cuda.synchronize()
+    evs = [hip.create(n_ev) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    stage_ms = {}
+    for j, nm in enumerate(names):
+        stage_ms[nm] = sum(hip.elapsed_ms(e[j], e[j + 1]) for e in evs) / args.steps
+    gpu_ms = sum(hip.elapsed_ms(e[0], e[-1]) for e in evs) / args.steps
+    hip.destroy(warm_ev)
+    for e in evs:
+        hip.destroy(e)
+    print(f"[bench] {args.steps} steps timed", file=sys.stderr, flush=True)
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    lens = inp["seq_lens"].cpu().tolist()
+    ab = algorithmic_bytes(wl, lens, cfg)
+    score_s = stage_ms["score"] * 1e-3
+    score_src = [os.path.join(ROOT, "hashed_top_sparse_amd", "csrc", f)
+                 for f in ("score_select.hip", "internal.h")]
+    traffic = counter_traffic(source_digest(score_src), wl.name)
+    roofline = {"bound": "hbm", "kernel": "score",
+                "achieved": ab["score"] / score_s / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": ab["score"] / score_s / 1e9 / HBM_PEAK_GBS,
+                "traffic": traffic,
+                "algorithmic_bytes_per_launch": ab["score"]}
+
+    result = {
+        "metric": METRIC,
+        "value": ab["keys"] / (ms_per_step * 1e-3),
+        "unit": "scored keys/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "seq_len": max_len,
+                   "q_heads": wl.num_q_heads, "kv_heads": Hkv, "head_dim": wl.head_dim,
+                   "code_bits": wl.code_bits, "top_k": wl.top_k, "window": wl.window,
+                   "sinks": wl.sinks, "page": PAGE, "parallelism": "single GPU"},
+        "latency_us": ms_per_step * 1e3,
+        "gpu_step_us": gpu_ms * 1e3,
+        "step_algorithmic_bytes": ab["total"],
+        "step_hbm_gbs": ab["total"] / (ms_per_step * 1e-3) / 1e9,
+        "step_frac_of_peak": ab["total"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "stages_us": {k: v * 1e3 for k, v in stage_ms.items()},
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_units, args.cpu_reps)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

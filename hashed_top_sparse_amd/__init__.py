@@ -19,8 +19,8 @@ from typing import Optional
 import torch
 
 __all__ = ["Config", "DkvError", "encode", "decode", "decode_debug",
-           "decode_workspace_size", "library_path", "load_library",
-           "EXPORTED_SYMBOLS"]
+           "decode_profiled", "decode_stage_names", "decode_workspace_size",
+           "library_path", "load_library", "EXPORTED_SYMBOLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libdkv.so")
@@ -28,7 +28,9 @@ _lib = None
 
 # Every symbol include/dkv.h declares.
 EXPORTED_SYMBOLS = ("dkv_encode", "dkv_decode_workspace_size", "dkv_decode",
-                    "dkv_decode_debug", "dkv_status_string", "dkv_abi_version")
+                    "dkv_decode_debug", "dkv_decode_profiled",
+                    "dkv_decode_num_stages", "dkv_decode_stage_name",
+                    "dkv_status_string", "dkv_abi_version")
 ABI_VERSION = 1
 
 STATUS = {0: "DKV_OK", 1: "DKV_ERR_INVALID_ARG", 2: "DKV_ERR_UNSUPPORTED",
@@ -97,6 +99,12 @@ def load_library():
     lib.dkv_decode.restype = ctypes.c_int
     lib.dkv_decode_debug.argtypes = dec + [P, P, P]
     lib.dkv_decode_debug.restype = ctypes.c_int
+    lib.dkv_decode_profiled.argtypes = dec + [P, P]
+    lib.dkv_decode_profiled.restype = ctypes.c_int
+    lib.dkv_decode_num_stages.argtypes = []
+    lib.dkv_decode_num_stages.restype = i32
+    lib.dkv_decode_stage_name.argtypes = [i32]
+    lib.dkv_decode_stage_name.restype = ctypes.c_char_p
     lib.dkv_status_string.argtypes = [ctypes.c_int]
     lib.dkv_status_string.restype = ctypes.c_char_p
     lib.dkv_abi_version.argtypes = []
@@ -233,3 +241,26 @@ def decode_debug(cfg: Config, q, k_pool, v_pool, codes, radii, block_table,
     _check(lib.dkv_decode_debug(*args, _ptr(q8_out, "q8_out", (torch.int8,)),
                                 _ptr(scores_out, "scores_out", _I32),
                                 _stream(stream)))
+
+
+def decode_stage_names():
+    """Names of the decode stages dkv_decode_profiled brackets with events."""
+    lib = load_library()
+    return [lib.dkv_decode_stage_name(i).decode() for i in range(lib.dkv_decode_num_stages())]
+
+
+def decode_profiled(cfg: Config, q, k_pool, v_pool, codes, radii, block_table,
+                    seq_lens, max_seq_len: int, proj, out, workspace, events,
+                    sel_idx=None, sel_cnt=None, stream=None) -> None:
+    """dkv_decode_profiled: ``events`` holds num_stages+1 hipEvent_t handles
+    (ints) that the library records before each stage and after the last."""
+    lib = load_library()
+    n = lib.dkv_decode_num_stages()
+    if len(events) < n + 1:
+        raise ValueError(f"need {n + 1} events, got {len(events)}")
+    arr = (ctypes.c_void_p * len(events))(*events)
+    c, args = _decode_args(cfg, q, k_pool, v_pool, codes, radii, block_table,
+                           seq_lens, max_seq_len, proj, out, workspace, sel_idx,
+                           sel_cnt)
+    _check(lib.dkv_decode_profiled(*args, ctypes.cast(arr, ctypes.c_void_p),
+                                   _stream(stream)))

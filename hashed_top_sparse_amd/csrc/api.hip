@@ -8,6 +8,8 @@
 namespace dkv {
 namespace {
 
+constexpr int kDecodeStages = 5;
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 bool valid_config(const dkv_config *cfg, dkv_status *why) {
@@ -53,6 +55,7 @@ bool make_dims(const dkv_config *cfg, int32_t batch, int32_t max_seq_len,
   d->G = d->Hq / d->Hkv;
   d->b = cfg->code_bits;
   d->W = d->b / 32;
+  d->KS = d->b > 128 ? d->b / 128 : 1;
   d->k = cfg->top_k;
   d->w = cfg->window;
   d->sigma = cfg->sinks;
@@ -64,6 +67,8 @@ bool make_dims(const dkv_config *cfg, int32_t batch, int32_t max_seq_len,
   d->num_blocks = num_blocks;
   const int cap = d->cap > 0 ? d->cap : 1;
   d->nsplit = (cap + kAttnRows - 1) / kAttnRows;
+  const int pages = (max_seq_len + kPage - 1) / kPage;
+  d->nchunks = (pages + kChunkPages - 1) / kChunkPages;
   if ((int64_t)d->B * d->Hkv > 65535 * 64) {
     *why = DKV_ERR_UNSUPPORTED;
     return false;
@@ -79,7 +84,8 @@ dkv_status decode_impl(const dkv_config *cfg, const void *q,
                        int32_t batch, int32_t max_seq_len, const void *proj,
                        float *out, int32_t *sel_idx, int32_t *sel_cnt,
                        void *workspace, size_t workspace_bytes, int8_t *q8_out,
-                       int32_t *scores_out, hipStream_t stream) {
+                       int32_t *scores_out, dkv_event_t *events,
+                       hipStream_t stream) {
   DecodeDims d;
   dkv_status why = DKV_OK;
   if (!make_dims(cfg, batch, max_seq_len, max_blocks_per_seq, num_blocks, &d,
@@ -97,9 +103,11 @@ dkv_status decode_impl(const dkv_config *cfg, const void *q,
 
   char *ws = static_cast<char *>(workspace);
   int8_t *q8 = q8_out ? q8_out : reinterpret_cast<int8_t *>(ws + plan.q8);
-  int32_t *scores =
-      scores_out ? scores_out : reinterpret_cast<int32_t *>(ws + plan.scores);
-  int32_t *sel = reinterpret_cast<int32_t *>(ws + plan.sel);
+  uint32_t *qop = reinterpret_cast<uint32_t *>(ws + plan.qop);
+  float *qneg = reinterpret_cast<float *>(ws + plan.qneg);
+  uint2 *cand = reinterpret_cast<uint2 *>(ws + plan.cand);
+  int32_t *cand_cnt = reinterpret_cast<int32_t *>(ws + plan.cand_cnt);
+  int32_t *rows = reinterpret_cast<int32_t *>(ws + plan.rows);
   int32_t *cnt = reinterpret_cast<int32_t *>(ws + plan.cnt);
   float *part = reinterpret_cast<float *>(ws + plan.part);
   const uint16_t *q16 = static_cast<const uint16_t *>(q);
@@ -107,17 +115,28 @@ dkv_status decode_impl(const dkv_config *cfg, const void *q,
   const uint16_t *v16 = static_cast<const uint16_t *>(v_pool);
   const uint16_t *p16 = static_cast<const uint16_t *>(proj);
 
-  if (launch_qprep(d, q16, p16, q8, stream) != hipSuccess)
+  // Stage boundaries: an event is recorded before each stage and after the
+  // last one when the caller asked for them.
+  int stage = 0;
+  auto mark = [&]() -> bool {
+    if (events == nullptr) return true;
+    return hipEventRecord(reinterpret_cast<hipEvent_t>(events[stage++]),
+                          stream) == hipSuccess;
+  };
+  if (!mark() || launch_qprep(d, q16, p16, q8, qop, qneg, stream) != hipSuccess)
     return DKV_ERR_LAUNCH;
-  if (launch_score(d, codes, radii, block_table, seq_lens, q8, scores,
-                   stream) != hipSuccess)
+  if (!mark() || launch_score(d, codes, radii, block_table, seq_lens, qop, qneg,
+                              cand, cand_cnt, scores_out, stream) != hipSuccess)
     return DKV_ERR_LAUNCH;
-  if (launch_select(d, scores, seq_lens, sel, cnt, sel_idx, sel_cnt, stream) !=
-      hipSuccess)
+  if (!mark() || launch_merge(d, cand, cand_cnt, seq_lens, block_table, rows,
+                              cnt, sel_idx, sel_cnt, stream) != hipSuccess)
     return DKV_ERR_LAUNCH;
-  if (launch_attend(d, q16, k16, v16, block_table, sel, cnt, part, out,
-                    stream) != hipSuccess)
+  if (!mark() || launch_attend(d, q16, k16, v16, rows, cnt, part, stream) !=
+                     hipSuccess)
     return DKV_ERR_LAUNCH;
+  if (!mark() || launch_combine(d, part, out, stream) != hipSuccess)
+    return DKV_ERR_LAUNCH;
+  if (!mark()) return DKV_ERR_LAUNCH;
   return DKV_OK;
 }
 
@@ -125,17 +144,24 @@ dkv_status decode_impl(const dkv_config *cfg, const void *q,
 
 WorkspacePlan plan_workspace(const DecodeDims &d) {
   WorkspacePlan p;
+  const size_t units = (size_t)d.B * d.Hkv;
   size_t off = 0;
   p.q8 = off;
   off += align256((size_t)d.B * d.Hq * d.b);
-  p.scores = off;
-  off += align256((size_t)d.B * d.Hkv * (size_t)d.max_seq_len * 4);
-  p.sel = off;
-  off += align256((size_t)d.B * d.Hkv * (size_t)d.cap * 4);
+  p.qop = off;
+  off += align256(units * d.KS * 64 * 8 * 4);
+  p.qneg = off;
+  off += align256((size_t)d.B * d.Hq * 4);
+  p.cand = off;
+  off += align256(units * d.nchunks * (size_t)d.k * 8);
+  p.cand_cnt = off;
+  off += align256(units * d.nchunks * 4);
+  p.rows = off;
+  off += align256(units * (size_t)d.cap * 4);
   p.cnt = off;
-  off += align256((size_t)d.B * d.Hkv * 4);
+  off += align256(units * 4);
   p.part = off;
-  off += align256((size_t)d.B * d.Hkv * d.nsplit * d.G * (kHeadDim + 2) * 4);
+  off += align256(units * d.nsplit * d.G * (kHeadDim + 2) * 4);
   p.total = off;
   return p;
 }
@@ -189,7 +215,7 @@ dkv_decode(const dkv_config *cfg, const void *q, const void *k_pool,
   return decode_impl(cfg, q, k_pool, v_pool, codes, radii, num_blocks,
                      block_table, max_blocks_per_seq, seq_lens, batch,
                      max_seq_len, proj, out, sel_idx, sel_cnt, workspace,
-                     workspace_bytes, nullptr, nullptr,
+                     workspace_bytes, nullptr, nullptr, nullptr,
                      reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -204,8 +230,38 @@ __attribute__((visibility("default"))) dkv_status dkv_decode_debug(
   return decode_impl(cfg, q, k_pool, v_pool, codes, radii, num_blocks,
                      block_table, max_blocks_per_seq, seq_lens, batch,
                      max_seq_len, proj, out, sel_idx, sel_cnt, workspace,
-                     workspace_bytes, q8_out, scores_out,
+                     workspace_bytes, q8_out, scores_out, nullptr,
                      reinterpret_cast<hipStream_t>(stream));
+}
+
+__attribute__((visibility("default"))) dkv_status dkv_decode_profiled(
+    const dkv_config *cfg, const void *q, const void *k_pool,
+    const void *v_pool, const uint32_t *codes, const uint8_t *radii,
+    int64_t num_blocks, const int32_t *block_table, int32_t max_blocks_per_seq,
+    const int32_t *seq_lens, int32_t batch, int32_t max_seq_len,
+    const void *proj, float *out, int32_t *sel_idx, int32_t *sel_cnt,
+    void *workspace, size_t workspace_bytes, dkv_event_t *stage_events,
+    dkv_stream_t stream) {
+  if (stage_events == nullptr) return DKV_ERR_INVALID_ARG;
+  for (int i = 0; i <= kDecodeStages; ++i)
+    if (stage_events[i] == nullptr) return DKV_ERR_INVALID_ARG;
+  return decode_impl(cfg, q, k_pool, v_pool, codes, radii, num_blocks,
+                     block_table, max_blocks_per_seq, seq_lens, batch,
+                     max_seq_len, proj, out, sel_idx, sel_cnt, workspace,
+                     workspace_bytes, nullptr, nullptr, stage_events,
+                     reinterpret_cast<hipStream_t>(stream));
+}
+
+__attribute__((visibility("default"))) int32_t dkv_decode_num_stages(void) {
+  return kDecodeStages;
+}
+
+__attribute__((visibility("default"))) const char *
+dkv_decode_stage_name(int32_t stage) {
+  static const char *const names[kDecodeStages] = {
+      "query_codes", "score", "merge", "attend", "combine"};
+  if (stage < 0 || stage >= kDecodeStages) return "";
+  return names[stage];
 }
 
 __attribute__((visibility("default"))) const char *

@@ -9,9 +9,10 @@
 //   m* = max m_p,  l* = sum l_p 2^(m_p - m*),  o = sum acc_p 2^(m_p - m*) / l*.
 //
 // Work mapping of the split kernel: 256 threads = 16 row groups of 16 lanes;
-// a row group reads one selected key row and value row (256 B each: 16 B
-// per lane), so a workgroup gathers 16 rows per step through the block
-// table.  All G query heads of the KV group share the gathered rows.
+// a row group reads a selected key row and value row (256 B each: 16 B per
+// lane) and keeps 4 rows in flight, so a workgroup has 64 row pairs of
+// gathers outstanding.  The selection list already holds physical row ids
+// (page*16 + slot).  All G query heads of the KV group share the rows.
 #include "internal.h"
 
 namespace dkv {
@@ -48,10 +49,9 @@ __device__ __forceinline__ void merge_state(float &m1, float &l1, float *a1,
 template <int G>
 __global__ __launch_bounds__(kThreads) void attend_split_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_pool,
-    const uint16_t *__restrict__ v_pool, int64_t num_blocks,
-    const int32_t *__restrict__ block_table, int max_blocks,
-    const int32_t *__restrict__ sel, const int32_t *__restrict__ cnt, int cap,
-    float *__restrict__ part, int Hq, int Hkv, int nsplit, float qscale) {
+    const uint16_t *__restrict__ v_pool, const int32_t *__restrict__ rows,
+    const int32_t *__restrict__ cnt, int cap, float *__restrict__ part, int Hq,
+    int Hkv, int nsplit, float qscale) {
   const int split = blockIdx.x;
   const int unit = blockIdx.y;
   const int s = unit / Hkv, g = unit % Hkv;
@@ -79,34 +79,67 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(
     for (int c = 0; c < 8; ++c) acc[h][c] = 0.f;
   }
 
-  const int32_t *L = sel + (int64_t)unit * cap;
-  for (int r = r0 + rg; r < r1; r += kRowGroups) {
-    const int pos = L[r];
-    if (pos < 0) continue;
-    const int blk = block_table[(int64_t)s * max_blocks + pos / kPage];
-    if (blk < 0 || blk >= num_blocks) continue;
-    const int64_t off =
-        (((int64_t)blk * kPage + pos % kPage) * Hkv + g) * kHeadDim + lane * 8;
-    const uint4 kraw = *reinterpret_cast<const uint4 *>(k_pool + off);
-    const uint4 vraw = *reinterpret_cast<const uint4 *>(v_pool + off);
-    float kf[8], vf[8];
-    unpack8(kraw, kf);
-    unpack8(vraw, vf);
+  const int32_t *L = rows + (int64_t)unit * cap;
+  constexpr int kBatch = 4; // rows per row group in flight
+  for (int rb = r0 + rg; rb < r1; rb += kBatch * kRowGroups) {
+    uint4 kraw[kBatch], vraw[kBatch];
+    bool ok[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int r = rb + i * kRowGroups;
+      const int idx = r < r1 ? L[r] : -1;
+      ok[i] = idx >= 0;
+      const int64_t off = ((int64_t)(ok[i] ? idx : 0) * Hkv + g) * kHeadDim + lane * 8;
+      kraw[i] = ok[i] ? *reinterpret_cast<const uint4 *>(k_pool + off) : make_uint4(0, 0, 0, 0);
+      vraw[i] = ok[i] ? *reinterpret_cast<const uint4 *>(v_pool + off) : make_uint4(0, 0, 0, 0);
+    }
+    float dot[G][kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      float kf[8];
+      unpack8(kraw[i], kf);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float d = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) d = fmaf(qv[h][c], kf[c], d);
+        dot[h][i] = d;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+#pragma unroll
+        for (int off2 = kLanesPerRow / 2; off2 > 0; off2 >>= 1)
+          dot[h][i] += __shfl_xor(dot[h][i], off2, kLanesPerRow);
+        if (!ok[i]) dot[h][i] = -INFINITY;
+      }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float dot = 0.f;
+      float mn = m[h];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) dot = fmaf(qv[h][c], kf[c], dot);
+      for (int i = 0; i < kBatch; ++i) mn = fmaxf(mn, dot[h][i]);
+      if (mn == -INFINITY) continue; // nothing valid yet
+      const float corr = exp2f(m[h] - mn);
+      float pr[kBatch];
+      float psum = 0.f;
 #pragma unroll
-      for (int off2 = kLanesPerRow / 2; off2 > 0; off2 >>= 1)
-        dot += __shfl_xor(dot, off2, kLanesPerRow);
-      const float mn = fmaxf(m[h], dot);
-      const float corr = exp2f(m[h] - mn); // m = -inf gives 0
-      const float p = exp2f(dot - mn);
-      l[h] = l[h] * corr + p;
+      for (int i = 0; i < kBatch; ++i) {
+        pr[i] = exp2f(dot[h][i] - mn);
+        psum += pr[i];
+      }
+      l[h] = l[h] * corr + psum;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) acc[h][c] = fmaf(p, vf[c], acc[h][c] * corr);
+      for (int c = 0; c < 8; ++c) acc[h][c] *= corr;
       m[h] = mn;
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        float vf[8];
+        unpack8(vraw[i], vf);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[h][c] = fmaf(pr[i], vf[c], acc[h][c]);
+      }
     }
   }
 
@@ -183,8 +216,7 @@ __global__ __launch_bounds__(kHeadDim) void attend_combine_kernel(
 
 hipError_t launch_attend(const DecodeDims &d, const uint16_t *q,
                          const uint16_t *k_pool, const uint16_t *v_pool,
-                         const int32_t *block_table, const int32_t *sel,
-                         const int32_t *cnt, float *part, float *out,
+                         const int32_t *rows, const int32_t *cnt, float *part,
                          hipStream_t stream) {
   // log2(e) / sqrt(128)
   const float qscale = 1.4426950408889634f * 0.08838834764831845f;
@@ -192,9 +224,8 @@ hipError_t launch_attend(const DecodeDims &d, const uint16_t *q,
 #define DKV_ATTEND_CASE(GG)                                                    \
   case GG:                                                                     \
     hipLaunchKernelGGL(attend_split_kernel<GG>, grid, dim3(kThreads), 0,       \
-                       stream, q, k_pool, v_pool, d.num_blocks, block_table,   \
-                       d.max_blocks, sel, cnt, d.cap, part, d.Hq, d.Hkv,       \
-                       d.nsplit, qscale);                                      \
+                       stream, q, k_pool, v_pool, rows, cnt, d.cap, part,      \
+                       d.Hq, d.Hkv, d.nsplit, qscale);                         \
     break;
   switch (d.G) {
     DKV_ATTEND_CASE(1)
@@ -205,8 +236,11 @@ hipError_t launch_attend(const DecodeDims &d, const uint16_t *q,
     return hipErrorInvalidValue;
   }
 #undef DKV_ATTEND_CASE
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const DecodeDims &d, const float *part, float *out,
+                          hipStream_t stream) {
   hipLaunchKernelGGL(attend_combine_kernel, dim3(d.B * d.Hq), dim3(kHeadDim),
                      0, stream, part, out, d.Hq, d.Hkv, d.G, d.nsplit);
   return hipGetLastError();

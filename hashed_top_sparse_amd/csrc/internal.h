@@ -10,24 +10,28 @@
 
 namespace dkv {
 
-constexpr int kPage = 16;     // tokens per page
-constexpr int kHeadDim = 128; // d
-constexpr int kAttnRows = 256; // selected rows per attention split
+constexpr int kPage = 16;       // tokens per page
+constexpr int kHeadDim = 128;   // d
+constexpr int kAttnRows = 256;  // selected rows per attention split
+constexpr int kChunkPages = 512;                 // pages scored per workgroup
+constexpr int kChunkKeys = kChunkPages * kPage;  // 8192 keys
 
 // Validated shape of one decode call.
 struct DecodeDims {
   int B, Hq, Hkv, G, b, W;   // W = b/32 code words per key
+  int KS;                    // 128-bit MFMA K-steps per key: max(1, b/128)
   int k, w, sigma, cap;      // cap = k + w + sigma (selection list length)
   int max_seq_len;           // caller's bound (workspace stride)
   int n_max;                 // min(max_seq_len, 16*max_blocks)
   int max_blocks;
   int64_t num_blocks;
+  int nchunks;               // score chunks per (sequence, KV head)
   int nsplit;                // attention splits per (sequence, KV head)
 };
 
 // Byte offsets of the decode workspace regions (each 256-byte aligned).
 struct WorkspacePlan {
-  size_t q8, scores, sel, cnt, part, total;
+  size_t q8, qop, qneg, cand, cand_cnt, rows, cnt, part, total;
 };
 
 WorkspacePlan plan_workspace(const DecodeDims &d);
@@ -40,24 +44,35 @@ hipError_t launch_encode(const uint16_t *k_pool, int64_t num_blocks,
                          int b, uint32_t *codes, uint8_t *radii,
                          hipStream_t stream);
 
+// Query codes q8 [B][Hq][b], the score MFMA operand qop
+// [B*Hkv][KS][64 lanes][8 dwords] and qneg [B][Hq] = -sum_j q8.
 hipError_t launch_qprep(const DecodeDims &d, const uint16_t *q,
-                        const uint16_t *proj, int8_t *q8, hipStream_t stream);
+                        const uint16_t *proj, int8_t *q8, uint32_t *qop,
+                        float *qneg, hipStream_t stream);
 
+// Scores every key of every chunk and writes each chunk's exact top-k
+// candidates (biased score, position) in position order.
 hipError_t launch_score(const DecodeDims &d, const uint32_t *codes,
                         const uint8_t *radii, const int32_t *block_table,
-                        const int32_t *seq_lens, const int8_t *q8,
-                        int32_t *scores, hipStream_t stream);
+                        const int32_t *seq_lens, const uint32_t *qop,
+                        const float *qneg, uint2 *cand, int32_t *cand_cnt,
+                        int32_t *scores_out, hipStream_t stream);
 
-hipError_t launch_select(const DecodeDims &d, const int32_t *scores,
-                         const int32_t *seq_lens, int32_t *sel, int32_t *cnt,
-                         int32_t *user_sel, int32_t *user_cnt,
-                         hipStream_t stream);
+// Merges the chunk candidates into the final selection: rows (physical row
+// ids blk*16+slot, -1 past the count), cnt, and the optional user lists.
+hipError_t launch_merge(const DecodeDims &d, const uint2 *cand,
+                        const int32_t *cand_cnt, const int32_t *seq_lens,
+                        const int32_t *block_table, int32_t *rows,
+                        int32_t *cnt, int32_t *user_sel, int32_t *user_cnt,
+                        hipStream_t stream);
 
 hipError_t launch_attend(const DecodeDims &d, const uint16_t *q,
                          const uint16_t *k_pool, const uint16_t *v_pool,
-                         const int32_t *block_table, const int32_t *sel,
-                         const int32_t *cnt, float *part, float *out,
+                         const int32_t *rows, const int32_t *cnt, float *part,
                          hipStream_t stream);
+
+hipError_t launch_combine(const DecodeDims &d, const float *part, float *out,
+                          hipStream_t stream);
 
 // ---------------------------------------------------------------- device
 __device__ __forceinline__ float bf16_to_float(uint32_t bits16) {
@@ -72,6 +87,32 @@ __device__ __forceinline__ int clamp_int(int x, int lo, int hi) {
 __device__ __forceinline__ int seq_len_clamped(const int32_t *seq_lens, int s,
                                                int n_max) {
   return clamp_int(seq_lens[s], 0, n_max);
+}
+
+// Exclusive prefix sum over a workgroup of NT threads (NT/64 waves), in
+// thread order.  tmp needs NT/64 words of LDS.  Every thread must call it.
+template <int NT>
+__device__ __forceinline__ uint32_t wg_exclusive_scan(uint32_t v, uint32_t *tmp,
+                                                      uint32_t *total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) tmp[wave] = x;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    const uint32_t t = tmp[i];
+    base += (i < wave) ? t : 0u;
+    tot += t;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + x - v;
 }
 
 } // namespace dkv

@@ -75,8 +75,9 @@
 extern "C" {
 #endif
 
-/* Same type as hipStream_t. */
+/* Same types as hipStream_t and hipEvent_t. */
 typedef struct ihipStream_t *dkv_stream_t;
+typedef struct ihipEvent_t *dkv_event_t;
 
 typedef enum {
   DKV_OK = 0,
@@ -198,6 +199,31 @@ dkv_status dkv_decode_debug(const dkv_config *cfg, const void *q,
                             int32_t *sel_idx, int32_t *sel_cnt, void *workspace,
                             size_t workspace_bytes, int8_t *q8_out,
                             int32_t *scores_out, dkv_stream_t stream);
+
+/*
+ * dkv_decode_profiled -- dkv_decode that also records stage_events[i] on
+ * `stream` right before decode stage i and stage_events[n] after the last
+ * stage, n = dkv_decode_num_stages() (at most DKV_MAX_DECODE_STAGES).  The
+ * caller creates the n+1 events (hipEventCreate) and reads the stage times
+ * with hipEventElapsedTime after synchronising.  For instrumentation: the
+ * event records add a little launch overhead.
+ */
+#define DKV_MAX_DECODE_STAGES 8
+dkv_status dkv_decode_profiled(const dkv_config *cfg, const void *q,
+                               const void *k_pool, const void *v_pool,
+                               const uint32_t *codes, const uint8_t *radii,
+                               int64_t num_blocks, const int32_t *block_table,
+                               int32_t max_blocks_per_seq,
+                               const int32_t *seq_lens, int32_t batch,
+                               int32_t max_seq_len, const void *proj,
+                               float *out, int32_t *sel_idx, int32_t *sel_cnt,
+                               void *workspace, size_t workspace_bytes,
+                               dkv_event_t *stage_events, dkv_stream_t stream);
+
+/* Number of decode stages and the static name of stage i ("" if out of
+ * range). */
+int32_t dkv_decode_num_stages(void);
+const char *dkv_decode_stage_name(int32_t stage);
 
 /* Static, NUL-terminated description of a status code. */
 const char *dkv_status_string(dkv_status status);
