@@ -80,7 +80,7 @@ def test_workspace_size():
     lib = dkv.load_library()
     c = _cfg()
     a = lib.dkv_decode_workspace_size(ctypes.byref(c), 4, 4096)
-    b = lib.dkv_decode_workspace_size(ctypes.byref(c), 4, 8192)
+    b = lib.dkv_decode_workspace_size(ctypes.byref(c), 4, 65536)
     assert 0 < a < b and a % 256 == 0
     bad = _cfg(code_bits=7)
     assert lib.dkv_decode_workspace_size(ctypes.byref(bad), 4, 4096) == 0
