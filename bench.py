@@ -247,7 +247,7 @@ def main():
     ab = algorithmic_bytes(wl, lens, cfg)
     score_s = stage_ms["score"] * 1e-3
     score_src = [os.path.join(ROOT, "hashed_top_sparse_amd", "csrc", f)
-                 for f in ("score_select.hip", "internal.h")]
+                 for f in ("score.hip", "internal.h")]
     traffic = counter_traffic(source_digest(score_src), wl.name)
     roofline = {"bound": "hbm", "kernel": "score",
                 "achieved": ab["score"] / score_s / 1e9, "peak": HBM_PEAK_GBS,

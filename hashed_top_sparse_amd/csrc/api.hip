@@ -3,6 +3,8 @@
 // the host and returns a status before any launch; nothing is allocated.
 #include <string.h>
 
+#include <algorithm>
+
 #include "internal.h"
 
 namespace dkv {
@@ -67,8 +69,14 @@ bool make_dims(const dkv_config *cfg, int32_t batch, int32_t max_seq_len,
   d->num_blocks = num_blocks;
   const int cap = d->cap > 0 ? d->cap : 1;
   d->nsplit = (cap + kAttnRows - 1) / kAttnRows;
-  const int pages = (max_seq_len + kPage - 1) / kPage;
-  d->nchunks = (pages + kChunkPages - 1) / kChunkPages;
+  const int64_t room = 4 * (int64_t)d->k + 16384;
+  d->cand_cap = (int)std::max<int64_t>(1, std::min<int64_t>(max_seq_len, room));
+  d->bm_words = (max_seq_len + 31) / 32;
+  // buffer views of the code and radius pools use 32-bit byte offsets
+  if ((uint64_t)num_blocks * d->Hkv * d->W * kPage * 4 > 0xFFFFFFFFull) {
+    *why = DKV_ERR_UNSUPPORTED;
+    return false;
+  }
   if ((int64_t)d->B * d->Hkv > 65535 * 64) {
     *why = DKV_ERR_UNSUPPORTED;
     return false;
@@ -105,8 +113,11 @@ dkv_status decode_impl(const dkv_config *cfg, const void *q,
   int8_t *q8 = q8_out ? q8_out : reinterpret_cast<int8_t *>(ws + plan.q8);
   uint32_t *qop = reinterpret_cast<uint32_t *>(ws + plan.qop);
   float *qneg = reinterpret_cast<float *>(ws + plan.qneg);
-  uint2 *cand = reinterpret_cast<uint2 *>(ws + plan.cand);
-  int32_t *cand_cnt = reinterpret_cast<int32_t *>(ws + plan.cand_cnt);
+  uint32_t *lthr = reinterpret_cast<uint32_t *>(ws + plan.lthr);
+  uint32_t *counter = reinterpret_cast<uint32_t *>(ws + plan.counter);
+  uint32_t *cand_u = reinterpret_cast<uint32_t *>(ws + plan.cand_u);
+  int32_t *cand_pos = reinterpret_cast<int32_t *>(ws + plan.cand_pos);
+  uint32_t *bitmap = reinterpret_cast<uint32_t *>(ws + plan.bitmap);
   int32_t *rows = reinterpret_cast<int32_t *>(ws + plan.rows);
   int32_t *cnt = reinterpret_cast<int32_t *>(ws + plan.cnt);
   float *part = reinterpret_cast<float *>(ws + plan.part);
@@ -123,13 +134,16 @@ dkv_status decode_impl(const dkv_config *cfg, const void *q,
     return hipEventRecord(reinterpret_cast<hipEvent_t>(events[stage++]),
                           stream) == hipSuccess;
   };
-  if (!mark() || launch_qprep(d, q16, p16, q8, qop, qneg, stream) != hipSuccess)
+  if (!mark() || launch_prep(d, q16, p16, codes, radii, block_table, seq_lens,
+                             q8, qop, qneg, lthr, counter, stream) != hipSuccess)
     return DKV_ERR_LAUNCH;
   if (!mark() || launch_score(d, codes, radii, block_table, seq_lens, qop, qneg,
-                              cand, cand_cnt, scores_out, stream) != hipSuccess)
+                              lthr, counter, cand_u, cand_pos, scores_out,
+                              stream) != hipSuccess)
     return DKV_ERR_LAUNCH;
-  if (!mark() || launch_merge(d, cand, cand_cnt, seq_lens, block_table, rows,
-                              cnt, sel_idx, sel_cnt, stream) != hipSuccess)
+  if (!mark() || launch_merge(d, cand_u, cand_pos, counter, seq_lens,
+                              block_table, bitmap, rows, cnt, sel_idx, sel_cnt,
+                              codes, radii, qop, qneg, stream) != hipSuccess)
     return DKV_ERR_LAUNCH;
   if (!mark() || launch_attend(d, q16, k16, v16, rows, cnt, part, stream) !=
                      hipSuccess)
@@ -152,10 +166,16 @@ WorkspacePlan plan_workspace(const DecodeDims &d) {
   off += align256(units * d.KS * 64 * 8 * 4);
   p.qneg = off;
   off += align256((size_t)d.B * d.Hq * 4);
-  p.cand = off;
-  off += align256(units * d.nchunks * (size_t)d.k * 8);
-  p.cand_cnt = off;
-  off += align256(units * d.nchunks * 4);
+  p.lthr = off;
+  off += align256(units * 4);
+  p.counter = off;
+  off += align256(units * 4);
+  p.cand_u = off;
+  off += align256(units * (size_t)d.cand_cap * 4);
+  p.cand_pos = off;
+  off += align256(units * (size_t)d.cand_cap * 4);
+  p.bitmap = off;
+  off += align256(units * (size_t)d.bm_words * 4);
   p.rows = off;
   off += align256(units * (size_t)d.cap * 4);
   p.cnt = off;
@@ -259,7 +279,7 @@ __attribute__((visibility("default"))) int32_t dkv_decode_num_stages(void) {
 __attribute__((visibility("default"))) const char *
 dkv_decode_stage_name(int32_t stage) {
   static const char *const names[kDecodeStages] = {
-      "query_codes", "score", "merge", "attend", "combine"};
+      "prep", "score", "merge", "attend", "combine"};
   if (stage < 0 || stage >= kDecodeStages) return "";
   return names[stage];
 }

@@ -13,8 +13,6 @@ namespace dkv {
 constexpr int kPage = 16;       // tokens per page
 constexpr int kHeadDim = 128;   // d
 constexpr int kAttnRows = 256;  // selected rows per attention split
-constexpr int kChunkPages = 512;                 // pages scored per workgroup
-constexpr int kChunkKeys = kChunkPages * kPage;  // 8192 keys
 
 // Validated shape of one decode call.
 struct DecodeDims {
@@ -25,13 +23,15 @@ struct DecodeDims {
   int n_max;                 // min(max_seq_len, 16*max_blocks)
   int max_blocks;
   int64_t num_blocks;
-  int nchunks;               // score chunks per (sequence, KV head)
+  int cand_cap;              // candidate list room per (sequence, KV head)
+  int bm_words;              // selection bitmap words per (sequence, KV head)
   int nsplit;                // attention splits per (sequence, KV head)
 };
 
 // Byte offsets of the decode workspace regions (each 256-byte aligned).
 struct WorkspacePlan {
-  size_t q8, qop, qneg, cand, cand_cnt, rows, cnt, part, total;
+  size_t q8, qop, qneg, lthr, counter, cand_u, cand_pos, bitmap, rows, cnt,
+      part, total;
 };
 
 WorkspacePlan plan_workspace(const DecodeDims &d);
@@ -44,26 +44,36 @@ hipError_t launch_encode(const uint16_t *k_pool, int64_t num_blocks,
                          int b, uint32_t *codes, uint8_t *radii,
                          hipStream_t stream);
 
-// Query codes q8 [B][Hq][b], the score MFMA operand qop
-// [B*Hkv][KS][64 lanes][8 dwords] and qneg [B][Hq] = -sum_j q8.
-hipError_t launch_qprep(const DecodeDims &d, const uint16_t *q,
-                        const uint16_t *proj, int8_t *q8, uint32_t *qop,
-                        float *qneg, hipStream_t stream);
+// Query codes q8 [B][Hq][b], the score matrix-core operand qop
+// [B*Hkv][KS][64 lanes][8 dwords], qneg [B][Hq] = -sum_j q8, and per
+// (sequence, KV head) the candidate threshold lthr (from a page sample) with
+// its candidate counter reset to 0.
+hipError_t launch_prep(const DecodeDims &d, const uint16_t *q,
+                       const uint16_t *proj, const uint32_t *codes,
+                       const uint8_t *radii, const int32_t *block_table,
+                       const int32_t *seq_lens, int8_t *q8, uint32_t *qop,
+                       float *qneg, uint32_t *lthr, uint32_t *counter,
+                       hipStream_t stream);
 
-// Scores every key of every chunk and writes each chunk's exact top-k
-// candidates (biased score, position) in position order.
+// Scores every cached key once and appends the candidates (u >= lthr) to
+// the per-(sequence, KV head) lists.
 hipError_t launch_score(const DecodeDims &d, const uint32_t *codes,
                         const uint8_t *radii, const int32_t *block_table,
                         const int32_t *seq_lens, const uint32_t *qop,
-                        const float *qneg, uint2 *cand, int32_t *cand_cnt,
+                        const float *qneg, const uint32_t *lthr,
+                        uint32_t *counter, uint32_t *cand_u, int32_t *cand_pos,
                         int32_t *scores_out, hipStream_t stream);
 
-// Merges the chunk candidates into the final selection: rows (physical row
-// ids blk*16+slot, -1 past the count), cnt, and the optional user lists.
-hipError_t launch_merge(const DecodeDims &d, const uint2 *cand,
-                        const int32_t *cand_cnt, const int32_t *seq_lens,
-                        const int32_t *block_table, int32_t *rows,
-                        int32_t *cnt, int32_t *user_sel, int32_t *user_cnt,
+// Final selection (sinks, window, exact top-k in position order): rows
+// (physical row ids blk*16+slot, -1 past the count), cnt, and the optional
+// user lists.
+hipError_t launch_merge(const DecodeDims &d, const uint32_t *cand_u,
+                        const int32_t *cand_pos, const uint32_t *counter,
+                        const int32_t *seq_lens, const int32_t *block_table,
+                        uint32_t *bitmap, int32_t *rows, int32_t *cnt,
+                        int32_t *user_sel, int32_t *user_cnt,
+                        const uint32_t *codes, const uint8_t *radii,
+                        const uint32_t *qop, const float *qneg,
                         hipStream_t stream);
 
 hipError_t launch_attend(const DecodeDims &d, const uint16_t *q,

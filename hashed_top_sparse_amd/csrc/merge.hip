@@ -5,49 +5,35 @@
 // recent tokens; [DySCO FAQ 3]: plus the first tokens (attention sinks).
 //   sinks   [0, min(sigma, N))
 //   window  [max(min(sigma, N), N - w), N)
-//   top-k   the min(k, |C|) best of C = [sigma, N - w) by (S desc, pos asc)
-// The score kernel left each chunk's exact top-k in position order; their
-// union holds the global top-k.  Two 12-bit radix histogram passes over the
-// union find the threshold score T and how many ties at T to keep, and a
-// workgroup scan writes the survivors in position order.
+//   top-k   the k_eff = min(k, |C|) best of C = [sigma, N - w) by
+//           (S desc, position asc)
 //
-// Output list per unit: sinks, window, then the top-k in ascending
-// position, as physical row ids (page*16 + slot, for the attention gather)
-// and, when asked, as logical positions; -1 past the count.
-#include "internal.h"
+// The streaming pass left every candidate with u >= L (the sampled
+// threshold).  If at least k_eff of them exist (and none was dropped for
+// lack of room), the top-k of C is exactly the top-k of that list:
+//   - the k_eff-th largest biased score T and the number of ties at T to
+//     keep come from two histogram passes (select_common.h);
+//   - if only some ties are kept, the lowest positions win: a second
+//     k-th-largest search over the inverted positions of the ties;
+//   - survivors are marked in a position bitmap, which is read back in
+//     order: the list is sinks, window, then the top-k in ascending
+//     position (deterministic).
+// Otherwise the workgroup rescans the (sequence, KV head)'s codes itself
+// and runs the same exact selection over every candidate score (slow, but
+// exact for any input).
+//
+// Output per unit: physical row ids (page*16 + slot) for the attention
+// gather and, when asked, logical positions; -1 past the count.
+#include "score_common.h"
+#include "select_common.h"
 
 namespace dkv {
 namespace {
 
 constexpr int kThreads = 1024;
-constexpr int kHistBits = 12;
-constexpr int kHistBins = 1 << kHistBits;
-constexpr int kMaxChunks = 4096;
-
-__device__ void find_threshold_bin(const uint32_t *hist, uint32_t kneed,
-                                   uint32_t *tmp, int *out_bin,
-                                   uint32_t *out_above) {
-  constexpr int kPer = kHistBins / kThreads;
-  const int top = kHistBins - 1 - kPer * threadIdx.x;
-  uint32_t local = 0;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) local += hist[top - i];
-  uint32_t total;
-  const uint32_t above = wg_exclusive_scan<kThreads>(local, tmp, &total);
-  if (above < kneed && kneed <= above + local) {
-    uint32_t run = above;
-    for (int i = 0; i < kPer; ++i) {
-      const uint32_t c = hist[top - i];
-      if (run + c >= kneed) {
-        *out_bin = top - i;
-        *out_above = run;
-        break;
-      }
-      run += c;
-    }
-  }
-  __syncthreads();
-}
+constexpr int kWaves = kThreads / 64;
+constexpr int kLdsScores = 32768;
+constexpr uint32_t kPosMax = 0x00FFFFFFu; // positions < 2^24
 
 __device__ __forceinline__ int row_of(const int32_t *bt, int pos,
                                       int64_t num_blocks) {
@@ -55,22 +41,26 @@ __device__ __forceinline__ int row_of(const int32_t *bt, int pos,
   return (blk >= 0 && blk < num_blocks) ? blk * kPage + pos % kPage : -1;
 }
 
+template <int KS, int G>
 __global__ __launch_bounds__(kThreads) void merge_kernel(
-    const uint2 *__restrict__ cand, const int32_t *__restrict__ cand_cnt,
-    int nchunks, const int32_t *__restrict__ seq_lens, int n_max,
+    const uint32_t *__restrict__ cand_u, const int32_t *__restrict__ cand_pos,
+    const uint32_t *__restrict__ counter, int cand_cap,
+    const int32_t *__restrict__ seq_lens, int n_max,
     const int32_t *__restrict__ block_table, int max_blocks,
     int64_t num_blocks, int Hkv, int k, int w, int sigma, int cap,
-    int32_t *__restrict__ rows, int32_t *__restrict__ cnt,
-    int32_t *__restrict__ user_sel, int32_t *__restrict__ user_cnt) {
-  __shared__ uint32_t hist[kHistBins];
-  __shared__ uint32_t tmp[kThreads / 64];
-  __shared__ uint32_t coff[kMaxChunks + 1]; // prefix offsets of chunk counts
-  __shared__ int sh_bin;
-  __shared__ uint32_t sh_above;
+    uint32_t *__restrict__ bitmap, int bm_stride, int32_t *__restrict__ rows,
+    int32_t *__restrict__ cnt, int32_t *__restrict__ user_sel,
+    int32_t *__restrict__ user_cnt, const uint32_t *__restrict__ codes,
+    const uint8_t *__restrict__ radii, uint32_t code_bytes,
+    uint32_t radius_bytes, int W, const uint32_t *__restrict__ qop,
+    const float *__restrict__ qneg) {
+  __shared__ uint32_t su[kLdsScores];
+  __shared__ SelectShared<kThreads> sel;
 
   const int unit = blockIdx.x;
-  const int s = unit / Hkv;
+  const int s = unit / Hkv, g = unit % Hkv;
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int N = seq_len_clamped(seq_lens, s, n_max);
   const int ns = sigma < N ? sigma : N;
   const int ws = (N - w > ns) ? N - w : ns;
@@ -94,87 +84,101 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
   }
 
   if (keff > 0) {
-    const int npages = (N + kPage - 1) / kPage;
-    const int nch = min(nchunks, (npages + kChunkPages - 1) / kChunkPages);
-    const int32_t *cc = cand_cnt + (int64_t)unit * nchunks;
-    const uint2 *cu = cand + (int64_t)unit * nchunks * (int64_t)k;
-    // chunk offsets in the flattened (chunk-major, position-ordered) list
-    if (tid == 0) {
-      uint32_t run = 0;
-      for (int c = 0; c < nch; ++c) {
-        coff[c] = run;
-        run += (uint32_t)cc[c];
-      }
-      coff[nch] = run;
-    }
-    __syncthreads();
-    const uint32_t nall = coff[nch];
-    auto elem = [&](uint32_t e) -> uint2 {
-      // chunk holding flattened index e (binary search over offsets)
-      int lo = 0, hi = nch - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (coff[mid] <= e) lo = mid; else hi = mid - 1;
-      }
-      return cu[(int64_t)lo * k + (e - coff[lo])];
-    };
-    // position-ordered contiguous ranges per thread
-    const uint32_t per = (nall + kThreads - 1) / kThreads;
-    const uint32_t e0 = min(nall, (uint32_t)tid * per);
-    const uint32_t e1 = min(nall, e0 + per);
-    if ((uint32_t)keff == nall) {
-      for (uint32_t e = e0; e < e1; ++e) {
-        const int pos = (int)elem(e).y;
-        R[base + e] = row_of(bt, pos, num_blocks);
-        if (U) U[base + e] = pos;
+    uint32_t *bm = bitmap + (int64_t)unit * bm_stride;
+    const int nwords = (N + 31) / 32;
+    const int c0 = sigma, c1 = N - w; // candidate positions [c0, c1)
+    if (keff == nc) {
+      // every candidate is selected
+      for (int i = tid; i < nwords; i += kThreads) {
+        const int p0 = i * 32;
+        uint32_t m = 0;
+        if (p0 + 32 > c0 && p0 < c1) {
+          const int a = max(c0, p0) - p0, e = min(c1, p0 + 32) - p0;
+          m = (e - a == 32) ? 0xFFFFFFFFu : (((1u << (e - a)) - 1u) << a);
+        }
+        bm[i] = m;
       }
     } else {
-      for (int i = tid; i < kHistBins; i += kThreads) hist[i] = 0;
+      for (int i = tid; i < nwords; i += kThreads) bm[i] = 0u;
       __syncthreads();
-      for (int c = 0; c < nch; ++c)
-        for (int i = tid; i < cc[c]; i += kThreads)
-          atomicAdd(&hist[cu[(int64_t)c * k + i].x >> kHistBits], 1u);
-      __syncthreads();
-      find_threshold_bin(hist, (uint32_t)keff, tmp, &sh_bin, &sh_above);
-      const uint32_t b1 = (uint32_t)sh_bin;
-      uint32_t kneed = (uint32_t)keff - sh_above;
-      for (int i = tid; i < kHistBins; i += kThreads) hist[i] = 0;
-      __syncthreads();
-      for (int c = 0; c < nch; ++c)
-        for (int i = tid; i < cc[c]; i += kThreads) {
-          const uint32_t u = cu[(int64_t)c * k + i].x;
-          if ((u >> kHistBits) == b1) atomicAdd(&hist[u & (kHistBins - 1)], 1u);
+      const uint32_t nlist = counter[unit];
+      uint32_t T, take_eq, n_eq;
+      if (nlist >= (uint32_t)keff && nlist <= (uint32_t)cand_cap) {
+        // ---- normal path: exact top-k of the candidate list
+        const uint32_t *cu = cand_u + (int64_t)unit * cand_cap;
+        const int32_t *cp = cand_pos + (int64_t)unit * cand_cap;
+        const bool staged = nlist <= (uint32_t)kLdsScores;
+        if (staged) {
+          for (uint32_t i = tid; i < nlist; i += kThreads) su[i] = cu[i];
+          __syncthreads();
         }
-      __syncthreads();
-      find_threshold_bin(hist, kneed, tmp, &sh_bin, &sh_above);
-      const uint32_t T = (b1 << kHistBits) | (uint32_t)sh_bin;
-      kneed -= sh_above;
-      uint32_t gt = 0, eq = 0;
-      for (uint32_t e = e0; e < e1; ++e) {
-        const uint32_t u = elem(e).x;
-        gt += u > T;
-        eq += u == T;
-      }
-      uint32_t tot;
-      uint32_t above = wg_exclusive_scan<kThreads>(gt, tmp, &tot);
-      uint32_t rank = wg_exclusive_scan<kThreads>(eq, tmp, &tot);
-      for (uint32_t e = e0; e < e1; ++e) {
-        const uint2 v = elem(e);
-        int slot = -1;
-        if (v.x > T) {
-          slot = (int)(above + (rank < kneed ? rank : kneed));
-          ++above;
-        } else if (v.x == T) {
-          if (rank < kneed) slot = (int)(above + rank);
-          ++rank;
+        auto score_of = [&](uint32_t i) -> uint32_t { return staged ? su[i] : cu[i]; };
+        wg_kth_largest<kThreads>(sel, [&](auto fn) {
+          for (uint32_t i = tid; i < nlist; i += kThreads) fn(score_of(i));
+        }, (uint32_t)keff, T, take_eq, n_eq);
+        uint32_t Pt = 0; // ties with (kPosMax - pos) >= Pt are kept
+        if (take_eq < n_eq) {
+          uint32_t t2, n2;
+          wg_kth_largest<kThreads>(sel, [&](auto fn) {
+            for (uint32_t i = tid; i < nlist; i += kThreads)
+              if (score_of(i) == T) fn(kPosMax - (uint32_t)cp[i]);
+          }, take_eq, Pt, t2, n2);
         }
-        if (slot >= 0) {
-          const int pos = (int)v.y;
-          R[base + slot] = row_of(bt, pos, num_blocks);
-          if (U) U[base + slot] = pos;
+        for (uint32_t i = tid; i < nlist; i += kThreads) {
+          const uint32_t u = score_of(i);
+          const int pos = cp[i];
+          if (u > T || (u == T && kPosMax - (uint32_t)pos >= Pt))
+            atomicOr(&bm[pos >> 5], 1u << (pos & 31));
         }
+      } else {
+        // ---- exact fallback: rescore every candidate key of the unit
+        const QueryOperand<KS> op = load_query_operand<KS, G>(
+            qop, qneg, unit, s, g, Hkv * G, lane);
+        const PoolView view = make_pool_view(codes, radii, code_bytes,
+                                             radius_bytes, W, Hkv, g, lane);
+        const int pc0 = c0 / kPage, pc1 = (c1 + kPage - 1) / kPage;
+        // fn(u, pos) for every candidate, lanes 0..15 of each wave
+        auto rescan = [&](auto fn) {
+          for (int p0 = pc0 + wave * 8; p0 < pc1; p0 += kWaves * 8) {
+            uint32_t cw[8][KS], r8[8];
+            bool ok[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              const int pg = p0 + u;
+              const int blk = pg < pc1 ? bt[pg] : -1;
+              ok[u] = blk >= 0 && blk < num_blocks;
+              load_page<KS>(view, blk, ok[u], cw[u], r8[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              const int S = score_page<KS, G>(op, cw[u], r8[u], ok[u]);
+              const int pos = (p0 + u) * kPage + lane;
+              if (lane < kPage && pos >= c0 && pos < c1)
+                fn((uint32_t)(S + (int)kScoreBias), pos);
+            }
+          }
+        };
+        wg_kth_largest<kThreads>(sel, [&](auto fn) {
+          rescan([&](uint32_t u, int) { fn(u); });
+        }, (uint32_t)keff, T, take_eq, n_eq);
+        uint32_t Pt = 0;
+        if (take_eq < n_eq) {
+          uint32_t t2, n2;
+          wg_kth_largest<kThreads>(sel, [&](auto fn) {
+            rescan([&](uint32_t u, int pos) {
+              if (u == T) fn(kPosMax - (uint32_t)pos);
+            });
+          }, take_eq, Pt, t2, n2);
+        }
+        rescan([&](uint32_t u, int pos) {
+          if (u > T || (u == T && kPosMax - (uint32_t)pos >= Pt))
+            atomicOr(&bm[pos >> 5], 1u << (pos & 31));
+        });
       }
     }
+    __syncthreads();
+    emit_bitmap<kThreads>(bm, nwords, bt, num_blocks, R + base,
+                          U ? U + base : nullptr, &sel.red[3][0]);
   }
   if (tid == 0) {
     cnt[unit] = total;
@@ -184,17 +188,37 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
 
 } // namespace
 
-hipError_t launch_merge(const DecodeDims &d, const uint2 *cand,
-                        const int32_t *cand_cnt, const int32_t *seq_lens,
-                        const int32_t *block_table, int32_t *rows,
-                        int32_t *cnt, int32_t *user_sel, int32_t *user_cnt,
+hipError_t launch_merge(const DecodeDims &d, const uint32_t *cand_u,
+                        const int32_t *cand_pos, const uint32_t *counter,
+                        const int32_t *seq_lens, const int32_t *block_table,
+                        uint32_t *bitmap, int32_t *rows, int32_t *cnt,
+                        int32_t *user_sel, int32_t *user_cnt,
+                        const uint32_t *codes, const uint8_t *radii,
+                        const uint32_t *qop, const float *qneg,
                         hipStream_t stream) {
-  if (d.nchunks > kMaxChunks) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(merge_kernel, dim3(d.B * d.Hkv), dim3(kThreads), 0,
-                     stream, cand, cand_cnt, d.nchunks, seq_lens, d.n_max,
-                     block_table, d.max_blocks, d.num_blocks, d.Hkv, d.k, d.w,
-                     d.sigma, d.cap, rows, cnt, user_sel, user_cnt);
-  return hipGetLastError();
+  const uint32_t code_bytes = (uint32_t)((uint64_t)d.num_blocks * d.Hkv * d.W * kPage * 4);
+  const uint32_t radius_bytes = (uint32_t)((uint64_t)d.num_blocks * d.Hkv * kPage);
+#define DKV_MERGE_CASE(KSV, GV)                                                \
+  if (d.KS == KSV && d.G == GV) {                                              \
+    hipLaunchKernelGGL((merge_kernel<KSV, GV>), dim3(d.B * d.Hkv),             \
+                       dim3(kThreads), 0, stream, cand_u, cand_pos, counter,   \
+                       d.cand_cap, seq_lens, d.n_max, block_table,             \
+                       d.max_blocks, d.num_blocks, d.Hkv, d.k, d.w, d.sigma,   \
+                       d.cap, bitmap, d.bm_words, rows, cnt, user_sel,         \
+                       user_cnt, codes, radii, code_bytes, radius_bytes, d.W,  \
+                       qop, qneg);                                             \
+    return hipGetLastError();                                                  \
+  }
+  DKV_MERGE_CASE(1, 1)
+  DKV_MERGE_CASE(1, 2)
+  DKV_MERGE_CASE(1, 4)
+  DKV_MERGE_CASE(1, 8)
+  DKV_MERGE_CASE(2, 1)
+  DKV_MERGE_CASE(2, 2)
+  DKV_MERGE_CASE(2, 4)
+  DKV_MERGE_CASE(2, 8)
+#undef DKV_MERGE_CASE
+  return hipErrorInvalidValue;
 }
 
 } // namespace dkv

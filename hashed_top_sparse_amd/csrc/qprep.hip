@@ -26,12 +26,27 @@
 //   result: lane L holds rows 4*(L/16)+i, i = 0..3, of column L%16.
 // The code word (4*ks + L/16) of key L%16 expands into nibble slots
 // p = 8m + e <-> bit j = 32*(4*ks + L/16) + 4e + m.
-#include "internal.h"
+//
+// Candidate threshold.  The same workgroup then scores a deterministic
+// sample of the (sequence, KV head)'s candidate pages -- every SP-th page
+// from the first candidate page, SP a power of two <= 32 chosen so the
+// sample holds at most 512 pages -- and sets L = the k_s-th largest sampled
+// biased score, k_s = ceil(2 * k_eff * n_sample / n_candidates), so about
+// 2*k_eff keys are expected to reach L.  The streaming pass keeps every key
+// with u >= L; the merge checks that at least k_eff did (then the exact
+// top-k is among them) and otherwise rescans exactly.  L = 0 keeps every
+// candidate (used when k_eff covers all of them or the sample is too small
+// to say more).
+#include "score_common.h"
+#include "select_common.h"
 
 namespace dkv {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
+constexpr int kMaxPairs = 4;      // G*b <= 8*256 = 4*512
+constexpr int kSamplePages = 512; // sample pages per (sequence, KV head)
+constexpr int kSampleKeys = kSamplePages * kPage;
 
 // e4m3 (bias 7) byte of a small integer v, |v| <= 60 with at most four
 // significant bits (exactly representable).
@@ -44,18 +59,29 @@ __device__ __forceinline__ uint32_t e4m3_of_int(int v) {
   return sign | ((uint32_t)(e + 7) << 3) | mant;
 }
 
-__global__ __launch_bounds__(kThreads) void qprep_kernel(
+template <int KS, int G>
+__global__ __launch_bounds__(kThreads) void prep_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ proj,
-    int8_t *__restrict__ q8, uint32_t *__restrict__ qop,
-    float *__restrict__ qneg, int Hq, int Hkv, int G, int b, int KS) {
+    const uint32_t *__restrict__ codes, const uint8_t *__restrict__ radii,
+    int64_t num_blocks, uint32_t code_bytes, uint32_t radius_bytes,
+    const int32_t *__restrict__ block_table, int max_blocks,
+    const int32_t *__restrict__ seq_lens, int n_max, int8_t *__restrict__ q8,
+    uint32_t *__restrict__ qop, float *__restrict__ qneg,
+    uint32_t *__restrict__ lthr, uint32_t *__restrict__ counter, int Hq,
+    int Hkv, int b, int W, int k, int w, int sigma) {
   const int unit = blockIdx.x;
   const int s = unit / Hkv;
   const int g = unit % Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __shared__ double sQ[8 * kHeadDim];
   __shared__ uint16_t sP[kHeadDim * 256];
   __shared__ int sq8[8 * 256];
+  __shared__ uint32_t sOp[2 * 512];
+  __shared__ uint32_t sSample[kSampleKeys];
   __shared__ double sMax[kThreads / 64];
   __shared__ int sSum[8];
+  __shared__ uint32_t sCount[kThreads / 64];
+  __shared__ SelectShared<kThreads> sel;
 
   const uint16_t *qg = q + ((int64_t)s * Hq + (int64_t)g * G) * kHeadDim;
   for (int i = threadIdx.x; i < G * kHeadDim; i += kThreads)
@@ -64,16 +90,18 @@ __global__ __launch_bounds__(kThreads) void qprep_kernel(
   if (threadIdx.x < 8) sSum[threadIdx.x] = 0;
   __syncthreads();
 
+  // p_hj in double precision, index order (one chain per (h, j) pair)
   const int npairs = G * b;
-  double p[8];
+  double p[kMaxPairs];
   double mloc = 0.0;
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
+  for (int r = 0; r < kMaxPairs; ++r) {
     const int idx = threadIdx.x + r * kThreads;
     p[r] = 0.0;
     if (idx < npairs) {
       const int h = idx / b, j = idx % b;
       double acc = 0.0;
+#pragma unroll 16
       for (int i = 0; i < kHeadDim; ++i)
         acc = fma(sQ[h * kHeadDim + i], (double)bf16_to_float(sP[i * b + j]), acc);
       p[r] = acc;
@@ -81,14 +109,14 @@ __global__ __launch_bounds__(kThreads) void qprep_kernel(
     }
   }
   for (int off = 32; off > 0; off >>= 1) mloc = fmax(mloc, __shfl_xor(mloc, off));
-  if ((threadIdx.x & 63) == 0) sMax[threadIdx.x >> 6] = mloc;
+  if (lane == 0) sMax[wave] = mloc;
   __syncthreads();
   double M = sMax[0];
   for (int i = 1; i < kThreads / 64; ++i) M = fmax(M, sMax[i]);
 
   int8_t *qo = q8 + ((int64_t)s * Hq + (int64_t)g * G) * b;
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
+  for (int r = 0; r < kMaxPairs; ++r) {
     const int idx = threadIdx.x + r * kThreads;
     if (idx < npairs) {
       int v = 0;
@@ -106,7 +134,7 @@ __global__ __launch_bounds__(kThreads) void qprep_kernel(
   if (threadIdx.x < G)
     qneg[(int64_t)s * Hq + (int64_t)g * G + threadIdx.x] = -(float)sSum[threadIdx.x];
 
-  // A operand dwords: [KS][64 lanes][8 dwords]
+  // matrix-core operand dwords: [KS][64 lanes][8 dwords]
   uint32_t *dst = qop + (int64_t)unit * KS * 64 * 8;
   for (int t = threadIdx.x; t < KS * 64 * 8; t += kThreads) {
     const int ks = t / 512, la = (t / 8) % 64, di = t % 8;
@@ -130,18 +158,120 @@ __global__ __launch_bounds__(kThreads) void qprep_kernel(
       }
     }
     dst[t] = word;
+    sOp[t] = word;
+  }
+  __syncthreads();
+
+  // ---- candidate threshold from a page sample
+  const int N = seq_len_clamped(seq_lens, s, n_max);
+  const int nc = max(0, N - w - sigma);
+  const int keff = min(k, nc);
+  // L = ~0 asks for no candidates (k_eff = 0, or every candidate is
+  // selected and the merge marks them directly)
+  uint32_t L = 0xFFFFFFFFu;
+  if (keff > 0 && keff < nc) {
+    L = 0;
+    const int pc0 = sigma / kPage, pc1 = (N - w + kPage - 1) / kPage;
+    const int ncp = pc1 - pc0;
+    int SP = 1;
+    while (SP < 32 && 2 * SP <= keff / 32) SP *= 2;
+    while ((ncp + SP - 1) / SP > kSamplePages) SP *= 2;
+    const int nsp = (ncp + SP - 1) / SP;
+    QueryOperand<KS> op;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) op.a[ks][i] = (int)sOp[(ks * 64 + lane) * 8 + i];
+    {
+      const int h0 = 2 * (lane >> 4), h1 = h0 + 1;
+      op.cinit = v4f{0.f, h0 < G ? -(float)sSum[h0 < G ? h0 : 0] : 0.f, 0.f,
+                     h1 < G ? -(float)sSum[h1 < G ? h1 : 0] : 0.f};
+    }
+    const PoolView view = make_pool_view(codes, radii, code_bytes, radius_bytes,
+                                         W, Hkv, g, lane);
+    const int32_t *bt = block_table + (int64_t)s * max_blocks;
+    uint32_t nvalid = 0;
+    // wave w samples pages t = w + 8*i; lane i holds the block id of its
+    // i-th page, and 8 pages' loads are in flight per step
+    constexpr int kWv = kThreads / 64;
+    const int tl = wave + kWv * lane;
+    const int blk_l = tl < nsp ? bt[pc0 + tl * SP] : -1;
+    for (int i0 = 0; wave + kWv * i0 < nsp; i0 += 8) {
+      uint32_t cw[8][KS], r8[8];
+      bool ok[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u;
+        const int blk = __builtin_amdgcn_readlane(blk_l, i & 63);
+        ok[u] = wave + kWv * i < nsp && blk >= 0 && blk < num_blocks;
+        load_page<KS>(view, blk, ok[u], cw[u], r8[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int t = wave + kWv * (i0 + u);
+        const int S = score_page<KS, G>(op, cw[u], r8[u], ok[u]);
+        if (lane < kPage && t < nsp) {
+          const int pos = (pc0 + t * SP) * kPage + lane;
+          const bool valid = pos >= sigma && pos < N - w;
+          sSample[t * kPage + lane] = valid ? (uint32_t)(S + (int)kScoreBias) : 0u;
+          nvalid += valid;
+        }
+      }
+    }
+    for (int off = 32; off > 0; off >>= 1) nvalid += __shfl_xor(nvalid, off);
+    if (lane == 0) sCount[wave] = nvalid;
+    __syncthreads();
+    uint32_t ns = 0;
+    for (int i = 0; i < kThreads / 64; ++i) ns += sCount[i];
+    const uint32_t ks_take = (uint32_t)min((int64_t)ns,
+        ((int64_t)2 * keff * ns + nc - 1) / nc);
+    if (ks_take > 0 && ks_take < ns) {
+      const int nkeys = nsp * kPage;
+      uint32_t T, take_eq, n_eq;
+      wg_kth_largest<kThreads>(sel, [&](auto fn) {
+        for (int i = threadIdx.x; i < nkeys; i += kThreads) {
+          const uint32_t v = sSample[i];
+          if (v != 0u) fn(v);
+        }
+      }, ks_take, T, take_eq, n_eq);
+      L = T;
+    }
+  }
+  if (threadIdx.x == 0) {
+    lthr[unit] = L;
+    counter[unit] = 0;
   }
 }
 
 } // namespace
 
-hipError_t launch_qprep(const DecodeDims &d, const uint16_t *q,
-                        const uint16_t *proj, int8_t *q8, uint32_t *qop,
-                        float *qneg, hipStream_t stream) {
-  hipLaunchKernelGGL(qprep_kernel, dim3(d.B * d.Hkv), dim3(kThreads), 0,
-                     stream, q, proj, q8, qop, qneg, d.Hq, d.Hkv, d.G, d.b,
-                     d.KS);
-  return hipGetLastError();
+hipError_t launch_prep(const DecodeDims &d, const uint16_t *q,
+                       const uint16_t *proj, const uint32_t *codes,
+                       const uint8_t *radii, const int32_t *block_table,
+                       const int32_t *seq_lens, int8_t *q8, uint32_t *qop,
+                       float *qneg, uint32_t *lthr, uint32_t *counter,
+                       hipStream_t stream) {
+  const uint32_t code_bytes = (uint32_t)((uint64_t)d.num_blocks * d.Hkv * d.W * kPage * 4);
+  const uint32_t radius_bytes = (uint32_t)((uint64_t)d.num_blocks * d.Hkv * kPage);
+#define DKV_PREP_CASE(KSV, GV)                                                 \
+  if (d.KS == KSV && d.G == GV) {                                              \
+    hipLaunchKernelGGL((prep_kernel<KSV, GV>), dim3(d.B * d.Hkv),              \
+                       dim3(kThreads), 0, stream, q, proj, codes, radii,       \
+                       d.num_blocks, code_bytes, radius_bytes, block_table,    \
+                       d.max_blocks, seq_lens, d.n_max, q8, qop, qneg, lthr,   \
+                       counter, d.Hq, d.Hkv, d.b, d.W, d.k, d.w, d.sigma);     \
+    return hipGetLastError();                                                  \
+  }
+  DKV_PREP_CASE(1, 1)
+  DKV_PREP_CASE(1, 2)
+  DKV_PREP_CASE(1, 4)
+  DKV_PREP_CASE(1, 8)
+  DKV_PREP_CASE(2, 1)
+  DKV_PREP_CASE(2, 2)
+  DKV_PREP_CASE(2, 4)
+  DKV_PREP_CASE(2, 8)
+#undef DKV_PREP_CASE
+  return hipErrorInvalidValue;
 }
 
 } // namespace dkv

@@ -1,251 +1,173 @@
-// score.hip -- code-domain score of every cached key, with an exact
-// chunk-local top-k so that only candidates leave the chip.
+// score.hip -- code-domain score of every cached key in one streaming pass;
+// keys reaching the (sequence, KV head)'s candidate threshold L leave the
+// chip as (biased score, position) candidates.
 //
-// [SPHERICAL KV, §2.1]: logits come straight from the stored radius and the
-// packed angle code; no dense key is rebuilt.  [DeepSeek, "starting from
-// DSA"]: a light indexer scores every cached key against the query.
-//   s_h = sum_j q8_hj * (bit_j ? +1 : -1)  for the G heads of a KV group,
-//   S   = r8 * max_h s_h                    (exact integer, |S| < 2^23).
+// [SPHERICAL KV, §2.1]: the logit comes straight from the stored radius and
+// the packed angle code, no dense key rebuilt; [DeepSeek, "starting from
+// DSA"]: a light indexer scores every cached key.  The per-page scoring is
+// in score_common.h (one fp8 x fp4 matrix-core op per 128 code bits).
 //
-// Work: one workgroup per (sequence, KV head, chunk of 512 pages = 8192
-// keys).  Each wave streams 64-page groups: one coalesced 256 B (b = 128)
-// code load per page (lane L reads dword L of the page's code block, which
-// is word L/16 of the key in slot L%16), the page's 16 radius bytes, and one
-// 16x16x128 fp8 x fp4 matrix-core op per 128 code bits:
-//   - the code word is expanded to fp4 with 5 bit operations: nibble values
-//     0.5/1/2/0.5 for bits j = 4e+m, m = 0..3 (masks 0x1.., 0x2.., 0x4..,
-//     and (w >> 3) & 0x1..);
-//   - the query operand (qprep.hip) holds 2*hi/f_m and 2*lo/f_m per head,
-//     so the result rows give 2*D_hi and 2*D_lo - Q exactly (the
-//     accumulator starts at -Q in the low rows);
-//   - s_h = 16*row(2h) + row(2h+1); max over the group's heads with one or
-//     two lane swaps; S = r8 * max in fp32 (exact below 2^24).
-// Biased scores u = S + 2^23 of the chunk stay in LDS.
-//
-// Chunk top-k ([DASH-KV Top-K pruning]): the global top-k of a (sequence,
-// KV head) is contained in the union of the chunks' top-k, so each chunk
-// keeps only min(k, #candidates) candidates of [sinks, N - window), chosen
-// exactly by (u desc, position asc): two 12-bit radix histogram passes in
-// LDS find the threshold score T and the number of ties at T to keep; a
-// workgroup scan then writes the survivors in position order.
-//
-// Workgroup order is XCD-aware: the Hkv workgroups of one (sequence, chunk)
-// get ids congruent mod 8 (same XCD, so the page's shared radius line and
-// block-table entries are served by one L2) and consecutive in dispatch.
-#include "internal.h"
+// Work: one wave per (sequence, 64-page group, KV head); the 8 waves of a
+// workgroup are consecutive KV heads of the same pages (for Hkv = 8: all of
+// them), so a page's radius line and block-table entries are shared in one
+// CU.  Each wave streams its 64 pages straight-line with two 8-page batches
+// of buffer loads in flight, scores them four pages at a time (the four
+// pages' results are gathered into one register, page j in lanes
+// 16j..16j+15, so the epilogue and the radius load run once for 64 keys),
+// keeps the 1024 biased scores in its own LDS
+// slice, then appends the candidates (positions in [sinks, N - window) with
+// u >= L) to the (sequence, KV head)'s list with one atomic add: ballots
+// give each lane its place, in position order within the wave.  The list
+// holds at most `cap` entries; the counter still counts every candidate, so
+// an overflow is visible to the merge, which then rescans exactly.
+#include "score_common.h"
 
 namespace dkv {
 namespace {
 
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
-constexpr uint32_t kBias = 1u << 23;
-constexpr int kHistBits = 12;
-constexpr int kHistBins = 1 << kHistBits;
-constexpr int kUnroll = 8; // pages in flight per wave
+constexpr int kGroupPages = 64;
+constexpr int kBatch = 8; // pages per load batch (two batches in flight)
 
-__device__ __forceinline__ v8i expand_code_word(uint32_t w) {
-  v8i r;
-  r[0] = (int)(w & 0x11111111u);
-  r[1] = (int)(w & 0x22222222u);
-  r[2] = (int)(w & 0x44444444u);
-  r[3] = (int)((w >> 3) & 0x11111111u);
-  r[4] = r[5] = r[6] = r[7] = 0;
-  return r;
-}
-
-// Finds, scanning bins from the top, the bin where the running count
-// reaches kneed: count(bins above) < kneed <= count(bins above) + bin.
-// Results land in *out_bin / *out_above (LDS); ends with a barrier.
-__device__ void find_threshold_bin(const uint32_t *hist, uint32_t kneed,
-                                   uint32_t *tmp, int *out_bin,
-                                   uint32_t *out_above) {
-  constexpr int kPer = kHistBins / kThreads;
-  const int top = kHistBins - 1 - kPer * threadIdx.x;
-  uint32_t local = 0;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) local += hist[top - i];
-  uint32_t total;
-  const uint32_t above = wg_exclusive_scan<kThreads>(local, tmp, &total);
-  if (above < kneed && kneed <= above + local) {
-    uint32_t run = above;
-    for (int i = 0; i < kPer; ++i) {
-      const uint32_t c = hist[top - i];
-      if (run + c >= kneed) {
-        *out_bin = top - i;
-        *out_above = run;
-        break;
-      }
-      run += c;
-    }
-  }
-  __syncthreads();
-}
+template <int KS>
+struct PageBatch {
+  uint32_t cw[2][4][KS]; // two quads of pages
+  uint32_t r8[2];        // radius of key (lane & 15) of page (lane >> 4)
+};
 
 template <int KS, int G>
-__global__ __launch_bounds__(kThreads) void score_chunk_kernel(
+__global__ __launch_bounds__(kThreads) void filter_kernel(
     const uint32_t *__restrict__ codes, const uint8_t *__restrict__ radii,
-    int64_t num_blocks, const int32_t *__restrict__ block_table,
-    int max_blocks, const int32_t *__restrict__ seq_lens, int n_max,
-    const uint32_t *__restrict__ qop, const float *__restrict__ qneg, int B,
-    int Hkv, int W, int nchunks, int k, int w, int sigma,
-    uint2 *__restrict__ cand, int32_t *__restrict__ cand_cnt,
+    int64_t num_blocks, uint32_t code_bytes, uint32_t radius_bytes,
+    const int32_t *__restrict__ block_table, int max_blocks,
+    const int32_t *__restrict__ seq_lens, int n_max,
+    const uint32_t *__restrict__ qop, const float *__restrict__ qneg,
+    const uint32_t *__restrict__ lthr, int B, int Hkv, int W, int ngroups,
+    int w, int sigma, uint32_t *__restrict__ counter,
+    uint32_t *__restrict__ cand_u, int32_t *__restrict__ cand_pos, int cap,
     int32_t *__restrict__ scores_out, int score_stride) {
-  __shared__ uint32_t su[kChunkKeys];
-  __shared__ uint32_t hist[kHistBins];
-  __shared__ uint32_t tmp[kWaves];
-  __shared__ int sh_bin;
-  __shared__ uint32_t sh_above;
-
-  // XCD-aware decode of the workgroup id.
-  const int wid = blockIdx.x;
-  const int xcd = wid & 7, j = wid >> 3;
-  const int sc = (j / Hkv) * 8 + xcd;
-  const int g = j % Hkv;
-  if (sc >= B * nchunks) return;
-  const int s = sc / nchunks, c = sc % nchunks;
-  const int unit = s * Hkv + g;
+  __shared__ uint32_t su[kWaves][kGroupPages * kPage];
+  const int lane = threadIdx.x & 63;
+  // wave-uniform (keeps the page offsets below in scalar registers)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t task = (int64_t)blockIdx.x * kWaves + wave;
+  const int g = (int)(task % Hkv);
+  const int64_t sg = task / Hkv;
+  const int grp = (int)(sg % ngroups);
+  const int s = (int)(sg / ngroups);
+  if (s >= B) return;
   const int N = seq_len_clamped(seq_lens, s, n_max);
   const int npages = (N + kPage - 1) / kPage;
-  const int p_begin = c * kChunkPages;
-  if (p_begin >= npages) return; // this chunk does not exist for s
-  const int p_end = min(npages, p_begin + kChunkPages);
-  const int key0 = p_begin * kPage;
-  const int key_end = min(N, p_end * kPage);
-  const int lo = max(sigma, key0), hi = min(N - w, key_end);
-  const int ncand = max(0, hi - lo);
-  const bool want_scores = scores_out != nullptr;
-  int32_t *cnt_out = cand_cnt + (int64_t)unit * nchunks + c;
-  if (ncand == 0 && !want_scores) {
-    if (threadIdx.x == 0) *cnt_out = 0;
-    return;
-  }
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int pg0 = grp * kGroupPages;
+  if (pg0 >= npages) return;
+  const int npg = min(kGroupPages, npages - pg0);
+  const int key0 = pg0 * kPage;
+  const int lo = max(sigma, key0), hi = min(N - w, key0 + npg * kPage);
+  if (hi <= lo && scores_out == nullptr) return; // no candidates in this group
+  const int unit = s * Hkv + g;
   const int Hq = Hkv * G;
-  v8i aop[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const uint4 *src = reinterpret_cast<const uint4 *>(
-        qop + (((int64_t)unit * KS + ks) * 64 + lane) * 8);
-    const uint4 x0 = src[0], x1 = src[1];
-    aop[ks][0] = (int)x0.x; aop[ks][1] = (int)x0.y;
-    aop[ks][2] = (int)x0.z; aop[ks][3] = (int)x0.w;
-    aop[ks][4] = (int)x1.x; aop[ks][5] = (int)x1.y;
-    aop[ks][6] = (int)x1.z; aop[ks][7] = (int)x1.w;
-  }
-  v4f cinit = {0.f, 0.f, 0.f, 0.f};
-  {
-    const int h0 = 2 * (lane >> 4), h1 = h0 + 1;
-    const float *qn = qneg + (int64_t)s * Hq + (int64_t)g * G;
-    if (h0 < G) cinit[1] = qn[h0];
-    if (h1 < G) cinit[3] = qn[h1];
-  }
 
-  const int32_t *bt = block_table + (int64_t)s * max_blocks;
-  const int code_dwords = W * kPage; // per (page, head)
-  for (int pg0 = p_begin + wave * 64; pg0 < p_end; pg0 += kWaves * 64) {
-    const int npg = min(64, p_end - pg0);
-    const int my_blk = lane < npg ? bt[pg0 + lane] : -1;
-    for (int jb = 0; jb < npg; jb += kUnroll) {
-      uint32_t cw[kUnroll][KS];
-      uint32_t r8[kUnroll];
+  const QueryOperand<KS> op = load_query_operand<KS, G>(qop, qneg, unit, s, g, Hq, lane);
+  const uint32_t L = lthr[unit];
+  const PoolView view = make_pool_view(codes, radii, code_bytes, radius_bytes, W,
+                                       Hkv, g, lane);
+  // Lane j holds page pg0 + j's byte offsets: its code block, and its radius
+  // line (past the end of the radius buffer for an invalid page or one past
+  // the sequence, so its radius loads as 0 and its score is 0).  Invalid
+  // pages read the code block of physical page 0; it is multiplied by 0.
+  uint32_t my_code_off = 0, my_rad_off = 0x80000000u;
+  {
+    const int blk = lane < npg ? block_table[(int64_t)s * max_blocks + pg0 + lane] : -1;
+    if (blk >= 0 && blk < num_blocks) {
+      const uint32_t ph = (uint32_t)blk * (uint32_t)Hkv + (uint32_t)g;
+      my_code_off = ph * view.page_code_bytes;
+      my_rad_off = ph * (uint32_t)kPage;
+    }
+  }
+  // ds_bpermute byte address of lane (quad page of this lane) + 4 * quad
+  const int rad_src = (lane >> 4) * 4;
+  uint32_t *mys = su[wave];
+
+  auto load_batch = [&](int jb, PageBatch<KS> &pb) {
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int jj = jb + u;
-        const int blk = __builtin_amdgcn_readlane(my_blk, jj < 64 ? jj : 63);
-        const bool ok = jj < npg && blk >= 0 && blk < num_blocks;
-        const int64_t base = ((int64_t)(ok ? blk : 0) * Hkv + g);
-        const uint32_t *cp = codes + base * code_dwords;
+    for (int q4 = 0; q4 < 2; ++q4) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int dw = 64 * ks + lane;
-          cw[u][ks] = (ok && dw < code_dwords) ? cp[dw] : 0u;
-        }
-        r8[u] = (ok && lane < kPage) ? (uint32_t)radii[base * kPage + lane] : 0u;
-      }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int jj = jb + u;
-        if (jj >= npg) break;
-        v4f acc = cinit;
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t soff = __builtin_amdgcn_readlane(my_code_off, jb + 4 * q4 + j);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              aop[ks], expand_code_word(cw[u][ks]), acc, 0, 4, 0, 127, 0, 127);
-        const float s0 = 16.f * acc[0] + acc[1];
-        float m = s0;
-        if (G >= 2) m = fmaxf(s0, 16.f * acc[2] + acc[3]);
-        if (G >= 4) m = fmaxf(m, __shfl_xor(m, 16));
-        if (G >= 8) m = fmaxf(m, __shfl_xor(m, 32));
-        const float S = (float)r8[u] * m;
-        if (lane < kPage) {
-          const int idx = (pg0 + jj - p_begin) * kPage + lane;
-          const int Si = (int)S;
-          su[idx] = (uint32_t)(Si + (int)kBias);
-          if (want_scores && key0 + idx < N)
-            scores_out[(int64_t)unit * score_stride + key0 + idx] = Si;
-        }
+          pb.cw[q4][j][ks] = __builtin_amdgcn_raw_buffer_load_b32(
+              view.code, view.code_voff + 256 * ks, soff, 0);
       }
+      // one radius byte per lane: key (lane & 15) of page (lane >> 4)
+      const uint32_t roff = (uint32_t)__builtin_amdgcn_ds_bpermute(
+          rad_src + 4 * (jb + 4 * q4), (int)my_rad_off);
+      pb.r8[q4] = __builtin_amdgcn_raw_buffer_load_b8(
+          view.radius, (int)(roff + (uint32_t)view.radius_voff), 0, 0);
+    }
+  };
+  auto score_batch = [&](int jb, const PageBatch<KS> &pb) {
+#pragma unroll
+    for (int q4 = 0; q4 < 2; ++q4) {
+      const int m = score_quad_max<KS, G>(op, pb.cw[q4]);
+      mys[(jb + 4 * q4) * kPage + lane] =
+          (uint32_t)(__mul24((int)pb.r8[q4], m) + (int)kScoreBias);
+    }
+  };
+  // Straight-line over the group's 64 pages (pages past npg score 0 and are
+  // ignored), so the wait counters stay exact and one batch's loads are in
+  // flight while the other batch is scored.
+  {
+    PageBatch<KS> pa, pb;
+    load_batch(0, pa);
+#pragma unroll
+    for (int jb = 0; jb < kGroupPages; jb += 2 * kBatch) {
+      load_batch(jb + kBatch, pb);
+      score_batch(jb, pa);
+      if (jb + 2 * kBatch < kGroupPages) load_batch(jb + 2 * kBatch, pa);
+      score_batch(jb + kBatch, pb);
     }
   }
-  __syncthreads();
+  // the wave's own LDS writes must be visible to all its lanes
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (scores_out != nullptr) {
+    int32_t *so = scores_out + (int64_t)unit * score_stride;
+    for (int e = lane; e < npg * kPage && key0 + e < N; e += 64)
+      so[key0 + e] = (int32_t)(mys[e] - kScoreBias);
+  }
+  if (hi <= lo) return;
 
-  // ---- exact top-k of the chunk's candidates [lo, hi)
-  const int klo = lo - key0, khi = hi - key0;
-  const int kc = min(k, ncand);
-  uint2 *out = cand + ((int64_t)unit * nchunks + c) * (int64_t)k;
-  if (kc == ncand) {
-    for (int i = threadIdx.x; i < ncand; i += kThreads)
-      out[i] = make_uint2(su[klo + i], (uint32_t)(key0 + klo + i));
-  } else if (kc > 0) {
-    for (int i = threadIdx.x; i < kHistBins; i += kThreads) hist[i] = 0;
-    __syncthreads();
-    for (int i = klo + threadIdx.x; i < khi; i += kThreads)
-      atomicAdd(&hist[su[i] >> kHistBits], 1u);
-    __syncthreads();
-    find_threshold_bin(hist, (uint32_t)kc, tmp, &sh_bin, &sh_above);
-    const uint32_t b1 = (uint32_t)sh_bin;
-    uint32_t kneed = (uint32_t)kc - sh_above;
-    for (int i = threadIdx.x; i < kHistBins; i += kThreads) hist[i] = 0;
-    __syncthreads();
-    for (int i = klo + threadIdx.x; i < khi; i += kThreads) {
-      const uint32_t u = su[i];
-      if ((u >> kHistBits) == b1) atomicAdd(&hist[u & (kHistBins - 1)], 1u);
-    }
-    __syncthreads();
-    find_threshold_bin(hist, kneed, tmp, &sh_bin, &sh_above);
-    const uint32_t T = (b1 << kHistBits) | (uint32_t)sh_bin;
-    kneed -= sh_above;
-    // position-ordered compaction over contiguous per-thread ranges
-    const int per = (ncand + kThreads - 1) / kThreads;
-    const int i0 = min(khi, klo + (int)threadIdx.x * per);
-    const int i1 = min(khi, i0 + per);
-    uint32_t gt = 0, eq = 0;
-    for (int i = i0; i < i1; ++i) {
-      const uint32_t u = su[i];
-      gt += u > T;
-      eq += u == T;
-    }
-    uint32_t tot;
-    uint32_t above = wg_exclusive_scan<kThreads>(gt, tmp, &tot);
-    uint32_t rank = wg_exclusive_scan<kThreads>(eq, tmp, &tot);
-    for (int i = i0; i < i1; ++i) {
-      const uint32_t u = su[i];
-      if (u > T) {
-        const uint32_t taken = rank < kneed ? rank : kneed;
-        out[above + taken] = make_uint2(u, (uint32_t)(key0 + i));
-        ++above;
-      } else if (u == T) {
-        if (rank < kneed) out[above + rank] = make_uint2(u, (uint32_t)(key0 + i));
-        ++rank;
-      }
-    }
+  // candidates of this group: positions in [lo, hi) with u >= L
+  constexpr int kRows = kGroupPages * kPage / 64;
+  uint32_t total = 0;
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    const int pos = key0 + r * 64 + lane;
+    const bool cand = pos >= lo && pos < hi && mys[r * 64 + lane] >= L;
+    total += __popcll(__ballot(cand));
   }
-  if (threadIdx.x == 0) *cnt_out = kc;
+  if (total == 0) return;
+  uint32_t base = 0;
+  if (lane == 0) base = atomicAdd(&counter[unit], total);
+  base = __builtin_amdgcn_readfirstlane(base);
+  uint32_t *ou = cand_u + (int64_t)unit * cap;
+  int32_t *op_ = cand_pos + (int64_t)unit * cap;
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    const int pos = key0 + r * 64 + lane;
+    const uint32_t u = mys[r * 64 + lane];
+    const bool cand = pos >= lo && pos < hi && u >= L;
+    const uint64_t m = __ballot(cand);
+    const uint32_t slot = base + lanes_below(m);
+    if (cand && slot < (uint32_t)cap) {
+      ou[slot] = u;
+      op_[slot] = pos;
+    }
+    base += __popcll(m);
+  }
 }
 
 } // namespace
@@ -253,21 +175,25 @@ __global__ __launch_bounds__(kThreads) void score_chunk_kernel(
 hipError_t launch_score(const DecodeDims &d, const uint32_t *codes,
                         const uint8_t *radii, const int32_t *block_table,
                         const int32_t *seq_lens, const uint32_t *qop,
-                        const float *qneg, uint2 *cand, int32_t *cand_cnt,
+                        const float *qneg, const uint32_t *lthr,
+                        uint32_t *counter, uint32_t *cand_u, int32_t *cand_pos,
                         int32_t *scores_out, hipStream_t stream) {
-  if (d.nchunks == 0) return hipSuccess;
-  const int64_t sc = (int64_t)d.B * d.nchunks;
-  const int64_t groups = (sc + 7) / 8;
-  const int64_t nwg = groups * 8 * d.Hkv;
+  const int pages = (d.n_max + kPage - 1) / kPage;
+  const int ngroups = (pages + kGroupPages - 1) / kGroupPages;
+  if (ngroups == 0) return hipSuccess;
+  const uint32_t code_bytes = (uint32_t)((uint64_t)d.num_blocks * d.Hkv * d.W * kPage * 4);
+  const uint32_t radius_bytes = (uint32_t)((uint64_t)d.num_blocks * d.Hkv * kPage);
+  const int64_t tasks = (int64_t)d.B * ngroups * d.Hkv;
+  const int64_t nwg = (tasks + kWaves - 1) / kWaves;
   if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
-  dim3 grid((unsigned)nwg);
 #define DKV_SCORE_CASE(KSV, GV)                                                \
   if (d.KS == KSV && d.G == GV) {                                              \
-    hipLaunchKernelGGL((score_chunk_kernel<KSV, GV>), grid, dim3(kThreads), 0, \
-                       stream, codes, radii, d.num_blocks, block_table,        \
-                       d.max_blocks, seq_lens, d.n_max, qop, qneg, d.B, d.Hkv, \
-                       d.W, d.nchunks, d.k, d.w, d.sigma, cand, cand_cnt,      \
-                       scores_out, d.max_seq_len);                             \
+    hipLaunchKernelGGL((filter_kernel<KSV, GV>), dim3((unsigned)nwg),          \
+                       dim3(kThreads), 0, stream, codes, radii, d.num_blocks,  \
+                       code_bytes, radius_bytes, block_table, d.max_blocks,    \
+                       seq_lens, d.n_max, qop, qneg, lthr, d.B, d.Hkv, d.W,    \
+                       ngroups, d.w, d.sigma, counter, cand_u, cand_pos,       \
+                       d.cand_cap, scores_out, d.max_seq_len);                 \
     return hipGetLastError();                                                  \
   }
   DKV_SCORE_CASE(1, 1)

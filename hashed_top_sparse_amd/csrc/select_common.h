@@ -1,0 +1,137 @@
+// select_common.h -- exact k-th largest over a workgroup's elements, and the
+// position-ordered list built from a selection bitmap.
+//
+// Selection order ([DASH-KV Top-K pruning]; ties to the lowest position):
+// values are biased scores u = S + 2^23 (or, for tie-breaking, inverted
+// positions); the k-th largest value T and the number of elements equal to
+// T to take are found with two histogram passes over 4096 bins: the first
+// over (u - min) >> shift, with the shift chosen so the elements' range
+// fits the bins, the second over the low bits inside the threshold bin.
+#pragma once
+
+#include "internal.h"
+
+namespace dkv {
+
+constexpr int kHistBits = 12;
+constexpr int kHistBins = 1 << kHistBits;
+
+template <int NT>
+struct SelectShared {
+  uint32_t hist[kHistBins];
+  uint32_t red[4][NT / 64];
+  int bin;
+  uint32_t above;
+};
+
+// Scanning bins from the top, finds the bin where the running count reaches
+// kneed: count(bins above) < kneed <= count(bins above) + bin.  Every
+// thread must call it; ends with a barrier.
+template <int NT>
+__device__ void find_threshold_bin(SelectShared<NT> &sh, uint32_t kneed) {
+  constexpr int kPer = kHistBins / NT;
+  const int top = kHistBins - 1 - kPer * (int)threadIdx.x;
+  uint32_t local = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) local += sh.hist[top - i];
+  uint32_t total;
+  const uint32_t above = wg_exclusive_scan<NT>(local, &sh.red[3][0], &total);
+  if (above < kneed && kneed <= above + local) {
+    uint32_t run = above;
+    for (int i = 0; i < kPer; ++i) {
+      const uint32_t c = sh.hist[top - i];
+      if (run + c >= kneed) {
+        sh.bin = top - i;
+        sh.above = run;
+        break;
+      }
+      run += c;
+    }
+  }
+  __syncthreads();
+}
+
+// Exact kneed-th largest value (1 <= kneed <= element count) of the
+// elements that visit(fn) hands to fn(uint32_t) -- each element exactly
+// once across the workgroup.  Returns T, the number of elements equal to T
+// (n_eq) and how many of those complete the top kneed (take_eq, >= 1).
+// Every thread must call it (barriers inside).
+template <int NT, class Visit>
+__device__ void wg_kth_largest(SelectShared<NT> &sh, Visit visit, uint32_t kneed,
+                               uint32_t &T, uint32_t &take_eq, uint32_t &n_eq) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t vmin = 0xFFFFFFFFu, vmax = 0u;
+  visit([&](uint32_t v) {
+    vmin = min(vmin, v);
+    vmax = max(vmax, v);
+  });
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    vmin = min(vmin, (uint32_t)__shfl_xor((int)vmin, off));
+    vmax = max(vmax, (uint32_t)__shfl_xor((int)vmax, off));
+  }
+  if (lane == 0) {
+    sh.red[0][wave] = vmin;
+    sh.red[1][wave] = vmax;
+  }
+  for (int i = threadIdx.x; i < kHistBins; i += NT) sh.hist[i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    vmin = min(vmin, sh.red[0][i]);
+    vmax = max(vmax, sh.red[1][i]);
+  }
+  const uint32_t range = vmax - vmin;
+  const int bits = range == 0 ? 0 : 32 - __clz(range);
+  const int shift = bits > kHistBits ? bits - kHistBits : 0;
+  visit([&](uint32_t v) { atomicAdd(&sh.hist[(v - vmin) >> shift], 1u); });
+  __syncthreads();
+  find_threshold_bin<NT>(sh, kneed);
+  const uint32_t b1 = (uint32_t)sh.bin;
+  const uint32_t kneed2 = kneed - sh.above;
+  __syncthreads();
+  for (int i = threadIdx.x; i < kHistBins; i += NT) sh.hist[i] = 0;
+  __syncthreads();
+  const uint32_t low_mask = (1u << shift) - 1u;
+  visit([&](uint32_t v) {
+    const uint32_t d = v - vmin;
+    if ((d >> shift) == b1) atomicAdd(&sh.hist[d & low_mask], 1u);
+  });
+  __syncthreads();
+  find_threshold_bin<NT>(sh, kneed2);
+  T = vmin + (b1 << shift) + (uint32_t)sh.bin;
+  take_eq = kneed2 - sh.above;
+  n_eq = sh.hist[sh.bin];
+  __syncthreads();
+}
+
+// Writes the positions of the set bits of bitmap[0, nwords) (bit p = word
+// p/32, bit p%32) in ascending order to pos_out[0..] / row_out[0..] (row =
+// page*16 + slot through the block table, -1 for an invalid page).  Every
+// thread must call it.
+template <int NT>
+__device__ void emit_bitmap(const uint32_t *bitmap, int nwords, const int32_t *bt,
+                            int64_t num_blocks, int32_t *row_out,
+                            int32_t *pos_out, uint32_t *tmp) {
+  const int per = (nwords + NT - 1) / NT;
+  const int w0 = min(nwords, (int)threadIdx.x * per);
+  const int w1 = min(nwords, w0 + per);
+  uint32_t c = 0;
+  for (int i = w0; i < w1; ++i) c += __popc(bitmap[i]);
+  uint32_t total;
+  uint32_t o = wg_exclusive_scan<NT>(c, tmp, &total);
+  for (int i = w0; i < w1; ++i) {
+    uint32_t m = bitmap[i];
+    while (m) {
+      const int bitp = __ffs(m) - 1;
+      m &= m - 1;
+      const int pos = i * 32 + bitp;
+      const int blk = bt[pos / kPage];
+      row_out[o] = (blk >= 0 && blk < num_blocks) ? blk * kPage + pos % kPage : -1;
+      if (pos_out) pos_out[o] = pos;
+      ++o;
+    }
+  }
+}
+
+} // namespace dkv

@@ -120,3 +120,44 @@ def test_full_size_workloads(name):
         assert recalls and all(r == 1.0 for r in recalls)
     print(name, "max abs err", max(st["max_abs"] for st in stats))
     torch.cuda.empty_cache()
+
+
+def _sample_stride(keff: int) -> int:
+    """The page-sample stride the threshold pass uses for k_eff (largest
+    power of two <= 32 with 2*SP <= k_eff/32, at least 1)."""
+    sp = 1
+    while sp < 32 and 2 * sp <= keff // 32:
+        sp *= 2
+    return sp
+
+
+def _scale_pages(inp, wl, pred, factor):
+    bt = inp["block_table"].cpu().numpy()
+    lens = inp["seq_lens"].cpu().numpy()
+    for s in range(wl.batch):
+        npg = (int(lens[s]) + 15) // 16
+        pages = [p for p in range(npg) if pred(p)]
+        blocks = torch.as_tensor(bt[s, pages].astype(np.int64), device=DEV)
+        inp["k_pool"][blocks] = (inp["k_pool"][blocks].float() * factor).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("factor", [4.0, 0.125])
+def test_threshold_fallback_stays_exact(factor):
+    """Keys on the sampled pages scaled up (the sampled threshold lets too
+    few keys through: underflow) or down (far too many: overflow).  Either
+    way the merge must rescan and stay exact."""
+    import dataclasses
+    base = workloads.get("small_gqa_b128")
+    # long enough that the overflow case exceeds the candidate list room
+    wl = dataclasses.replace(base, name="adversarial", batch=1, seq_len=40000,
+                             needles=0)
+    print(f"[case] adversarial factor={factor}", flush=True)
+    cfg = config_of(wl)
+    inp = workloads.make_inputs(wl, DEV)
+    keff = min(wl.top_k, wl.seq_len - wl.window - wl.sinks)
+    sp = _sample_stride(keff)
+    _scale_pages(inp, wl, lambda p: p % sp == 0, factor)
+    codes, radii = gpu_encode_all(cfg, inp)
+    gpu = gpu_decode(cfg, inp, codes, radii, debug=True)
+    for g in range(wl.num_kv_heads):
+        check_unit(cfg, inp, gpu, codes, radii, 0, g)
