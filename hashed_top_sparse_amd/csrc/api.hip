@@ -156,6 +156,20 @@ dkv_status decode_impl(const dkv_config *cfg, const void *q,
 
 } // namespace
 
+int device_cu_count() {
+  static int cached[64] = {0}; // per device id; a racing first call stores the same value
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
+          hipSuccess ||
+      n <= 0)
+    n = 256;
+  if (dev < 64) cached[dev] = n;
+  return n;
+}
+
 WorkspacePlan plan_workspace(const DecodeDims &d) {
   WorkspacePlan p;
   const size_t units = (size_t)d.B * d.Hkv;

@@ -36,6 +36,9 @@ struct WorkspacePlan {
 
 WorkspacePlan plan_workspace(const DecodeDims &d);
 
+// Compute units of the current device (cached per device id).
+int device_cu_count();
+
 // Kernel launchers (one per translation unit that owns the kernel).
 hipError_t launch_encode(const uint16_t *k_pool, int64_t num_blocks,
                          const int32_t *block_table, int max_blocks, int batch,

@@ -7,33 +7,108 @@
 // DSA"]: a light indexer scores every cached key.  The per-page scoring is
 // in score_common.h (one fp8 x fp4 matrix-core op per 128 code bits).
 //
-// Work: one wave per (sequence, 64-page group, KV head); the 8 waves of a
-// workgroup are consecutive KV heads of the same pages (for Hkv = 8: all of
-// them), so a page's radius line and block-table entries are shared in one
-// CU.  Each wave streams its 64 pages straight-line with two 8-page batches
-// of buffer loads in flight, scores them four pages at a time (the four
-// pages' results are gathered into one register, page j in lanes
-// 16j..16j+15, so the epilogue and the radius load run once for 64 keys),
-// keeps the 1024 biased scores in its own LDS
-// slice, then appends the candidates (positions in [sinks, N - window) with
-// u >= L) to the (sequence, KV head)'s list with one atomic add: ballots
-// give each lane its place, in position order within the wave.  The list
-// holds at most `cap` entries; the counter still counts every candidate, so
-// an overflow is visible to the merge, which then rescans exactly.
+// Work: persistent waves (4 per workgroup, 2 workgroups per CU), each
+// streaming a static stride of 64-page tasks (sequence, page group, KV
+// head); task ids run KV head fastest, then sequence, then page group, so
+// the waves working at any one time spread over every (sequence, KV head)
+// counter, and the heads of one page block are read together.  The code
+// pages of a wave, and their radius lines, go to a 17 KB ring in LDS by
+// direct buffer-to-LDS loads issued a full ring ahead (about 60 loads,
+// 15 KB, in flight per wave).  Each page quad is scored from the
+// ring (four matrix-core ops, results gathered into one register: page j
+// in lanes 16j..16j+15) and the ring slot is refilled at once with the
+// page one ring further on (the next task's pages once the current task's
+// are all issued).  The 1024 biased scores of a task stay in 16 registers;
+// its candidates (positions in [sinks, N - window) with u >= L) are
+// counted by ballots and reserved with one atomic add on the (sequence,
+// KV head) counter, and written out one task later, so the atomic's round
+// trip overlaps the next task's stream.  The list holds at most `cap`
+// entries; the counter still counts every candidate, so an overflow is
+// visible to the merge, which then rescans exactly.
+#include <algorithm>
+#include <type_traits>
+
 #include "score_common.h"
 
 namespace dkv {
 namespace {
 
-constexpr int kThreads = 512;
+constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kGroupPages = 64;
-constexpr int kBatch = 8; // pages per load batch (two batches in flight)
+constexpr int kGroupPages = 64;              // pages per task
+constexpr int kTaskQuads = kGroupPages / 4;  // page quads per task
+constexpr int kRingDwords = 4096;            // 16 KB code ring per wave
+constexpr int kRadRingDwords = 256;          // radius lines of up to 16 quads
+constexpr uint32_t kRadiusOob = 0x80000000u; // past any radius buffer
 
-template <int KS>
-struct PageBatch {
-  uint32_t cw[2][4][KS]; // two quads of pages
-  uint32_t r8[2];        // radius of key (lane & 15) of page (lane >> 4)
+// Buffer-to-LDS loads are invisible to the compiler's wait-count
+// tracking: a read of a ring slot must first wait until at most `n` vector
+// memory operations are outstanding, n being a lower bound on the number
+// issued after the slot's own loads (loads complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vm_at_most() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [I0, N).
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// Reads ring quad slot SLOT: this lane's code word of each page and K-step
+// (page p, K-step ks at word 64*(KS*p + ks) + lane; `base` = ring byte
+// address + 4*lane) and its radius byte (key lane&15 of page lane>>4;
+// `rbase` = radius ring byte address + lane).  Written as one asm block
+// that also waits for the reads: the compiler cannot order these reads
+// against the buffer-to-LDS loads, the explicit wait above does.
+template <int KS, int SLOT>
+__device__ __forceinline__ void read_quad(uint32_t base, uint32_t rbase,
+                                          uint32_t (&cw)[4][KS], uint32_t &r8) {
+  constexpr int o = 4 * KS * SLOT; // in 256-byte units
+  if constexpr (KS == 1) {
+    uint64_t a, b;
+    asm volatile(
+        "ds_read2st64_b32 %0, %3 offset0:%5 offset1:%6\n\t"
+        "ds_read2st64_b32 %1, %3 offset0:%7 offset1:%8\n\t"
+        "ds_read_u8 %2, %4 offset:%9\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a), "=&v"(b), "=&v"(r8)
+        : "v"(base), "v"(rbase), "n"(o), "n"(o + 1), "n"(o + 2), "n"(o + 3),
+          "n"(64 * SLOT)
+        : "memory");
+    cw[0][0] = (uint32_t)a;
+    cw[1][0] = (uint32_t)(a >> 32);
+    cw[2][0] = (uint32_t)b;
+    cw[3][0] = (uint32_t)(b >> 32);
+  } else {
+    static_assert(KS == 2, "K-steps");
+    uint64_t a, b, c, d;
+    asm volatile(
+        "ds_read2st64_b32 %0, %5 offset0:%7 offset1:%8\n\t"
+        "ds_read2st64_b32 %1, %5 offset0:%9 offset1:%10\n\t"
+        "ds_read2st64_b32 %2, %5 offset0:%11 offset1:%12\n\t"
+        "ds_read2st64_b32 %3, %5 offset0:%13 offset1:%14\n\t"
+        "ds_read_u8 %4, %6 offset:%15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a), "=&v"(b), "=&v"(c), "=&v"(d), "=&v"(r8)
+        : "v"(base), "v"(rbase), "n"(o), "n"(o + 1), "n"(o + 2), "n"(o + 3),
+          "n"(o + 4), "n"(o + 5), "n"(o + 6), "n"(o + 7), "n"(64 * SLOT)
+        : "memory");
+    cw[0][0] = (uint32_t)a; cw[0][1] = (uint32_t)(a >> 32);
+    cw[1][0] = (uint32_t)b; cw[1][1] = (uint32_t)(b >> 32);
+    cw[2][0] = (uint32_t)c; cw[2][1] = (uint32_t)(c >> 32);
+    cw[3][0] = (uint32_t)d; cw[3][1] = (uint32_t)(d >> 32);
+  }
+}
+
+// One task of the stream (all fields wave-uniform); unit < 0: none.
+struct Task {
+  int s, g, unit, N, key0, npg, lo, hi;
 };
 
 template <int KS, int G>
@@ -44,130 +119,217 @@ __global__ __launch_bounds__(kThreads) void filter_kernel(
     const int32_t *__restrict__ seq_lens, int n_max,
     const uint32_t *__restrict__ qop, const float *__restrict__ qneg,
     const uint32_t *__restrict__ lthr, int B, int Hkv, int W, int ngroups,
-    int w, int sigma, uint32_t *__restrict__ counter,
+    int ntasks, int w, int sigma, uint32_t *__restrict__ counter,
     uint32_t *__restrict__ cand_u, int32_t *__restrict__ cand_pos, int cap,
     int32_t *__restrict__ scores_out, int score_stride) {
-  __shared__ uint32_t su[kWaves][kGroupPages * kPage];
+  constexpr int kPageDwords = 64 * KS;
+  constexpr int kRingPages = kRingDwords / kPageDwords;
+  constexpr int kRingQuads = kRingPages / 4;
+  // loads issued after a quad's own: the other ring quads' code and radius
+  constexpr int kAfter =
+      (kRingQuads - 1) * (4 * KS + 1) < 63 ? (kRingQuads - 1) * (4 * KS + 1) : 63;
+  static_assert(kRingQuads <= kTaskQuads && kTaskQuads % kRingQuads == 0, "ring");
+  __shared__ __attribute__((aligned(16))) uint32_t ring[kWaves][kRingDwords];
+  __shared__ __attribute__((aligned(16))) uint32_t rring[kWaves][kRadRingDwords];
+
   const int lane = threadIdx.x & 63;
-  // wave-uniform (keeps the page offsets below in scalar registers)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t task = (int64_t)blockIdx.x * kWaves + wave;
-  const int g = (int)(task % Hkv);
-  const int64_t sg = task / Hkv;
-  const int grp = (int)(sg % ngroups);
-  const int s = (int)(sg / ngroups);
-  if (s >= B) return;
-  const int N = seq_len_clamped(seq_lens, s, n_max);
-  const int npages = (N + kPage - 1) / kPage;
-  const int pg0 = grp * kGroupPages;
-  if (pg0 >= npages) return;
-  const int npg = min(kGroupPages, npages - pg0);
-  const int key0 = pg0 * kPage;
-  const int lo = max(sigma, key0), hi = min(N - w, key0 + npg * kPage);
-  if (hi <= lo && scores_out == nullptr) return; // no candidates in this group
-  const int unit = s * Hkv + g;
+  const int stride = gridDim.x * kWaves;
   const int Hq = Hkv * G;
-
-  const QueryOperand<KS> op = load_query_operand<KS, G>(qop, qneg, unit, s, g, Hq, lane);
-  const uint32_t L = lthr[unit];
+  uint32_t *myring = ring[wave];
+  uint32_t *myrad = rring[wave];
+  // LDS byte addresses of this lane's word in ring slot 0 and its radius byte
+  const uint32_t ring_base =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)myring + 4u * lane;
+  const uint32_t rad_base =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)myrad + (uint32_t)lane;
   const PoolView view = make_pool_view(codes, radii, code_bytes, radius_bytes, W,
-                                       Hkv, g, lane);
-  // Lane j holds page pg0 + j's byte offsets: its code block, and its radius
-  // line (past the end of the radius buffer for an invalid page or one past
-  // the sequence, so its radius loads as 0 and its score is 0).  Invalid
-  // pages read the code block of physical page 0; it is multiplied by 0.
-  uint32_t my_code_off = 0, my_rad_off = 0x80000000u;
-  {
-    const int blk = lane < npg ? block_table[(int64_t)s * max_blocks + pg0 + lane] : -1;
-    if (blk >= 0 && blk < num_blocks) {
-      const uint32_t ph = (uint32_t)blk * (uint32_t)Hkv + (uint32_t)g;
-      my_code_off = ph * view.page_code_bytes;
-      my_rad_off = ph * (uint32_t)kPage;
-    }
-  }
-  // ds_bpermute byte address of lane (quad page of this lane) + 4 * quad
-  const int rad_src = (lane >> 4) * 4;
-  uint32_t *mys = su[wave];
+                                       Hkv, 0, lane);
 
-  auto load_batch = [&](int jb, PageBatch<KS> &pb) {
+  // task id -> task, or none if its page group is past the sequence
+  auto decode = [&](int t, Task &T) -> bool {
+    T.g = t % Hkv;
+    const int r = t / Hkv;
+    T.s = r % B;
+    const int grp = r / B;
+    T.N = seq_len_clamped(seq_lens, T.s, n_max);
+    T.key0 = grp * kGroupPages * kPage;
+    if (T.key0 >= T.N) return false;
+    T.unit = T.s * Hkv + T.g;
+    T.npg = min(kGroupPages, (T.N - T.key0 + kPage - 1) / kPage);
+    T.lo = max(sigma, T.key0);
+    T.hi = min(T.N - w, T.key0 + T.npg * kPage);
+    return true;
+  };
+  // the first non-empty task at or after t in this wave's stride
+  auto find = [&](int t, Task &T) -> int {
+    for (; t < ntasks; t += stride)
+      if (decode(t, T)) return t;
+    T.unit = -1;
+    return ntasks;
+  };
+  // Lane j: the task's block id of page j (-1 past the task), loaded one
+  // task before its offsets are needed so the load is long done by then.
+  auto load_blk = [&](const Task &T) -> int {
+    int blk = -1;
+    if (T.unit >= 0 && lane < T.npg)
+      blk = block_table[(int64_t)T.s * max_blocks + T.key0 / kPage + lane];
+    return blk;
+  };
+  // Lane j: byte offsets of page j (code block, radius line); invalid
+  // pages read physical page 0's code and a radius of 0.
+  auto page_offsets = [&](const Task &T, int blk, uint32_t &code_off,
+                          uint32_t &rad_off) {
+    const bool ok = blk >= 0 && blk < num_blocks;
+    const uint32_t ph = (uint32_t)blk * (uint32_t)Hkv + (uint32_t)T.g;
+    code_off = ok ? ph * view.page_code_bytes : 0u;
+    rad_off = ok ? ph * (uint32_t)kPage : kRadiusOob;
+  };
+  // Loads quad q of a task into ring quad slot `slot`: per page and K-step
+  // one buffer-to-LDS load (lane L's dword lands at slot word L), and one
+  // for the quad's four radius lines (lanes 0..15, four bytes each).
+  auto issue_quad = [&](uint32_t code_off, uint32_t rad_off, int q, int slot) {
 #pragma unroll
-    for (int q4 = 0; q4 < 2; ++q4) {
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t soff = __builtin_amdgcn_readlane(code_off, 4 * q + j);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t soff = __builtin_amdgcn_readlane(my_code_off, jb + 4 * q4 + j);
+      for (int ks = 0; ks < KS; ++ks)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            view.code,
+            (__attribute__((address_space(3))) void *)(myring +
+                                                       (4 * slot + j) * kPageDwords +
+                                                       64 * ks),
+            4, view.code_voff + 256 * ks, soff, 0, 0);
+    }
+    const uint32_t roff = (uint32_t)__builtin_amdgcn_ds_bpermute(
+                              (4 * q + (lane >> 2)) * 4, (int)rad_off) +
+                          4u * (uint32_t)(lane & 3);
+    if (lane < 16)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          view.radius,
+          (__attribute__((address_space(3))) void *)(myrad + 16 * slot), 4,
+          (int)roff, 0, 0, 0);
+  };
+  auto load_op = [&](const Task &T, QueryOperand<KS> &op, uint32_t &L) {
+    const int unit = T.unit >= 0 ? T.unit : 0;
+    op = load_query_operand<KS, G>(qop, qneg, unit, unit / Hkv, unit % Hkv, Hq, lane);
+    L = lthr[unit];
+  };
+
+  Task C, N1;
+  int tC = find(blockIdx.x * kWaves + wave, C);
+  if (C.unit < 0) return;
+  int tN = find(tC + stride, N1);
+  uint32_t cC, rC, cN, rN;
+  {
+    const int blkC = load_blk(C), blkN = load_blk(N1);
+    page_offsets(C, blkC, cC, rC);
+    page_offsets(N1, blkN, cN, rN);
+  }
+  QueryOperand<KS> opC;
+  uint32_t LC;
+  load_op(C, opC, LC);
+  // everything above has landed before the stream starts, so no wait in
+  // the loop below is ever for a load of this prologue
+  wait_vm_at_most<0>();
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          pb.cw[q4][j][ks] = __builtin_amdgcn_raw_buffer_load_b32(
-              view.code, view.code_voff + 256 * ks, soff, 0);
+  for (int q = 0; q < kRingQuads; ++q) issue_quad(cC, rC, q, q);
+  // an address the compiler cannot prove uniform keeps the atomic add below
+  // a single lane-0 operation whose result is read one task later
+  uint32_t opaque_zero;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(opaque_zero));
+
+  // the previous task, whose candidates are still to be written
+  Task P;
+  P.unit = -1;
+  uint32_t pu[kTaskQuads], p_base = 0, p_total = 0, p_L = 0;
+
+  auto write_previous = [&]() {
+    if (P.unit < 0 || p_total == 0) return;
+    uint32_t base = __builtin_amdgcn_readfirstlane(p_base);
+    uint32_t *ou = cand_u + (int64_t)P.unit * cap;
+    int32_t *op_ = cand_pos + (int64_t)P.unit * cap;
+#pragma unroll
+    for (int r = 0; r < kTaskQuads; ++r) {
+      const int pos = P.key0 + r * 64 + lane;
+      const bool cand = pos >= P.lo && pos < P.hi && pu[r] >= p_L;
+      const uint64_t m = __ballot(cand);
+      const uint32_t slot = base + lanes_below(m);
+      if (cand && slot < (uint32_t)cap) {
+        ou[slot] = pu[r];
+        op_[slot] = pos;
       }
-      // one radius byte per lane: key (lane & 15) of page (lane >> 4)
-      const uint32_t roff = (uint32_t)__builtin_amdgcn_ds_bpermute(
-          rad_src + 4 * (jb + 4 * q4), (int)my_rad_off);
-      pb.r8[q4] = __builtin_amdgcn_raw_buffer_load_b8(
-          view.radius, (int)(roff + (uint32_t)view.radius_voff), 0, 0);
+      base += __popcll(m);
     }
   };
-  auto score_batch = [&](int jb, const PageBatch<KS> &pb) {
-#pragma unroll
-    for (int q4 = 0; q4 < 2; ++q4) {
-      const int m = score_quad_max<KS, G>(op, pb.cw[q4]);
-      mys[(jb + 4 * q4) * kPage + lane] =
-          (uint32_t)(__mul24((int)pb.r8[q4], m) + (int)kScoreBias);
-    }
-  };
-  // Straight-line over the group's 64 pages (pages past npg score 0 and are
-  // ignored), so the wait counters stay exact and one batch's loads are in
-  // flight while the other batch is scored.
-  {
-    PageBatch<KS> pa, pb;
-    load_batch(0, pa);
-#pragma unroll
-    for (int jb = 0; jb < kGroupPages; jb += 2 * kBatch) {
-      load_batch(jb + kBatch, pb);
-      score_batch(jb, pa);
-      if (jb + 2 * kBatch < kGroupPages) load_batch(jb + 2 * kBatch, pa);
-      score_batch(jb + kBatch, pb);
-    }
-  }
-  // the wave's own LDS writes must be visible to all its lanes
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  if (scores_out != nullptr) {
-    int32_t *so = scores_out + (int64_t)unit * score_stride;
-    for (int e = lane; e < npg * kPage && key0 + e < N; e += 64)
-      so[key0 + e] = (int32_t)(mys[e] - kScoreBias);
-  }
-  if (hi <= lo) return;
 
-  // candidates of this group: positions in [lo, hi) with u >= L
-  constexpr int kRows = kGroupPages * kPage / 64;
-  uint32_t total = 0;
+  while (true) {
+    // look ahead: the task after next (its page offsets) and the next
+    // task's query operand
+    Task N2 = {0, 0, -1, 0, 0, 0, 0, 0};
+    const int tN2 = N1.unit >= 0 ? find(tN + stride, N2) : ntasks;
+    if (N1.unit < 0) N2.unit = -1;
+    const int blkN2 = load_blk(N2);
+    QueryOperand<KS> opN;
+    uint32_t LN;
+    load_op(N1, opN, LN);
+
+    uint32_t u[kTaskQuads];
+    static_for<0, kTaskQuads>([&](auto qc) {
+      constexpr int q = decltype(qc)::value;
+      constexpr int slot = q % kRingQuads;
+      wait_vm_at_most<kAfter>();
+      uint32_t cw[4][KS], r8;
+      read_quad<KS, slot>(ring_base, rad_base, cw, r8);
+      constexpr int tq = q + kRingQuads; // stream position one ring ahead
+      if constexpr (tq < kTaskQuads)
+        issue_quad(cC, rC, tq, slot);
+      else
+        issue_quad(cN, rN, tq - kTaskQuads, slot);
+      const int m = score_quad_max<KS, G>(opC, cw);
+      u[q] = (uint32_t)(__mul24((int)r8, m) + (int)kScoreBias);
+    });
+
+    if (scores_out != nullptr) {
+      int32_t *so = scores_out + (int64_t)C.unit * score_stride;
 #pragma unroll
-  for (int r = 0; r < kRows; ++r) {
-    const int pos = key0 + r * 64 + lane;
-    const bool cand = pos >= lo && pos < hi && mys[r * 64 + lane] >= L;
-    total += __popcll(__ballot(cand));
-  }
-  if (total == 0) return;
-  uint32_t base = 0;
-  if (lane == 0) base = atomicAdd(&counter[unit], total);
-  base = __builtin_amdgcn_readfirstlane(base);
-  uint32_t *ou = cand_u + (int64_t)unit * cap;
-  int32_t *op_ = cand_pos + (int64_t)unit * cap;
-#pragma unroll
-  for (int r = 0; r < kRows; ++r) {
-    const int pos = key0 + r * 64 + lane;
-    const uint32_t u = mys[r * 64 + lane];
-    const bool cand = pos >= lo && pos < hi && u >= L;
-    const uint64_t m = __ballot(cand);
-    const uint32_t slot = base + lanes_below(m);
-    if (cand && slot < (uint32_t)cap) {
-      ou[slot] = u;
-      op_[slot] = pos;
+      for (int q = 0; q < kTaskQuads; ++q) {
+        const int pos = C.key0 + 64 * q + lane;
+        if (pos < C.N) so[pos] = (int32_t)(u[q] - kScoreBias);
+      }
     }
-    base += __popcll(m);
+    write_previous();
+    // count this task's candidates and reserve their slots; the atomic's
+    // result is read one task later
+    uint32_t total = 0;
+#pragma unroll
+    for (int r = 0; r < kTaskQuads; ++r) {
+      const int pos = C.key0 + r * 64 + lane;
+      total += __popcll(__ballot(pos >= C.lo && pos < C.hi && u[r] >= LC));
+    }
+    if (total != 0 && lane == 0)
+      p_base = atomicAdd(counter + C.unit + opaque_zero, total);
+    P = C;
+    p_total = total;
+    p_L = LC;
+#pragma unroll
+    for (int r = 0; r < kTaskQuads; ++r) pu[r] = u[r];
+
+    // rotate the stream
+    if (N1.unit < 0) break;
+    C = N1;
+    tC = tN;
+    cC = cN;
+    rC = rN;
+    opC = opN;
+    LC = LN;
+    N1 = N2;
+    tN = tN2;
+    page_offsets(N2, blkN2, cN, rN);
   }
+  write_previous();
+  // no buffer-to-LDS load may still be in flight when the wave ends
+  wait_vm_at_most<0>();
 }
 
 } // namespace
@@ -179,21 +341,24 @@ hipError_t launch_score(const DecodeDims &d, const uint32_t *codes,
                         uint32_t *counter, uint32_t *cand_u, int32_t *cand_pos,
                         int32_t *scores_out, hipStream_t stream) {
   const int pages = (d.n_max + kPage - 1) / kPage;
-  const int ngroups = (pages + kGroupPages - 1) / kGroupPages;
+  const int64_t ngroups = (pages + kGroupPages - 1) / kGroupPages;
   if (ngroups == 0) return hipSuccess;
+  const int64_t ntasks = (int64_t)d.B * ngroups * d.Hkv;
+  if (ntasks > 0x7FFFFFFF - 65536) return hipErrorInvalidValue;
   const uint32_t code_bytes = (uint32_t)((uint64_t)d.num_blocks * d.Hkv * d.W * kPage * 4);
   const uint32_t radius_bytes = (uint32_t)((uint64_t)d.num_blocks * d.Hkv * kPage);
-  const int64_t tasks = (int64_t)d.B * ngroups * d.Hkv;
-  const int64_t nwg = (tasks + kWaves - 1) / kWaves;
-  if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
+  // persistent grid: two workgroups per CU, fewer for small calls
+  const int64_t nwg = std::min<int64_t>((ntasks + kWaves - 1) / kWaves,
+                                        2 * (int64_t)device_cu_count());
 #define DKV_SCORE_CASE(KSV, GV)                                                \
   if (d.KS == KSV && d.G == GV) {                                              \
     hipLaunchKernelGGL((filter_kernel<KSV, GV>), dim3((unsigned)nwg),          \
                        dim3(kThreads), 0, stream, codes, radii, d.num_blocks,  \
                        code_bytes, radius_bytes, block_table, d.max_blocks,    \
                        seq_lens, d.n_max, qop, qneg, lthr, d.B, d.Hkv, d.W,    \
-                       ngroups, d.w, d.sigma, counter, cand_u, cand_pos,       \
-                       d.cand_cap, scores_out, d.max_seq_len);                 \
+                       (int)ngroups, (int)ntasks, d.w, d.sigma, counter,       \
+                       cand_u, cand_pos, d.cand_cap, scores_out,               \
+                       d.max_seq_len);                                         \
     return hipGetLastError();                                                  \
   }
   DKV_SCORE_CASE(1, 1)
