@@ -69,8 +69,7 @@ bool make_dims(const dkv_config *cfg, int32_t batch, int32_t max_seq_len,
   d->num_blocks = num_blocks;
   const int cap = d->cap > 0 ? d->cap : 1;
   d->nsplit = (cap + kAttnRows - 1) / kAttnRows;
-  const int64_t room = 4 * (int64_t)d->k + 16384;
-  d->cand_cap = (int)std::max<int64_t>(1, std::min<int64_t>(max_seq_len, room));
+  d->cand_groups = (max_seq_len + kGroupKeys - 1) / kGroupKeys;
   d->bm_words = (max_seq_len + 31) / 32;
   // buffer views of the code and radius pools use 32-bit byte offsets
   if ((uint64_t)num_blocks * d->Hkv * d->W * kPage * 4 > 0xFFFFFFFFull) {
@@ -114,9 +113,8 @@ dkv_status decode_impl(const dkv_config *cfg, const void *q,
   uint32_t *qop = reinterpret_cast<uint32_t *>(ws + plan.qop);
   float *qneg = reinterpret_cast<float *>(ws + plan.qneg);
   uint32_t *lthr = reinterpret_cast<uint32_t *>(ws + plan.lthr);
-  uint32_t *counter = reinterpret_cast<uint32_t *>(ws + plan.counter);
-  uint32_t *cand_u = reinterpret_cast<uint32_t *>(ws + plan.cand_u);
-  int32_t *cand_pos = reinterpret_cast<int32_t *>(ws + plan.cand_pos);
+  uint2 *cand = reinterpret_cast<uint2 *>(ws + plan.cand);
+  uint32_t *tcount = reinterpret_cast<uint32_t *>(ws + plan.tcount);
   uint32_t *bitmap = reinterpret_cast<uint32_t *>(ws + plan.bitmap);
   int32_t *rows = reinterpret_cast<int32_t *>(ws + plan.rows);
   int32_t *cnt = reinterpret_cast<int32_t *>(ws + plan.cnt);
@@ -135,13 +133,13 @@ dkv_status decode_impl(const dkv_config *cfg, const void *q,
                           stream) == hipSuccess;
   };
   if (!mark() || launch_prep(d, q16, p16, codes, radii, block_table, seq_lens,
-                             q8, qop, qneg, lthr, counter, stream) != hipSuccess)
+                             q8, qop, qneg, lthr, stream) != hipSuccess)
     return DKV_ERR_LAUNCH;
   if (!mark() || launch_score(d, codes, radii, block_table, seq_lens, qop, qneg,
-                              lthr, counter, cand_u, cand_pos, scores_out,
-                              stream) != hipSuccess)
+                              lthr, cand, tcount, scores_out, stream) !=
+                     hipSuccess)
     return DKV_ERR_LAUNCH;
-  if (!mark() || launch_merge(d, cand_u, cand_pos, counter, seq_lens,
+  if (!mark() || launch_merge(d, cand, tcount, seq_lens,
                               block_table, bitmap, rows, cnt, sel_idx, sel_cnt,
                               codes, radii, qop, qneg, stream) != hipSuccess)
     return DKV_ERR_LAUNCH;
@@ -182,12 +180,10 @@ WorkspacePlan plan_workspace(const DecodeDims &d) {
   off += align256((size_t)d.B * d.Hq * 4);
   p.lthr = off;
   off += align256(units * 4);
-  p.counter = off;
-  off += align256(units * 4);
-  p.cand_u = off;
-  off += align256(units * (size_t)d.cand_cap * 4);
-  p.cand_pos = off;
-  off += align256(units * (size_t)d.cand_cap * 4);
+  p.cand = off;
+  off += align256(units * (size_t)d.cand_groups * kGroupKeys * 8);
+  p.tcount = off;
+  off += align256(units * (size_t)d.cand_groups * 4);
   p.bitmap = off;
   off += align256(units * (size_t)d.bm_words * 4);
   p.rows = off;

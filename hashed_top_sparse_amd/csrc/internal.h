@@ -13,6 +13,9 @@ namespace dkv {
 constexpr int kPage = 16;       // tokens per page
 constexpr int kHeadDim = 128;   // d
 constexpr int kAttnRows = 256;  // selected rows per attention split
+constexpr int kGroupPages = 64; // pages per candidate group (one scoring task)
+constexpr int kGroupKeys = kGroupPages * kPage;
+constexpr int kLdsPerCu = 160 * 1024; // gfx950 LDS per compute unit
 
 // Validated shape of one decode call.
 struct DecodeDims {
@@ -23,15 +26,15 @@ struct DecodeDims {
   int n_max;                 // min(max_seq_len, 16*max_blocks)
   int max_blocks;
   int64_t num_blocks;
-  int cand_cap;              // candidate list room per (sequence, KV head)
+  int cand_groups;           // candidate groups per (sequence, KV head):
+                             // ceil(max_seq_len / kGroupKeys)
   int bm_words;              // selection bitmap words per (sequence, KV head)
   int nsplit;                // attention splits per (sequence, KV head)
 };
 
 // Byte offsets of the decode workspace regions (each 256-byte aligned).
 struct WorkspacePlan {
-  size_t q8, qop, qneg, lthr, counter, cand_u, cand_pos, bitmap, rows, cnt,
-      part, total;
+  size_t q8, qop, qneg, lthr, cand, tcount, bitmap, rows, cnt, part, total;
 };
 
 WorkspacePlan plan_workspace(const DecodeDims &d);
@@ -49,29 +52,30 @@ hipError_t launch_encode(const uint16_t *k_pool, int64_t num_blocks,
 
 // Query codes q8 [B][Hq][b], the score matrix-core operand qop
 // [B*Hkv][KS][64 lanes][8 dwords], qneg [B][Hq] = -sum_j q8, and per
-// (sequence, KV head) the candidate threshold lthr (from a page sample) with
-// its candidate counter reset to 0.
+// (sequence, KV head) the candidate threshold lthr (from a page sample).
 hipError_t launch_prep(const DecodeDims &d, const uint16_t *q,
                        const uint16_t *proj, const uint32_t *codes,
                        const uint8_t *radii, const int32_t *block_table,
                        const int32_t *seq_lens, int8_t *q8, uint32_t *qop,
-                       float *qneg, uint32_t *lthr, uint32_t *counter,
-                       hipStream_t stream);
+                       float *qneg, uint32_t *lthr, hipStream_t stream);
 
-// Scores every cached key once and appends the candidates (u >= lthr) to
-// the per-(sequence, KV head) lists.
+// Scores every cached key once; the candidates (u >= lthr) of each
+// (sequence, KV head, group of kGroupKeys positions) go to that group's
+// region of cand [B*Hkv][cand_groups][kGroupKeys] as (u, position) in
+// position order, with their number in tcount [B*Hkv][cand_groups].  Groups
+// at or past a sequence's length are not written.
 hipError_t launch_score(const DecodeDims &d, const uint32_t *codes,
                         const uint8_t *radii, const int32_t *block_table,
                         const int32_t *seq_lens, const uint32_t *qop,
-                        const float *qneg, const uint32_t *lthr,
-                        uint32_t *counter, uint32_t *cand_u, int32_t *cand_pos,
-                        int32_t *scores_out, hipStream_t stream);
+                        const float *qneg, const uint32_t *lthr, uint2 *cand,
+                        uint32_t *tcount, int32_t *scores_out,
+                        hipStream_t stream);
 
 // Final selection (sinks, window, exact top-k in position order): rows
 // (physical row ids blk*16+slot, -1 past the count), cnt, and the optional
 // user lists.
-hipError_t launch_merge(const DecodeDims &d, const uint32_t *cand_u,
-                        const int32_t *cand_pos, const uint32_t *counter,
+hipError_t launch_merge(const DecodeDims &d, const uint2 *cand,
+                        const uint32_t *tcount,
                         const int32_t *seq_lens, const int32_t *block_table,
                         uint32_t *bitmap, int32_t *rows, int32_t *cnt,
                         int32_t *user_sel, int32_t *user_cnt,

@@ -9,8 +9,9 @@
 //           (S desc, position asc)
 //
 // The streaming pass left every candidate with u >= L (the sampled
-// threshold).  If at least k_eff of them exist (and none was dropped for
-// lack of room), the top-k of C is exactly the top-k of that list:
+// threshold) in the region of its group of kGroupKeys positions, with the
+// group's count.  If at least k_eff of them exist, the top-k of C is exactly
+// the top-k of the candidates:
 //   - the k_eff-th largest biased score T and the number of ties at T to
 //     keep come from two histogram passes (select_common.h);
 //   - if only some ties are kept, the lowest positions win: a second
@@ -43,8 +44,8 @@ __device__ __forceinline__ int row_of(const int32_t *bt, int pos,
 
 template <int KS, int G>
 __global__ __launch_bounds__(kThreads) void merge_kernel(
-    const uint32_t *__restrict__ cand_u, const int32_t *__restrict__ cand_pos,
-    const uint32_t *__restrict__ counter, int cand_cap,
+    const uint2 *__restrict__ cand, const uint32_t *__restrict__ tcount,
+    int cand_groups,
     const int32_t *__restrict__ seq_lens, int n_max,
     const int32_t *__restrict__ block_table, int max_blocks,
     int64_t num_blocks, int Hkv, int k, int w, int sigma, int cap,
@@ -56,6 +57,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
     const float *__restrict__ qneg) {
   __shared__ uint32_t su[kLdsScores];
   __shared__ SelectShared<kThreads> sel;
+  __shared__ uint32_t n_staged;
 
   const int unit = blockIdx.x;
   const int s = unit / Hkv, g = unit % Hkv;
@@ -101,35 +103,55 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
     } else {
       for (int i = tid; i < nwords; i += kThreads) bm[i] = 0u;
       __syncthreads();
-      const uint32_t nlist = counter[unit];
+      // the candidates of the unit's groups (those below N were written)
+      const int ngs = (N + kGroupKeys - 1) / kGroupKeys;
+      const uint32_t *tc = tcount + (int64_t)unit * cand_groups;
+      const uint2 *cb = cand + (int64_t)unit * cand_groups * kGroupKeys;
+      uint32_t part = 0;
+      for (int gi = tid; gi < ngs; gi += kThreads) part += tc[gi];
+      uint32_t nlist;
+      wg_exclusive_scan<kThreads>(part, &sel.red[2][0], &nlist);
+      // fn(u, pos) for every candidate, each once across the workgroup
+      auto for_each = [&](auto fn) {
+        for (int gi = wave; gi < ngs; gi += kWaves) {
+          const uint32_t n = tc[gi];
+          const uint2 *reg = cb + (int64_t)gi * kGroupKeys;
+          for (uint32_t j = lane; j < n; j += 64) {
+            const uint2 e = reg[j];
+            fn(e.x, (int)e.y);
+          }
+        }
+      };
       uint32_t T, take_eq, n_eq;
-      if (nlist >= (uint32_t)keff && nlist <= (uint32_t)cand_cap) {
-        // ---- normal path: exact top-k of the candidate list
-        const uint32_t *cu = cand_u + (int64_t)unit * cand_cap;
-        const int32_t *cp = cand_pos + (int64_t)unit * cand_cap;
+      if (nlist >= (uint32_t)keff) {
+        // ---- normal path: exact top-k of the candidates
         const bool staged = nlist <= (uint32_t)kLdsScores;
         if (staged) {
-          for (uint32_t i = tid; i < nlist; i += kThreads) su[i] = cu[i];
+          if (tid == 0) n_staged = 0;
+          __syncthreads();
+          for_each([&](uint32_t u, int) { su[atomicAdd(&n_staged, 1u)] = u; });
           __syncthreads();
         }
-        auto score_of = [&](uint32_t i) -> uint32_t { return staged ? su[i] : cu[i]; };
         wg_kth_largest<kThreads>(sel, [&](auto fn) {
-          for (uint32_t i = tid; i < nlist; i += kThreads) fn(score_of(i));
+          if (staged) {
+            for (uint32_t i = tid; i < nlist; i += kThreads) fn(su[i]);
+          } else {
+            for_each([&](uint32_t u, int) { fn(u); });
+          }
         }, (uint32_t)keff, T, take_eq, n_eq);
         uint32_t Pt = 0; // ties with (kPosMax - pos) >= Pt are kept
         if (take_eq < n_eq) {
           uint32_t t2, n2;
           wg_kth_largest<kThreads>(sel, [&](auto fn) {
-            for (uint32_t i = tid; i < nlist; i += kThreads)
-              if (score_of(i) == T) fn(kPosMax - (uint32_t)cp[i]);
+            for_each([&](uint32_t u, int pos) {
+              if (u == T) fn(kPosMax - (uint32_t)pos);
+            });
           }, take_eq, Pt, t2, n2);
         }
-        for (uint32_t i = tid; i < nlist; i += kThreads) {
-          const uint32_t u = score_of(i);
-          const int pos = cp[i];
+        for_each([&](uint32_t u, int pos) {
           if (u > T || (u == T && kPosMax - (uint32_t)pos >= Pt))
             atomicOr(&bm[pos >> 5], 1u << (pos & 31));
-        }
+        });
       } else {
         // ---- exact fallback: rescore every candidate key of the unit
         const QueryOperand<KS> op = load_query_operand<KS, G>(
@@ -188,8 +210,8 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
 
 } // namespace
 
-hipError_t launch_merge(const DecodeDims &d, const uint32_t *cand_u,
-                        const int32_t *cand_pos, const uint32_t *counter,
+hipError_t launch_merge(const DecodeDims &d, const uint2 *cand,
+                        const uint32_t *tcount,
                         const int32_t *seq_lens, const int32_t *block_table,
                         uint32_t *bitmap, int32_t *rows, int32_t *cnt,
                         int32_t *user_sel, int32_t *user_cnt,
@@ -201,8 +223,8 @@ hipError_t launch_merge(const DecodeDims &d, const uint32_t *cand_u,
 #define DKV_MERGE_CASE(KSV, GV)                                                \
   if (d.KS == KSV && d.G == GV) {                                              \
     hipLaunchKernelGGL((merge_kernel<KSV, GV>), dim3(d.B * d.Hkv),             \
-                       dim3(kThreads), 0, stream, cand_u, cand_pos, counter,   \
-                       d.cand_cap, seq_lens, d.n_max, block_table,             \
+                       dim3(kThreads), 0, stream, cand, tcount,                \
+                       d.cand_groups, seq_lens, d.n_max, block_table,          \
                        d.max_blocks, d.num_blocks, d.Hkv, d.k, d.w, d.sigma,   \
                        d.cap, bitmap, d.bm_words, rows, cnt, user_sel,         \
                        user_cnt, codes, radii, code_bytes, radius_bytes, d.W,  \

@@ -67,7 +67,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     const int32_t *__restrict__ block_table, int max_blocks,
     const int32_t *__restrict__ seq_lens, int n_max, int8_t *__restrict__ q8,
     uint32_t *__restrict__ qop, float *__restrict__ qneg,
-    uint32_t *__restrict__ lthr, uint32_t *__restrict__ counter, int Hq,
+    uint32_t *__restrict__ lthr, int Hq,
     int Hkv, int b, int W, int k, int w, int sigma) {
   const int unit = blockIdx.x;
   const int s = unit / Hkv;
@@ -237,10 +237,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
       L = T;
     }
   }
-  if (threadIdx.x == 0) {
-    lthr[unit] = L;
-    counter[unit] = 0;
-  }
+  if (threadIdx.x == 0) lthr[unit] = L;
 }
 
 } // namespace
@@ -249,8 +246,7 @@ hipError_t launch_prep(const DecodeDims &d, const uint16_t *q,
                        const uint16_t *proj, const uint32_t *codes,
                        const uint8_t *radii, const int32_t *block_table,
                        const int32_t *seq_lens, int8_t *q8, uint32_t *qop,
-                       float *qneg, uint32_t *lthr, uint32_t *counter,
-                       hipStream_t stream) {
+                       float *qneg, uint32_t *lthr, hipStream_t stream) {
   const uint32_t code_bytes = (uint32_t)((uint64_t)d.num_blocks * d.Hkv * d.W * kPage * 4);
   const uint32_t radius_bytes = (uint32_t)((uint64_t)d.num_blocks * d.Hkv * kPage);
 #define DKV_PREP_CASE(KSV, GV)                                                 \
@@ -259,7 +255,7 @@ hipError_t launch_prep(const DecodeDims &d, const uint16_t *q,
                        dim3(kThreads), 0, stream, q, proj, codes, radii,       \
                        d.num_blocks, code_bytes, radius_bytes, block_table,    \
                        d.max_blocks, seq_lens, d.n_max, q8, qop, qneg, lthr,   \
-                       counter, d.Hq, d.Hkv, d.b, d.W, d.k, d.w, d.sigma);     \
+                       d.Hq, d.Hkv, d.b, d.W, d.k, d.w, d.sigma);              \
     return hipGetLastError();                                                  \
   }
   DKV_PREP_CASE(1, 1)

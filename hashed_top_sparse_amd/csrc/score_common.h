@@ -124,18 +124,24 @@ __device__ __forceinline__ int score_page(const QueryOperand<KS> &op,
 template <int KS, int G>
 __device__ __forceinline__ int score_quad_max(const QueryOperand<KS> &op,
                                               const uint32_t (&cw)[4][KS]) {
+  // the four pages' matrix ops first (independent accumulators), then
+  // their epilogues
+  v4f acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    acc[j] = op.cinit;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          op.a[ks], expand_code_word(cw[j][ks]), acc[j], 0, 4, 0, 127, 0, 127);
+  }
   int x[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    v4f acc = op.cinit;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-          op.a[ks], expand_code_word(cw[j][ks]), acc, 0, 4, 0, 127, 0, 127);
-    // all 64 lanes take part: keep the op in wave-uniform control flow
-    asm volatile("" : "+v"(acc));
-    float m = 16.f * acc[0] + acc[1];
-    if (G >= 2) m = fmaxf(m, 16.f * acc[2] + acc[3]);
+    float m = 16.f * acc[j][0] + acc[j][1];
+    if (G >= 2) m = fmaxf(m, 16.f * acc[j][2] + acc[j][3]);
+    // all 64 lanes take part: keep the ops in wave-uniform control flow
+    asm volatile("" : "+v"(m));
     if (G >= 8) m = max_rows32(m);
     x[j] = (int)m;
   }
