@@ -33,7 +33,8 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
-constexpr int kLdsScores = 32768;
+constexpr int kStage = 12288;        // candidates staged in LDS as (u, pos)
+constexpr int kMaxGroupsLds = 4096;  // groups whose count prefix fits in LDS
 constexpr uint32_t kPosMax = 0x00FFFFFFu; // positions < 2^24
 
 __device__ __forceinline__ int row_of(const int32_t *bt, int pos,
@@ -55,9 +56,9 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
     const uint8_t *__restrict__ radii, uint32_t code_bytes,
     uint32_t radius_bytes, int W, const uint32_t *__restrict__ qop,
     const float *__restrict__ qneg) {
-  __shared__ uint32_t su[kLdsScores];
+  __shared__ uint2 st[kStage];
+  __shared__ uint32_t gpre[kMaxGroupsLds + 1];
   __shared__ SelectShared<kThreads> sel;
-  __shared__ uint32_t n_staged;
 
   const int unit = blockIdx.x;
   const int s = unit / Hkv, g = unit % Hkv;
@@ -103,16 +104,40 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
     } else {
       for (int i = tid; i < nwords; i += kThreads) bm[i] = 0u;
       __syncthreads();
-      // the candidates of the unit's groups (those below N were written)
+      // the candidates of the unit's groups (those below N were written):
+      // count prefix over the groups, in LDS when it fits
       const int ngs = (N + kGroupKeys - 1) / kGroupKeys;
       const uint32_t *tc = tcount + (int64_t)unit * cand_groups;
       const uint2 *cb = cand + (int64_t)unit * cand_groups * kGroupKeys;
-      uint32_t part = 0;
-      for (int gi = tid; gi < ngs; gi += kThreads) part += tc[gi];
+      const bool pre_lds = ngs <= kMaxGroupsLds;
       uint32_t nlist;
-      wg_exclusive_scan<kThreads>(part, &sel.red[2][0], &nlist);
-      // fn(u, pos) for every candidate, each once across the workgroup
-      auto for_each = [&](auto fn) {
+      {
+        constexpr int kPer = kMaxGroupsLds / kThreads;
+        uint32_t c[kPer], part = 0;
+        if (pre_lds) {
+#pragma unroll
+          for (int i = 0; i < kPer; ++i) {
+            const int gi = tid * kPer + i;
+            c[i] = gi < ngs ? tc[gi] : 0u;
+            part += c[i];
+          }
+        } else {
+          for (int gi = tid; gi < ngs; gi += kThreads) part += tc[gi];
+        }
+        uint32_t off = wg_exclusive_scan<kThreads>(part, &sel.red[2][0], &nlist);
+        if (pre_lds) {
+#pragma unroll
+          for (int i = 0; i < kPer; ++i) {
+            const int gi = tid * kPer + i;
+            if (gi < ngs) gpre[gi] = off;
+            off += c[i];
+          }
+          if (tid == 0) gpre[ngs] = nlist;
+        }
+      }
+      // fn(u, pos) for every candidate, each once across the workgroup,
+      // straight from the group regions (for units too large to stage)
+      auto for_each_global = [&](auto fn) {
         for (int gi = wave; gi < ngs; gi += kWaves) {
           const uint32_t n = tc[gi];
           const uint2 *reg = cb + (int64_t)gi * kGroupKeys;
@@ -125,19 +150,43 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
       uint32_t T, take_eq, n_eq;
       if (nlist >= (uint32_t)keff) {
         // ---- normal path: exact top-k of the candidates
-        const bool staged = nlist <= (uint32_t)kLdsScores;
+        const bool staged = pre_lds && nlist <= (uint32_t)kStage;
+        __syncthreads();
         if (staged) {
-          if (tid == 0) n_staged = 0;
-          __syncthreads();
-          for_each([&](uint32_t u, int) { su[atomicAdd(&n_staged, 1u)] = u; });
+          // candidate i is entry i - gpre[g] of group g, gpre[g] <= i < gpre[g+1];
+          // four independent loads in flight per thread
+          for (uint32_t i0 = 0; i0 < nlist; i0 += 4 * kThreads) {
+            uint2 e[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const uint32_t i = i0 + r * kThreads + tid;
+              e[r] = make_uint2(0u, 0u);
+              if (i < nlist) {
+                int lo = 0, hi = ngs; // largest g with gpre[g] <= i
+                while (hi - lo > 1) {
+                  const int mid = (lo + hi) >> 1;
+                  if (gpre[mid] <= i) lo = mid; else hi = mid;
+                }
+                e[r] = cb[(int64_t)lo * kGroupKeys + (i - gpre[lo])];
+              }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const uint32_t i = i0 + r * kThreads + tid;
+              if (i < nlist) st[i] = e[r];
+            }
+          }
           __syncthreads();
         }
-        wg_kth_largest<kThreads>(sel, [&](auto fn) {
+        auto for_each = [&](auto fn) {
           if (staged) {
-            for (uint32_t i = tid; i < nlist; i += kThreads) fn(su[i]);
+            for (uint32_t i = tid; i < nlist; i += kThreads) fn(st[i].x, (int)st[i].y);
           } else {
-            for_each([&](uint32_t u, int) { fn(u); });
+            for_each_global(fn);
           }
+        };
+        wg_kth_largest<kThreads>(sel, [&](auto fn) {
+          for_each([&](uint32_t u, int) { fn(u); });
         }, (uint32_t)keff, T, take_eq, n_eq);
         uint32_t Pt = 0; // ties with (kPosMax - pos) >= Pt are kept
         if (take_eq < n_eq) {
