@@ -13,7 +13,10 @@ every sequence is scored once per step), the step latency, per-stage times
 from HIP events recorded on the launch stream inside the timed region, the
 roofline of the dominant kernel (the score stage: it streams every key's
 code and radius), and the CPU oracle timed on a bounded sample of the same
-workload on this host's cores.
+workload on this host's cores.  The timed steps run back to back, as a
+serving loop would; a second, cold measurement (median over steps, each
+after a 1 GiB write that evicts the last-level cache, outside the events) is
+reported beside it.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10]
 """
@@ -109,7 +112,7 @@ def counter_traffic(kernel_src_digest: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(wl, inp, units: int, reps: int) -> dict:
+def cpu_baseline(wl, inp, units: int, seconds: float) -> dict:
     """The CPU oracle (as it stands) on a bounded sample of the workload."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import numpy as np
@@ -138,11 +141,16 @@ def cpu_baseline(wl, inp, units: int, reps: int) -> dict:
         K[i, :n] = logical_rows(inp["k_pool"], bt, s, n, g)
         V[i, :n] = logical_rows(inp["v_pool"], bt, s, n, g)
         codes[i, :n], radii[i, :n] = oracle.encode_keys(K[i, :n], P)   # untimed
+    # repeat the decode step until about `seconds` of CPU work is timed
+    reps = 0
     t0 = time.perf_counter()
-    for _ in range(reps):
+    while True:
         oracle.decode_units(q, P, codes, radii, K, V, N, wl.top_k, wl.window,
                             wl.sinks, want_scores=False)
-    dt = time.perf_counter() - t0
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= seconds or reps >= 100000:
+            break
     keys = float(N.sum()) * reps
     return {"value": keys / dt, "unit": "scored keys/s", "cores": oracle.num_threads(),
             "kind": "oracle",
@@ -160,7 +168,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-units", type=int, default=16)
-    ap.add_argument("--cpu-reps", type=int, default=8)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cold-steps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (for "
@@ -235,6 +244,27 @@ def main():
         hip.destroy(e)
     print(f"[bench] {args.steps} steps timed", file=sys.stderr, flush=True)
 
+    # cold steps: a 1 GiB write between steps (outside the events) evicts the
+    # last-level cache, so every step streams its codes and rows from HBM
+    cold = {}
+    if args.cold_steps > 0:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        cevs = [hip.create(n_ev) for _ in range(args.cold_steps)]
+        for i in range(args.cold_steps):
+            flush.fill_(float(i))
+            step(cevs[i])
+        torch.cuda.synchronize()
+        import statistics
+        per = [hip.elapsed_ms(e[0], e[-1]) for e in cevs]
+        cold["step_us_median"] = statistics.median(per) * 1e3
+        for j, nm in enumerate(names):
+            cold[nm + "_us_median"] = statistics.median(
+                hip.elapsed_ms(e[j], e[j + 1]) for e in cevs) * 1e3
+        for e in cevs:
+            hip.destroy(e)
+        del flush
+        print(f"[bench] {args.cold_steps} cold steps timed", file=sys.stderr, flush=True)
+
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -247,7 +277,7 @@ def main():
     ab = algorithmic_bytes(wl, lens, cfg)
     score_s = stage_ms["score"] * 1e-3
     score_src = [os.path.join(ROOT, "hashed_top_sparse_amd", "csrc", f)
-                 for f in ("score.hip", "internal.h")]
+                 for f in ("score.hip", "score_common.h", "internal.h")]
     traffic = counter_traffic(source_digest(score_src), wl.name)
     roofline = {"bound": "hbm", "kernel": "score",
                 "achieved": ab["score"] / score_s / 1e9, "peak": HBM_PEAK_GBS,
@@ -278,12 +308,13 @@ def main():
         "step_hbm_gbs": ab["total"] / (ms_per_step * 1e-3) / 1e9,
         "step_frac_of_peak": ab["total"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "stages_us": {k: v * 1e3 for k, v in stage_ms.items()},
+        "cold": cold,
         "roofline": roofline,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_units, args.cpu_reps)
+        result["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_units, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

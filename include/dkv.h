@@ -123,9 +123,10 @@ typedef struct {
  *   proj         device, bf16 [d][b]
  *   codes        device, uint32 [num_blocks][Hkv][b/32][16] (output)
  *   radii        device, uint8  [num_blocks][Hkv][16]       (output)
- * Bits are bit-exact with the definition above: the projection runs on bf16
- * matrix cores in fp32 and every sign the fp32 error bound cannot certify
- * is recomputed in double precision in index order.
+ * Bits are bit-exact with the definition above: the projection is summed in
+ * double precision in index order (a product of two bf16 values is exact in
+ * double), and the radius code comes from an exact double-precision
+ * threshold table.
  */
 dkv_status dkv_encode(const dkv_config *cfg, const void *k_pool,
                       int64_t num_blocks, const int32_t *block_table,
