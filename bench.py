@@ -176,9 +176,10 @@ def main():
                          "scaling PMC byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not "
-              "supported (the path shards by KV head / sequence with no exchange; "
-              "see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py: runs on one GPU only; --gpus {args.gpus} is not "
+              "supported (units of (sequence, KV head) are independent, so the "
+              "path would shard by KV head or sequence with no exchange)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
