@@ -197,7 +197,7 @@ def main():
     B, Hkv = wl.batch, wl.num_kv_heads
     nb = inp["k_pool"].shape[0]
     dev = inp["k_pool"].device
-    codes = torch.zeros((nb, Hkv, wl.code_bits // 32, PAGE), dtype=torch.int32, device=dev)
+    codes = torch.zeros((nb, Hkv, PAGE, wl.code_bits // 32), dtype=torch.int32, device=dev)
     radii = torch.zeros((nb, Hkv, PAGE), dtype=torch.uint8, device=dev)
     zeros = torch.zeros(B, dtype=torch.int32, device=dev)
     dkv.encode(cfg, inp["k_pool"], inp["block_table"], zeros, inp["seq_lens"],
@@ -216,53 +216,77 @@ def main():
     names = ["encode_current"] + dkv.decode_stage_names()
     n_ev = len(names) + 1
 
-    def step(evs):
-        hip.record(evs[0], sh)
+    def step(evs=None):
+        """One decode step: encode the newest token of every sequence, then
+        dkv_decode.  With evs, HIP events bracket every stage."""
+        if evs is not None:
+            hip.record(evs[0], sh)
         dkv.encode(cfg, inp["k_pool"], inp["block_table"], cur_start,
                    inp["seq_lens"], 1, inp["proj"], codes, radii, stream=stream)
-        dkv.decode_profiled(cfg, inp["q"], inp["k_pool"], inp["v_pool"], codes, radii,
-                            inp["block_table"], inp["seq_lens"], max_len, inp["proj"],
-                            out, ws, evs[1:], stream=stream)
+        if evs is None:
+            dkv.decode(cfg, inp["q"], inp["k_pool"], inp["v_pool"], codes, radii,
+                       inp["block_table"], inp["seq_lens"], max_len, inp["proj"],
+                       out, ws, stream=stream)
+        else:
+            dkv.decode_profiled(cfg, inp["q"], inp["k_pool"], inp["v_pool"], codes,
+                                radii, inp["block_table"], inp["seq_lens"], max_len,
+                                inp["proj"], out, ws, evs[1:], stream=stream)
 
-    warm_ev = hip.create(n_ev)
+    # Timed steps: the plain call, nothing recorded between its kernels.
     for _ in range(args.warmup):
-        step(warm_ev)
+        step()
     torch.cuda.synchronize()
-    evs = [hip.create(n_ev) for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    edge = hip.create(2)
     t0 = time.perf_counter()
+    hip.record(edge[0], sh)
     for i in range(args.steps):
-        step(evs[i])
+        step()
+    hip.record(edge[1], sh)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    gpu_ms = hip.elapsed_ms(edge[0], edge[1]) / args.steps
+    hip.destroy(edge)
+    print(f"[bench] {args.steps} steps timed", file=sys.stderr, flush=True)
+
+    # Stage breakdown: the same steps again with an event before every stage
+    # (each record adds a little to the stage it opens).
+    evs = [hip.create(n_ev) for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
     stage_ms = {}
     for j, nm in enumerate(names):
         stage_ms[nm] = sum(hip.elapsed_ms(e[j], e[j + 1]) for e in evs) / args.steps
-    gpu_ms = sum(hip.elapsed_ms(e[0], e[-1]) for e in evs) / args.steps
-    hip.destroy(warm_ev)
     for e in evs:
         hip.destroy(e)
-    print(f"[bench] {args.steps} steps timed", file=sys.stderr, flush=True)
 
-    # cold steps: a 1 GiB write between steps (outside the events) evicts the
-    # last-level cache, so every step streams its codes and rows from HBM
+    # Cold steps: between steps (outside the events) a 1 GiB buffer is read,
+    # which evicts the 256 MB last-level cache, so every step streams its
+    # codes and rows from HBM ("cold").  The same with a 1 GiB write instead
+    # ("cold_dirty") also leaves the cache full of dirty lines, whose write-
+    # back then competes with the step's reads.
     cold = {}
     if args.cold_steps > 0:
-        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-        cevs = [hip.create(n_ev) for _ in range(args.cold_steps)]
-        for i in range(args.cold_steps):
-            flush.fill_(float(i))
-            step(cevs[i])
-        torch.cuda.synchronize()
         import statistics
-        per = [hip.elapsed_ms(e[0], e[-1]) for e in cevs]
-        cold["step_us_median"] = statistics.median(per) * 1e3
-        for j, nm in enumerate(names):
-            cold[nm + "_us_median"] = statistics.median(
-                hip.elapsed_ms(e[j], e[j + 1]) for e in cevs) * 1e3
-        for e in cevs:
-            hip.destroy(e)
+        flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        for mode in ("cold", "cold_dirty"):
+            cevs = [hip.create(n_ev) for _ in range(args.cold_steps)]
+            for i in range(args.cold_steps):
+                if mode == "cold":
+                    flush.sum()
+                else:
+                    flush.fill_(float(i))
+                step(cevs[i])
+            torch.cuda.synchronize()
+            rec = {"step_us_median": statistics.median(
+                hip.elapsed_ms(e[0], e[-1]) for e in cevs) * 1e3}
+            for j, nm in enumerate(names):
+                rec[nm + "_us_median"] = statistics.median(
+                    hip.elapsed_ms(e[j], e[j + 1]) for e in cevs) * 1e3
+            cold[mode] = rec
+            for e in cevs:
+                hip.destroy(e)
         del flush
         print(f"[bench] {args.cold_steps} cold steps timed", file=sys.stderr, flush=True)
 

@@ -161,7 +161,7 @@ def encode(cfg: Config, k_pool, block_table, enc_start, enc_end,
     B, max_blocks = block_table.shape
     _expect(k_pool, "k_pool", (nb, cfg.page_size, cfg.num_kv_heads, cfg.head_dim))
     _expect(proj, "proj", (cfg.head_dim, cfg.code_bits))
-    _expect(codes, "codes", (nb, cfg.num_kv_heads, cfg.code_bits // 32, cfg.page_size))
+    _expect(codes, "codes", (nb, cfg.num_kv_heads, cfg.page_size, cfg.code_bits // 32))
     _expect(radii, "radii", (nb, cfg.num_kv_heads, cfg.page_size))
     _expect(enc_start, "enc_start", (B,))
     _expect(enc_end, "enc_end", (B,))
@@ -191,7 +191,7 @@ def _decode_args(cfg, q, k_pool, v_pool, codes, radii, block_table, seq_lens,
     _expect(q, "q", (B, Hq, d))
     _expect(k_pool, "k_pool", (nb, cfg.page_size, Hkv, d))
     _expect(v_pool, "v_pool", (nb, cfg.page_size, Hkv, d))
-    _expect(codes, "codes", (nb, Hkv, b // 32, cfg.page_size))
+    _expect(codes, "codes", (nb, Hkv, cfg.page_size, b // 32))
     _expect(radii, "radii", (nb, Hkv, cfg.page_size))
     _expect(seq_lens, "seq_lens", (B,))
     _expect(proj, "proj", (d, b))

@@ -14,6 +14,10 @@ constexpr int kDecodeStages = 5;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Kernels read pool rows, code words, radius lines and the projection with
+// 16-byte loads.
+bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
 bool valid_config(const dkv_config *cfg, dkv_status *why) {
   if (cfg == nullptr) {
     *why = DKV_ERR_INVALID_ARG;
@@ -102,6 +106,9 @@ dkv_status decode_impl(const dkv_config *cfg, const void *q,
       codes == nullptr || radii == nullptr || block_table == nullptr ||
       seq_lens == nullptr || proj == nullptr || out == nullptr ||
       max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return DKV_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) ||
+      !aligned16(codes) || !aligned16(radii) || !aligned16(proj))
     return DKV_ERR_INVALID_ARG;
   const WorkspacePlan plan = plan_workspace(d);
   if (workspace == nullptr || workspace_bytes < plan.total ||
@@ -214,6 +221,9 @@ dkv_encode(const dkv_config *cfg, const void *k_pool, int64_t num_blocks,
       enc_end == nullptr || proj == nullptr || codes == nullptr ||
       radii == nullptr || num_blocks <= 0 || max_blocks_per_seq <= 0 ||
       batch <= 0 || batch > 65535 || max_encode_len < 0)
+    return DKV_ERR_INVALID_ARG;
+  if (!aligned16(k_pool) || !aligned16(codes) || !aligned16(radii) ||
+      !aligned16(proj))
     return DKV_ERR_INVALID_ARG;
   if (max_encode_len > DKV_MAX_SEQ_LEN) return DKV_ERR_UNSUPPORTED;
   hipError_t e = launch_encode(

@@ -10,8 +10,9 @@
 //
 // Work mapping of the split kernel: 256 threads = 16 row groups of 16 lanes;
 // a row group reads a selected key row and value row (256 B each: 16 B per
-// lane) and keeps 4 rows in flight, so a workgroup has 64 row pairs of
-// gathers outstanding.  The selection list already holds physical row ids
+// lane), four rows per batch with the next batch in flight, so a workgroup
+// has up to 128 row pairs of gathers outstanding; the split's row ids are
+// read once into LDS; the 16-lane dot-product sums use DPP row operations.  The selection list already holds physical row ids
 // (page*16 + slot).  All G query heads of the KV group share the rows.
 #include "internal.h"
 
@@ -32,6 +33,20 @@ __device__ __forceinline__ void unpack8(const uint4 &v, float (&f)[8]) {
   f[5] = __uint_as_float(v.z & 0xFFFF0000u);
   f[6] = __uint_as_float(v.w << 16);
   f[7] = __uint_as_float(v.w & 0xFFFF0000u);
+}
+
+// Sum over the 16 lanes of a DPP row, in every lane of the row: quad xor 1,
+// quad xor 2, half-row mirror (the other quad), row mirror (the other half).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float sum_row16(float x) {
+  x += dpp_mov<0xB1>(x);  // quad_perm [1,0,3,2]
+  x += dpp_mov<0x4E>(x);  // quad_perm [2,3,0,1]
+  x += dpp_mov<0x141>(x); // row_half_mirror
+  x += dpp_mov<0x140>(x); // row_mirror
+  return x;
 }
 
 // Merge online-softmax state (m2, l2, a2) into (m1, l1, a1).
@@ -79,48 +94,56 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(
     for (int c = 0; c < 8; ++c) acc[h][c] = 0.f;
   }
 
-  const int32_t *L = rows + (int64_t)unit * cap;
-  constexpr int kBatch = 4; // rows per row group in flight
-  for (int rb = r0 + rg; rb < r1; rb += kBatch * kRowGroups) {
-    uint4 kraw[kBatch], vraw[kBatch];
-    bool ok[kBatch];
+  // the split's row ids, once, into LDS
+  __shared__ int32_t sid[kAttnRows];
+  {
+    const int r = r0 + (int)threadIdx.x;
+    sid[threadIdx.x] = r < r1 ? rows[(int64_t)unit * cap + r] : -1;
+  }
+  __syncthreads();
+
+  // Row group rg takes rows rg, rg+16, ... of the split: four batches of
+  // four, the next batch's loads issued before the current batch is used.
+  constexpr int kBatch = 4;
+  constexpr int kBatches = kAttnRows / (kBatch * kRowGroups);
+  auto load_batch = [&](int b, uint4 (&kr)[kBatch], uint4 (&vr)[kBatch], bool (&ok)[kBatch]) {
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
-      const int r = rb + i * kRowGroups;
-      const int idx = r < r1 ? L[r] : -1;
+      const int idx = sid[(b * kBatch + i) * kRowGroups + rg];
       ok[i] = idx >= 0;
       const int64_t off = ((int64_t)(ok[i] ? idx : 0) * Hkv + g) * kHeadDim + lane * 8;
-      kraw[i] = ok[i] ? *reinterpret_cast<const uint4 *>(k_pool + off) : make_uint4(0, 0, 0, 0);
-      vraw[i] = ok[i] ? *reinterpret_cast<const uint4 *>(v_pool + off) : make_uint4(0, 0, 0, 0);
+      kr[i] = make_uint4(0, 0, 0, 0);
+      vr[i] = make_uint4(0, 0, 0, 0);
+      if (ok[i]) {
+        kr[i] = *reinterpret_cast<const uint4 *>(k_pool + off);
+        vr[i] = *reinterpret_cast<const uint4 *>(v_pool + off);
+      }
     }
+  };
+  auto use_batch = [&](const uint4 (&kr)[kBatch], const uint4 (&vr)[kBatch],
+                       const bool (&ok)[kBatch]) {
     float dot[G][kBatch];
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       float kf[8];
-      unpack8(kraw[i], kf);
+      unpack8(kr[i], kf);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float d = 0.f;
 #pragma unroll
         for (int c = 0; c < 8; ++c) d = fmaf(qv[h][c], kf[c], d);
-        dot[h][i] = d;
+        dot[h][i] = ok[i] ? sum_row16(d) : -INFINITY;
       }
     }
+    float vf[kBatch][8];
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int i = 0; i < kBatch; ++i) {
-#pragma unroll
-        for (int off2 = kLanesPerRow / 2; off2 > 0; off2 >>= 1)
-          dot[h][i] += __shfl_xor(dot[h][i], off2, kLanesPerRow);
-        if (!ok[i]) dot[h][i] = -INFINITY;
-      }
+    for (int i = 0; i < kBatch; ++i) unpack8(vr[i], vf[i]);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float mn = m[h];
 #pragma unroll
       for (int i = 0; i < kBatch; ++i) mn = fmaxf(mn, dot[h][i]);
-      if (mn == -INFINITY) continue; // nothing valid yet
+      if (mn == -INFINITY) continue; // nothing valid yet (uniform per row group)
       const float corr = exp2f(m[h] - mn);
       float pr[kBatch];
       float psum = 0.f;
@@ -130,16 +153,26 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(
         psum += pr[i];
       }
       l[h] = l[h] * corr + psum;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) acc[h][c] *= corr;
       m[h] = mn;
 #pragma unroll
-      for (int i = 0; i < kBatch; ++i) {
-        float vf[8];
-        unpack8(vraw[i], vf);
+      for (int c = 0; c < 8; ++c) {
+        float a = acc[h][c] * corr;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc[h][c] = fmaf(pr[i], vf[c], acc[h][c]);
+        for (int i = 0; i < kBatch; ++i) a = fmaf(pr[i], vf[i][c], a);
+        acc[h][c] = a;
       }
+    }
+  };
+  {
+    uint4 ka[kBatch], va[kBatch], kb[kBatch], vb[kBatch];
+    bool oa[kBatch], ob[kBatch];
+    load_batch(0, ka, va, oa);
+#pragma unroll
+    for (int b = 0; b < kBatches; b += 2) {
+      if (b + 1 < kBatches) load_batch(b + 1, kb, vb, ob);
+      use_batch(ka, va, oa);
+      if (b + 2 < kBatches) load_batch(b + 2, ka, va, oa);
+      if (b + 1 < kBatches) use_batch(kb, vb, ob);
     }
   }
 
@@ -186,7 +219,11 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(
   }
 }
 
-// One workgroup of 128 threads per (sequence, query head).
+// Merge of the split states: one workgroup of 128 threads (one per dim)
+// per (sequence, query head).  Splits are taken 16 at a time, all 16
+// states loaded before any is used so the loads overlap.
+constexpr int kCombineChunk = 16;
+
 __global__ __launch_bounds__(kHeadDim) void attend_combine_kernel(
     const float *__restrict__ part, float *__restrict__ out, int Hq, int Hkv,
     int G, int nsplit) {
@@ -195,19 +232,31 @@ __global__ __launch_bounds__(kHeadDim) void attend_combine_kernel(
   const int g = hq / G, h = hq % G;
   const int unit = s * Hkv + g;
   const int dim = threadIdx.x;
-  float mm = -INFINITY;
-  for (int p = 0; p < nsplit; ++p)
-    mm = fmaxf(mm, part[(((int64_t)unit * nsplit + p) * G + h) * kPartStride]);
-  float ll = 0.f, aa = 0.f;
-  if (mm != -INFINITY) {
-    for (int p = 0; p < nsplit; ++p) {
-      const float *src = part + (((int64_t)unit * nsplit + p) * G + h) * kPartStride;
-      const float mp = src[0];
-      if (mp == -INFINITY) continue;
-      const float c = exp2f(mp - mm);
-      ll = fmaf(src[1], c, ll);
-      aa = fmaf(src[2 + dim], c, aa);
+  const float *src0 = part + ((int64_t)unit * nsplit * G + h) * kPartStride;
+  const int64_t stride = (int64_t)G * kPartStride;
+  float mm = -INFINITY, ll = 0.f, aa = 0.f;
+  for (int p0 = 0; p0 < nsplit; p0 += kCombineChunk) {
+    float mp[kCombineChunk], lp[kCombineChunk], ap[kCombineChunk];
+#pragma unroll
+    for (int i = 0; i < kCombineChunk; ++i) {
+      const int p = p0 + i < nsplit ? p0 + i : p0;
+      const float *src = src0 + p * stride;
+      mp[i] = p0 + i < nsplit ? src[0] : -INFINITY;
+      lp[i] = src[1];
+      ap[i] = src[2 + dim];
     }
+    float mc = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kCombineChunk; ++i) mc = fmaxf(mc, mp[i]);
+    if (mc == -INFINITY) continue;
+    float lc = 0.f, ac = 0.f;
+#pragma unroll
+    for (int i = 0; i < kCombineChunk; ++i) {
+      const float c = (mp[i] == -INFINITY) ? 0.f : exp2f(mp[i] - mc);
+      lc = fmaf(lp[i], c, lc);
+      ac = fmaf(ap[i], c, ac);
+    }
+    merge_state(mm, ll, &aa, mc, lc, &ac, 1);
   }
   out[(int64_t)sh * kHeadDim + dim] = (ll > 0.f) ? aa / ll : 0.f;
 }

@@ -47,6 +47,8 @@ constexpr int kThreads = 512;
 constexpr int kMaxPairs = 4;      // G*b <= 8*256 = 4*512
 constexpr int kSamplePages = 512; // sample pages per (sequence, KV head)
 constexpr int kSampleKeys = kSamplePages * kPage;
+constexpr int kWv = kThreads / 64;
+constexpr int kPre = 32; // sample pages per wave whose loads start first
 
 // e4m3 (bias 7) byte of a small integer v, |v| <= 60 with at most four
 // significant bits (exactly representable).
@@ -73,8 +75,8 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
   const int s = unit / Hkv;
   const int g = unit % Hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __shared__ double sQ[8 * kHeadDim];
-  __shared__ uint16_t sP[kHeadDim * 256];
+  __shared__ __align__(16) uint16_t sQ[8 * kHeadDim];
+  __shared__ __align__(16) uint16_t sP[kHeadDim * 256];
   __shared__ int sq8[8 * 256];
   __shared__ uint32_t sOp[2 * 512];
   __shared__ uint32_t sSample[kSampleKeys];
@@ -83,10 +85,46 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
   __shared__ uint32_t sCount[kThreads / 64];
   __shared__ SelectShared<kThreads> sel;
 
+  // ---- sample plan (it needs only N); the sample pages' loads are issued
+  // first so they are in flight while the query is projected
+  const int N = seq_len_clamped(seq_lens, s, n_max);
+  const int nc = max(0, N - w - sigma);
+  const int keff = min(k, nc);
+  const bool sample = keff > 0 && keff < nc;
+  int pc0 = 0, SP = 1, nsp = 0;
+  if (sample) {
+    pc0 = sigma / kPage;
+    const int ncp = (N - w + kPage - 1) / kPage - pc0;
+    while (SP < 32 && 2 * SP <= keff / 32) SP *= 2;
+    while ((ncp + SP - 1) / SP > kSamplePages) SP *= 2;
+    nsp = (ncp + SP - 1) / SP;
+  }
+  const PoolView view = make_pool_view(codes, radii, code_bytes, radius_bytes,
+                                       W, Hkv, g, lane);
+  // wave v samples pages t = v + 8*i; lane i holds the block id of its
+  // i-th page
+  const int32_t *bt = block_table + (int64_t)s * max_blocks;
+  const int tl = wave + kWv * lane;
+  const int blk_l = tl < nsp ? bt[pc0 + tl * SP] : -1;
+  uint32_t pcw[kPre][KS], pr8[kPre];
+  bool pok[kPre];
+  if (nsp > 0) {
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+      const int blk = __builtin_amdgcn_readlane(blk_l, u);
+      pok[u] = wave + kWv * u < nsp && blk >= 0 && blk < num_blocks;
+      load_page<KS>(view, blk, pok[u], pcw[u], pr8[u]);
+    }
+  }
+
   const uint16_t *qg = q + ((int64_t)s * Hq + (int64_t)g * G) * kHeadDim;
   for (int i = threadIdx.x; i < G * kHeadDim; i += kThreads)
-    sQ[i] = (double)bf16_to_float(qg[i]);
-  for (int i = threadIdx.x; i < kHeadDim * b; i += kThreads) sP[i] = proj[i];
+    sQ[i] = qg[i];
+  { // proj is 16-byte aligned (checked on the host)
+    const uint4 *src = reinterpret_cast<const uint4 *>(proj);
+    uint4 *dst = reinterpret_cast<uint4 *>(sP);
+    for (int i = threadIdx.x; i < kHeadDim * b / 8; i += kThreads) dst[i] = src[i];
+  }
   if (threadIdx.x < 8) sSum[threadIdx.x] = 0;
   __syncthreads();
 
@@ -100,10 +138,33 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     p[r] = 0.0;
     if (idx < npairs) {
       const int h = idx / b, j = idx % b;
+      // Batches of 8 terms: the next batch's LDS reads are issued before
+      // the current batch's multiply-adds, which stay in index order.
+      const uint4 *qrow = reinterpret_cast<const uint4 *>(sQ + h * kHeadDim);
+      const uint16_t *pcol = sP + j;
+      uint4 qa = qrow[0];
+      uint32_t pa[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) pa[u] = pcol[u * b];
       double acc = 0.0;
-#pragma unroll 16
-      for (int i = 0; i < kHeadDim; ++i)
-        acc = fma(sQ[h * kHeadDim + i], (double)bf16_to_float(sP[i * b + j]), acc);
+#pragma unroll 2
+      for (int i0 = 0; i0 < kHeadDim; i0 += 8) {
+        uint4 qn = qa;
+        uint32_t pn[8];
+        const int i1 = i0 + 8 < kHeadDim ? i0 + 8 : i0; // last batch reloads itself
+        qn = qrow[i1 / 8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) pn[u] = pcol[(i1 + u) * b];
+        const uint32_t qw[4] = {qa.x, qa.y, qa.z, qa.w};
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const uint32_t qb = (u & 1) ? (qw[u / 2] >> 16) : (qw[u / 2] & 0xFFFFu);
+          acc = fma((double)bf16_to_float(qb), (double)bf16_to_float(pa[u]), acc);
+        }
+        qa = qn;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) pa[u] = pn[u];
+      }
       p[r] = acc;
       mloc = fmax(mloc, fabs(acc));
     }
@@ -114,29 +175,35 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
   double M = sMax[0];
   for (int i = 1; i < kThreads / 64; ++i) M = fmax(M, sMax[i]);
 
-  int8_t *qo = q8 + ((int64_t)s * Hq + (int64_t)g * G) * b;
+  // Global stores wait until the end of the kernel: a barrier would
+  // otherwise wait for them to complete.
+  int qv[kMaxPairs];
 #pragma unroll
   for (int r = 0; r < kMaxPairs; ++r) {
     const int idx = threadIdx.x + r * kThreads;
-    if (idx < npairs) {
+    qv[r] = 0;
+    if (idx < npairs) { // wave-uniform: npairs and b are multiples of 64
       int v = 0;
       if (M != 0.0) {
         const double scaled = p[r] * 127.0;
         const double ratio = scaled / M;
         v = (int)fmin(127.0, fmax(-127.0, rint(ratio)));
       }
-      qo[idx] = (int8_t)v;
+      qv[r] = v;
       sq8[idx] = v;
-      atomicAdd(&sSum[idx / b], v);
+      int sum = v; // one head per wave
+      for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+      if (lane == 0) atomicAdd(&sSum[idx / b], sum);
     }
   }
   __syncthreads();
-  if (threadIdx.x < G)
-    qneg[(int64_t)s * Hq + (int64_t)g * G + threadIdx.x] = -(float)sSum[threadIdx.x];
 
   // matrix-core operand dwords: [KS][64 lanes][8 dwords]
-  uint32_t *dst = qop + (int64_t)unit * KS * 64 * 8;
-  for (int t = threadIdx.x; t < KS * 64 * 8; t += kThreads) {
+  constexpr int kOpWords = KS * 64 * 8;
+  uint32_t opw[kOpWords / kThreads];
+#pragma unroll
+  for (int r = 0; r < kOpWords / kThreads; ++r) {
+    const int t = threadIdx.x + r * kThreads;
     const int ks = t / 512, la = (t / 8) % 64, di = t % 8;
     const int row = la % 16, gA = la / 16;
     const int h = row / 2, part = row % 2;
@@ -157,26 +224,17 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
         word |= e4m3_of_int(v) << (8 * bi);
       }
     }
-    dst[t] = word;
+    opw[r] = word;
     sOp[t] = word;
   }
   __syncthreads();
 
-  // ---- candidate threshold from a page sample
-  const int N = seq_len_clamped(seq_lens, s, n_max);
-  const int nc = max(0, N - w - sigma);
-  const int keff = min(k, nc);
+  // ---- candidate threshold from the page sample
   // L = ~0 asks for no candidates (k_eff = 0, or every candidate is
   // selected and the merge marks them directly)
   uint32_t L = 0xFFFFFFFFu;
-  if (keff > 0 && keff < nc) {
+  if (sample) {
     L = 0;
-    const int pc0 = sigma / kPage, pc1 = (N - w + kPage - 1) / kPage;
-    const int ncp = pc1 - pc0;
-    int SP = 1;
-    while (SP < 32 && 2 * SP <= keff / 32) SP *= 2;
-    while ((ncp + SP - 1) / SP > kSamplePages) SP *= 2;
-    const int nsp = (ncp + SP - 1) / SP;
     QueryOperand<KS> op;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -187,16 +245,21 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
       op.cinit = v4f{0.f, h0 < G ? -(float)sSum[h0 < G ? h0 : 0] : 0.f, 0.f,
                      h1 < G ? -(float)sSum[h1 < G ? h1 : 0] : 0.f};
     }
-    const PoolView view = make_pool_view(codes, radii, code_bytes, radius_bytes,
-                                         W, Hkv, g, lane);
-    const int32_t *bt = block_table + (int64_t)s * max_blocks;
     uint32_t nvalid = 0;
-    // wave w samples pages t = w + 8*i; lane i holds the block id of its
-    // i-th page, and 8 pages' loads are in flight per step
-    constexpr int kWv = kThreads / 64;
-    const int tl = wave + kWv * lane;
-    const int blk_l = tl < nsp ? bt[pc0 + tl * SP] : -1;
-    for (int i0 = 0; wave + kWv * i0 < nsp; i0 += 8) {
+    auto keep = [&](int t, int S) {
+      if (lane < kPage && t < nsp) {
+        const int pos = (pc0 + t * SP) * kPage + lane;
+        const bool valid = pos >= sigma && pos < N - w;
+        sSample[t * kPage + lane] = valid ? (uint32_t)(S + (int)kScoreBias) : 0u;
+        nvalid += valid;
+      }
+    };
+#pragma unroll
+    for (int u = 0; u < kPre; ++u)
+      keep(wave + kWv * u, score_page<KS, G>(op, pcw[u], pr8[u], pok[u]));
+    // pages past the first kPre of each wave (long sequences with a small
+    // stride): 8 loads in flight per step
+    for (int i0 = kPre; wave + kWv * i0 < nsp; i0 += 8) {
       uint32_t cw[8][KS], r8[8];
       bool ok[8];
 #pragma unroll
@@ -207,37 +270,38 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
         load_page<KS>(view, blk, ok[u], cw[u], r8[u]);
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int t = wave + kWv * (i0 + u);
-        const int S = score_page<KS, G>(op, cw[u], r8[u], ok[u]);
-        if (lane < kPage && t < nsp) {
-          const int pos = (pc0 + t * SP) * kPage + lane;
-          const bool valid = pos >= sigma && pos < N - w;
-          sSample[t * kPage + lane] = valid ? (uint32_t)(S + (int)kScoreBias) : 0u;
-          nvalid += valid;
-        }
-      }
+      for (int u = 0; u < 8; ++u)
+        keep(wave + kWv * (i0 + u), score_page<KS, G>(op, cw[u], r8[u], ok[u]));
     }
     for (int off = 32; off > 0; off >>= 1) nvalid += __shfl_xor(nvalid, off);
     if (lane == 0) sCount[wave] = nvalid;
     __syncthreads();
     uint32_t ns = 0;
-    for (int i = 0; i < kThreads / 64; ++i) ns += sCount[i];
+    for (int i = 0; i < kWv; ++i) ns += sCount[i];
     const uint32_t ks_take = (uint32_t)min((int64_t)ns,
         ((int64_t)2 * keff * ns + nc - 1) / nc);
     if (ks_take > 0 && ks_take < ns) {
       const int nkeys = nsp * kPage;
-      uint32_t T, take_eq, n_eq;
-      wg_kth_largest<kThreads>(sel, [&](auto fn) {
+      L = wg_kth_largest_floor<kThreads>(sel, [&](auto fn) {
         for (int i = threadIdx.x; i < nkeys; i += kThreads) {
           const uint32_t v = sSample[i];
           if (v != 0u) fn(v);
         }
-      }, ks_take, T, take_eq, n_eq);
-      L = T;
+      }, ks_take);
     }
   }
   if (threadIdx.x == 0) lthr[unit] = L;
+  int8_t *qo = q8 + ((int64_t)s * Hq + (int64_t)g * G) * b;
+#pragma unroll
+  for (int r = 0; r < kMaxPairs; ++r) {
+    const int idx = threadIdx.x + r * kThreads;
+    if (idx < npairs) qo[idx] = (int8_t)qv[r];
+  }
+  uint32_t *dst = qop + (int64_t)unit * kOpWords;
+#pragma unroll
+  for (int r = 0; r < kOpWords / kThreads; ++r) dst[threadIdx.x + r * kThreads] = opw[r];
+  if (threadIdx.x < G)
+    qneg[(int64_t)s * Hq + (int64_t)g * G + threadIdx.x] = -(float)sSum[threadIdx.x];
 }
 
 } // namespace

@@ -7,26 +7,22 @@
 // DSA"]: a light indexer scores every cached key.  The per-page scoring is
 // in score_common.h (one fp8 x fp4 matrix-core op per 128 code bits).
 //
-// Work: persistent waves (4 per workgroup, up to 4 workgroups per CU),
-// each streaming a static stride of 64-page tasks (sequence, page group, KV
-// head); task ids run KV head fastest, then sequence, then page group, so
-// the heads of one page block are read together.  A wave's code pages go to
-// an 8 KB ring in LDS by direct buffer-to-LDS loads of 1 KB (one page quad
-// for 128-bit codes: lanes 16j..16j+15 fetch page j's 256 bytes, each lane
-// at its own page address), issued a ring ahead; each task's 64 radius
-// lines arrive the same way in one 1 KB load, double-buffered.  Each page
-// quad is scored from the ring (four matrix-core ops, results gathered into
-// one register: page j in lanes 16j..16j+15), and its ring slot is refilled
-// at once with the quad one ring further on (the next task's quads once the
-// current task's are all issued).  The 1024 biased scores of a task stay in
-// 16 registers; its candidates (positions in [sinks, N - window) with
-// u >= L) go, compacted by ballots in position order, to the task's own
-// region of the candidate buffer (room for every key of the group, so no
-// atomics and no overflow), and the task's count beside it.  A task always
-// issues the same number of stores, all lanes active (kTaskStores: one per
-// score row, the lanes without a candidate writing to the region's last
-// slot, which is read only when every key is a candidate, plus the count),
-// so both the ring waits and the compiler's own wait counts include them.
+// Work: persistent waves (4 per workgroup), each streaming a static stride
+// of 64-page tasks (sequence, page group, KV head); task ids run KV head
+// fastest, then sequence, then page group, so the heads of one page block
+// are read together.  Codes are key-major, so one 16-byte load per lane
+// brings a page quad: lanes 16j..16j+15 read page j's 16 keys (each lane a
+// whole 128-bit key; 64-bit keys use 8-byte loads, 256-bit keys two loads).
+// Four gfx950 row swaps (v_permlane32_swap, v_permlane16_swap) transpose
+// that into the matrix-core operand of each page (lane L: word L/16 of key
+// L%16).  Each lane also loads one radius byte per quad.  A wave keeps
+// kDepth quads of loads in flight in registers (the compiler's own wait
+// counts order them), continuing into the next task; the block ids of the
+// task after next are loaded one task ahead.  Candidates (positions in
+// [sinks, N - window) with u >= L) are compacted per quad by ballots, in
+// position order, into the task's own region of the candidate buffer (room
+// for every key of the group, so no atomics and no overflow), and the
+// task's count is written beside it.
 #include <algorithm>
 #include <type_traits>
 
@@ -37,21 +33,13 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kTaskQuads = kGroupPages / 4;  // page quads per task
-constexpr int kRingBytes = 8192;             // code ring per wave
-constexpr int kRadBytes = 1024;              // radius lines of one task
-constexpr uint32_t kRadiusOob = 0x80000000u; // past any radius buffer
-constexpr int kTaskStores = kTaskQuads + 1;  // stores issued per task
-
-// Buffer-to-LDS loads are invisible to the compiler's wait-count
-// tracking: a read of a ring slot must first wait until at most `n` vector
-// memory operations are outstanding, n being a lower bound on the number
-// issued after the slot's own loads (loads complete in issue order).
-template <int N>
-__device__ __forceinline__ void wait_vm_at_most() {
-  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
+constexpr int kTaskQuads = kGroupPages / 4; // page quads per task
+constexpr int kDepth = 4;                   // quads of loads in flight per wave
+static_assert(kTaskQuads % kDepth == 0 && kTaskQuads >= 2 * kDepth, "prefetch rounds");
+// quad of a task at which the task after next and the next task's operand
+// are loaded: kDepth quads before the next task's first prefetch
+constexpr int kLookahead = kTaskQuads - 2 * kDepth;
+constexpr int kStageCand = 128; // candidates per task staged in LDS
 
 // Compile-time loop: f(std::integral_constant<int, I>) for I in [I0, N).
 template <int I, int N, typename F>
@@ -62,119 +50,70 @@ __device__ __forceinline__ void static_for(F &&f) {
   }
 }
 
-// One LDS round trip per page quad, as a single asm block that also waits
-// for its results (the compiler cannot order reads of the ring against the
-// buffer-to-LDS loads; the explicit vmcnt wait before it does):
-//   - the page byte offsets of the KS refill loads (ds_bpermute of the
-//     refilled task's per-page offsets; `lp4` = 4 * page of this lane within
-//     a load, OFFB = 4 * first page of the refill);
-//   - this lane's code word of each page and K-step of ring slot SLOT (page
-//     p, K-step ks at word 64*(KS*p + ks) + lane; `base` = ring byte address
-//     + 4*lane);
-//   - its radius byte (key lane&15 of page 4*Q + lane>>4; `rbase` = radius
-//     buffer byte address + lane).
-template <int KS, int SLOT, int Q, int OFFB>
-__device__ __forceinline__ void read_quad(uint32_t base, uint32_t rbase,
-                                          uint32_t lp4, uint32_t page_off,
-                                          uint32_t (&cw)[4][KS], uint32_t &r8,
-                                          uint32_t (&vo)[KS]) {
-  constexpr int o = 4 * KS * SLOT; // in 256-byte units
-  if constexpr (KS == 1) {
-    uint64_t a, b;
-    asm volatile(
-        "ds_bpermute_b32 %3, %6, %7 offset:%8\n\t"
-        "ds_read2st64_b32 %0, %4 offset0:%9 offset1:%10\n\t"
-        "ds_read2st64_b32 %1, %4 offset0:%11 offset1:%12\n\t"
-        "ds_read_u8 %2, %5 offset:%13\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a), "=&v"(b), "=&v"(r8), "=&v"(vo[0])
-        : "v"(base), "v"(rbase), "v"(lp4), "v"(page_off), "n"(OFFB), "n"(o),
-          "n"(o + 1), "n"(o + 2), "n"(o + 3), "n"(64 * Q)
-        : "memory");
-    cw[0][0] = (uint32_t)a;
-    cw[1][0] = (uint32_t)(a >> 32);
-    cw[2][0] = (uint32_t)b;
-    cw[3][0] = (uint32_t)(b >> 32);
-  } else {
-    static_assert(KS == 2, "K-steps");
-    uint64_t a, b, c, d;
-    asm volatile(
-        "ds_bpermute_b32 %5, %9, %10 offset:%11\n\t"
-        "ds_bpermute_b32 %6, %9, %10 offset:%12\n\t"
-        "ds_read2st64_b32 %0, %7 offset0:%13 offset1:%14\n\t"
-        "ds_read2st64_b32 %1, %7 offset0:%15 offset1:%16\n\t"
-        "ds_read2st64_b32 %2, %7 offset0:%17 offset1:%18\n\t"
-        "ds_read2st64_b32 %3, %7 offset0:%19 offset1:%20\n\t"
-        "ds_read_u8 %4, %8 offset:%21\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(a), "=&v"(b), "=&v"(c), "=&v"(d), "=&v"(r8), "=&v"(vo[0]),
-          "=&v"(vo[1])
-        : "v"(base), "v"(rbase), "v"(lp4), "v"(page_off), "n"(OFFB),
-          "n"(OFFB + 8), "n"(o), "n"(o + 1), "n"(o + 2), "n"(o + 3), "n"(o + 4),
-          "n"(o + 5), "n"(o + 6), "n"(o + 7), "n"(64 * Q)
-        : "memory");
-    cw[0][0] = (uint32_t)a; cw[0][1] = (uint32_t)(a >> 32);
-    cw[1][0] = (uint32_t)b; cw[1][1] = (uint32_t)(b >> 32);
-    cw[2][0] = (uint32_t)c; cw[2][1] = (uint32_t)(c >> 32);
-    cw[3][0] = (uint32_t)d; cw[3][1] = (uint32_t)(d >> 32);
-  }
-}
-
-// An empty use of a register value: the compiler waits for its load here
-// (32-bit operands only, which the host pass of the compiler also accepts).
-__device__ __forceinline__ void mark_loaded(uint32_t x) { asm volatile("" ::"v"(x)); }
-
-// One 1 KB buffer-to-LDS load: lane L's 16 bytes at voff land at lds + 16*L.
-__device__ __forceinline__ void load_kb_to_lds(__amdgpu_buffer_rsrc_t rsrc,
-                                               uint32_t *lds, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      rsrc, (__attribute__((address_space(3))) void *)lds, 16, (int)voff, 0, 0, 0);
-}
-
 // One task of the stream (all fields wave-uniform); unit < 0: none.
 struct Task {
   int s, g, grp, unit, N, key0, npg, lo, hi;
 };
 
-template <int KS, int G>
-__global__ __launch_bounds__(kThreads) void filter_kernel(
+// Loaded code words of one page quad: lane 16j+c holds the KS*4 words of
+// key c of page j (words 4ks..4ks+3 in d[ks]).
+template <int KS>
+struct QuadLoad {
+  uint32_t d[KS][4];
+};
+
+// An empty use of a register value: the compiler waits for its load here
+// (32-bit operands only, which the host pass of the compiler also accepts).
+__device__ __forceinline__ void mark_loaded(uint32_t x) { asm volatile("" ::"v"(x)); }
+
+// 4x4 transpose across the four 16-lane rows: afterwards x[j] in row a holds
+// what x[a] held in row j (for every lane position in the row).
+__device__ __forceinline__ void transpose_rows(uint32_t (&x)[4]) {
+  auto a = __builtin_amdgcn_permlane32_swap(x[0], x[2], false, false);
+  auto b = __builtin_amdgcn_permlane32_swap(x[1], x[3], false, false);
+  auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+  auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  x[0] = c[0];
+  x[1] = c[1];
+  x[2] = d[0];
+  x[3] = d[1];
+}
+
+// W: code words per key (2, 4 or 8); KS: 128-bit matrix-core K-steps.
+template <int W, int G, int KS = (W > 4 ? W / 4 : 1)>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KS == 1 ? 6 : 4, 8))) void filter_kernel(
     const uint32_t *__restrict__ codes, const uint8_t *__restrict__ radii,
     int64_t num_blocks, uint32_t code_bytes, uint32_t radius_bytes,
     const int32_t *__restrict__ block_table, int max_blocks,
     const int32_t *__restrict__ seq_lens, int n_max,
     const uint32_t *__restrict__ qop, const float *__restrict__ qneg,
-    const uint32_t *__restrict__ lthr, int B, int Hkv, int W, int ngroups,
+    const uint32_t *__restrict__ lthr, int B, int Hkv, int ngroups,
     int ntasks, int w, int sigma, uint2 *__restrict__ cand,
     uint32_t *__restrict__ tcount, int cand_groups,
     int32_t *__restrict__ scores_out, int score_stride) {
-  constexpr int kQuadBytes = 1024 * KS;
-  constexpr int kRingQuads = kRingBytes / kQuadBytes;
-  // vector memory operations issued after a ring quad's loads, at least:
-  // the other ring quads' loads, and the previous task's stores when the
-  // quad was loaded during the previous task
-  constexpr int kAfterSame = (kRingQuads - 1) * KS;
-  constexpr int kAfterCross = kAfterSame + kTaskStores;
-  static_assert(kAfterCross < 64, "vmcnt is 6 bits");
-  static_assert(kRingQuads <= kTaskQuads && kTaskQuads % kRingQuads == 0, "ring");
-  __shared__ __attribute__((aligned(16))) uint32_t ring[kWaves][kRingBytes / 4];
-  __shared__ __attribute__((aligned(16))) uint32_t rring[kWaves][2][kRadBytes / 4];
-
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int stride = gridDim.x * kWaves;
   const int Hq = Hkv * G;
-  uint32_t *myring = ring[wave];
-  const uint32_t ring_base =
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)myring + 4u * lane;
-  // radius halves: the current task's and the next task's
-  uint32_t *rad_cur = rring[wave][0], *rad_next = rring[wave][1];
-  const PoolView view = make_pool_view(codes, radii, code_bytes, radius_bytes, W,
-                                       Hkv, 0, lane);
-  const int code_dwords = W * kPage;
-  // this lane's page within a 1 KB load and its 16-byte chunk of that page
-  // (for 64-bit codes the upper half of each 256-byte slot repeats the page)
-  const uint32_t lp4 = (uint32_t)(lane / (16 * KS)) * 4u;
-  const uint32_t chunk = 16u * (uint32_t)(lane & (code_dwords / 4 - 1));
+  const __amdgpu_buffer_rsrc_t code_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t *>(codes), 0, code_bytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rad_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(radii), 0, radius_bytes, kBufferWord3);
+  const uint32_t page_bytes = (uint32_t)(kPage * W * 4);
+  // physical page id past the pools: its code and radius loads read 0
+  const uint32_t ph_none = (uint32_t)(num_blocks * Hkv);
+  const uint32_t key_byte = (uint32_t)((lane & 15) * W * 4);
+  const int row = lane >> 4;
+  // per-wave tables of the current and the next task's page ids (lane j
+  // writes page j), read back per page quad by row: one LDS read per quad
+  __shared__ uint32_t ptab[kWaves][2][kGroupPages];
+  uint32_t *tabC = ptab[wave][0], *tab1 = ptab[wave][1];
+  // the current task's radius lines (16 bytes per page, page order), and
+  // its candidates staged before they are written out
+  __shared__ __attribute__((aligned(16))) uint8_t rtab[kWaves][kGroupKeys];
+  __shared__ uint2 cstage[kWaves][kStageCand];
+  uint8_t *radC = rtab[wave];
+  uint2 *cst = cstage[wave];
 
   // task id -> task, or none if its page group is past the sequence
   auto decode = [&](int t, Task &T) -> bool {
@@ -183,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void filter_kernel(
     T.s = r % B;
     T.grp = r / B;
     T.N = seq_len_clamped(seq_lens, T.s, n_max);
-    T.key0 = T.grp * kGroupPages * kPage;
+    T.key0 = T.grp * kGroupKeys;
     if (T.key0 >= T.N) return false;
     T.unit = T.s * Hkv + T.g;
     T.npg = min(kGroupPages, (T.N - T.key0 + kPage - 1) / kPage);
@@ -192,165 +131,204 @@ __global__ __launch_bounds__(kThreads) void filter_kernel(
     return true;
   };
   // the first non-empty task at or after t in this wave's stride
-  auto find = [&](int t, Task &T) -> int {
+  auto find = [&](int t, Task &T) {
     for (; t < ntasks; t += stride)
       if (decode(t, T)) return t;
     T.unit = -1;
     return ntasks;
   };
-  // Lane j: the task's block id of page j (-1 past the task), loaded one
-  // task before its offsets are needed so the load is long done by then.
-  auto load_blk = [&](const Task &T) -> int {
+  // Lane j: physical page id (page block index) of the task's page j, or
+  // ph_none past the task or for an invalid block id.
+  auto load_pages = [&](const Task &T) -> int {
     int blk = -1;
     if (T.unit >= 0 && lane < T.npg)
       blk = block_table[(int64_t)T.s * max_blocks + T.key0 / kPage + lane];
     return blk;
   };
-  // Lane j: byte offsets of page j (code block, radius line); invalid
-  // pages read physical page 0's code and a radius of 0.
-  auto page_offsets = [&](const Task &T, int blk, uint32_t &code_off,
-                          uint32_t &rad_off) {
-    const bool ok = blk >= 0 && blk < num_blocks;
-    const uint32_t ph = (uint32_t)blk * (uint32_t)Hkv + (uint32_t)T.g;
-    code_off = ok ? ph * view.page_code_bytes : 0u;
-    rad_off = ok ? ph * (uint32_t)kPage : kRadiusOob;
+  auto page_ids = [&](const Task &T, int blk) -> uint32_t {
+    return (blk >= 0 && blk < num_blocks) ? (uint32_t)blk * (uint32_t)Hkv + (uint32_t)T.g
+                                          : ph_none;
   };
-  auto load_op = [&](const Task &T, QueryOperand<KS> &op, uint32_t &L) {
+  auto load_op = [&](const Task &T, QueryOperandRaw<KS> &op, uint32_t &L) {
     const int unit = T.unit >= 0 ? T.unit : 0;
-    op = load_query_operand<KS, G>(qop, qneg, unit, unit / Hkv, unit % Hkv, Hq, lane);
+    load_query_operand_raw<KS, G>(qop, qneg, unit, unit / Hkv, unit % Hkv, Hq, lane, op);
     L = lthr[unit];
   };
+  // Loads a page quad; `mine` is the page id of this lane's page (page
+  // lane>>4 of the quad).
+  auto load_quad = [&](uint32_t mine, QuadLoad<KS> &ql) {
+    const int voff = (int)(mine * page_bytes + key_byte);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if constexpr (W == 2) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(code_rsrc, voff, 0, 0);
+        ql.d[ks][0] = v[0];
+        ql.d[ks][1] = v[1];
+        ql.d[ks][2] = 0u;
+        ql.d[ks][3] = 0u;
+      } else {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(code_rsrc, voff + 16 * ks, 0, 0);
+        ql.d[ks][0] = v[0];
+        ql.d[ks][1] = v[1];
+        ql.d[ks][2] = v[2];
+        ql.d[ks][3] = v[3];
+      }
+    }
+  };
 
-  Task C, N1;
-  int tC = find(blockIdx.x * kWaves + wave, C);
+  // ---- prologue: the first task, its successor, their page ids, operand
+  Task C, T1;
+  const int tC = find(blockIdx.x * kWaves + wave, C);
   if (C.unit < 0) return;
-  int tN = find(tC + stride, N1);
-  uint32_t cC, rC, cN, rN;
-  {
-    const int blkC = load_blk(C), blkN = load_blk(N1);
-    page_offsets(C, blkC, cC, rC);
-    page_offsets(N1, blkN, cN, rN);
-  }
+  int t1 = find(tC + stride, T1);
+  tabC[lane] = page_ids(C, load_pages(C));
+  tab1[lane] = page_ids(T1, load_pages(T1));
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   QueryOperand<KS> opC;
   uint32_t LC;
-  load_op(C, opC, LC);
-  // everything above has landed before the stream starts, so no wait in
-  // the loop below is ever for a load of this prologue; the empty asm uses
-  // tell the compiler so too (it does not read the wait above), otherwise
-  // it would wait for them again, behind the whole ring, in every task
-  wait_vm_at_most<0>();
+  {
+    QueryOperandRaw<KS> raw;
+    load_op(C, raw, LC);
+    opC = finish_query_operand<KS, G>(raw, lane);
+  }
+  // The loop below carries opC; uses here make the compiler wait for its
+  // loads now, before the stream starts, instead of (merging this path into
+  // the loop head) in every task.
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
     for (int i = 0; i < 8; ++i) mark_loaded((uint32_t)opC.a[ks][i]);
 #pragma unroll
   for (int i = 0; i < 4; ++i) mark_loaded(__float_as_uint(opC.cinit[i]));
-  mark_loaded(cC);
-  mark_loaded(rC);
-  mark_loaded(cN);
-  mark_loaded(rN);
-  load_kb_to_lds(view.radius, rad_cur, rC);
-  static_for<0, kRingQuads>([&](auto qc) {
+  // radius lines: lane j loads page j's 16 bytes (a task ahead of use)
+  auto load_radius = [&](uint32_t ph) -> uint4 {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rad_rsrc, (int)(ph * (uint32_t)kPage), 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+  };
+  auto store_radius = [&](const uint4 &v) {
+    *reinterpret_cast<uint4 *>(radC + 16 * lane) = v;
+  };
+  store_radius(load_radius(tabC[lane]));
+  uint4 radN = load_radius(tab1[lane]);
+  QuadLoad<KS> buf[kDepth];
+  static_for<0, kDepth>([&](auto qc) {
     constexpr int q = decltype(qc)::value;
-#pragma unroll
-    for (int m = 0; m < KS; ++m) {
-      const uint32_t page = 4 * q + m * (4 / KS) + (lane / (16 * KS));
-      const uint32_t vo = (uint32_t)__builtin_amdgcn_ds_bpermute((int)page * 4, (int)cC);
-      load_kb_to_lds(view.code, myring + (q * kQuadBytes + 1024 * m) / 4, vo + chunk);
-    }
+    load_quad(tabC[4 * q + row], buf[q]);
   });
-  // the stores a finished task would have issued, so that the first task's
-  // ring waits count the same operations as every later one (written to the
-  // last slot of C's region, which is never read unless C's own candidate
-  // writes, issued later by this wave, fill it); written as asm so that
-  // exactly kTaskStores store instructions are issued
-  {
-    const uint64_t dummy = reinterpret_cast<uint64_t>(
-        cand + ((int64_t)C.unit * cand_groups + C.grp) * kGroupKeys + (kGroupKeys - 1));
-    const uint64_t zero = 0;
-#pragma unroll
-    for (int r = 0; r < kTaskStores; ++r)
-      asm volatile("global_store_dwordx2 %0, %1, off" ::"v"(dummy), "v"(zero)
-                   : "memory");
-  }
 
-  while (true) {
-    // look ahead: the task after next (its block ids) and the next task's
-    // query operand
-    Task N2 = {0, 0, 0, -1, 0, 0, 0, 0, 0};
-    const int tN2 = N1.unit >= 0 ? find(tN + stride, N2) : ntasks;
-    if (N1.unit < 0) N2.unit = -1;
-    const int blkN2 = load_blk(N2);
-    QueryOperand<KS> opN;
-    uint32_t LN;
-    load_op(N1, opN, LN);
-    const uint32_t rad_base =
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)rad_cur +
-        (uint32_t)lane;
-
-    uint32_t u[kTaskQuads];
+  // One task: score C's 16 quads while prefetching, then rotate the stream.
+  // The first call is peeled off the loop so that the loop head is only
+  // entered in the state a task leaves (the compiler's wait counts at the
+  // loop head then match the steady state).
+  auto run_task = [&]() -> bool {
+    Task T2 = {0, 0, 0, -1, 0, 0, 0, 0, 0};
+    int t2 = ntasks;
+    int blk2 = -1; // raw block ids, turned into page ids one task later
+    QueryOperandRaw<KS> op1;
+    uint32_t L1 = 0;
+    const int64_t t_idx = (int64_t)C.unit * cand_groups + C.grp;
+    uint2 *reg = cand + t_idx * kGroupKeys;
+    uint32_t nc = 0;
     static_for<0, kTaskQuads>([&](auto qc) {
       constexpr int q = decltype(qc)::value;
-      constexpr int slot = q % kRingQuads;
-      constexpr int tq = q + kRingQuads; // stream position one ring ahead
-      constexpr bool next = tq >= kTaskQuads;
-      constexpr int rq = next ? tq - kTaskQuads : tq; // refilled task's quad
-      // the next task's radius lines go out before its first code
-      if constexpr (next && rq == 0) load_kb_to_lds(view.radius, rad_next, rN);
-      wait_vm_at_most<(q >= kRingQuads) ? kAfterSame : kAfterCross>();
-      uint32_t cw[4][KS], r8, vo[KS];
-      read_quad<KS, slot, q, 16 * rq>(ring_base, rad_base, lp4, next ? cN : cC,
-                                      cw, r8, vo);
-#pragma unroll
-      for (int m = 0; m < KS; ++m)
-        load_kb_to_lds(view.code, myring + (slot * kQuadBytes + 1024 * m) / 4,
-                       vo[m] + chunk);
-      const int mx = score_quad_max<KS, G>(opC, cw);
-      u[q] = (uint32_t)(__mul24((int)r8, mx) + (int)kScoreBias);
-    });
-
-    if (scores_out != nullptr) {
-      int32_t *so = scores_out + (int64_t)C.unit * score_stride;
-#pragma unroll
-      for (int q = 0; q < kTaskQuads; ++q) {
-        const int pos = C.key0 + 64 * q + lane;
-        if (pos < C.N) so[pos] = (int32_t)(u[q] - kScoreBias);
+      constexpr int slot = q % kDepth;
+      if constexpr (q == kLookahead) {
+        // the task after next (its page ids, used one task from now) and
+        // the next task's operand (used from the next task's first quad)
+        if (T1.unit >= 0) t2 = find(t1 + stride, T2);
+        blk2 = load_pages(T2);
+        load_op(T1, op1, L1);
       }
-    }
-    // this task's candidates, in position order, to its own region
-    {
-      const int64_t t_idx = (int64_t)C.unit * cand_groups + C.grp;
-      uint2 *reg = cand + t_idx * kGroupKeys;
-      uint32_t nc = 0;
+      // ---- score quad q of C
+      uint32_t x[KS][4];
 #pragma unroll
-      for (int r = 0; r < kTaskQuads; ++r) {
-        const int pos = C.key0 + r * 64 + lane;
-        const bool c = pos >= C.lo && pos < C.hi && u[r] >= LC;
-        const uint64_t m = __ballot(c);
-        const uint32_t slot = c ? nc + lanes_below(m) : kGroupKeys - 1;
-        reg[slot] = make_uint2(u[r], (uint32_t)pos);
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[ks][i] = buf[slot].d[ks][i];
+      // radius byte of key lane&15 of page 4q + lane>>4
+      const uint32_t r8 = radC[64 * q + lane];
+      // ---- refill the slot: the quad kDepth further on (C's, or T1's
+      // first ones)
+      if constexpr (q + kDepth < kTaskQuads)
+        load_quad(tabC[4 * (q + kDepth) + row], buf[slot]);
+      else
+        load_quad(tab1[4 * (q + kDepth - kTaskQuads) + row], buf[slot]);
+      uint32_t cw[4][KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        transpose_rows(x[ks]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cw[j][ks] = x[ks][j];
+      }
+      const int mx = score_quad_max_seq<KS, G>(opC, cw);
+      const uint32_t u = (uint32_t)(__mul24((int)r8, mx) + (int)kScoreBias);
+      const int qpos = C.key0 + 64 * q; // first position of the quad
+      const int pos = qpos + lane;
+      if (scores_out != nullptr) {
+        if (pos < C.N)
+          scores_out[(int64_t)C.unit * score_stride + pos] = (int32_t)(u - kScoreBias);
+      }
+      // whole quad inside [lo, hi) (the common case): only the threshold
+      const bool inside = qpos >= C.lo && qpos + 64 <= C.hi;
+      const bool c = inside ? u >= LC : (pos >= C.lo && pos < C.hi && u >= LC);
+      const uint64_t m = __ballot(c);
+      if (m != 0) {
+        // staged in LDS (no vector-memory store inside the stream); past
+        // the stage, straight to the region (rare)
+        const uint32_t slot = nc + lanes_below(m);
+        const uint64_t v = ((uint64_t)(uint32_t)pos << 32) | u; // (u, pos)
+        // address-space-qualified pointers keep these an LDS store and a
+        // global store (a merged flat store would count against both wait
+        // counters)
+        if (c && slot < (uint32_t)kStageCand)
+          ((__attribute__((address_space(3))) uint64_t *)cst)[slot] = v;
+        if (nc + __popcll(m) > (uint32_t)kStageCand) { // wave-uniform, rare
+          if (c && slot >= (uint32_t)kStageCand)
+            ((__attribute__((address_space(1))) uint64_t *)reg)[slot] = v;
+        }
         nc += __popcll(m);
+      }
+    });
+    // Write the staged candidates with a fixed number of stores, every lane
+    // active (lanes past the count write the region's last slot, which is
+    // read only when all 1024 keys are candidates -- and then no lane is
+    // past the count here), and the count.
+    {
+      const uint32_t ns = min(nc, (uint32_t)kStageCand);
+#pragma unroll
+      for (int r = 0; r < kStageCand / 64; ++r) {
+        const uint32_t e = (uint32_t)(64 * r + lane);
+        const uint2 v = cst[e < ns ? e : 0];
+        reg[e < ns ? e : kGroupKeys - 1] = v;
       }
       tcount[t_idx] = nc;
     }
 
     // rotate the stream
-    if (N1.unit < 0) break;
-    C = N1;
-    tC = tN;
-    cC = cN;
-    rC = rN;
-    opC = opN;
-    LC = LN;
-    N1 = N2;
-    tN = tN2;
-    page_offsets(N2, blkN2, cN, rN);
-    uint32_t *t = rad_cur;
-    rad_cur = rad_next;
-    rad_next = t;
-  }
-  // no buffer-to-LDS load may still be in flight when the wave ends
-  wait_vm_at_most<0>();
+    if (T1.unit < 0) return false;
+    C = T1;
+    opC = finish_query_operand<KS, G>(op1, lane);
+    LC = L1;
+    T1 = T2;
+    t1 = t2;
+    {
+      uint32_t *t = tabC;
+      tabC = tab1;
+      tab1 = t;
+    }
+    // the old current table is no longer read: T2's page ids go there
+    tab1[lane] = page_ids(T2, blk2);
+    // the new current task's radius lines (loaded a task ago) into LDS, and
+    // the new next task's lines requested
+    store_radius(radN);
+    radN = load_radius(tab1[lane]);
+    return true;
+  };
+  if (run_task())
+    while (run_task()) {
+    }
 }
 
 } // namespace
@@ -368,29 +346,36 @@ hipError_t launch_score(const DecodeDims &d, const uint32_t *codes,
   if (ntasks > 0x7FFFFFFF - 65536) return hipErrorInvalidValue;
   const uint32_t code_bytes = (uint32_t)((uint64_t)d.num_blocks * d.Hkv * d.W * kPage * 4);
   const uint32_t radius_bytes = (uint32_t)((uint64_t)d.num_blocks * d.Hkv * kPage);
-  // persistent grid: as many workgroups as fit in a CU's LDS
-  constexpr int kLdsPerWg = kWaves * (kRingBytes + 2 * kRadBytes);
-  const int wg_per_cu = std::max(1, std::min(8, kLdsPerCu / kLdsPerWg));
-  const int64_t nwg = std::min<int64_t>((ntasks + kWaves - 1) / kWaves,
-                                        (int64_t)wg_per_cu * device_cu_count());
-#define DKV_SCORE_CASE(KSV, GV)                                                \
-  if (d.KS == KSV && d.G == GV) {                                              \
-    hipLaunchKernelGGL((filter_kernel<KSV, GV>), dim3((unsigned)nwg),          \
+#define DKV_SCORE_CASE(WV, GV)                                                 \
+  if (d.W == WV && d.G == GV) {                                                \
+    static int per_cu = 0; /* resident workgroups per CU (register-bound) */  \
+    if (per_cu <= 0 &&                                                         \
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(                          \
+            &per_cu, filter_kernel<WV, GV>, kThreads, 0) != hipSuccess)        \
+      per_cu = 1;                                                              \
+    const int64_t nwg = std::min<int64_t>((ntasks + kWaves - 1) / kWaves,       \
+                                          (int64_t)std::max(1, per_cu) *        \
+                                              device_cu_count());               \
+    hipLaunchKernelGGL((filter_kernel<WV, GV>), dim3((unsigned)nwg),           \
                        dim3(kThreads), 0, stream, codes, radii, d.num_blocks,  \
                        code_bytes, radius_bytes, block_table, d.max_blocks,    \
-                       seq_lens, d.n_max, qop, qneg, lthr, d.B, d.Hkv, d.W,    \
+                       seq_lens, d.n_max, qop, qneg, lthr, d.B, d.Hkv,         \
                        (int)ngroups, (int)ntasks, d.w, d.sigma, cand, tcount,  \
                        d.cand_groups, scores_out, d.max_seq_len);              \
     return hipGetLastError();                                                  \
   }
-  DKV_SCORE_CASE(1, 1)
-  DKV_SCORE_CASE(1, 2)
-  DKV_SCORE_CASE(1, 4)
-  DKV_SCORE_CASE(1, 8)
   DKV_SCORE_CASE(2, 1)
   DKV_SCORE_CASE(2, 2)
   DKV_SCORE_CASE(2, 4)
   DKV_SCORE_CASE(2, 8)
+  DKV_SCORE_CASE(4, 1)
+  DKV_SCORE_CASE(4, 2)
+  DKV_SCORE_CASE(4, 4)
+  DKV_SCORE_CASE(4, 8)
+  DKV_SCORE_CASE(8, 1)
+  DKV_SCORE_CASE(8, 2)
+  DKV_SCORE_CASE(8, 4)
+  DKV_SCORE_CASE(8, 8)
 #undef DKV_SCORE_CASE
   return hipErrorInvalidValue;
 }

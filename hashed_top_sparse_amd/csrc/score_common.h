@@ -8,9 +8,10 @@
 //
 // The per-page work is one 16x16x128 fp8 x fp4 matrix-core op per 128 code
 // bits (operand layout: see qprep.hip):
-//   - lane L loads dword L (+64 per K-step) of the page's code block, which
-//     is word L/16 of the key in slot L%16; the word is expanded to fp4 with
-//     5 bit operations (nibble values 0.5/1/2/0.5 for bits 4e+m, m = 0..3);
+//   - lane L holds word L/16 (+4 per K-step) of the key in slot L%16 (code
+//     blocks are key-major: a key's b/32 words are contiguous); the word is
+//     expanded to fp4 with 5 bit operations (nibble values 0.5/1/2/0.5 for
+//     bits 4e+m, m = 0..3);
 //   - the query operand holds 2*hi/f_m and 2*lo/f_m per head (q8 = 16*hi +
 //     lo), and the accumulator starts at -Q in the low rows, so row 2h gives
 //     2*D_hi and row 2h+1 gives 2*D_lo - Q exactly (D = sum_j q8_j*bit_j);
@@ -59,6 +60,47 @@ load_query_operand(const uint32_t *qop, const float *qneg, int unit, int s,
   return op;
 }
 
+// The operand's loaded parts, kept raw until used (the accumulator's start
+// value is selected per lane only then), so a load issued well ahead is not
+// waited for at once.
+template <int KS>
+struct QueryOperandRaw {
+  v8i a[KS];
+  float q0, q1;
+};
+
+template <int KS, int G>
+__device__ __forceinline__ void load_query_operand_raw(const uint32_t *qop,
+                                                       const float *qneg, int unit,
+                                                       int s, int g, int Hq, int lane,
+                                                       QueryOperandRaw<KS> &r) {
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(
+        qop + (((int64_t)unit * KS + ks) * 64 + lane) * 8);
+    const uint4 x0 = src[0], x1 = src[1];
+    r.a[ks][0] = (int)x0.x; r.a[ks][1] = (int)x0.y;
+    r.a[ks][2] = (int)x0.z; r.a[ks][3] = (int)x0.w;
+    r.a[ks][4] = (int)x1.x; r.a[ks][5] = (int)x1.y;
+    r.a[ks][6] = (int)x1.z; r.a[ks][7] = (int)x1.w;
+  }
+  const int h0 = 2 * (lane >> 4), h1 = h0 + 1;
+  const float *qn = qneg + (int64_t)s * Hq + (int64_t)g * G;
+  r.q0 = qn[h0 < G ? h0 : 0];
+  r.q1 = qn[h1 < G ? h1 : 0];
+}
+
+template <int KS, int G>
+__device__ __forceinline__ QueryOperand<KS> finish_query_operand(
+    const QueryOperandRaw<KS> &r, int lane) {
+  QueryOperand<KS> op;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) op.a[ks] = r.a[ks];
+  const int h0 = 2 * (lane >> 4), h1 = h0 + 1;
+  op.cinit = v4f{0.f, h0 < G ? r.q0 : 0.f, 0.f, h1 < G ? r.q1 : 0.f};
+  return op;
+}
+
 __device__ __forceinline__ v8i expand_code_word(uint32_t w) {
   v8i r;
   r[0] = (int)(w & 0x11111111u);
@@ -93,8 +135,15 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
 // are given; valid in lanes 0..15 (slot = lane).  Every lane must call it.
 template <int KS, int G>
 __device__ __forceinline__ int score_page(const QueryOperand<KS> &op,
-                                          const uint32_t (&cw)[KS], uint32_t r8,
+                                          uint32_t (&cw_in)[KS], uint32_t r8,
                                           bool ok) {
+  // The loaded words are first read here: without this the compiler may
+  // move their first use (the radius conversion) up to the loads and wait
+  // for each load as it is issued.
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(cw_in[ks]));
+  asm volatile("" : "+v"(r8));
+  const uint32_t (&cw)[KS] = cw_in;
   v4f acc = op.cinit;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
@@ -159,6 +208,43 @@ __device__ __forceinline__ int score_quad_max(const QueryOperand<KS> &op,
   return (int)c[0];
 }
 
+// score_quad_max with the four pages scored one after another (one
+// accumulator and one expanded operand live at a time: fewer registers, for
+// kernels that need many waves per SIMD); the maxima stay in fp32 (exact
+// integers) through the row swaps and are converted once.
+template <int KS, int G>
+__device__ __forceinline__ int score_quad_max_seq(const QueryOperand<KS> &op,
+                                                  const uint32_t (&cw)[4][KS]) {
+  float x[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v4f acc = op.cinit;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          op.a[ks], expand_code_word(cw[j][ks]), acc, 0, 4, 0, 127, 0, 127);
+    float m = 16.f * acc[0] + acc[1];
+    if (G >= 2) m = fmaxf(m, 16.f * acc[2] + acc[3]);
+    // all 64 lanes take part: keep the op in wave-uniform control flow, and
+    // in page order
+    asm volatile("" : "+v"(m));
+    if (G >= 8) m = max_rows32(m);
+    x[j] = m;
+  }
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[0]),
+                                                  __float_as_uint(x[1]), false, false);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[2]),
+                                                  __float_as_uint(x[3]), false, false);
+  float y01 = __uint_as_float(a[0]), y23 = __uint_as_float(b[0]);
+  if (G >= 4) {
+    y01 = fmaxf(y01, __uint_as_float(a[1]));
+    y23 = fmaxf(y23, __uint_as_float(b[1]));
+  }
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(y01),
+                                                  __float_as_uint(y23), false, false);
+  return (int)__uint_as_float(c[0]);
+}
+
 // Raw buffer views of the code and radius pools (byte sizes < 2^32).
 struct PoolView {
   __amdgpu_buffer_rsrc_t code, radius;
@@ -181,9 +267,11 @@ __device__ __forceinline__ PoolView make_pool_view(const uint32_t *codes,
   v.page_code_bytes = (uint32_t)code_dwords * 4u;
   v.Hkv = Hkv;
   v.g = g;
-  // For b = 64 the upper 32 lanes re-read the block's first 32 words: the
-  // query operand is zero at those k and fp4 has no NaN/Inf, so they add 0.
-  v.code_voff = (lane & (code_dwords - 1)) * 4;
+  // Lane L: word L/16 of key L%16 (key-major block, W = b/32 words per
+  // key).  For b = 64 the upper 32 lanes re-read words 0 and 1: the query
+  // operand is zero at those k and fp4 has no NaN/Inf, so they add 0.
+  const int W_ = code_dwords / kPage;
+  v.code_voff = (lane & 15) * W_ * 4 + ((lane >> 4) & (W_ - 1)) * 4;
   v.radius_voff = lane & (kPage - 1);
   return v;
 }
@@ -198,7 +286,7 @@ __device__ __forceinline__ void load_page(const PoolView &v, int blk, bool ok,
       (uint32_t)v.g;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
-    cw[ks] = __builtin_amdgcn_raw_buffer_load_b32(v.code, v.code_voff + 256 * ks,
+    cw[ks] = __builtin_amdgcn_raw_buffer_load_b32(v.code, v.code_voff + 16 * ks,
                                                   ph * v.page_code_bytes, 0);
   r8 = __builtin_amdgcn_raw_buffer_load_b8(v.radius, v.radius_voff,
                                            ph * (uint32_t)kPage, 0);

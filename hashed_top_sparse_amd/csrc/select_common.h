@@ -51,6 +51,58 @@ __device__ void find_threshold_bin(SelectShared<NT> &sh, uint32_t kneed) {
   __syncthreads();
 }
 
+// Value range of the elements visit(fn) hands out, and the histogram of
+// (v - vmin) >> shift with the shift chosen so the range fits the bins.
+// Every thread must call it; ends with a barrier.
+template <int NT, class Visit>
+__device__ void wg_histogram(SelectShared<NT> &sh, Visit visit, uint32_t &vmin,
+                             int &shift) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+  visit([&](uint32_t v) {
+    lo = min(lo, v);
+    hi = max(hi, v);
+  });
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    lo = min(lo, (uint32_t)__shfl_xor((int)lo, off));
+    hi = max(hi, (uint32_t)__shfl_xor((int)hi, off));
+  }
+  if (lane == 0) {
+    sh.red[0][wave] = lo;
+    sh.red[1][wave] = hi;
+  }
+  for (int i = threadIdx.x; i < kHistBins; i += NT) sh.hist[i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    lo = min(lo, sh.red[0][i]);
+    hi = max(hi, sh.red[1][i]);
+  }
+  const uint32_t range = hi - lo;
+  const int bits = range == 0 ? 0 : 32 - __clz(range);
+  shift = bits > kHistBits ? bits - kHistBits : 0;
+  vmin = lo;
+  const int sh_ = shift;
+  visit([&](uint32_t v) { atomicAdd(&sh.hist[(v - lo) >> sh_], 1u); });
+  __syncthreads();
+}
+
+// A lower bound of the kneed-th largest element (1 <= kneed <= element
+// count): the lowest value of the histogram bin that holds it, so at least
+// kneed elements are >= the result.  Every thread must call it.
+template <int NT, class Visit>
+__device__ uint32_t wg_kth_largest_floor(SelectShared<NT> &sh, Visit visit,
+                                         uint32_t kneed) {
+  uint32_t vmin;
+  int shift;
+  wg_histogram<NT>(sh, visit, vmin, shift);
+  find_threshold_bin<NT>(sh, kneed);
+  const uint32_t T = vmin + ((uint32_t)sh.bin << shift);
+  __syncthreads();
+  return T;
+}
+
 // Exact kneed-th largest value (1 <= kneed <= element count) of the
 // elements that visit(fn) hands to fn(uint32_t) -- each element exactly
 // once across the workgroup.  Returns T, the number of elements equal to T
@@ -59,33 +111,9 @@ __device__ void find_threshold_bin(SelectShared<NT> &sh, uint32_t kneed) {
 template <int NT, class Visit>
 __device__ void wg_kth_largest(SelectShared<NT> &sh, Visit visit, uint32_t kneed,
                                uint32_t &T, uint32_t &take_eq, uint32_t &n_eq) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t vmin = 0xFFFFFFFFu, vmax = 0u;
-  visit([&](uint32_t v) {
-    vmin = min(vmin, v);
-    vmax = max(vmax, v);
-  });
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    vmin = min(vmin, (uint32_t)__shfl_xor((int)vmin, off));
-    vmax = max(vmax, (uint32_t)__shfl_xor((int)vmax, off));
-  }
-  if (lane == 0) {
-    sh.red[0][wave] = vmin;
-    sh.red[1][wave] = vmax;
-  }
-  for (int i = threadIdx.x; i < kHistBins; i += NT) sh.hist[i] = 0;
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < NT / 64; ++i) {
-    vmin = min(vmin, sh.red[0][i]);
-    vmax = max(vmax, sh.red[1][i]);
-  }
-  const uint32_t range = vmax - vmin;
-  const int bits = range == 0 ? 0 : 32 - __clz(range);
-  const int shift = bits > kHistBits ? bits - kHistBits : 0;
-  visit([&](uint32_t v) { atomicAdd(&sh.hist[(v - vmin) >> shift], 1u); });
-  __syncthreads();
+  uint32_t vmin;
+  int shift;
+  wg_histogram<NT>(sh, visit, vmin, shift);
   find_threshold_bin<NT>(sh, kneed);
   const uint32_t b1 = (uint32_t)sh.bin;
   const uint32_t kneed2 = kneed - sh.above;

@@ -39,9 +39,9 @@
  * Memory layouts (all device memory, row-major, little-endian):
  *   bf16 tensors are passed as 16-bit bit patterns.
  *   k_pool, v_pool  [num_blocks][16][Hkv][d]   bf16  (16-token pages)
- *   codes           [num_blocks][Hkv][b/32][16] uint32 (word-major per page:
- *                   word w of the key in slot t of the page is at index
- *                   ((blk*Hkv + h)*(b/32) + w)*16 + t)
+ *   codes           [num_blocks][Hkv][16][b/32] uint32 (key-major: the b/32
+ *                   words of the key in slot t of the page are contiguous,
+ *                   word w at index ((blk*Hkv + h)*16 + t)*(b/32) + w)
  *   radii           [num_blocks][Hkv][16]      uint8
  *   block_table     [batch][max_blocks_per_seq] int32 physical page ids
  *                   (the same id indexes k_pool, v_pool, codes and radii)
@@ -49,6 +49,9 @@
  *   q               [batch][Hq][d]             bf16  (head h is in KV group
  *                                                      h / G)
  *   out             [batch][Hq][d]             fp32
+ *   q, k_pool, v_pool, codes, radii and proj must be 16-byte aligned (a
+ *   misaligned pointer returns DKV_ERR_INVALID_ARG); allocations from the
+ *   HIP or torch allocators always are.
  *
  * Ownership and execution: the caller owns every buffer; the library
  * allocates no device or host memory and keeps no mutable global state, so
@@ -121,7 +124,7 @@ typedef struct {
  *   max_encode_len  host bound on enc_end[s]-enc_start[s] for every s (sizes
  *                the grid; tokens beyond it are not encoded)
  *   proj         device, bf16 [d][b]
- *   codes        device, uint32 [num_blocks][Hkv][b/32][16] (output)
+ *   codes        device, uint32 [num_blocks][Hkv][16][b/32] (output)
  *   radii        device, uint8  [num_blocks][Hkv][16]       (output)
  * Bits are bit-exact with the definition above: the projection is summed in
  * double precision in index order (a product of two bf16 values is exact in

@@ -34,11 +34,11 @@ def logical_rows(pool: torch.Tensor, bt: np.ndarray, s: int, N: int, g: int) -> 
 
 
 def logical_codes(codes: torch.Tensor, bt: np.ndarray, s: int, N: int, g: int) -> np.ndarray:
-    """Codes pool [num_blocks][Hkv][W][16] uint32 (as int32 tensor) -> [N][W]."""
+    """Codes pool [num_blocks][Hkv][16][W] uint32 (as int32 tensor) -> [N][W]."""
     nb = (N + PAGE - 1) // PAGE
     blocks = torch.as_tensor(np.asarray(bt[s, :nb], dtype=np.int64), device=codes.device)
-    sel = codes.index_select(0, blocks)[:, g]          # [nb][W][16]
-    out = sel.permute(0, 2, 1).reshape(nb * PAGE, -1)[:N]
+    sel = codes.index_select(0, blocks)[:, g]          # [nb][16][W]
+    out = sel.reshape(nb * PAGE, -1)[:N]
     return out.cpu().numpy().view(np.uint32).copy()
 
 

@@ -32,7 +32,7 @@ def gpu_encode_all(cfg: dkv.Config, inp: dict):
     """Encode every cached token of every sequence with dkv_encode."""
     dev = inp["k_pool"].device
     nb = inp["k_pool"].shape[0]
-    codes = torch.zeros((nb, cfg.num_kv_heads, cfg.code_bits // 32, PAGE),
+    codes = torch.zeros((nb, cfg.num_kv_heads, PAGE, cfg.code_bits // 32),
                         dtype=torch.int32, device=dev)
     radii = torch.zeros((nb, cfg.num_kv_heads, PAGE), dtype=torch.uint8, device=dev)
     B = inp["block_table"].shape[0]

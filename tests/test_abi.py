@@ -74,6 +74,7 @@ def test_decode_rejects_bad_arguments():
     assert _decode(_cfg(), workspace=None) == 3
     assert _decode(_cfg(), ws_bytes=16) == 3
     assert _decode(_cfg(), workspace=ctypes.c_void_p(0x10004)) == 3   # misaligned
+    assert _decode(_cfg(), q=ctypes.c_void_p(0x10008)) == 1           # q not 16-byte aligned
 
 
 def test_workspace_size():
@@ -103,6 +104,10 @@ def test_encode_rejects_bad_arguments():
     a4 = list(args)
     a4[0] = None       # k_pool
     assert lib.dkv_encode(ctypes.byref(c), *a4) == 1
+    for i in (0, 8, 9, 10):  # k_pool, proj, codes, radii not 16-byte aligned
+        a5 = list(args)
+        a5[i] = ctypes.c_void_p(0x10002)
+        assert lib.dkv_encode(ctypes.byref(c), *a5) == 1
 
 
 def test_python_binding_refuses_host_tensors():

@@ -13,6 +13,9 @@ import pytest
 import torch
 
 import workloads
+import hashed_top_sparse_amd as dkv
+import oracle
+from helpers import PAGE, logical_codes, logical_radii, logical_rows, tensor_bits
 from parity import check_unit, config_of, gpu_decode, gpu_encode_all
 
 pytestmark = pytest.mark.gpu
@@ -40,6 +43,59 @@ def test_small_workloads_every_unit(name):
     stats = _run(workloads.get(name))
     recalls = [st["recall"] for st in stats if st["recall"] is not None]
     assert all(r == 1.0 for r in recalls)
+
+
+@pytest.mark.parametrize("name,over", [
+    ("small_mha_b64", {}),
+    ("small_gqa_b128", {}),
+    ("small_gqa_b256_lognormal", {}),
+    ("small_gqa_b128", dict(num_q_heads=32, num_kv_heads=8)),
+])
+def test_append_encode_writes_exactly_its_range(name, over):
+    """dkv_encode over a per-sequence range [start, end): the one-token
+    append of a decode step and ragged chunks.  Codes and radii inside the
+    range are bit-exact to the oracle; every other slot keeps its old
+    contents."""
+    import dataclasses
+    wl = dataclasses.replace(workloads.get(name), **over)
+    print(f"[case] append {wl.name} {over}", flush=True)
+    cfg = config_of(wl)
+    inp = workloads.make_inputs(wl, DEV)
+    nb, Hkv, W = inp["k_pool"].shape[0], wl.num_kv_heads, wl.code_bits // 32
+    sentinel_code, sentinel_r = 0x5A5A5A5A, 0xA5
+    codes = torch.full((nb, Hkv, PAGE, W), sentinel_code, dtype=torch.int32, device=DEV)
+    radii = torch.full((nb, Hkv, PAGE), sentinel_r, dtype=torch.uint8, device=DEV)
+    lens = inp["seq_lens"].cpu().numpy()
+    # sequence 0: the newest token only; sequence 1: a chunk that starts and
+    # ends inside pages and spans more than one 16-token tile
+    ranges = [(int(lens[0]) - 1, int(lens[0])),
+              (int(lens[1]) // 3 + 5, int(lens[1]) - 7)]
+    start = torch.tensor([a for a, _ in ranges], dtype=torch.int32, device=DEV)
+    end = torch.tensor([e for _, e in ranges], dtype=torch.int32, device=DEV)
+    dkv.encode(cfg, inp["k_pool"], inp["block_table"][:2], start, end,
+               max(e - a for a, e in ranges), inp["proj"], codes, radii)
+    torch.cuda.synchronize()
+    bt = inp["block_table"].cpu().numpy()
+    P = tensor_bits(inp["proj"])
+    written = 0
+    for s, (a, e) in enumerate(ranges):
+        N = int(lens[s])
+        for g in range(Hkv):
+            K = logical_rows(inp["k_pool"], bt, s, N, g)
+            o_codes, o_radii = oracle.encode_keys(K[a:e], P)
+            g_codes = logical_codes(codes, bt, s, N, g)
+            g_radii = logical_radii(radii, bt, s, N, g)
+            assert np.array_equal(g_codes[a:e], o_codes), (s, g)
+            assert np.array_equal(g_radii[a:e], o_radii), (s, g)
+            written += e - a
+    c = codes.cpu().numpy().view(np.uint32)
+    r = radii.cpu().numpy()
+    assert int((c != sentinel_code).any(axis=-1).sum()) <= written
+    # no slot outside the ranges was written: count untouched radius bytes,
+    # allowing for encoded radii that happen to equal the sentinel
+    hits = sum(int((logical_radii(radii, bt, s, int(lens[s]), g)[a:e] == sentinel_r).sum())
+               for s, (a, e) in enumerate(ranges) for g in range(Hkv))
+    assert int((r == sentinel_r).sum()) == r.size - written + hits
 
 
 @pytest.mark.parametrize("over", [
