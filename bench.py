@@ -202,7 +202,6 @@ def main():
     zeros = torch.zeros(B, dtype=torch.int32, device=dev)
     dkv.encode(cfg, inp["k_pool"], inp["block_table"], zeros, inp["seq_lens"],
                inp["max_seq_len"], inp["proj"], codes, radii)
-    cur_start = (inp["seq_lens"] - 1).contiguous()
     max_len = inp["max_seq_len"]
     ws = torch.empty(dkv.decode_workspace_size(cfg, B, max_len), dtype=torch.uint8,
                      device=dev)
@@ -213,24 +212,16 @@ def main():
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
     hip = HipEvents()
-    names = ["encode_current"] + dkv.decode_stage_names()
+    names = dkv.decode_stage_names()
     n_ev = len(names) + 1
 
     def step(evs=None):
-        """One decode step: encode the newest token of every sequence, then
-        dkv_decode.  With evs, HIP events bracket every stage."""
-        if evs is not None:
-            hip.record(evs[0], sh)
-        dkv.encode(cfg, inp["k_pool"], inp["block_table"], cur_start,
-                   inp["seq_lens"], 1, inp["proj"], codes, radii, stream=stream)
-        if evs is None:
-            dkv.decode(cfg, inp["q"], inp["k_pool"], inp["v_pool"], codes, radii,
-                       inp["block_table"], inp["seq_lens"], max_len, inp["proj"],
-                       out, ws, stream=stream)
-        else:
-            dkv.decode_profiled(cfg, inp["q"], inp["k_pool"], inp["v_pool"], codes,
-                                radii, inp["block_table"], inp["seq_lens"], max_len,
-                                inp["proj"], out, ws, evs[1:], stream=stream)
+        """One decode step: dkv_decode_append encodes the newest key of every
+        sequence and runs the step.  With evs, HIP events bracket every
+        stage."""
+        dkv.decode_append(cfg, inp["q"], inp["k_pool"], inp["v_pool"], codes, radii,
+                          inp["block_table"], inp["seq_lens"], max_len, inp["proj"],
+                          out, ws, events=evs, stream=stream)
 
     # Timed steps: the plain call, nothing recorded between its kernels.
     for _ in range(args.warmup):

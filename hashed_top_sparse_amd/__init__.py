@@ -19,7 +19,8 @@ from typing import Optional
 import torch
 
 __all__ = ["Config", "DkvError", "encode", "decode", "decode_debug",
-           "decode_profiled", "decode_stage_names", "decode_workspace_size",
+           "decode_profiled", "decode_append", "decode_stage_names",
+           "decode_workspace_size",
            "library_path", "load_library", "EXPORTED_SYMBOLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -28,10 +29,10 @@ _lib = None
 
 # Every symbol include/dkv.h declares.
 EXPORTED_SYMBOLS = ("dkv_encode", "dkv_decode_workspace_size", "dkv_decode",
-                    "dkv_decode_debug", "dkv_decode_profiled",
+                    "dkv_decode_debug", "dkv_decode_profiled", "dkv_decode_append",
                     "dkv_decode_num_stages", "dkv_decode_stage_name",
                     "dkv_status_string", "dkv_abi_version")
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 STATUS = {0: "DKV_OK", 1: "DKV_ERR_INVALID_ARG", 2: "DKV_ERR_UNSUPPORTED",
           3: "DKV_ERR_WORKSPACE", 4: "DKV_ERR_LAUNCH"}
@@ -101,6 +102,8 @@ def load_library():
     lib.dkv_decode_debug.restype = ctypes.c_int
     lib.dkv_decode_profiled.argtypes = dec + [P, P]
     lib.dkv_decode_profiled.restype = ctypes.c_int
+    lib.dkv_decode_append.argtypes = dec + [P, P]
+    lib.dkv_decode_append.restype = ctypes.c_int
     lib.dkv_decode_num_stages.argtypes = []
     lib.dkv_decode_num_stages.restype = i32
     lib.dkv_decode_stage_name.argtypes = [i32]
@@ -241,6 +244,27 @@ def decode_debug(cfg: Config, q, k_pool, v_pool, codes, radii, block_table,
     _check(lib.dkv_decode_debug(*args, _ptr(q8_out, "q8_out", (torch.int8,)),
                                 _ptr(scores_out, "scores_out", _I32),
                                 _stream(stream)))
+
+
+def decode_append(cfg: Config, q, k_pool, v_pool, codes, radii, block_table,
+                  seq_lens, max_seq_len: int, proj, out, workspace, sel_idx=None,
+                  sel_cnt=None, events=None, stream=None) -> None:
+    """dkv_decode_append: encode every sequence's newest key (position
+    seq_lens-1) into ``codes``/``radii``, then one decode step.  ``events``:
+    optional num_stages+1 hipEvent_t handles, as for decode_profiled."""
+    lib = load_library()
+    arr = None
+    if events is not None:
+        n = lib.dkv_decode_num_stages()
+        if len(events) < n + 1:
+            raise ValueError(f"need {n + 1} events, got {len(events)}")
+        arr = (ctypes.c_void_p * len(events))(*events)
+    c, args = _decode_args(cfg, q, k_pool, v_pool, codes, radii, block_table,
+                           seq_lens, max_seq_len, proj, out, workspace, sel_idx,
+                           sel_cnt)
+    _check(lib.dkv_decode_append(
+        *args, ctypes.cast(arr, ctypes.c_void_p) if arr is not None else None,
+        _stream(stream)))
 
 
 def decode_stage_names():

@@ -95,7 +95,7 @@ dkv_status decode_impl(const dkv_config *cfg, const void *q,
                        int32_t batch, int32_t max_seq_len, const void *proj,
                        float *out, int32_t *sel_idx, int32_t *sel_cnt,
                        void *workspace, size_t workspace_bytes, int8_t *q8_out,
-                       int32_t *scores_out, dkv_event_t *events,
+                       int32_t *scores_out, dkv_event_t *events, bool append,
                        hipStream_t stream) {
   DecodeDims d;
   dkv_status why = DKV_OK;
@@ -139,8 +139,12 @@ dkv_status decode_impl(const dkv_config *cfg, const void *q,
     return hipEventRecord(reinterpret_cast<hipEvent_t>(events[stage++]),
                           stream) == hipSuccess;
   };
-  if (!mark() || launch_prep(d, q16, p16, codes, radii, block_table, seq_lens,
-                             q8, qop, qneg, lthr, stream) != hipSuccess)
+  // append: the prep kernel also encodes each sequence's newest key
+  uint32_t *codes_w = append ? const_cast<uint32_t *>(codes) : nullptr;
+  uint8_t *radii_w = append ? const_cast<uint8_t *>(radii) : nullptr;
+  if (!mark() || launch_prep(d, q16, p16, codes, radii, k16, codes_w, radii_w,
+                             block_table, seq_lens, q8, qop, qneg, lthr,
+                             stream) != hipSuccess)
     return DKV_ERR_LAUNCH;
   if (!mark() || launch_score(d, codes, radii, block_table, seq_lens, qop, qneg,
                               lthr, cand, tcount, scores_out, stream) !=
@@ -255,7 +259,7 @@ dkv_decode(const dkv_config *cfg, const void *q, const void *k_pool,
   return decode_impl(cfg, q, k_pool, v_pool, codes, radii, num_blocks,
                      block_table, max_blocks_per_seq, seq_lens, batch,
                      max_seq_len, proj, out, sel_idx, sel_cnt, workspace,
-                     workspace_bytes, nullptr, nullptr, nullptr,
+                     workspace_bytes, nullptr, nullptr, nullptr, false,
                      reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -270,7 +274,7 @@ __attribute__((visibility("default"))) dkv_status dkv_decode_debug(
   return decode_impl(cfg, q, k_pool, v_pool, codes, radii, num_blocks,
                      block_table, max_blocks_per_seq, seq_lens, batch,
                      max_seq_len, proj, out, sel_idx, sel_cnt, workspace,
-                     workspace_bytes, q8_out, scores_out, nullptr,
+                     workspace_bytes, q8_out, scores_out, nullptr, false,
                      reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -288,7 +292,25 @@ __attribute__((visibility("default"))) dkv_status dkv_decode_profiled(
   return decode_impl(cfg, q, k_pool, v_pool, codes, radii, num_blocks,
                      block_table, max_blocks_per_seq, seq_lens, batch,
                      max_seq_len, proj, out, sel_idx, sel_cnt, workspace,
-                     workspace_bytes, nullptr, nullptr, stage_events,
+                     workspace_bytes, nullptr, nullptr, stage_events, false,
+                     reinterpret_cast<hipStream_t>(stream));
+}
+
+__attribute__((visibility("default"))) dkv_status dkv_decode_append(
+    const dkv_config *cfg, const void *q, const void *k_pool,
+    const void *v_pool, uint32_t *codes, uint8_t *radii, int64_t num_blocks,
+    const int32_t *block_table, int32_t max_blocks_per_seq,
+    const int32_t *seq_lens, int32_t batch, int32_t max_seq_len,
+    const void *proj, float *out, int32_t *sel_idx, int32_t *sel_cnt,
+    void *workspace, size_t workspace_bytes, dkv_event_t *stage_events,
+    dkv_stream_t stream) {
+  if (stage_events != nullptr)
+    for (int i = 0; i <= kDecodeStages; ++i)
+      if (stage_events[i] == nullptr) return DKV_ERR_INVALID_ARG;
+  return decode_impl(cfg, q, k_pool, v_pool, codes, radii, num_blocks,
+                     block_table, max_blocks_per_seq, seq_lens, batch,
+                     max_seq_len, proj, out, sel_idx, sel_cnt, workspace,
+                     workspace_bytes, nullptr, nullptr, stage_events, true,
                      reinterpret_cast<hipStream_t>(stream));
 }
 

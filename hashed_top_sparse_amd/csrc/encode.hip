@@ -18,7 +18,7 @@
 // 64 sign bits of a column chunk are packed with one wave ballot.  Lanes 0
 // and 1 also run the radius chains of the wave's two pairs.  P is staged
 // once per workgroup in LDS.
-#include "internal.h"
+#include "encode_common.h"
 
 namespace dkv {
 namespace {
@@ -26,30 +26,6 @@ namespace {
 constexpr int kTile = 16;    // tokens per workgroup
 constexpr int kThreads = 256; // four waves
 constexpr int kRound = 8;     // (token, KV head) pairs staged at a time
-
-// Nearest doubles to 2^(f/8), f = 0..7.
-__constant__ double kEighthOctave[8] = {
-    0x1.0000000000000p+0, 0x1.172b83c7d517bp+0, 0x1.306fe0a31b715p+0,
-    0x1.4bfdad5362a27p+0, 0x1.6a09e667f3bcdp+0, 0x1.8ace5422aa0dbp+0,
-    0x1.ae89f995ad3adp+0, 0x1.d5818dcfba487p+0};
-
-// r8 from |k|^2: with r2 = M * 2^e, M in [1,2), the unclamped code is
-// 64 + 8e + f where f is the largest index with M >= C[f].
-__device__ int radius_code(double r2) {
-  if (!(r2 > 0.0)) return 0;
-  int e;
-  double mant = frexp(r2, &e); // r2 = mant * 2^e, mant in [0.5, 1)
-  double M = mant * 2.0;
-  e -= 1;
-  int f = 0;
-#pragma unroll
-  for (int i = 1; i < 8; ++i)
-    if (M >= kEighthOctave[i]) f = i;
-  long m = 64L + 8L * e + f;
-  if (m < 1) return 0;
-  if (m > 255) return 255;
-  return (int)m;
-}
 
 template <int C> // C = b / 64 column chunks
 __global__ __launch_bounds__(kThreads) void encode_kernel(

@@ -55,7 +55,9 @@ hipError_t launch_encode(const uint16_t *k_pool, int64_t num_blocks,
 // (sequence, KV head) the candidate threshold lthr (from a page sample).
 hipError_t launch_prep(const DecodeDims &d, const uint16_t *q,
                        const uint16_t *proj, const uint32_t *codes,
-                       const uint8_t *radii, const int32_t *block_table,
+                       const uint8_t *radii, const uint16_t *k_pool,
+                       uint32_t *codes_w, uint8_t *radii_w,
+                       const int32_t *block_table,
                        const int32_t *seq_lens, int8_t *q8, uint32_t *qop,
                        float *qneg, uint32_t *lthr, hipStream_t stream);
 

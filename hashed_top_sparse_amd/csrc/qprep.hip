@@ -37,6 +37,9 @@
 // top-k is among them) and otherwise rescans exactly.  L = 0 keeps every
 // candidate (used when k_eff covers all of them or the sample is too small
 // to say more).
+#include <type_traits>
+
+#include "encode_common.h"
 #include "score_common.h"
 #include "select_common.h"
 
@@ -64,7 +67,8 @@ __device__ __forceinline__ uint32_t e4m3_of_int(int v) {
 template <int KS, int G>
 __global__ __launch_bounds__(kThreads) void prep_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ proj,
-    const uint32_t *__restrict__ codes, const uint8_t *__restrict__ radii,
+    const uint32_t *codes, const uint8_t *radii, const uint16_t *__restrict__ k_pool,
+    uint32_t *codes_w, uint8_t *radii_w, // non-null: encode the newest key
     int64_t num_blocks, uint32_t code_bytes, uint32_t radius_bytes,
     const int32_t *__restrict__ block_table, int max_blocks,
     const int32_t *__restrict__ seq_lens, int n_max, int8_t *__restrict__ q8,
@@ -117,6 +121,22 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     }
   }
 
+  // ---- append: the workgroup also encodes position N-1 of sequence s for
+  // KV head g (the key the caller has just written), as the encode kernel
+  // would: its projection chains run beside the query's below
+  __shared__ __align__(16) uint16_t sK[kHeadDim];
+  int a_blk = -1;
+  if (codes_w != nullptr && N > 0) {
+    const int blk = bt[(N - 1) / kPage];
+    if (blk >= 0 && blk < num_blocks) a_blk = blk;
+  }
+  const int a_slot = (N - 1) % kPage;
+  if (a_blk >= 0 && threadIdx.x < kHeadDim / 2) {
+    const uint32_t *krow = reinterpret_cast<const uint32_t *>(
+        k_pool + (((int64_t)a_blk * kPage + a_slot) * Hkv + g) * kHeadDim);
+    reinterpret_cast<uint32_t *>(sK)[threadIdx.x] = krow[threadIdx.x];
+  }
+
   const uint16_t *qg = q + ((int64_t)s * Hq + (int64_t)g * G) * kHeadDim;
   for (int i = threadIdx.x; i < G * kHeadDim; i += kThreads)
     sQ[i] = qg[i];
@@ -128,47 +148,70 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
   if (threadIdx.x < 8) sSum[threadIdx.x] = 0;
   __syncthreads();
 
-  // p_hj in double precision, index order (one chain per (h, j) pair)
+  // p_hj in double precision, index order (one chain per (h, j) pair).
+  // Batches of 8 terms: the next batch's LDS reads are issued before the
+  // current batch's multiply-adds, which stay in index order.  With KEY,
+  // the thread also runs the newest key's chain for the same column j and
+  // the key's |k|^2 chain.
   const int npairs = G * b;
   double p[kMaxPairs];
   double mloc = 0.0;
+  double pk = 0.0, r2 = 0.0;
+  auto project = [&](auto key_tag, int h, int j) {
+    constexpr bool KEY = decltype(key_tag)::value;
+    const uint4 *qrow = reinterpret_cast<const uint4 *>(sQ + h * kHeadDim);
+    const uint4 *krow = reinterpret_cast<const uint4 *>(sK);
+    const uint16_t *pcol = sP + j;
+    uint4 qa = qrow[0], ka = KEY ? krow[0] : make_uint4(0, 0, 0, 0);
+    uint32_t pa[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) pa[u] = pcol[u * b];
+    double acc = 0.0;
+#pragma unroll 2
+    for (int i0 = 0; i0 < kHeadDim; i0 += 8) {
+      uint32_t pn[8];
+      const int i1 = i0 + 8 < kHeadDim ? i0 + 8 : i0; // last batch reloads itself
+      const uint4 qn = qrow[i1 / 8];
+      const uint4 kn = KEY ? krow[i1 / 8] : ka;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) pn[u] = pcol[(i1 + u) * b];
+      const uint32_t qw[4] = {qa.x, qa.y, qa.z, qa.w};
+      const uint32_t kw[4] = {ka.x, ka.y, ka.z, ka.w};
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t qb = (u & 1) ? (qw[u / 2] >> 16) : (qw[u / 2] & 0xFFFFu);
+        const double pd = (double)bf16_to_float(pa[u]);
+        acc = fma((double)bf16_to_float(qb), pd, acc);
+        if (KEY) {
+          const uint32_t kb = (u & 1) ? (kw[u / 2] >> 16) : (kw[u / 2] & 0xFFFFu);
+          const double kd = (double)bf16_to_float(kb);
+          pk = fma(kd, pd, pk);
+          r2 = fma(kd, kd, r2);
+        }
+      }
+      qa = qn;
+      ka = kn;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) pa[u] = pn[u];
+    }
+    return acc;
+  };
+  // threads 0..b-1 hold (h = 0, j = thread) at r = 0: the key's columns
+  const bool key_wave = a_blk >= 0 && (int)threadIdx.x < b; // wave-uniform
 #pragma unroll
   for (int r = 0; r < kMaxPairs; ++r) {
     const int idx = threadIdx.x + r * kThreads;
     p[r] = 0.0;
     if (idx < npairs) {
       const int h = idx / b, j = idx % b;
-      // Batches of 8 terms: the next batch's LDS reads are issued before
-      // the current batch's multiply-adds, which stay in index order.
-      const uint4 *qrow = reinterpret_cast<const uint4 *>(sQ + h * kHeadDim);
-      const uint16_t *pcol = sP + j;
-      uint4 qa = qrow[0];
-      uint32_t pa[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) pa[u] = pcol[u * b];
-      double acc = 0.0;
-#pragma unroll 2
-      for (int i0 = 0; i0 < kHeadDim; i0 += 8) {
-        uint4 qn = qa;
-        uint32_t pn[8];
-        const int i1 = i0 + 8 < kHeadDim ? i0 + 8 : i0; // last batch reloads itself
-        qn = qrow[i1 / 8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) pn[u] = pcol[(i1 + u) * b];
-        const uint32_t qw[4] = {qa.x, qa.y, qa.z, qa.w};
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const uint32_t qb = (u & 1) ? (qw[u / 2] >> 16) : (qw[u / 2] & 0xFFFFu);
-          acc = fma((double)bf16_to_float(qb), (double)bf16_to_float(pa[u]), acc);
-        }
-        qa = qn;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) pa[u] = pn[u];
-      }
+      const double acc = (r == 0 && key_wave) ? project(std::true_type{}, h, j)
+                                             : project(std::false_type{}, h, j);
       p[r] = acc;
       mloc = fmax(mloc, fabs(acc));
     }
   }
+  // the newest key's code bits of columns 64*wave .. 64*wave+63
+  const uint64_t key_bits = __ballot(pk > 0.0);
   for (int off = 32; off > 0; off >>= 1) mloc = fmax(mloc, __shfl_xor(mloc, off));
   if (lane == 0) sMax[wave] = mloc;
   __syncthreads();
@@ -302,13 +345,22 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
   for (int r = 0; r < kOpWords / kThreads; ++r) dst[threadIdx.x + r * kThreads] = opw[r];
   if (threadIdx.x < G)
     qneg[(int64_t)s * Hq + (int64_t)g * G + threadIdx.x] = -(float)sSum[threadIdx.x];
+  if (key_wave) {
+    const int W32 = b / 32;
+    uint32_t *cw = codes_w + (((int64_t)a_blk * Hkv + g) * kPage + a_slot) * W32;
+    if (lane < 2) cw[2 * wave + lane] = lane ? (uint32_t)(key_bits >> 32) : (uint32_t)key_bits;
+    if (threadIdx.x == 0)
+      radii_w[((int64_t)a_blk * Hkv + g) * kPage + a_slot] = (uint8_t)radius_code(r2);
+  }
 }
 
 } // namespace
 
 hipError_t launch_prep(const DecodeDims &d, const uint16_t *q,
                        const uint16_t *proj, const uint32_t *codes,
-                       const uint8_t *radii, const int32_t *block_table,
+                       const uint8_t *radii, const uint16_t *k_pool,
+                       uint32_t *codes_w, uint8_t *radii_w,
+                       const int32_t *block_table,
                        const int32_t *seq_lens, int8_t *q8, uint32_t *qop,
                        float *qneg, uint32_t *lthr, hipStream_t stream) {
   const uint32_t code_bytes = (uint32_t)((uint64_t)d.num_blocks * d.Hkv * d.W * kPage * 4);
@@ -317,6 +369,7 @@ hipError_t launch_prep(const DecodeDims &d, const uint16_t *q,
   if (d.KS == KSV && d.G == GV) {                                              \
     hipLaunchKernelGGL((prep_kernel<KSV, GV>), dim3(d.B * d.Hkv),              \
                        dim3(kThreads), 0, stream, q, proj, codes, radii,       \
+                       k_pool, codes_w, radii_w,                               \
                        d.num_blocks, code_bytes, radius_bytes, block_table,    \
                        d.max_blocks, seq_lens, d.n_max, q8, qop, qneg, lthr,   \
                        d.Hq, d.Hkv, d.b, d.W, d.k, d.w, d.sigma);              \

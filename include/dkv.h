@@ -224,6 +224,31 @@ dkv_status dkv_decode_profiled(const dkv_config *cfg, const void *q,
                                void *workspace, size_t workspace_bytes,
                                dkv_event_t *stage_events, dkv_stream_t stream);
 
+/*
+ * dkv_decode_append -- one decode step that first encodes each sequence's
+ * newest key: for every sequence s with N = seq_lens[s] >= 1 and every KV
+ * head, the key at position N-1 (already written to k_pool by the caller)
+ * gets its code and radius in codes/radii exactly as dkv_encode over
+ * [N-1, N) would write them, then the step runs as dkv_decode.  The
+ * encode happens inside the decode's first kernel, so a decode step costs
+ * one call and no extra launch ([SPHERICAL KV, §2.3]: dense keys are
+ * mapped to codes as they are written to the paged cache).
+ *   codes, radii  device, written at position N-1 of every sequence
+ *   stage_events  optional (NULL: none), as for dkv_decode_profiled
+ * Every other argument and every output as for dkv_decode.  Positions
+ * before N-1 must already hold their codes.
+ */
+dkv_status dkv_decode_append(const dkv_config *cfg, const void *q,
+                             const void *k_pool, const void *v_pool,
+                             uint32_t *codes, uint8_t *radii,
+                             int64_t num_blocks, const int32_t *block_table,
+                             int32_t max_blocks_per_seq,
+                             const int32_t *seq_lens, int32_t batch,
+                             int32_t max_seq_len, const void *proj,
+                             float *out, int32_t *sel_idx, int32_t *sel_cnt,
+                             void *workspace, size_t workspace_bytes,
+                             dkv_event_t *stage_events, dkv_stream_t stream);
+
 /* Number of decode stages and the static name of stage i ("" if out of
  * range). */
 int32_t dkv_decode_num_stages(void);
@@ -233,7 +258,7 @@ const char *dkv_decode_stage_name(int32_t stage);
 const char *dkv_status_string(dkv_status status);
 
 /* ABI version of this header (bumped on any signature or layout change). */
-#define DKV_ABI_VERSION 1
+#define DKV_ABI_VERSION 2
 int32_t dkv_abi_version(void);
 
 #ifdef __cplusplus

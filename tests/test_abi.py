@@ -77,6 +77,23 @@ def test_decode_rejects_bad_arguments():
     assert _decode(_cfg(), q=ctypes.c_void_p(0x10008)) == 1           # q not 16-byte aligned
 
 
+def test_decode_append_rejects_bad_arguments():
+    lib = dkv.load_library()
+    c = _cfg()
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 200, FAKE, 64, FAKE, 2, 1000, FAKE,
+            FAKE, None, None, FAKE, 1 << 30]
+    assert lib.dkv_decode_append(None, *args, None, None) == 1
+    a2 = list(args)
+    a2[0] = None       # q
+    assert lib.dkv_decode_append(ctypes.byref(c), *a2, None, None) == 1
+    a3 = list(args)
+    a3[3] = ctypes.c_void_p(0x10004)   # codes not 16-byte aligned
+    assert lib.dkv_decode_append(ctypes.byref(c), *a3, None, None) == 1
+    events = (ctypes.c_void_p * 8)(*([0x1000] * 3 + [0] * 5))   # a null event
+    assert lib.dkv_decode_append(ctypes.byref(c), *args,
+                                 ctypes.cast(events, ctypes.c_void_p), None) == 1
+
+
 def test_workspace_size():
     lib = dkv.load_library()
     c = _cfg()

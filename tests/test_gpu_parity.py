@@ -145,6 +145,54 @@ def test_forced_ties_go_to_lowest_positions():
             assert np.array_equal(top, np.arange(wl.sinks, wl.sinks + wl.top_k))
 
 
+def _run_append(wl, units=None):
+    """dkv_encode over [0, N-1) of every sequence into sentinel-filled
+    pools, then dkv_decode_append: the newest key of every sequence must be
+    encoded by the decode call itself, and the step must match the oracle."""
+    print(f"[case] append-decode {wl.name}", flush=True)
+    cfg = config_of(wl)
+    inp = workloads.make_inputs(wl, DEV)
+    nb, Hkv = inp["k_pool"].shape[0], wl.num_kv_heads
+    codes = torch.full((nb, Hkv, PAGE, wl.code_bits // 32), 0x5A5A5A5A,
+                       dtype=torch.int32, device=DEV)
+    radii = torch.full((nb, Hkv, PAGE), 0xA5, dtype=torch.uint8, device=DEV)
+    B = wl.batch
+    start = torch.zeros(B, dtype=torch.int32, device=DEV)
+    end = torch.clamp(inp["seq_lens"] - 1, min=0).to(torch.int32)
+    dkv.encode(cfg, inp["k_pool"], inp["block_table"], start, end,
+               inp["max_seq_len"], inp["proj"], codes, radii)
+    ws = torch.empty(dkv.decode_workspace_size(cfg, B, inp["max_seq_len"]),
+                     dtype=torch.uint8, device=DEV)
+    out = torch.full((B, cfg.num_q_heads, cfg.head_dim), float("nan"), device=DEV)
+    sel = torch.full((B, Hkv, cfg.select_cap), -7, dtype=torch.int32, device=DEV)
+    cnt = torch.full((B, Hkv), -7, dtype=torch.int32, device=DEV)
+    dkv.decode_append(cfg, inp["q"], inp["k_pool"], inp["v_pool"], codes, radii,
+                      inp["block_table"], inp["seq_lens"], inp["max_seq_len"],
+                      inp["proj"], out, ws, sel, cnt)
+    torch.cuda.synchronize()
+    gpu = {"out": out, "sel": sel, "cnt": cnt}
+    if units is None:
+        units = [(s, g) for s in range(B) for g in range(Hkv)]
+    for s, g in units:
+        check_unit(cfg, inp, gpu, codes, radii, s, g)  # codes of all N keys
+    return gpu, codes, radii, inp, cfg
+
+
+@pytest.mark.parametrize("name", sorted(workloads.SMALL))
+def test_decode_append_encodes_newest_key(name):
+    _run_append(workloads.get(name))
+
+
+def test_decode_append_equals_encode_then_decode():
+    wl = workloads.get("small_ragged_b128")
+    gpu, codes, radii, inp, cfg = _run_append(wl)
+    ref = gpu_decode(cfg, inp, codes, radii, debug=False)
+    assert torch.equal(gpu["out"], ref["out"])
+    assert torch.equal(gpu["cnt"], ref["cnt"])
+    assert torch.equal(torch.sort(gpu["sel"], dim=-1).values,
+                       torch.sort(ref["sel"], dim=-1).values)
+
+
 def test_decode_is_deterministic():
     wl = workloads.get("small_ragged_b128")
     cfg = config_of(wl)
@@ -175,6 +223,12 @@ def test_full_size_workloads(name):
     if wl.needles:
         assert recalls and all(r == 1.0 for r in recalls)
     print(name, "max abs err", max(st["max_abs"] for st in stats))
+    torch.cuda.empty_cache()
+
+
+def test_full_size_decode_append():
+    """The benchmarked step: dkv_decode_append at 16 x 128K."""
+    _run_append(workloads.get("gqa32x8_bs16_n128k_b128"), [(0, 0), (9, 5), (15, 7)])
     torch.cuda.empty_cache()
 
 
