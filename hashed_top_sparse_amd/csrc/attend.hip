@@ -96,9 +96,9 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(
 
   // the split's row ids, once, into LDS
   __shared__ int32_t sid[kAttnRows];
-  {
-    const int r = r0 + (int)threadIdx.x;
-    sid[threadIdx.x] = r < r1 ? rows[(int64_t)unit * cap + r] : -1;
+  for (int i = threadIdx.x; i < kAttnRows; i += kThreads) {
+    const int r = r0 + i;
+    sid[i] = r < r1 ? rows[(int64_t)unit * cap + r] : -1;
   }
   __syncthreads();
 
@@ -106,6 +106,7 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(
   // four, the next batch's loads issued before the current batch is used.
   constexpr int kBatch = 4;
   constexpr int kBatches = kAttnRows / (kBatch * kRowGroups);
+  static_assert(kBatches * kBatch * kRowGroups == kAttnRows, "whole batches");
   auto load_batch = [&](int b, uint4 (&kr)[kBatch], uint4 (&vr)[kBatch], bool (&ok)[kBatch]) {
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {

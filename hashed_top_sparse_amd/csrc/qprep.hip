@@ -287,6 +287,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
       const int h0 = 2 * (lane >> 4), h1 = h0 + 1;
       op.cinit = v4f{0.f, h0 < G ? -(float)sSum[h0 < G ? h0 : 0] : 0.f, 0.f,
                      h1 < G ? -(float)sSum[h1 < G ? h1 : 0] : 0.f};
+      op.scale = unit_scale();
     }
     uint32_t nvalid = 0;
     auto keep = [&](int t, int S) {

@@ -39,7 +39,12 @@ static_assert(kTaskQuads % kDepth == 0 && kTaskQuads >= 2 * kDepth, "prefetch ro
 // quad of a task at which the task after next and the next task's operand
 // are loaded: kDepth quads before the next task's first prefetch
 constexpr int kLookahead = kTaskQuads - 2 * kDepth;
-constexpr int kStageCand = 128; // candidates per task staged in LDS
+constexpr int kStageCand = 128;
+// Workgroups per CU: one wave per SIMD each, four waves per SIMD in all.
+// More resident waves do not help (the kernel is bound by instruction
+// issue), and four per SIMD keeps each wave's task count equal when the
+// task count is a multiple of 4 x 4 x CUs.
+constexpr int kWgPerCu = 4; // candidates per task staged in LDS
 
 // Compile-time loop: f(std::integral_constant<int, I>) for I in [I0, N).
 template <int I, int N, typename F>
@@ -79,9 +84,10 @@ __device__ __forceinline__ void transpose_rows(uint32_t (&x)[4]) {
   x[3] = d[1];
 }
 
-// W: code words per key (2, 4 or 8); KS: 128-bit matrix-core K-steps.
-template <int W, int G, int KS = (W > 4 ? W / 4 : 1)>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KS == 1 ? 6 : 4, 8))) void filter_kernel(
+// W: code words per key (2, 4 or 8); KS: 128-bit matrix-core K-steps;
+// DBG: also write every score to scores_out (inspection builds only).
+template <int W, int G, bool DBG, int KS = (W > 4 ? W / 4 : 1)>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void filter_kernel(
     const uint32_t *__restrict__ codes, const uint8_t *__restrict__ radii,
     int64_t num_blocks, uint32_t code_bytes, uint32_t radius_bytes,
     const int32_t *__restrict__ block_table, int max_blocks,
@@ -127,7 +133,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KS == 
     T.unit = T.s * Hkv + T.g;
     T.npg = min(kGroupPages, (T.N - T.key0 + kPage - 1) / kPage);
     T.lo = max(sigma, T.key0);
-    T.hi = min(T.N - w, T.key0 + T.npg * kPage);
+    T.hi = max(T.lo, min(T.N - w, T.key0 + T.npg * kPage)); // empty: hi == lo
     return true;
   };
   // the first non-empty task at or after t in this wave's stride
@@ -266,18 +272,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KS == 
       const uint32_t u = (uint32_t)(__mul24((int)r8, mx) + (int)kScoreBias);
       const int qpos = C.key0 + 64 * q; // first position of the quad
       const int pos = qpos + lane;
-      if (scores_out != nullptr) {
+      if constexpr (DBG) {
         if (pos < C.N)
           scores_out[(int64_t)C.unit * score_stride + pos] = (int32_t)(u - kScoreBias);
       }
-      // whole quad inside [lo, hi) (the common case): only the threshold
-      const bool inside = qpos >= C.lo && qpos + 64 <= C.hi;
-      const bool c = inside ? u >= LC : (pos >= C.lo && pos < C.hi && u >= LC);
+      // a candidate: position in [lo, hi) and u >= L (no branches: both
+      // tests are single compares, the range one on pos - lo unsigned)
+      const bool c = ((uint32_t)(pos - C.lo) < (uint32_t)(C.hi - C.lo)) & (u >= LC);
       const uint64_t m = __ballot(c);
       if (m != 0) {
         // staged in LDS (no vector-memory store inside the stream); past
         // the stage, straight to the region (rare)
-        const uint32_t slot = nc + lanes_below(m);
+        const uint32_t slot = __builtin_amdgcn_mbcnt_hi(
+            (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, nc));
         const uint64_t v = ((uint64_t)(uint32_t)pos << 32) | u; // (u, pos)
         // address-space-qualified pointers keep these an LDS store and a
         // global store (a merged flat store would count against both wait
@@ -346,23 +353,22 @@ hipError_t launch_score(const DecodeDims &d, const uint32_t *codes,
   if (ntasks > 0x7FFFFFFF - 65536) return hipErrorInvalidValue;
   const uint32_t code_bytes = (uint32_t)((uint64_t)d.num_blocks * d.Hkv * d.W * kPage * 4);
   const uint32_t radius_bytes = (uint32_t)((uint64_t)d.num_blocks * d.Hkv * kPage);
-#define DKV_SCORE_CASE(WV, GV)                                                 \
-  if (d.W == WV && d.G == GV) {                                                \
-    static int per_cu = 0; /* resident workgroups per CU (register-bound) */  \
-    if (per_cu <= 0 &&                                                         \
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(                          \
-            &per_cu, filter_kernel<WV, GV>, kThreads, 0) != hipSuccess)        \
-      per_cu = 1;                                                              \
+#define DKV_SCORE_LAUNCH(WV, GV, DV)                                           \
+  {                                                                            \
     const int64_t nwg = std::min<int64_t>((ntasks + kWaves - 1) / kWaves,       \
-                                          (int64_t)std::max(1, per_cu) *        \
-                                              device_cu_count());               \
-    hipLaunchKernelGGL((filter_kernel<WV, GV>), dim3((unsigned)nwg),           \
+                                          (int64_t)kWgPerCu * device_cu_count()); \
+    hipLaunchKernelGGL((filter_kernel<WV, GV, DV>), dim3((unsigned)nwg),       \
                        dim3(kThreads), 0, stream, codes, radii, d.num_blocks,  \
                        code_bytes, radius_bytes, block_table, d.max_blocks,    \
                        seq_lens, d.n_max, qop, qneg, lthr, d.B, d.Hkv,         \
                        (int)ngroups, (int)ntasks, d.w, d.sigma, cand, tcount,  \
                        d.cand_groups, scores_out, d.max_seq_len);              \
     return hipGetLastError();                                                  \
+  }
+#define DKV_SCORE_CASE(WV, GV)                                                 \
+  if (d.W == WV && d.G == GV) {                                                \
+    if (scores_out != nullptr) DKV_SCORE_LAUNCH(WV, GV, true)                  \
+    DKV_SCORE_LAUNCH(WV, GV, false)                                            \
   }
   DKV_SCORE_CASE(2, 1)
   DKV_SCORE_CASE(2, 2)
@@ -377,6 +383,7 @@ hipError_t launch_score(const DecodeDims &d, const uint32_t *codes,
   DKV_SCORE_CASE(8, 4)
   DKV_SCORE_CASE(8, 8)
 #undef DKV_SCORE_CASE
+#undef DKV_SCORE_LAUNCH
   return hipErrorInvalidValue;
 }
 

@@ -34,7 +34,16 @@ template <int KS>
 struct QueryOperand {
   v8i a[KS];
   v4f cinit;
+  int scale; // E8M0 block scale 2^0 (127), held in a register
 };
+
+// 127 in a register the compiler cannot see through (a constant operand
+// would be rematerialised before every matrix op).
+__device__ __forceinline__ int unit_scale() {
+  int s = 127;
+  asm("" : "+v"(s));
+  return s;
+}
 
 // The score operand of (sequence s, KV head g): qop [unit][KS][64][8]
 // dwords and qneg [B][Hq] = -sum_j q8.
@@ -57,6 +66,7 @@ load_query_operand(const uint32_t *qop, const float *qneg, int unit, int s,
   const float *qn = qneg + (int64_t)s * Hq + (int64_t)g * G;
   const float q0 = qn[h0 < G ? h0 : 0], q1 = qn[h1 < G ? h1 : 0];
   op.cinit = v4f{0.f, h0 < G ? q0 : 0.f, 0.f, h1 < G ? q1 : 0.f};
+  op.scale = unit_scale();
   return op;
 }
 
@@ -98,6 +108,7 @@ __device__ __forceinline__ QueryOperand<KS> finish_query_operand(
   for (int ks = 0; ks < KS; ++ks) op.a[ks] = r.a[ks];
   const int h0 = 2 * (lane >> 4), h1 = h0 + 1;
   op.cinit = v4f{0.f, h0 < G ? r.q0 : 0.f, 0.f, h1 < G ? r.q1 : 0.f};
+  op.scale = unit_scale();
   return op;
 }
 
@@ -111,18 +122,27 @@ __device__ __forceinline__ v8i expand_code_word(uint32_t w) {
   return r;
 }
 
+// max of two scores.  The scores are finite (integers), so the plain
+// instruction is enough: fmaxf would first canonicalise operands that come
+// from a lane permute.
+__device__ __forceinline__ float max_score(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // After v_permlane16_swap(m, m) the two results hold 16-lane rows
 // {0,0,2,2} and {1,1,3,3}; after v_permlane32_swap rows {0,1,0,1} and
 // {2,3,2,3}.  The max of the pair is the max over the row pair.
 __device__ __forceinline__ float max_rows16(float m) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(m),
                                                   __float_as_uint(m), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max_score(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float max_rows32(float m) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m),
                                                   __float_as_uint(m), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max_score(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // Number of set bits of `mask` in lanes below the calling lane.
@@ -148,7 +168,7 @@ __device__ __forceinline__ int score_page(const QueryOperand<KS> &op,
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
     acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-        op.a[ks], expand_code_word(cw[ks]), acc, 0, 4, 0, 127, 0, 127);
+        op.a[ks], expand_code_word(cw[ks]), acc, 0, 4, 0, op.scale, 0, op.scale);
   // The matrix op needs all 64 lanes: pin its result in wave-uniform control
   // flow so the compiler cannot sink it into a lane-divergent branch.
   asm volatile("" : "+v"(acc));
@@ -182,7 +202,7 @@ __device__ __forceinline__ int score_quad_max(const QueryOperand<KS> &op,
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-          op.a[ks], expand_code_word(cw[j][ks]), acc[j], 0, 4, 0, 127, 0, 127);
+          op.a[ks], expand_code_word(cw[j][ks]), acc[j], 0, 4, 0, op.scale, 0, op.scale);
   }
   int x[4];
 #pragma unroll
@@ -222,9 +242,10 @@ __device__ __forceinline__ int score_quad_max_seq(const QueryOperand<KS> &op,
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-          op.a[ks], expand_code_word(cw[j][ks]), acc, 0, 4, 0, 127, 0, 127);
+          op.a[ks], expand_code_word(cw[j][ks]), acc, 0, 4, 0, op.scale, 0,
+          op.scale);
     float m = 16.f * acc[0] + acc[1];
-    if (G >= 2) m = fmaxf(m, 16.f * acc[2] + acc[3]);
+    if (G >= 2) m = max_score(m, 16.f * acc[2] + acc[3]);
     // all 64 lanes take part: keep the op in wave-uniform control flow, and
     // in page order
     asm volatile("" : "+v"(m));
@@ -237,8 +258,8 @@ __device__ __forceinline__ int score_quad_max_seq(const QueryOperand<KS> &op,
                                                   __float_as_uint(x[3]), false, false);
   float y01 = __uint_as_float(a[0]), y23 = __uint_as_float(b[0]);
   if (G >= 4) {
-    y01 = fmaxf(y01, __uint_as_float(a[1]));
-    y23 = fmaxf(y23, __uint_as_float(b[1]));
+    y01 = max_score(y01, __uint_as_float(a[1]));
+    y23 = max_score(y23, __uint_as_float(b[1]));
   }
   const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(y01),
                                                   __float_as_uint(y23), false, false);
