@@ -16,9 +16,13 @@
 //     keep come from two histogram passes (select_common.h);
 //   - if only some ties are kept, the lowest positions win: a second
 //     k-th-largest search over the inverted positions of the ties;
-//   - survivors are marked in a position bitmap, which is read back in
-//     order: the list is sinks, window, then the top-k in ascending
-//     position (deterministic).
+//   - the staged candidates are in ascending position order (groups in
+//     order, and the streaming pass writes a group's candidates in
+//     position order), so the survivors are compacted with a prefix sum
+//     over that order: the list is sinks, window, then the top-k in
+//     ascending position (deterministic).  Candidate lists too long to
+//     stage, and the fallback below, mark survivors in a position bitmap
+//     and read it back in order instead.
 // Otherwise the workgroup rescans the (sequence, KV head)'s codes itself
 // and runs the same exact selection over every candidate score (slow, but
 // exact for any input).
@@ -90,20 +94,16 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
     uint32_t *bm = bitmap + (int64_t)unit * bm_stride;
     const int nwords = (N + 31) / 32;
     const int c0 = sigma, c1 = N - w; // candidate positions [c0, c1)
+    bool use_bitmap = true;
     if (keff == nc) {
-      // every candidate is selected
-      for (int i = tid; i < nwords; i += kThreads) {
-        const int p0 = i * 32;
-        uint32_t m = 0;
-        if (p0 + 32 > c0 && p0 < c1) {
-          const int a = max(c0, p0) - p0, e = min(c1, p0 + 32) - p0;
-          m = (e - a == 32) ? 0xFFFFFFFFu : (((1u << (e - a)) - 1u) << a);
-        }
-        bm[i] = m;
+      // every candidate is selected, in position order
+      for (int i = tid; i < keff; i += kThreads) {
+        const int pos = c0 + i;
+        R[base + i] = row_of(bt, pos, num_blocks);
+        if (U) U[base + i] = pos;
       }
+      use_bitmap = false;
     } else {
-      for (int i = tid; i < nwords; i += kThreads) bm[i] = 0u;
-      __syncthreads();
       // the candidates of the unit's groups (those below N were written):
       // count prefix over the groups, in LDS when it fits
       const int ngs = (N + kGroupKeys - 1) / kGroupKeys;
@@ -151,6 +151,9 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
       if (nlist >= (uint32_t)keff) {
         // ---- normal path: exact top-k of the candidates
         const bool staged = pre_lds && nlist <= (uint32_t)kStage;
+        if (!staged) {
+          for (int i = tid; i < nwords; i += kThreads) bm[i] = 0u;
+        }
         __syncthreads();
         if (staged) {
           // candidate i is entry i - gpre[g] of group g, gpre[g] <= i < gpre[g+1];
@@ -185,23 +188,55 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
             for_each_global(fn);
           }
         };
-        wg_kth_largest<kThreads>(sel, [&](auto fn) {
-          for_each([&](uint32_t u, int) { fn(u); });
-        }, (uint32_t)keff, T, take_eq, n_eq);
-        uint32_t Pt = 0; // ties with (kPosMax - pos) >= Pt are kept
-        if (take_eq < n_eq) {
-          uint32_t t2, n2;
+        // the cut: survivors are u > Tu, or u == Tu and pos <= Tpos
+        uint32_t Tu = 0, Tpos = 0;
+        bool cut = false;
+        if (staged)
+          cut = wg_topk_cut<kThreads>(sel, for_each, (uint32_t)keff, Tu, Tpos);
+        uint32_t Pt = 0; // otherwise: ties with (kPosMax - pos) >= Pt are kept
+        if (!cut) {
           wg_kth_largest<kThreads>(sel, [&](auto fn) {
-            for_each([&](uint32_t u, int pos) {
-              if (u == T) fn(kPosMax - (uint32_t)pos);
-            });
-          }, take_eq, Pt, t2, n2);
+            for_each([&](uint32_t u, int) { fn(u); });
+          }, (uint32_t)keff, T, take_eq, n_eq);
+          if (take_eq < n_eq) {
+            uint32_t t2, n2;
+            wg_kth_largest<kThreads>(sel, [&](auto fn) {
+              for_each([&](uint32_t u, int pos) {
+                if (u == T) fn(kPosMax - (uint32_t)pos);
+              });
+            }, take_eq, Pt, t2, n2);
+          }
         }
-        for_each([&](uint32_t u, int pos) {
-          if (u > T || (u == T && kPosMax - (uint32_t)pos >= Pt))
-            atomicOr(&bm[pos >> 5], 1u << (pos & 31));
-        });
+        auto keep = [&](uint32_t u, int pos) {
+          return cut ? (u > Tu || (u == Tu && (uint32_t)pos <= Tpos))
+                     : (u > T || (u == T && kPosMax - (uint32_t)pos >= Pt));
+        };
+        if (staged) {
+          // stable compaction of the survivors: thread t takes a contiguous
+          // run of the staged list
+          const uint32_t per = (nlist + kThreads - 1) / kThreads;
+          const uint32_t i0 = min(nlist, tid * per), i1 = min(nlist, i0 + per);
+          uint32_t c = 0;
+          for (uint32_t i = i0; i < i1; ++i) c += keep(st[i].x, (int)st[i].y);
+          uint32_t tot;
+          uint32_t o = wg_exclusive_scan<kThreads>(c, &sel.red[3][0], &tot);
+          for (uint32_t i = i0; i < i1; ++i) {
+            const int pos = (int)st[i].y;
+            if (keep(st[i].x, pos)) {
+              R[base + o] = row_of(bt, pos, num_blocks);
+              if (U) U[base + o] = pos;
+              ++o;
+            }
+          }
+          use_bitmap = false;
+        } else {
+          for_each([&](uint32_t u, int pos) {
+            if (keep(u, pos)) atomicOr(&bm[pos >> 5], 1u << (pos & 31));
+          });
+        }
       } else {
+        for (int i = tid; i < nwords; i += kThreads) bm[i] = 0u;
+        __syncthreads();
         // ---- exact fallback: rescore every candidate key of the unit
         const QueryOperand<KS> op = load_query_operand<KS, G>(
             qop, qneg, unit, s, g, Hkv * G, lane);
@@ -247,9 +282,11 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
         });
       }
     }
-    __syncthreads();
-    emit_bitmap<kThreads>(bm, nwords, bt, num_blocks, R + base,
-                          U ? U + base : nullptr, &sel.red[3][0]);
+    if (use_bitmap) { // workgroup-uniform
+      __syncthreads();
+      emit_bitmap<kThreads>(bm, nwords, bt, num_blocks, R + base,
+                            U ? U + base : nullptr, &sel.red[3][0]);
+    }
   }
   if (tid == 0) {
     cnt[unit] = total;

@@ -16,12 +16,16 @@ namespace dkv {
 constexpr int kHistBits = 12;
 constexpr int kHistBins = 1 << kHistBits;
 
+constexpr int kCutList = 64; // threshold-bin entries one wave ranks
+
 template <int NT>
 struct SelectShared {
   uint32_t hist[kHistBins];
   uint32_t red[4][NT / 64];
   int bin;
   uint32_t above;
+  uint2 cut_list[kCutList];
+  uint32_t cut_n, cut_u, cut_pos;
 };
 
 // Scanning bins from the top, finds the bin where the running count reaches
@@ -131,6 +135,55 @@ __device__ void wg_kth_largest(SelectShared<NT> &sh, Visit visit, uint32_t kneed
   take_eq = kneed2 - sh.above;
   n_eq = sh.hist[sh.bin];
   __syncthreads();
+}
+
+// The top kneed (1 <= kneed <= element count) of (u, pos) pairs under the
+// order (u descending, pos ascending), positions distinct: visit2(fn) hands
+// every pair to fn(u, pos) once across the workgroup.  On success the cut
+// (Tu, Tpos) is returned: a pair is in the top kneed iff u > Tu, or u == Tu
+// and pos <= Tpos.  One histogram pass finds the bin of the kneed-th
+// largest u; when that bin holds at most kCutList pairs, one wave ranks
+// them exactly.  Returns false otherwise (the caller then searches with
+// wg_kth_largest).  Every thread must call it.
+template <int NT, class Visit2>
+__device__ bool wg_topk_cut(SelectShared<NT> &sh, Visit2 visit2, uint32_t kneed,
+                            uint32_t &Tu, uint32_t &Tpos) {
+  uint32_t vmin;
+  int shift;
+  wg_histogram<NT>(sh, [&](auto fn) {
+    visit2([&](uint32_t u, int) { fn(u); });
+  }, vmin, shift);
+  find_threshold_bin<NT>(sh, kneed);
+  const uint32_t b1 = (uint32_t)sh.bin;
+  const uint32_t kneed2 = kneed - sh.above; // >= 1
+  const uint32_t nb1 = sh.hist[b1];
+  if (nb1 > (uint32_t)kCutList) return false; // workgroup-uniform
+  if (threadIdx.x == 0) sh.cut_n = 0;
+  __syncthreads();
+  visit2([&](uint32_t u, int pos) {
+    if (((u - vmin) >> shift) == b1)
+      sh.cut_list[atomicAdd(&sh.cut_n, 1u)] = make_uint2(u, (uint32_t)pos);
+  });
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const uint2 e = lane < (int)nb1 ? sh.cut_list[lane] : make_uint2(0u, 0xFFFFFFFFu);
+    uint32_t rank = 0; // pairs ahead of e in the order
+    for (int j = 0; j < (int)nb1; ++j) {
+      const uint32_t uj = (uint32_t)__shfl((int)e.x, j);
+      const uint32_t pj = (uint32_t)__shfl((int)e.y, j);
+      rank += (uj > e.x) || (uj == e.x && pj < e.y);
+    }
+    if (lane < (int)nb1 && rank == kneed2 - 1) {
+      sh.cut_u = e.x;
+      sh.cut_pos = e.y;
+    }
+  }
+  __syncthreads();
+  Tu = sh.cut_u;
+  Tpos = sh.cut_pos;
+  __syncthreads();
+  return true;
 }
 
 // Writes the positions of the set bits of bitmap[0, nwords) (bit p = word

@@ -193,6 +193,47 @@ def test_decode_append_equals_encode_then_decode():
                        torch.sort(ref["sel"], dim=-1).values)
 
 
+@pytest.mark.parametrize("copies_before,copies_after", [(3, 3), (0, 5), (6, 0)])
+def test_ties_at_the_cut_split_by_position(copies_before, copies_after):
+    """A few exact copies of the key that sits at rank k_eff (same code, same
+    radius, so the same score) are planted before and after it: the ties at
+    the threshold fall in a small score bin and must be split by position."""
+    wl = workloads.get("small_gqa_b128")
+    print(f"[case] ties at cut {copies_before}+{copies_after}", flush=True)
+    cfg = config_of(wl)
+    inp = workloads.make_inputs(wl, DEV)
+    s, g = 0, 1
+    N = int(inp["seq_lens"][s])
+    bt = inp["block_table"].cpu().numpy()
+    P = tensor_bits(inp["proj"])
+    K = logical_rows(inp["k_pool"], bt, s, N, g)
+    codes0, radii0 = oracle.encode_keys(K, P)
+    G = cfg.group
+    q = tensor_bits(inp["q"][s, g * G:(g + 1) * G])
+    V = logical_rows(inp["v_pool"], bt, s, N, g)
+    r = oracle.decode_unit(q, P, codes0, radii0, K, V, cfg.top_k, cfg.window, cfg.sinks)
+    cand = np.arange(cfg.sinks, N - cfg.window)
+    order = cand[np.lexsort((cand, -r["scores"][cand].astype(np.int64)))]
+    keff = min(cfg.top_k, len(cand))
+    pstar = int(order[keff - 1])
+    # copy targets: candidate positions well away from pstar, not already in
+    # the top k_eff + 20 (so they really add ties)
+    top = set(order[:keff + 20].tolist())
+    before = [p for p in range(cfg.sinks + 5, pstar) if p not in top][::37][:copies_before]
+    after = [p for p in range(pstar + 1, N - cfg.window) if p not in top][::37][:copies_after]
+    src_blk, src_slot = int(bt[s, pstar // PAGE]), pstar % PAGE
+    for p in before + after:
+        blk, slot = int(bt[s, p // PAGE]), p % PAGE
+        inp["k_pool"][blk, slot, g] = inp["k_pool"][src_blk, src_slot, g]
+    codes, radii = gpu_encode_all(cfg, inp)
+    gpu = gpu_decode(cfg, inp, codes, radii, debug=True)
+    st = check_unit(cfg, inp, gpu, codes, radii, s, g)
+    sc = gpu["scores"][s, g, :N].cpu().numpy()
+    assert (sc[before + after] == sc[pstar]).all()   # the ties are real
+    for gg in range(wl.num_kv_heads):
+        check_unit(cfg, inp, gpu, codes, radii, 1, gg)
+
+
 def test_decode_is_deterministic():
     wl = workloads.get("small_ragged_b128")
     cfg = config_of(wl)
