@@ -4,24 +4,33 @@
 // [DySCO review, item 1]: attention is softmax(q k^T / sqrt(d)) v.
 // [DeepSeek DSA]: the real attention only reads the selected history.
 // Each split keeps an online-softmax state (m, l, acc[d]) per query head in
-// fp32 (logits are pre-multiplied by log2(e)/sqrt(d) so exp2 is used); the
-// combine kernel merges the split states:
+// fp32 (logits are scaled by log2(e)/sqrt(d) so exp2 is used); the combine
+// kernel merges the split states:
 //   m* = max m_p,  l* = sum l_p 2^(m_p - m*),  o = sum acc_p 2^(m_p - m*) / l*.
 //
-// Work mapping of the split kernel: 256 threads = 16 row groups of 16 lanes;
-// a row group reads a selected key row and value row (256 B each: 16 B per
-// lane), four rows per batch with the next batch in flight, so a workgroup
-// has up to 128 row pairs of gathers outstanding; the split's row ids are
-// read once into LDS; the 16-lane dot-product sums use DPP row operations.  The selection list already holds physical row ids
-// (page*16 + slot).  All G query heads of the KV group share the rows.
+// Work mapping of the split kernel: 4 waves, each taking its quarter of the
+// split's rows in tiles of 16.  Per tile:
+//   - logits on the matrix cores: S = K Q^T with four 16x16x32 bf16 ops
+//     (K rows as the 16 M rows, the G query heads as N columns, d = 128 in
+//     four K-steps of 32).  Lane L loads 64 contiguous bytes of key row
+//     L%16 (dims 32*(L/16) .. +32) and holds the same dims of query head
+//     L%16, so both operands use one k order; bf16 x bf16 products are
+//     exact in fp32.  S row r, head h ends in lane 16*(r/4) + h, element
+//     r%4;
+//   - the online softmax runs in that layout (the four lanes of a head are
+//     combined with lane-row swaps), and hands the weights p and the
+//     rescale factors to the value pass through a per-wave LDS tile;
+//   - values on the vector units: 16-lane row groups, lane l holding dims
+//     8l .. 8l+7 of rows g, g+4, g+8, g+12 of the tile.
+// The next tile's key and value rows are loaded while the current one is
+// used.  The selection list already holds physical row ids (page*16 +
+// slot); all G query heads of the KV group share the rows.
 #include "internal.h"
 
 namespace dkv {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kLanesPerRow = 16;
-constexpr int kRowGroups = kThreads / kLanesPerRow;
 constexpr int kPartStride = kHeadDim + 2; // m, l, acc[128]
 
 __device__ __forceinline__ void unpack8(const uint4 &v, float (&f)[8]) {
@@ -33,20 +42,6 @@ __device__ __forceinline__ void unpack8(const uint4 &v, float (&f)[8]) {
   f[5] = __uint_as_float(v.z & 0xFFFF0000u);
   f[6] = __uint_as_float(v.w << 16);
   f[7] = __uint_as_float(v.w & 0xFFFF0000u);
-}
-
-// Sum over the 16 lanes of a DPP row, in every lane of the row: quad xor 1,
-// quad xor 2, half-row mirror (the other quad), row mirror (the other half).
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float sum_row16(float x) {
-  x += dpp_mov<0xB1>(x);  // quad_perm [1,0,3,2]
-  x += dpp_mov<0x4E>(x);  // quad_perm [2,3,0,1]
-  x += dpp_mov<0x141>(x); // row_half_mirror
-  x += dpp_mov<0x140>(x); // row_mirror
-  return x;
 }
 
 // Merge online-softmax state (m2, l2, a2) into (m1, l1, a1).
@@ -61,6 +56,38 @@ __device__ __forceinline__ void merge_state(float &m1, float &l1, float *a1,
   m1 = m;
 }
 
+typedef __bf16 v8bf16 __attribute__((ext_vector_type(8)));
+typedef float v4f32 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ v8bf16 as_bf16x8(const uint4 &u) {
+  return __builtin_bit_cast(v8bf16, u);
+}
+
+// max / sum over the four 16-lane rows (lanes l, l^16, l^32, l^48)
+__device__ __forceinline__ float max_4rows(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_4rows(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+constexpr int kWaves = kThreads / 64;
+constexpr int kTileRows = 16;
+constexpr int kWaveRows = kAttnRows / kWaves;
+constexpr int kTiles = kWaveRows / kTileRows;
+static_assert(kTiles * kTileRows * kWaves == kAttnRows, "whole tiles");
+constexpr int kPStride = 8; // floats per row of the p tile (G <= 8)
+
 template <int G>
 __global__ __launch_bounds__(kThreads) void attend_split_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_pool,
@@ -70,29 +97,12 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(
   const int split = blockIdx.x;
   const int unit = blockIdx.y;
   const int s = unit / Hkv, g = unit % Hkv;
-  const int lane = threadIdx.x % kLanesPerRow;
-  const int rg = threadIdx.x / kLanesPerRow;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int lrow = lane & 15, lgrp = lane >> 4;
   const int n = cnt[unit];
   const int r0 = split * kAttnRows;
   const int r1 = (r0 + kAttnRows < n) ? r0 + kAttnRows : n;
-
-  float qv[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const uint4 raw = *reinterpret_cast<const uint4 *>(
-        q + ((int64_t)s * Hq + (int64_t)g * G + h) * kHeadDim + lane * 8);
-    unpack8(raw, qv[h]);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) qv[h][c] *= qscale;
-  }
-  float m[G], l[G], acc[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = -INFINITY;
-    l[h] = 0.f;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc[h][c] = 0.f;
-  }
 
   // the split's row ids, once, into LDS
   __shared__ int32_t sid[kAttnRows];
@@ -100,108 +110,147 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(
     const int r = r0 + i;
     sid[i] = r < r1 ? rows[(int64_t)unit * cap + r] : -1;
   }
+
+  // query operand: head lrow (zero past G), dims 32*lgrp .. +32
+  uint4 qb[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) qb[c] = make_uint4(0u, 0u, 0u, 0u);
+  if (lrow < G) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(
+        q + ((int64_t)s * Hq + (int64_t)g * G + lrow) * kHeadDim + 32 * lgrp);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qb[c] = src[c];
+  }
   __syncthreads();
 
-  // Row group rg takes rows rg, rg+16, ... of the split: four batches of
-  // four, the next batch's loads issued before the current batch is used.
-  constexpr int kBatch = 4;
-  constexpr int kBatches = kAttnRows / (kBatch * kRowGroups);
-  static_assert(kBatches * kBatch * kRowGroups == kAttnRows, "whole batches");
-  auto load_batch = [&](int b, uint4 (&kr)[kBatch], uint4 (&vr)[kBatch], bool (&ok)[kBatch]) {
+  // per-wave hand-off tile: p[row][head] and the rescale factors
+  __shared__ __attribute__((aligned(16))) float sp[kWaves][kTileRows][kPStride];
+  __shared__ __attribute__((aligned(16))) float sc[kWaves][kPStride];
+
+  float m = -INFINITY, l = 0.f; // state of head lrow (all four lane rows)
+  float acc[G][8];
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      const int idx = sid[(b * kBatch + i) * kRowGroups + rg];
-      ok[i] = idx >= 0;
-      const int64_t off = ((int64_t)(ok[i] ? idx : 0) * Hkv + g) * kHeadDim + lane * 8;
-      kr[i] = make_uint4(0, 0, 0, 0);
-      vr[i] = make_uint4(0, 0, 0, 0);
-      if (ok[i]) {
-        kr[i] = *reinterpret_cast<const uint4 *>(k_pool + off);
-        vr[i] = *reinterpret_cast<const uint4 *>(v_pool + off);
-      }
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[h][c] = 0.f;
+
+  const int row0 = wave * kWaveRows;
+  auto load_tile = [&](int t, uint4 (&kr)[4], uint4 (&vr)[4], uint32_t &kvalid) {
+    const int base = row0 + t * kTileRows;
+    const int kid = sid[base + lrow];
+    kvalid = kid >= 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) kr[c] = make_uint4(0u, 0u, 0u, 0u);
+    if (kid >= 0) {
+      const uint4 *src = reinterpret_cast<const uint4 *>(
+          k_pool + ((int64_t)kid * Hkv + g) * kHeadDim + 32 * lgrp);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) kr[c] = src[c];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int vid = sid[base + lgrp + 4 * i];
+      vr[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (vid >= 0)
+        vr[i] = *reinterpret_cast<const uint4 *>(
+            v_pool + ((int64_t)vid * Hkv + g) * kHeadDim + 8 * lrow);
     }
   };
-  auto use_batch = [&](const uint4 (&kr)[kBatch], const uint4 (&vr)[kBatch],
-                       const bool (&ok)[kBatch]) {
-    float dot[G][kBatch];
+  auto use_tile = [&](const uint4 (&kr)[4], const uint4 (&vr)[4], uint32_t kvalid) {
+    // ---- logits of the tile's 16 rows for every head
+    v4f32 S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      float kf[8];
-      unpack8(kr[i], kf);
+    for (int c = 0; c < 4; ++c)
+      S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[c]), as_bf16x8(qb[c]),
+                                                  S, 0, 0, 0);
+    // rows whose id is valid: bit r of the ballot (lanes r, r+16, ... agree)
+    const uint32_t vmask = (uint32_t)__ballot(kvalid != 0) & 0xFFFFu;
+    float x[4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * lgrp + i;
+      x[i] = ((vmask >> r) & 1u) ? S[i] * qscale : -INFINITY;
+      tmax = fmaxf(tmax, x[i]);
+    }
+    tmax = max_4rows(tmax);
+    const float mn = fmaxf(m, tmax);
+    float corr = 1.f, psum = 0.f;
+    float p[4];
+    if (mn == -INFINITY) { // nothing valid yet for this head
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = 0.f;
+    } else {
+      corr = exp2f(m - mn);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = exp2f(x[i] - mn);
+        psum += p[i];
+      }
+    }
+    psum = sum_4rows(psum);
+    l = l * corr + psum;
+    m = mn;
+    // ---- hand p and corr to the row groups
+    if (lrow < G) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sp[wave][4 * lgrp + i][lrow] = p[i];
+      if (lgrp == 0) sc[wave][lrow] = corr;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float cr[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) cr[h] = sc[wave][h];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[h][c] *= cr[h];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float vf[8];
+      unpack8(vr[i], vf);
+      const int r = lgrp + 4 * i;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        float d = 0.f;
+        const float ph = sp[wave][r][h];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) d = fmaf(qv[h][c], kf[c], d);
-        dot[h][i] = ok[i] ? sum_row16(d) : -INFINITY;
+        for (int c = 0; c < 8; ++c) acc[h][c] = fmaf(ph, vf[c], acc[h][c]);
       }
     }
-    float vf[kBatch][8];
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) unpack8(vr[i], vf[i]);
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float mn = m[h];
-#pragma unroll
-      for (int i = 0; i < kBatch; ++i) mn = fmaxf(mn, dot[h][i]);
-      if (mn == -INFINITY) continue; // nothing valid yet (uniform per row group)
-      const float corr = exp2f(m[h] - mn);
-      float pr[kBatch];
-      float psum = 0.f;
-#pragma unroll
-      for (int i = 0; i < kBatch; ++i) {
-        pr[i] = exp2f(dot[h][i] - mn);
-        psum += pr[i];
-      }
-      l[h] = l[h] * corr + psum;
-      m[h] = mn;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        float a = acc[h][c] * corr;
-#pragma unroll
-        for (int i = 0; i < kBatch; ++i) a = fmaf(pr[i], vf[i][c], a);
-        acc[h][c] = a;
-      }
-    }
+    // the tile is read before the next one is written
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
   };
   {
-    uint4 ka[kBatch], va[kBatch], kb[kBatch], vb[kBatch];
-    bool oa[kBatch], ob[kBatch];
-    load_batch(0, ka, va, oa);
+    uint4 ka[4], va[4], kb[4], vb[4];
+    uint32_t oka, okb;
+    load_tile(0, ka, va, oka);
 #pragma unroll
-    for (int b = 0; b < kBatches; b += 2) {
-      if (b + 1 < kBatches) load_batch(b + 1, kb, vb, ob);
-      use_batch(ka, va, oa);
-      if (b + 2 < kBatches) load_batch(b + 2, ka, va, oa);
-      if (b + 1 < kBatches) use_batch(kb, vb, ob);
+    for (int t = 0; t < kTiles; t += 2) {
+      if (t + 1 < kTiles) load_tile(t + 1, kb, vb, okb);
+      use_tile(ka, va, oka);
+      if (t + 2 < kTiles) load_tile(t + 2, ka, va, oka);
+      if (t + 1 < kTiles) use_tile(kb, vb, okb);
     }
   }
 
-  // Merge the 16 row groups: first the 4 groups of a wave (lanes l, l+16,
-  // l+32, l+48 hold the same dims), then the 4 waves through LDS.
+  // The wave's state: m, l per head (lane lrow), acc per row group over its
+  // rows, all relative to the same m: sum the four row groups.
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
+  for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int off2 = 16; off2 < 64; off2 <<= 1) {
-      const float m2 = __shfl_xor(m[h], off2);
-      const float l2 = __shfl_xor(l[h], off2);
-      float a2[8];
+    for (int c = 0; c < 8; ++c) acc[h][c] = sum_4rows(acc[h][c]);
+  __shared__ float sm[kWaves][G][kPartStride];
+  if (lgrp == 0) {
 #pragma unroll
-      for (int c = 0; c < 8; ++c) a2[c] = __shfl_xor(acc[h][c], off2);
-      merge_state(m[h], l[h], acc[h], m2, l2, a2, 8);
-    }
-  }
-  __shared__ float sm[4][G][kPartStride];
-  const int wave = threadIdx.x / 64;
-  if ((threadIdx.x & 63) < kLanesPerRow) {
+    for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      if (lane == 0) {
-        sm[wave][h][0] = m[h];
-        sm[wave][h][1] = l[h];
-      }
-#pragma unroll
-      for (int c = 0; c < 8; ++c) sm[wave][h][2 + lane * 8 + c] = acc[h][c];
+      for (int c = 0; c < 8; ++c) sm[wave][h][2 + 8 * lrow + c] = acc[h][c];
+    if (lrow < G) {
+      sm[wave][lrow][0] = m;
+      sm[wave][lrow][1] = l;
     }
   }
   __syncthreads();
@@ -209,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(
   for (int t = threadIdx.x; t < G * kHeadDim; t += kThreads) {
     const int h = t / kHeadDim, dim = t % kHeadDim;
     float mm = sm[0][h][0], ll = sm[0][h][1], aa = sm[0][h][2 + dim];
-    for (int wv = 1; wv < 4; ++wv)
+    for (int wv = 1; wv < kWaves; ++wv)
       merge_state(mm, ll, &aa, sm[wv][h][0], sm[wv][h][1], &sm[wv][h][2 + dim], 1);
     float *dst = part + (((int64_t)unit * nsplit + split) * G + h) * kPartStride;
     if (dim == 0) {
