@@ -73,6 +73,32 @@ def gpu_decode(cfg: dkv.Config, inp: dict, codes, radii, debug: bool = True,
     return res
 
 
+def gpu_decode_append(cfg: dkv.Config, inp: dict):
+    """dkv_encode over [0, N-1) of every sequence into sentinel-filled pools,
+    then dkv_decode_append (which must encode position N-1 itself).  Returns
+    (result dict, codes, radii)."""
+    dev = inp["k_pool"].device
+    nb = inp["k_pool"].shape[0]
+    Hkv, B = cfg.num_kv_heads, inp["block_table"].shape[0]
+    codes = torch.full((nb, Hkv, PAGE, cfg.code_bits // 32), 0x5A5A5A5A,
+                       dtype=torch.int32, device=dev)
+    radii = torch.full((nb, Hkv, PAGE), 0xA5, dtype=torch.uint8, device=dev)
+    start = torch.zeros(B, dtype=torch.int32, device=dev)
+    end = torch.clamp(inp["seq_lens"] - 1, min=0).to(torch.int32)
+    dkv.encode(cfg, inp["k_pool"], inp["block_table"], start, end,
+               inp["max_seq_len"], inp["proj"], codes, radii)
+    ws = torch.empty(dkv.decode_workspace_size(cfg, B, inp["max_seq_len"]),
+                     dtype=torch.uint8, device=dev)
+    out = torch.full((B, cfg.num_q_heads, cfg.head_dim), float("nan"), device=dev)
+    sel = torch.full((B, Hkv, cfg.select_cap), -7, dtype=torch.int32, device=dev)
+    cnt = torch.full((B, Hkv), -7, dtype=torch.int32, device=dev)
+    dkv.decode_append(cfg, inp["q"], inp["k_pool"], inp["v_pool"], codes, radii,
+                      inp["block_table"], inp["seq_lens"], inp["max_seq_len"],
+                      inp["proj"], out, ws, sel, cnt)
+    torch.cuda.synchronize()
+    return {"out": out, "sel": sel, "cnt": cnt}, codes, radii
+
+
 def check_unit(cfg: dkv.Config, inp: dict, gpu: dict, codes, radii, s: int, g: int,
                check_codes: bool = True, needles=None) -> dict:
     """Compares one (sequence s, KV head g) unit with the oracle."""

@@ -16,7 +16,7 @@ import workloads
 import hashed_top_sparse_amd as dkv
 import oracle
 from helpers import PAGE, logical_codes, logical_radii, logical_rows, tensor_bits
-from parity import check_unit, config_of, gpu_decode, gpu_encode_all
+from parity import check_unit, config_of, gpu_decode, gpu_decode_append, gpu_encode_all
 
 pytestmark = pytest.mark.gpu
 
@@ -146,33 +146,14 @@ def test_forced_ties_go_to_lowest_positions():
 
 
 def _run_append(wl, units=None):
-    """dkv_encode over [0, N-1) of every sequence into sentinel-filled
-    pools, then dkv_decode_append: the newest key of every sequence must be
-    encoded by the decode call itself, and the step must match the oracle."""
+    """The newest key of every sequence must be encoded by
+    dkv_decode_append itself, and the step must match the oracle."""
     print(f"[case] append-decode {wl.name}", flush=True)
     cfg = config_of(wl)
     inp = workloads.make_inputs(wl, DEV)
-    nb, Hkv = inp["k_pool"].shape[0], wl.num_kv_heads
-    codes = torch.full((nb, Hkv, PAGE, wl.code_bits // 32), 0x5A5A5A5A,
-                       dtype=torch.int32, device=DEV)
-    radii = torch.full((nb, Hkv, PAGE), 0xA5, dtype=torch.uint8, device=DEV)
-    B = wl.batch
-    start = torch.zeros(B, dtype=torch.int32, device=DEV)
-    end = torch.clamp(inp["seq_lens"] - 1, min=0).to(torch.int32)
-    dkv.encode(cfg, inp["k_pool"], inp["block_table"], start, end,
-               inp["max_seq_len"], inp["proj"], codes, radii)
-    ws = torch.empty(dkv.decode_workspace_size(cfg, B, inp["max_seq_len"]),
-                     dtype=torch.uint8, device=DEV)
-    out = torch.full((B, cfg.num_q_heads, cfg.head_dim), float("nan"), device=DEV)
-    sel = torch.full((B, Hkv, cfg.select_cap), -7, dtype=torch.int32, device=DEV)
-    cnt = torch.full((B, Hkv), -7, dtype=torch.int32, device=DEV)
-    dkv.decode_append(cfg, inp["q"], inp["k_pool"], inp["v_pool"], codes, radii,
-                      inp["block_table"], inp["seq_lens"], inp["max_seq_len"],
-                      inp["proj"], out, ws, sel, cnt)
-    torch.cuda.synchronize()
-    gpu = {"out": out, "sel": sel, "cnt": cnt}
+    gpu, codes, radii = gpu_decode_append(cfg, inp)
     if units is None:
-        units = [(s, g) for s in range(B) for g in range(Hkv)]
+        units = [(s, g) for s in range(wl.batch) for g in range(wl.num_kv_heads)]
     for s, g in units:
         check_unit(cfg, inp, gpu, codes, radii, s, g)  # codes of all N keys
     return gpu, codes, radii, inp, cfg
