@@ -105,7 +105,9 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
       use_bitmap = false;
     } else {
       // the candidates of the unit's groups (those below N were written):
-      // count prefix over the groups, in LDS when it fits
+      // count prefix over the groups, in LDS when it fits.  A count is at
+      // most the group's size; it is clamped to it anyway, so a corrupt
+      // count cannot send a read past the group's region.
       const int ngs = (N + kGroupKeys - 1) / kGroupKeys;
       const uint32_t *tc = tcount + (int64_t)unit * cand_groups;
       const uint2 *cb = cand + (int64_t)unit * cand_groups * kGroupKeys;
@@ -118,11 +120,12 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
 #pragma unroll
           for (int i = 0; i < kPer; ++i) {
             const int gi = tid * kPer + i;
-            c[i] = gi < ngs ? tc[gi] : 0u;
+            c[i] = gi < ngs ? min(tc[gi], (uint32_t)kGroupKeys) : 0u;
             part += c[i];
           }
         } else {
-          for (int gi = tid; gi < ngs; gi += kThreads) part += tc[gi];
+          for (int gi = tid; gi < ngs; gi += kThreads)
+            part += min(tc[gi], (uint32_t)kGroupKeys);
         }
         uint32_t off = wg_exclusive_scan<kThreads>(part, &sel.red[2][0], &nlist);
         if (pre_lds) {
@@ -139,7 +142,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
       // straight from the group regions (for units too large to stage)
       auto for_each_global = [&](auto fn) {
         for (int gi = wave; gi < ngs; gi += kWaves) {
-          const uint32_t n = tc[gi];
+          const uint32_t n = min(tc[gi], (uint32_t)kGroupKeys);
           const uint2 *reg = cb + (int64_t)gi * kGroupKeys;
           for (uint32_t j = lane; j < n; j += 64) {
             const uint2 e = reg[j];

@@ -39,12 +39,11 @@ static_assert(kTaskQuads % kDepth == 0 && kTaskQuads >= 2 * kDepth, "prefetch ro
 // quad of a task at which the task after next and the next task's operand
 // are loaded: kDepth quads before the next task's first prefetch
 constexpr int kLookahead = kTaskQuads - 2 * kDepth;
-constexpr int kStageCand = 128;
 // Workgroups per CU: one wave per SIMD each, four waves per SIMD in all.
 // More resident waves do not help (the kernel is bound by instruction
 // issue), and four per SIMD keeps each wave's task count equal when the
 // task count is a multiple of 4 x 4 x CUs.
-constexpr int kWgPerCu = 4; // candidates per task staged in LDS
+constexpr int kWgPerCu = 4;
 
 // Compile-time loop: f(std::integral_constant<int, I>) for I in [I0, N).
 template <int I, int N, typename F>
@@ -117,7 +116,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
   // the current task's radius lines (16 bytes per page, page order), and
   // its candidates staged before they are written out
   __shared__ __attribute__((aligned(16))) uint8_t rtab[kWaves][kGroupKeys];
-  __shared__ uint2 cstage[kWaves][kStageCand];
+  // (u, index in the task) of every candidate of the current task
+  __shared__ uint2 cstage[kWaves][kGroupKeys];
   uint8_t *radC = rtab[wave];
   uint2 *cst = cstage[wave];
 
@@ -276,39 +276,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
         if (pos < C.N)
           scores_out[(int64_t)C.unit * score_stride + pos] = (int32_t)(u - kScoreBias);
       }
-      // a candidate: position in [lo, hi) and u >= L (no branches: both
-      // tests are single compares, the range one on pos - lo unsigned)
-      const bool c = ((uint32_t)(pos - C.lo) < (uint32_t)(C.hi - C.lo)) & (u >= LC);
-      const uint64_t m = __ballot(c);
-      if (m != 0) {
-        // staged in LDS (no vector-memory store inside the stream); past
-        // the stage, straight to the region (rare)
-        const uint32_t slot = __builtin_amdgcn_mbcnt_hi(
-            (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, nc));
-        const uint64_t v = ((uint64_t)(uint32_t)pos << 32) | u; // (u, pos)
-        // address-space-qualified pointers keep these an LDS store and a
-        // global store (a merged flat store would count against both wait
-        // counters)
-        if (c && slot < (uint32_t)kStageCand)
-          ((__attribute__((address_space(3))) uint64_t *)cst)[slot] = v;
-        if (nc + __popcll(m) > (uint32_t)kStageCand) { // wave-uniform, rare
-          if (c && slot >= (uint32_t)kStageCand)
-            ((__attribute__((address_space(1))) uint64_t *)reg)[slot] = v;
-        }
-        nc += __popcll(m);
-      }
+      // A candidate: position in [lo, hi) and u >= L, each test one
+      // compare (the range one on pos - lo, unsigned).  It is appended to
+      // the wave's LDS list of the task without a branch: its slot is the
+      // running count plus the candidates in lower lanes.
+      const bool inr = (uint32_t)(pos - C.lo) < (uint32_t)(C.hi - C.lo);
+      const bool ge = u >= LC;
+      const uint64_t m = __ballot(inr) & __ballot(ge);
+      const uint32_t cslot = __builtin_amdgcn_mbcnt_hi(
+          (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, nc));
+      // an address-space-qualified pointer keeps this an LDS store (a flat
+      // store would count against the vector-memory wait counter)
+      if (inr && ge)
+        ((__attribute__((address_space(3))) uint64_t *)cst)[cslot] =
+            ((uint64_t)(uint32_t)(64 * q + lane) << 32) | u;
+      nc += (uint32_t)__popcll(m);
     });
-    // Write the staged candidates with a fixed number of stores, every lane
-    // active (lanes past the count write the region's last slot, which is
-    // read only when all 1024 keys are candidates -- and then no lane is
-    // past the count here), and the count.
+    // Write the task's candidates (u, position) to its region: one store
+    // with every lane active (lanes past the count write the region's last
+    // slot, which is read only when all 1024 keys are candidates -- and then
+    // no lane is past the count), more only past 64 candidates (rare), then
+    // the count.
     {
-      const uint32_t ns = min(nc, (uint32_t)kStageCand);
-#pragma unroll
-      for (int r = 0; r < kStageCand / 64; ++r) {
-        const uint32_t e = (uint32_t)(64 * r + lane);
+      const uint32_t ns = nc;
+      auto flush = [&](uint32_t e) {
         const uint2 v = cst[e < ns ? e : 0];
-        reg[e < ns ? e : kGroupKeys - 1] = v;
+        reg[e < ns ? e : kGroupKeys - 1] = make_uint2(v.x, (uint32_t)C.key0 + v.y);
+      };
+      flush((uint32_t)lane);
+      if (ns > 64u) { // wave-uniform
+        for (uint32_t e0 = 64; e0 < ns; e0 += 64) flush(e0 + (uint32_t)lane);
       }
       tcount[t_idx] = nc;
     }
