@@ -75,6 +75,11 @@ bool make_dims(const dkv_config *cfg, int32_t batch, int32_t max_seq_len,
   d->nsplit = (cap + kAttnRows - 1) / kAttnRows;
   d->cand_groups = (max_seq_len + kGroupKeys - 1) / kGroupKeys;
   d->bm_words = (max_seq_len + 31) / 32;
+  // candidate regions are numbered with 32-bit ids
+  if ((int64_t)d->B * d->Hkv * d->cand_groups >= (int64_t)1 << 31) {
+    *why = DKV_ERR_UNSUPPORTED;
+    return false;
+  }
   // buffer views of the code and radius pools use 32-bit byte offsets
   if ((uint64_t)num_blocks * d->Hkv * d->W * kPage * 4 > 0xFFFFFFFFull) {
     *why = DKV_ERR_UNSUPPORTED;

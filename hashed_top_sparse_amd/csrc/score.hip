@@ -44,6 +44,8 @@ constexpr int kLookahead = kTaskQuads - 2 * kDepth;
 // issue), and four per SIMD keeps each wave's task count equal when the
 // task count is a multiple of 4 x 4 x CUs.
 constexpr int kWgPerCu = 4;
+constexpr int kCandList = kGroupKeys; // per-wave candidate list (8 KB of LDS)
+constexpr int kTaskTable = 16;        // tasks recorded before a forced write
 
 // Compile-time loop: f(std::integral_constant<int, I>) for I in [I0, N).
 template <int I, int N, typename F>
@@ -116,10 +118,38 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
   // the current task's radius lines (16 bytes per page, page order), and
   // its candidates staged before they are written out
   __shared__ __attribute__((aligned(16))) uint8_t rtab[kWaves][kGroupKeys];
-  // (u, index in the task) of every candidate of the current task
-  __shared__ uint2 cstage[kWaves][kGroupKeys];
+  // The wave's candidates, (u, index in the task), kept in LDS until the
+  // wave has streamed all its tasks, then written out with the counts: a
+  // global store inside the stream would hold up the completion of every
+  // load issued after it (one in-order counter covers loads and stores).
+  // Per task: (region, first position, entries in the list, count).  A
+  // task that finds the list full writes the rest of its candidates to its
+  // region at once (rare).
+  __shared__ uint2 cstage[kWaves][kCandList];
+  __shared__ uint32_t ttab[kWaves][kTaskTable][4];
   uint8_t *radC = rtab[wave];
   uint2 *cst = cstage[wave];
+  uint32_t (*tt)[4] = ttab[wave];
+  uint32_t used = 0;  // list entries in use
+  int ntab = 0;       // tasks recorded
+  // Writes every recorded task's listed candidates and its count.  Lanes
+  // past a task's list length repeat its last entry (same bytes, same slot).
+  auto flush_all = [&]() {
+    uint32_t start = 0;
+    for (int k = 0; k < ntab; ++k) {
+      const uint32_t t_idx = tt[k][0], key0 = tt[k][1], nbuf = tt[k][2], ncount = tt[k][3];
+      uint2 *reg = cand + (int64_t)t_idx * kGroupKeys;
+      for (uint32_t e0 = 0; e0 < nbuf; e0 += 64) {
+        const uint32_t e = min(e0 + (uint32_t)lane, nbuf - 1);
+        const uint2 v = cst[start + e];
+        reg[e] = make_uint2(v.x, key0 + v.y);
+      }
+      if (lane == 0) tcount[t_idx] = ncount;
+      start += nbuf;
+    }
+    used = 0;
+    ntab = 0;
+  };
 
   // task id -> task, or none if its page group is past the sequence
   auto decode = [&](int t, Task &T) -> bool {
@@ -236,7 +266,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     uint32_t L1 = 0;
     const int64_t t_idx = (int64_t)C.unit * cand_groups + C.grp;
     uint2 *reg = cand + t_idx * kGroupKeys;
-    uint32_t nc = 0;
+    uint32_t nc = 0; // the task's candidates so far
     static_for<0, kTaskQuads>([&](auto qc) {
       constexpr int q = decltype(qc)::value;
       constexpr int slot = q % kDepth;
@@ -278,36 +308,38 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
       }
       // A candidate: position in [lo, hi) and u >= L, each test one
       // compare (the range one on pos - lo, unsigned).  It is appended to
-      // the wave's LDS list of the task without a branch: its slot is the
+      // the wave's LDS list without a branch: its slot in the task is the
       // running count plus the candidates in lower lanes.
       const bool inr = (uint32_t)(pos - C.lo) < (uint32_t)(C.hi - C.lo);
       const bool ge = u >= LC;
       const uint64_t m = __ballot(inr) & __ballot(ge);
       const uint32_t cslot = __builtin_amdgcn_mbcnt_hi(
           (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, nc));
+      const uint32_t lslot = used + cslot;
       // an address-space-qualified pointer keeps this an LDS store (a flat
       // store would count against the vector-memory wait counter)
-      if (inr && ge)
-        ((__attribute__((address_space(3))) uint64_t *)cst)[cslot] =
+      if (inr && ge && lslot < (uint32_t)kCandList)
+        ((__attribute__((address_space(3))) uint64_t *)cst)[lslot] =
             ((uint64_t)(uint32_t)(64 * q + lane) << 32) | u;
+      if (used + nc + (uint32_t)__popcll(m) > (uint32_t)kCandList) { // rare
+        if (inr && ge && lslot >= (uint32_t)kCandList)
+          ((__attribute__((address_space(1))) uint64_t *)reg)[cslot] =
+              ((uint64_t)(uint32_t)pos << 32) | u;
+      }
       nc += (uint32_t)__popcll(m);
     });
-    // Write the task's candidates (u, position) to its region: one store
-    // with every lane active (lanes past the count write the region's last
-    // slot, which is read only when all 1024 keys are candidates -- and then
-    // no lane is past the count), more only past 64 candidates (rare), then
-    // the count.
+    // record the task: its first min(nc, room) candidates are in the list
     {
-      const uint32_t ns = nc;
-      auto flush = [&](uint32_t e) {
-        const uint2 v = cst[e < ns ? e : 0];
-        reg[e < ns ? e : kGroupKeys - 1] = make_uint2(v.x, (uint32_t)C.key0 + v.y);
-      };
-      flush((uint32_t)lane);
-      if (ns > 64u) { // wave-uniform
-        for (uint32_t e0 = 64; e0 < ns; e0 += 64) flush(e0 + (uint32_t)lane);
+      const uint32_t nbuf = min(nc, (uint32_t)kCandList - used);
+      if (lane == 0) {
+        tt[ntab][0] = (uint32_t)t_idx;
+        tt[ntab][1] = (uint32_t)C.key0;
+        tt[ntab][2] = nbuf;
+        tt[ntab][3] = nc;
       }
-      tcount[t_idx] = nc;
+      used += nbuf;
+      ++ntab;
+      if (ntab == kTaskTable) flush_all(); // many tasks per wave (rare)
     }
 
     // rotate the stream
@@ -333,6 +365,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
   if (run_task())
     while (run_task()) {
     }
+  flush_all();
 }
 
 } // namespace
