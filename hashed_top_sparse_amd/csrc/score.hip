@@ -253,6 +253,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     constexpr int q = decltype(qc)::value;
     load_quad(tabC[4 * q + row], buf[q]);
   });
+  // LDS values of the current quad (see run_task)
+  uint32_t r8c = radC[lane];
+  uint32_t refc = tabC[4 * kDepth + row];
 
   // One task: score C's 16 quads while prefetching, then rotate the stream.
   // The first call is peeled off the loop so that the loop head is only
@@ -283,14 +286,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[ks][i] = buf[slot].d[ks][i];
-      // radius byte of key lane&15 of page 4q + lane>>4
-      const uint32_t r8 = radC[64 * q + lane];
+      // radius byte of key lane&15 of page 4q + lane>>4, and the page id
+      // of the refill below, both read from LDS one quad ahead
+      const uint32_t r8 = r8c;
       // ---- refill the slot: the quad kDepth further on (C's, or T1's
       // first ones)
-      if constexpr (q + kDepth < kTaskQuads)
-        load_quad(tabC[4 * (q + kDepth) + row], buf[slot]);
-      else
-        load_quad(tab1[4 * (q + kDepth - kTaskQuads) + row], buf[slot]);
+      load_quad(refc, buf[slot]);
+      // ---- the next quad's LDS reads, before this quad's candidate write
+      // (LDS operations complete in order)
+      if constexpr (q + 1 < kTaskQuads) {
+        r8c = radC[64 * (q + 1) + lane];
+        refc = (q + 1 + kDepth < kTaskQuads) ? tabC[4 * (q + 1 + kDepth) + row]
+                                            : tab1[4 * (q + 1 + kDepth - kTaskQuads) + row];
+      }
       uint32_t cw[4][KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -360,6 +368,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     // the new next task's lines requested
     store_radius(radN);
     radN = load_radius(tab1[lane]);
+    r8c = radC[lane];
+    refc = tabC[4 * kDepth + row];
     return true;
   };
   if (run_task())
