@@ -89,35 +89,56 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
   __shared__ uint32_t sCount[kThreads / 64];
   __shared__ SelectShared<kThreads> sel;
 
-  // ---- sample plan (it needs only N); the sample pages' loads are issued
-  // first so they are in flight while the query is projected
-  const int N = seq_len_clamped(seq_lens, s, n_max);
-  const int nc = max(0, N - w - sigma);
-  const int keff = min(k, nc);
-  const bool sample = keff > 0 && keff < nc;
-  int pc0 = 0, SP = 1, nsp = 0;
-  if (sample) {
-    pc0 = sigma / kPage;
-    const int ncp = (N - w + kPage - 1) / kPage - pc0;
-    while (SP < 32 && 2 * SP <= keff / 32) SP *= 2;
-    while ((ncp + SP - 1) / SP > kSamplePages) SP *= 2;
-    nsp = (ncp + SP - 1) / SP;
-  }
-  const PoolView view = make_pool_view(codes, radii, code_bytes, radius_bytes,
-                                       W, Hkv, g, lane);
-  // wave v samples pages t = v + 8*i; lane i holds the block id of its
-  // i-th page
+  // ---- sample plan: every SP-th candidate page from page pc0, nsp pages
+  struct Plan {
+    int nc, keff, pc0, SP, nsp;
+  };
+  auto plan_for = [&](int n) {
+    Plan P;
+    P.nc = max(0, n - w - sigma);
+    P.keff = min(k, P.nc);
+    P.pc0 = 0;
+    P.SP = 1;
+    P.nsp = 0;
+    if (P.keff > 0 && P.keff < P.nc) {
+      P.pc0 = sigma / kPage;
+      const int ncp = (n - w + kPage - 1) / kPage - P.pc0;
+      while (P.SP < 32 && 2 * P.SP <= P.keff / 32) P.SP *= 2;
+      while ((ncp + P.SP - 1) / P.SP > kSamplePages) P.SP *= 2;
+      P.nsp = (ncp + P.SP - 1) / P.SP;
+    }
+    return P;
+  };
+  // The sample pages' loads go first so they are in flight while the query
+  // is projected.  Their block ids are read with the plan of the longest
+  // length (n_max) before the sequence's own length has arrived; when that
+  // length gives another stride or start (ragged batches) they are read
+  // again.  Wave v samples pages t = v + 8*i; lane i holds the block id of
+  // its i-th page.
   const int32_t *bt = block_table + (int64_t)s * max_blocks;
   const int tl = wave + kWv * lane;
-  const int blk_l = tl < nsp ? bt[pc0 + tl * SP] : -1;
+  const Plan spec = plan_for(n_max);
+  int blk_l = tl < spec.nsp ? bt[spec.pc0 + tl * spec.SP] : -1;
+  const int N = seq_len_clamped(seq_lens, s, n_max);
+  const Plan pl = plan_for(N);
+  const int nc = pl.nc, keff = pl.keff, pc0 = pl.pc0, SP = pl.SP, nsp = pl.nsp;
+  const bool sample = nsp > 0;
+  if (SP != spec.SP || pc0 != spec.pc0 || nsp > spec.nsp) // workgroup-uniform
+    blk_l = tl < nsp ? bt[pc0 + tl * SP] : -1;
+  else if (tl >= nsp)
+    blk_l = -1;
+  const PoolView view = make_pool_view(codes, radii, code_bytes, radius_bytes,
+                                       W, Hkv, g, lane);
   uint32_t pcw[kPre][KS], pr8[kPre];
-  bool pok[kPre];
+  uint32_t pokm = 0; // bit u: preloaded page u is a valid sample page
+  static_assert(kPre <= 32, "page mask");
   if (nsp > 0) {
 #pragma unroll
     for (int u = 0; u < kPre; ++u) {
       const int blk = __builtin_amdgcn_readlane(blk_l, u);
-      pok[u] = wave + kWv * u < nsp && blk >= 0 && blk < num_blocks;
-      load_page<KS>(view, blk, pok[u], pcw[u], pr8[u]);
+      const bool ok = wave + kWv * u < nsp && blk >= 0 && blk < num_blocks;
+      pokm |= (uint32_t)ok << u;
+      load_page<KS>(view, blk, ok, pcw[u], pr8[u]);
     }
   }
 
@@ -298,9 +319,35 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
         nvalid += valid;
       }
     };
+    // the preloaded pages four at a time: after the quad step, lane L holds
+    // key L%16 of page 4a + L/16
+    const int lq = lane >> 4;
 #pragma unroll
-    for (int u = 0; u < kPre; ++u)
-      keep(wave + kWv * u, score_page<KS, G>(op, pcw[u], pr8[u], pok[u]));
+    for (int a = 0; a < kPre / 4; ++a) {
+      uint32_t cw[4][KS], r8s[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // first use of the loaded words is here (see score_page)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          cw[j][ks] = pcw[4 * a + j][ks];
+          asm volatile("" : "+v"(cw[j][ks]));
+        }
+        r8s[j] = pr8[4 * a + j];
+        asm volatile("" : "+v"(r8s[j]));
+      }
+      const int mx = score_quad_max_seq<KS, G>(op, cw);
+      const uint32_t r8 = lq == 0 ? r8s[0] : lq == 1 ? r8s[1] : lq == 2 ? r8s[2] : r8s[3];
+      const bool ok = (pokm >> (4 * a + lq)) & 1u;
+      const int t = wave + kWv * (4 * a + lq);
+      if (t < nsp) {
+        const int pos = (pc0 + t * SP) * kPage + (lane & 15);
+        const bool valid = ok && pos >= sigma && pos < N - w;
+        sSample[t * kPage + (lane & 15)] =
+            valid ? (uint32_t)(__mul24((int)r8, mx) + (int)kScoreBias) : 0u;
+        nvalid += valid;
+      }
+    }
     // pages past the first kPre of each wave (long sequences with a small
     // stride): 8 loads in flight per step
     for (int i0 = kPre; wave + kWv * i0 < nsp; i0 += 8) {
