@@ -12,8 +12,9 @@
 // split's rows in tiles of 16.  Per tile:
 //   - logits on the matrix cores: S = K Q^T with four 16x16x32 bf16 ops
 //     (K rows as the 16 M rows, the G query heads as N columns, d = 128 in
-//     four K-steps of 32).  Lane L loads 64 contiguous bytes of key row
-//     L%16 (dims 32*(L/16) .. +32) and holds the same dims of query head
+//     four K-steps of 32).  For K-step c, lane L loads dims 32c + 8(L/16)
+//     .. +8 of key row L%16 (so one load instruction reads 64 contiguous
+//     bytes of each of 16 rows) and holds the same dims of query head
 //     L%16, so both operands use one k order; bf16 x bf16 products are
 //     exact in fp32.  S row r, head h ends in lane 16*(r/4) + h, element
 //     r%4;
@@ -111,15 +112,15 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(
     sid[i] = r < r1 ? rows[(int64_t)unit * cap + r] : -1;
   }
 
-  // query operand: head lrow (zero past G), dims 32*lgrp .. +32
+  // query operand: head lrow (zero past G); K-step c takes dims
+  // 32c + 8*lgrp .. +8, the same dims the key rows give this lane
   uint4 qb[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) qb[c] = make_uint4(0u, 0u, 0u, 0u);
   if (lrow < G) {
-    const uint4 *src = reinterpret_cast<const uint4 *>(
-        q + ((int64_t)s * Hq + (int64_t)g * G + lrow) * kHeadDim + 32 * lgrp);
+    const uint16_t *src = q + ((int64_t)s * Hq + (int64_t)g * G + lrow) * kHeadDim + 8 * lgrp;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) qb[c] = src[c];
+    for (int c = 0; c < 4; ++c) qb[c] = *reinterpret_cast<const uint4 *>(src + 32 * c);
   }
   __syncthreads();
 
@@ -142,10 +143,10 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(
 #pragma unroll
     for (int c = 0; c < 4; ++c) kr[c] = make_uint4(0u, 0u, 0u, 0u);
     if (kid >= 0) {
-      const uint4 *src = reinterpret_cast<const uint4 *>(
-          k_pool + ((int64_t)kid * Hkv + g) * kHeadDim + 32 * lgrp);
+      // load c: the row's bytes 64c .. 64c+63, 16 per lane row group
+      const uint16_t *src = k_pool + ((int64_t)kid * Hkv + g) * kHeadDim + 8 * lgrp;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) kr[c] = src[c];
+      for (int c = 0; c < 4; ++c) kr[c] = *reinterpret_cast<const uint4 *>(src + 32 * c);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
