@@ -159,27 +159,36 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
         }
         __syncthreads();
         if (staged) {
-          // candidate i is entry i - gpre[g] of group g, gpre[g] <= i < gpre[g+1];
-          // four independent loads in flight per thread
-          for (uint32_t i0 = 0; i0 < nlist; i0 += 4 * kThreads) {
+          // group g's candidates go to st[gpre[g] ..): wave v copies groups
+          // v, v+16, ..., four groups' first 64 entries in flight at once
+          for (int g0 = wave; g0 < ngs; g0 += 4 * kWaves) {
             uint2 e[4];
+            uint32_t dst[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const uint32_t i = i0 + r * kThreads + tid;
+              const int gi = g0 + r * kWaves;
               e[r] = make_uint2(0u, 0u);
-              if (i < nlist) {
-                int lo = 0, hi = ngs; // largest g with gpre[g] <= i
-                while (hi - lo > 1) {
-                  const int mid = (lo + hi) >> 1;
-                  if (gpre[mid] <= i) lo = mid; else hi = mid;
+              dst[r] = 0xFFFFFFFFu;
+              if (gi < ngs) {
+                const uint32_t b = gpre[gi], n = gpre[gi + 1] - b;
+                if ((uint32_t)lane < n) {
+                  e[r] = cb[(int64_t)gi * kGroupKeys + lane];
+                  dst[r] = b + (uint32_t)lane;
                 }
-                e[r] = cb[(int64_t)lo * kGroupKeys + (i - gpre[lo])];
               }
             }
 #pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (dst[r] != 0xFFFFFFFFu) st[dst[r]] = e[r];
+            // entries past the first 64 of a group (rare)
+#pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const uint32_t i = i0 + r * kThreads + tid;
-              if (i < nlist) st[i] = e[r];
+              const int gi = g0 + r * kWaves;
+              if (gi < ngs) {
+                const uint32_t b = gpre[gi], n = gpre[gi + 1] - b;
+                for (uint32_t j = 64u + (uint32_t)lane; j < n; j += 64u)
+                  st[b + j] = cb[(int64_t)gi * kGroupKeys + j];
+              }
             }
           }
           __syncthreads();
@@ -191,6 +200,15 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
             for_each_global(fn);
           }
         };
+        // the compaction below gives thread t the run [i0, i1) of the staged
+        // list; the physical rows of its first four entries are looked up
+        // now, so the block-table loads overlap the cut
+        const uint32_t per = (nlist + kThreads - 1) / kThreads;
+        const uint32_t i0 = min(nlist, tid * per), i1 = min(nlist, i0 + per);
+        int rowv[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          rowv[k] = (staged && i0 + k < i1) ? row_of(bt, (int)st[i0 + k].y, num_blocks) : -1;
         // the cut: survivors are u > Tu, or u == Tu and pos <= Tpos
         uint32_t Tu = 0, Tpos = 0;
         bool cut = false;
@@ -215,15 +233,25 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
                      : (u > T || (u == T && kPosMax - (uint32_t)pos >= Pt));
         };
         if (staged) {
-          // stable compaction of the survivors: thread t takes a contiguous
-          // run of the staged list
-          const uint32_t per = (nlist + kThreads - 1) / kThreads;
-          const uint32_t i0 = min(nlist, tid * per), i1 = min(nlist, i0 + per);
+          // stable compaction of the survivors: thread t takes the run
+          // [i0, i1) of the staged list
           uint32_t c = 0;
           for (uint32_t i = i0; i < i1; ++i) c += keep(st[i].x, (int)st[i].y);
           uint32_t tot;
           uint32_t o = wg_exclusive_scan<kThreads>(c, &sel.red[3][0], &tot);
-          for (uint32_t i = i0; i < i1; ++i) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const uint32_t i = i0 + k;
+            if (i < i1) {
+              const int pos = (int)st[i].y;
+              if (keep(st[i].x, pos)) {
+                R[base + o] = rowv[k];
+                if (U) U[base + o] = pos;
+                ++o;
+              }
+            }
+          }
+          for (uint32_t i = i0 + 4; i < i1; ++i) {
             const int pos = (int)st[i].y;
             if (keep(st[i].x, pos)) {
               R[base + o] = row_of(bt, pos, num_blocks);

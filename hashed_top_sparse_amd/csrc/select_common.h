@@ -169,10 +169,15 @@ __device__ bool wg_topk_cut(SelectShared<NT> &sh, Visit2 visit2, uint32_t kneed,
     const int lane = threadIdx.x;
     const uint2 e = lane < (int)nb1 ? sh.cut_list[lane] : make_uint2(0u, 0xFFFFFFFFu);
     uint32_t rank = 0; // pairs ahead of e in the order
-    for (int j = 0; j < (int)nb1; ++j) {
-      const uint32_t uj = (uint32_t)__shfl((int)e.x, j);
-      const uint32_t pj = (uint32_t)__shfl((int)e.y, j);
-      rank += (uj > e.x) || (uj == e.x && pj < e.y);
+    // the list is read back with broadcast LDS reads, eight at a time
+    for (int j0 = 0; j0 < (int)nb1; j0 += 8) {
+      uint2 f[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) f[t] = sh.cut_list[j0 + t];
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        if (j0 + t < (int)nb1)
+          rank += (f[t].x > e.x) || (f[t].x == e.x && f[t].y < e.y);
     }
     if (lane < (int)nb1 && rank == kneed2 - 1) {
       sh.cut_u = e.x;
