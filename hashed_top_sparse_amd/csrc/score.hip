@@ -44,7 +44,9 @@ constexpr int kLookahead = kTaskQuads - 2 * kDepth;
 // issue), and four per SIMD keeps each wave's task count equal when the
 // task count is a multiple of 4 x 4 x CUs.
 constexpr int kWgPerCu = 4;
-constexpr int kCandList = kGroupKeys; // per-wave candidate list (8 KB of LDS)
+// per-wave candidate list: kCandList entries, then one spare entry per lane
+// (8 KB of LDS in all)
+constexpr int kCandList = kGroupKeys - 64;
 constexpr int kTaskTable = 16;        // tasks recorded before a forced write
 
 // Compile-time loop: f(std::integral_constant<int, I>) for I in [I0, N).
@@ -106,6 +108,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
       const_cast<uint32_t *>(codes), 0, code_bytes, kBufferWord3);
   const __amdgpu_buffer_rsrc_t rad_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t *>(radii), 0, radius_bytes, kBufferWord3);
+  // Sequence lengths and thresholds are read with vector loads: a scalar
+  // load in the stream would make every wait on the LDS counter a full wait
+  // (scalar loads complete out of order), including the candidate writes.
+  const __amdgpu_buffer_rsrc_t len_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int32_t *>(seq_lens), 0, (uint32_t)B * 4u, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t thr_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t *>(lthr), 0, (uint32_t)(B * Hkv) * 4u, kBufferWord3);
   const uint32_t page_bytes = (uint32_t)(kPage * W * 4);
   // physical page id past the pools: its code and radius loads read 0
   const uint32_t ph_none = (uint32_t)(num_blocks * Hkv);
@@ -125,7 +134,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
   // Per task: (region, first position, entries in the list, count).  A
   // task that finds the list full writes the rest of its candidates to its
   // region at once (rare).
-  __shared__ uint2 cstage[kWaves][kCandList];
+  __shared__ uint2 cstage[kWaves][kCandList + 64];
   __shared__ uint32_t ttab[kWaves][kTaskTable][4];
   uint8_t *radC = rtab[wave];
   uint2 *cst = cstage[wave];
@@ -157,7 +166,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     const int r = t / Hkv;
     T.s = r % B;
     T.grp = r / B;
-    T.N = seq_len_clamped(seq_lens, T.s, n_max);
+    T.N = clamp_int(__builtin_amdgcn_readfirstlane(
+                        __builtin_amdgcn_raw_buffer_load_b32(len_rsrc, T.s * 4, 0, 0)),
+                    0, n_max);
     T.key0 = T.grp * kGroupKeys;
     if (T.key0 >= T.N) return false;
     T.unit = T.s * Hkv + T.g;
@@ -188,7 +199,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
   auto load_op = [&](const Task &T, QueryOperandRaw<KS> &op, uint32_t &L) {
     const int unit = T.unit >= 0 ? T.unit : 0;
     load_query_operand_raw<KS, G>(qop, qneg, unit, unit / Hkv, unit % Hkv, Hq, lane, op);
-    L = lthr[unit];
+    L = __builtin_amdgcn_raw_buffer_load_b32(thr_rsrc, unit * 4, 0, 0); // uniform
   };
   // Loads a page quad; `mine` is the page id of this lane's page (page
   // lane>>4 of the quad).
@@ -324,11 +335,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
       const uint32_t cslot = __builtin_amdgcn_mbcnt_hi(
           (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, nc));
       const uint32_t lslot = used + cslot;
-      // an address-space-qualified pointer keeps this an LDS store (a flat
-      // store would count against the vector-memory wait counter)
-      if (inr && ge && lslot < (uint32_t)kCandList)
-        ((__attribute__((address_space(3))) uint64_t *)cst)[lslot] =
-            ((uint64_t)(uint32_t)(64 * q + lane) << 32) | u;
+      // Every lane writes (a branch around the write would leave the
+      // compiler unsure whether it was issued, and every later LDS wait
+      // would then wait for it): lanes without a listed candidate write
+      // their spare entry.  An address-space-qualified pointer keeps this an
+      // LDS store (a flat store would count against the vector-memory wait
+      // counter).
+      const uint32_t wslot = (inr && ge && lslot < (uint32_t)kCandList)
+                                 ? lslot : (uint32_t)(kCandList + lane);
+      ((__attribute__((address_space(3))) uint64_t *)cst)[wslot] =
+          ((uint64_t)(uint32_t)(64 * q + lane) << 32) | u;
       if (used + nc + (uint32_t)__popcll(m) > (uint32_t)kCandList) { // rare
         if (inr && ge && lslot >= (uint32_t)kCandList)
           ((__attribute__((address_space(1))) uint64_t *)reg)[cslot] =
