@@ -15,6 +15,8 @@ Parity status of each function (what pins it is listed in the tests):
   radius_code              pinned (closed form, exact-rational constants)
   query_int8               pinned (textbook symmetric int8 properties,
                            exact-rational rounding bound)
+  radius_weight            pinned (mode 1: 60-digit decimal 2^(r/16) rounded,
+                           exact powers of two at r = 16m, monotone)
   score                    pinned (Python-integer brute force, identities)
   select                   pinned (brute-force sort, special cases)
   attend                   pinned (dense softmax attention special case,
@@ -57,15 +59,17 @@ def _load():
     lib.orc_encode_keys.restype = None
     lib.orc_query_int8.argtypes = [P, i32, P, i32, i32, P]
     lib.orc_query_int8.restype = None
-    lib.orc_score.argtypes = [P, i32, i32, P, i32]
+    lib.orc_radius_weight.argtypes = [i32, i32]
+    lib.orc_radius_weight.restype = ctypes.c_int32
+    lib.orc_score.argtypes = [P, i32, i32, P, ctypes.c_int32]
     lib.orc_score.restype = ctypes.c_int32
     lib.orc_select.argtypes = [P, i32, i32, i32, i32, P]
     lib.orc_select.restype = i32
     lib.orc_attend.argtypes = [P, i32, P, P, i32, P, i32, P]
     lib.orc_attend.restype = None
-    lib.orc_decode_unit.argtypes = [i32] * 6 + [P] * 6 + [i32] + [P] * 4
+    lib.orc_decode_unit.argtypes = [i32] * 7 + [P] * 6 + [i32] + [P] * 4
     lib.orc_decode_unit.restype = i32
-    lib.orc_decode_units.argtypes = [i32] * 7 + [P] * 7 + [i32, P, P, P, i32, P, P]
+    lib.orc_decode_units.argtypes = [i32] * 8 + [P] * 7 + [i32, P, P, P, i32, P, P]
     lib.orc_decode_units.restype = None
     lib.orc_num_threads.argtypes = []
     lib.orc_num_threads.restype = i32
@@ -131,15 +135,21 @@ def query_int8(q: np.ndarray, P: np.ndarray) -> np.ndarray:
     return out
 
 
-def score(q8: np.ndarray, code: np.ndarray, r8: int) -> int:
-    """S1 for one key: q8 [G][b], code uint32 [b/32], r8 -> int."""
+def radius_weight(r8: int, mode: int = 0) -> int:
+    """W1: the score weight of radius code r8 (mode 0: r8; mode 1: linear)."""
+    return int(_load().orc_radius_weight(int(r8), int(mode)))
+
+
+def score(q8: np.ndarray, code: np.ndarray, wgt: int) -> int:
+    """S1 for one key: q8 [G][b], code uint32 [b/32], radius weight -> int."""
     q8 = _c(q8, np.int8)
     code = _c(code, np.uint32)
     G, b = q8.shape
-    return int(_load().orc_score(_p(q8), G, b, _p(code), int(r8)))
+    return int(_load().orc_score(_p(q8), G, b, _p(code), int(wgt)))
 
 
-def scores(q8: np.ndarray, codes: np.ndarray, radii: np.ndarray) -> np.ndarray:
+def scores(q8: np.ndarray, codes: np.ndarray, radii: np.ndarray,
+           radius_mode: int = 0) -> np.ndarray:
     """S1 for every key: codes [N][b/32], radii [N] -> int32 [N]."""
     lib = _load()
     q8 = _c(q8, np.int8)
@@ -147,7 +157,8 @@ def scores(q8: np.ndarray, codes: np.ndarray, radii: np.ndarray) -> np.ndarray:
     G, b = q8.shape
     out = np.empty(codes.shape[0], np.int32)
     for i in range(codes.shape[0]):
-        out[i] = lib.orc_score(_p(q8), G, b, _p(codes[i]), int(radii[i]))
+        wgt = lib.orc_radius_weight(int(radii[i]), int(radius_mode))
+        out[i] = lib.orc_score(_p(q8), G, b, _p(codes[i]), wgt)
     return out
 
 
@@ -173,7 +184,8 @@ def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, sel: np.ndarray) -> np.n
     return out
 
 
-def decode_unit(q, P, codes, radii, K, V, k: int, w: int, sigma: int):
+def decode_unit(q, P, codes, radii, K, V, k: int, w: int, sigma: int,
+                radius_mode: int = 0):
     """One (sequence, KV head) decode step.
 
     q [G][d]; P [d][b]; codes [N][b/32]; radii [N]; K, V [N][d] (logical
@@ -192,14 +204,14 @@ def decode_unit(q, P, codes, radii, K, V, k: int, w: int, sigma: int):
     cap = max(1, min(N, sigma + w + k))
     sel = np.full(cap, -1, np.int32)
     out = np.zeros((G, d), np.float64)
-    n = _load().orc_decode_unit(G, d, b, k, w, sigma, _p(q), _p(P), _p(codes),
+    n = _load().orc_decode_unit(G, d, b, k, w, sigma, radius_mode, _p(q), _p(P), _p(codes),
                                 _p(radii), _p(K), _p(V), N, _p(q8), _p(S),
                                 _p(sel), _p(out))
     return {"q8": q8, "scores": S[:N].copy(), "sel": sel[:n].copy(), "out": out}
 
 
 def decode_units(q, P, codes, radii, K, V, N, k: int, w: int, sigma: int,
-                 want_scores: bool = True):
+                 want_scores: bool = True, radius_mode: int = 0):
     """Many units at once (OpenMP over units).
 
     q [U][G][d]; codes [U][Nmax][b/32]; radii [U][Nmax]; K, V [U][Nmax][d];
@@ -221,7 +233,7 @@ def decode_units(q, P, codes, radii, K, V, N, k: int, w: int, sigma: int,
     sel = np.full((U, cap), -1, np.int32)
     cnt = np.zeros(U, np.int32)
     out = np.zeros((U, G, d), np.float64)
-    _load().orc_decode_units(U, G, d, b, k, w, sigma, _p(q), _p(P), _p(codes),
+    _load().orc_decode_units(U, G, d, b, k, w, sigma, radius_mode, _p(q), _p(P), _p(codes),
                              _p(radii), _p(K), _p(V), _p(N), Nmax, _p(q8),
                              _p(S) if S is not None else None, _p(sel), cap,
                              _p(cnt), _p(out))

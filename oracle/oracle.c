@@ -164,13 +164,33 @@ ORC_EXPORT void orc_query_int8(const uint16_t *q, int G, const uint16_t *P,
 }
 
 /* ---------------------------------------------------------------------- */
+/* W1 -- radius weight of a key in the score.  [SKV §2.1]: the approximate
+ * logit multiplies the similarity of the angle codes by the key's radius
+ * as decoded from its stored code.  Two readings, chosen per call:
+ *   mode 0: the weight is the u8 log code r8 itself;
+ *   mode 1: the weight grows linearly with the radius the code stands
+ *           for.  Code r8 covers |k| in [2^((r8-64)/16), 2^((r8-63)/16));
+ *           its lower edge scaled by 2^4 and rounded to the nearest integer
+ *           is w = rne(2^(r8/16)), from 1 (r8 = 0) to 62757 (r8 = 255).
+ *           2^4 is the largest power-of-two scale that keeps
+ *           |S| <= 62757 * 127 * 256 < 2^31.
+ * 2^(r8/16) is irrational unless 16 divides r8, so it is never a tie; it
+ * lies at least 1.8e-7 (relative) from the nearest half-integer, far above
+ * the error of exp2 in double precision. */
+ORC_EXPORT int32_t orc_radius_weight(int r8, int mode) {
+  if (mode == 0) return r8;
+  return (int32_t)nearbyint(exp2((double)r8 / 16.0));
+}
+
+/* ---------------------------------------------------------------------- */
 /* S1 -- code-domain score.  [SKV §2.1]: the logit is approximated from the
  * stored radius times a cosine-like similarity computed on the angle codes,
  * with no dense key rebuilt.  [DSA, "starting from DSA"]: a light indexer
  * scores every cached key.  Reading: s_h = sum_j q8_hj * (bit_j ? +1 : -1)
- * per query head of the group, S = r8 * max_h s_h, all exact integers. */
+ * per query head of the group, S = wgt * max_h s_h, all exact integers,
+ * where wgt is the key's radius weight (W1; r8 itself in mode 0). */
 ORC_EXPORT int32_t orc_score(const int8_t *q8, int G, int b,
-                             const uint32_t *code, int r8) {
+                             const uint32_t *code, int32_t wgt) {
   int32_t best = 0;
   for (int h = 0; h < G; ++h) {
     int32_t s = 0;
@@ -181,7 +201,7 @@ ORC_EXPORT int32_t orc_score(const int8_t *q8, int G, int b,
     }
     if (h == 0 || s > best) best = s;
   }
-  return (int32_t)r8 * best;
+  return wgt * best;
 }
 
 /* ---------------------------------------------------------------------- */
@@ -262,11 +282,13 @@ ORC_EXPORT void orc_attend(const uint16_t *q, int G, const uint16_t *K,
 }
 
 /* ---------------------------------------------------------------------- */
-/* One decode step for one (sequence, KV head) unit: Q1, S1 for every
- * cached key, T1, A1.  q: [G][d] (the group's query heads); codes [N][b/32];
- * radii [N]; K, V: [N][d] in logical token order.  scores (length N) may be
- * NULL.  sel must hold min(N, sigma+w+k) entries.  Returns the count. */
+/* One decode step for one (sequence, KV head) unit: Q1, S1 (with the W1
+ * weight of radius_mode) for every cached key, T1, A1.  q: [G][d] (the
+ * group's query heads); codes [N][b/32]; radii [N]; K, V: [N][d] in logical
+ * token order.  scores (length N) may be NULL.  sel must hold
+ * min(N, sigma+w+k) entries.  Returns the count. */
 ORC_EXPORT int orc_decode_unit(int G, int d, int b, int k, int w, int sigma,
+                               int radius_mode,
                                const uint16_t *q, const uint16_t *P,
                                const uint32_t *codes, const uint8_t *radii,
                                const uint16_t *K, const uint16_t *V, int N,
@@ -276,7 +298,8 @@ ORC_EXPORT int orc_decode_unit(int G, int d, int b, int k, int w, int sigma,
                       : (int32_t *)malloc(sizeof(int32_t) * (size_t)(N > 0 ? N : 1));
   orc_query_int8(q, G, P, d, b, q8);
   for (int i = 0; i < N; ++i)
-    S[i] = orc_score(q8, G, b, codes + (size_t)i * (b / 32), radii[i]);
+    S[i] = orc_score(q8, G, b, codes + (size_t)i * (b / 32),
+                     orc_radius_weight(radii[i], radius_mode));
   int n = orc_select(S, N, k, w, sigma, sel);
   orc_attend(q, G, K, V, d, sel, n, out);
   if (!scores) free(S);
@@ -289,7 +312,7 @@ ORC_EXPORT int orc_decode_unit(int G, int d, int b, int k, int w, int sigma,
  *   N [U], q8 [U][G][b], scores [U][Nmax] (or NULL), sel [U][sel_cap],
  *   sel_cnt [U], out [U][G][d]. */
 ORC_EXPORT void orc_decode_units(int U, int G, int d, int b, int k, int w,
-                                 int sigma, const uint16_t *q,
+                                 int sigma, int radius_mode, const uint16_t *q,
                                  const uint16_t *P, const uint32_t *codes,
                                  const uint8_t *radii, const uint16_t *K,
                                  const uint16_t *V, const int32_t *N, int Nmax,
@@ -299,7 +322,7 @@ ORC_EXPORT void orc_decode_units(int U, int G, int d, int b, int k, int w,
   for (int u = 0; u < U; ++u) {
     size_t tok = (size_t)u * (size_t)Nmax;
     sel_cnt[u] = orc_decode_unit(
-        G, d, b, k, w, sigma, q + (size_t)u * G * d, P,
+        G, d, b, k, w, sigma, radius_mode, q + (size_t)u * G * d, P,
         codes + tok * (b / 32), radii + tok, K + tok * d, V + tok * d, N[u],
         q8 + (size_t)u * G * b, scores ? scores + tok : NULL,
         sel + (size_t)u * sel_cap, out + (size_t)u * G * d);

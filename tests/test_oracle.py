@@ -257,6 +257,60 @@ def test_score_takes_group_maximum():
     assert oracle.score(q8, ~ones, 2) == 2 * 5 * b      # head 0 wins
 
 
+# ---------------------------------------------------------- W1 radius weight
+def _rne_pow2_sixteenth(r: int) -> int:
+    """rne(2^(r/16)) from 60-digit decimal arithmetic (not libm)."""
+    from decimal import ROUND_HALF_EVEN, Decimal, getcontext
+    getcontext().prec = 60
+    v = Decimal(2) ** (Decimal(r) / Decimal(16))
+    return int(v.to_integral_value(rounding=ROUND_HALF_EVEN))
+
+
+def test_radius_weight_log_mode_is_the_code():
+    for r in range(256):
+        assert oracle.radius_weight(r, 0) == r
+
+
+def test_radius_weight_linear_matches_high_precision():
+    """mode 1: w = rne(2^(r8/16)), checked against decimal arithmetic."""
+    for r in range(256):
+        assert oracle.radius_weight(r, 1) == _rne_pow2_sixteenth(r), r
+
+
+def test_radius_weight_linear_closed_forms():
+    w = [oracle.radius_weight(r, 1) for r in range(256)]
+    # exact powers of two where 16 divides r8 (the code's zero point 64
+    # stands for |k| = 1, weight 2^4)
+    for m in range(16):
+        assert w[16 * m] == 2 ** m
+    assert w[64] == 16
+    # linear in the radius: one octave of radius (16 codes) doubles the
+    # weight up to the rounding of each side
+    for r in range(240):
+        assert abs(w[r + 16] - 2 * w[r]) <= 1
+    assert all(a <= b for a, b in zip(w, w[1:]))
+    # the largest score magnitude fits a signed 32-bit integer
+    assert w[255] * 127 * 256 < 2 ** 31
+    assert w[255] == 62757
+
+
+def test_score_with_linear_weight_matches_brute_force():
+    rng = np.random.default_rng(13)
+    for G, b in [(1, 64), (4, 128), (8, 256)]:
+        for _ in range(20):
+            q8 = rng.integers(-127, 128, size=(G, b)).astype(np.int8)
+            code = rng.integers(0, 2 ** 32, size=b // 32, dtype=np.uint64).astype(np.uint32)
+            r8 = int(rng.integers(0, 256))
+            wgt = _rne_pow2_sixteenth(r8)
+            assert oracle.score(q8, code, oracle.radius_weight(r8, 1)) == \
+                wgt * brute_score(q8, code, 1)
+    # extreme magnitude: all q8 = 127, all bits set, b = 256, r8 = 255
+    q8 = np.full((1, 256), 127, np.int8)
+    ones = np.full(8, 0xFFFFFFFF, np.uint32)
+    assert oracle.score(q8, ones, oracle.radius_weight(255, 1)) == 62757 * 127 * 256
+    assert oracle.score(q8, ~ones, oracle.radius_weight(255, 1)) == -62757 * 127 * 256
+
+
 # ---------------------------------------------------------------- T1 select
 @pytest.mark.parametrize("N,k,w,sigma", [
     (500, 40, 16, 4), (1000, 64, 64, 4), (90, 10, 50, 4), (60, 10, 50, 4),

@@ -61,12 +61,14 @@ def test_pipeline_dense_limit_equals_sdpa():
         break
 
 
-def test_decode_unit_is_the_composition():
+@pytest.mark.parametrize("mode", [0, 1])
+def test_decode_unit_is_the_composition(mode):
     for wl, s, g, q, P, K, V, _ in _units("small_ragged_b128"):
         codes, radii = oracle.encode_keys(K, P)
-        r = oracle.decode_unit(q, P, codes, radii, K, V, wl.top_k, wl.window, wl.sinks)
+        r = oracle.decode_unit(q, P, codes, radii, K, V, wl.top_k, wl.window, wl.sinks,
+                               radius_mode=mode)
         q8 = oracle.query_int8(q, P)
-        S = oracle.scores(q8, codes, radii)
+        S = oracle.scores(q8, codes, radii, radius_mode=mode)
         sel = oracle.select(S, wl.top_k, wl.window, wl.sinks)
         out = oracle.attend(q, K, V, sel)
         assert np.array_equal(r["q8"], q8)
@@ -77,7 +79,8 @@ def test_decode_unit_is_the_composition():
             break
 
 
-def test_decode_units_batch_equals_single_units():
+@pytest.mark.parametrize("mode", [0, 1])
+def test_decode_units_batch_equals_single_units(mode):
     units = list(_units("small_gqa_b128"))[:3]
     wl = units[0][0]
     Nmax = max(u[5].shape[0] for u in units)
@@ -94,11 +97,12 @@ def test_decode_units_batch_equals_single_units():
         n = u[5].shape[0]
         K[i, :n], V[i, :n], N[i] = u[5], u[6], n
         codes[i, :n], radii[i, :n] = oracle.encode_keys(u[5], P)
-    r = oracle.decode_units(q, P, codes, radii, K, V, N, wl.top_k, wl.window, wl.sinks)
+    r = oracle.decode_units(q, P, codes, radii, K, V, N, wl.top_k, wl.window, wl.sinks,
+                            radius_mode=mode)
     for i, u in enumerate(units):
         n = N[i]
         one = oracle.decode_unit(q[i], P, codes[i, :n], radii[i, :n], K[i, :n], V[i, :n],
-                                 wl.top_k, wl.window, wl.sinks)
+                                 wl.top_k, wl.window, wl.sinks, radius_mode=mode)
         assert np.array_equal(r["sel"][i], one["sel"])
         assert np.array_equal(r["out"][i], one["out"])
         assert np.array_equal(r["scores"][i, :n], one["scores"])
