@@ -32,7 +32,9 @@ EXPORTED_SYMBOLS = ("dkv_encode", "dkv_decode_workspace_size", "dkv_decode",
                     "dkv_decode_debug", "dkv_decode_profiled", "dkv_decode_append",
                     "dkv_decode_num_stages", "dkv_decode_stage_name",
                     "dkv_status_string", "dkv_abi_version")
-ABI_VERSION = 2
+ABI_VERSION = 3
+RADIUS_LOG = 0
+RADIUS_LINEAR = 1
 
 STATUS = {0: "DKV_OK", 1: "DKV_ERR_INVALID_ARG", 2: "DKV_ERR_UNSUPPORTED",
           3: "DKV_ERR_WORKSPACE", 4: "DKV_ERR_LAUNCH"}
@@ -47,7 +49,7 @@ class DkvError(RuntimeError):
 class _CConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "head_dim", "num_q_heads", "num_kv_heads", "code_bits", "page_size",
-        "top_k", "window", "sinks")]
+        "top_k", "window", "sinks", "radius_weight")]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -60,11 +62,14 @@ class Config:
     sinks: int
     head_dim: int = 128
     page_size: int = 16
+    # score weight of the radius code: RADIUS_LOG (w = r8) or RADIUS_LINEAR
+    # (w = rne(2^(r8/16)))
+    radius_weight: int = 0
 
     def _c(self) -> _CConfig:
         return _CConfig(self.head_dim, self.num_q_heads, self.num_kv_heads,
                         self.code_bits, self.page_size, self.top_k, self.window,
-                        self.sinks)
+                        self.sinks, self.radius_weight)
 
     @property
     def group(self) -> int:

@@ -35,7 +35,9 @@ bool valid_config(const dkv_config *cfg, dkv_status *why) {
       !(cfg->code_bits == 64 || cfg->code_bits == 128 ||
         cfg->code_bits == 256) ||
       !(G == 1 || G == 2 || G == 4 || G == 8) || sel > DKV_MAX_SELECT ||
-      cfg->num_kv_heads > 4096) {
+      cfg->num_kv_heads > 4096 ||
+      !(cfg->radius_weight == DKV_RADIUS_LOG ||
+        cfg->radius_weight == DKV_RADIUS_LINEAR)) {
     *why = DKV_ERR_UNSUPPORTED;
     return false;
   }
@@ -65,6 +67,7 @@ bool make_dims(const dkv_config *cfg, int32_t batch, int32_t max_seq_len,
   d->k = cfg->top_k;
   d->w = cfg->window;
   d->sigma = cfg->sinks;
+  d->lin = cfg->radius_weight == DKV_RADIUS_LINEAR;
   d->cap = d->k + d->w + d->sigma;
   d->max_seq_len = max_seq_len;
   const int64_t by_blocks = (int64_t)kPage * max_blocks;

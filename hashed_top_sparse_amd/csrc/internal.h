@@ -22,6 +22,7 @@ struct DecodeDims {
   int B, Hq, Hkv, G, b, W;   // W = b/32 code words per key
   int KS;                    // 128-bit MFMA K-steps per key: max(1, b/128)
   int k, w, sigma, cap;      // cap = k + w + sigma (selection list length)
+  bool lin;                  // linear radius weight (DKV_RADIUS_LINEAR)
   int max_seq_len;           // caller's bound (workspace stride)
   int n_max;                 // min(max_seq_len, 16*max_blocks)
   int max_blocks;

@@ -59,7 +59,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
     int32_t *__restrict__ user_cnt, const uint32_t *__restrict__ codes,
     const uint8_t *__restrict__ radii, uint32_t code_bytes,
     uint32_t radius_bytes, int W, const uint32_t *__restrict__ qop,
-    const float *__restrict__ qneg) {
+    const float *__restrict__ qneg, bool lin) {
   __shared__ uint2 st[kStage];
   __shared__ uint32_t gpre[kMaxGroupsLds + 1];
   __shared__ SelectShared<kThreads> sel;
@@ -288,10 +288,10 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-              const int S = score_page<KS, G>(op, cw[u], r8[u], ok[u]);
+              const int S = score_page<KS, G>(op, cw[u], r8[u], ok[u], lin);
               const int pos = (p0 + u) * kPage + lane;
               if (lane < kPage && pos >= c0 && pos < c1)
-                fn((uint32_t)(S + (int)kScoreBias), pos);
+                fn(biased_score(S), pos);
             }
           }
         };
@@ -345,7 +345,7 @@ hipError_t launch_merge(const DecodeDims &d, const uint2 *cand,
                        d.max_blocks, d.num_blocks, d.Hkv, d.k, d.w, d.sigma,   \
                        d.cap, bitmap, d.bm_words, rows, cnt, user_sel,         \
                        user_cnt, codes, radii, code_bytes, radius_bytes, d.W,  \
-                       qop, qneg);                                             \
+                       qop, qneg, d.lin);                                      \
     return hipGetLastError();                                                  \
   }
   DKV_MERGE_CASE(1, 1)

@@ -74,7 +74,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     const int32_t *__restrict__ seq_lens, int n_max, int8_t *__restrict__ q8,
     uint32_t *__restrict__ qop, float *__restrict__ qneg,
     uint32_t *__restrict__ lthr, int Hq,
-    int Hkv, int b, int W, int k, int w, int sigma) {
+    int Hkv, int b, int W, int k, int w, int sigma, bool lin) {
   const int unit = blockIdx.x;
   const int s = unit / Hkv;
   const int g = unit % Hkv;
@@ -315,7 +315,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
       if (lane < kPage && t < nsp) {
         const int pos = (pc0 + t * SP) * kPage + lane;
         const bool valid = pos >= sigma && pos < N - w;
-        sSample[t * kPage + lane] = valid ? (uint32_t)(S + (int)kScoreBias) : 0u;
+        sSample[t * kPage + lane] = valid ? biased_score(S) : 0u;
         nvalid += valid;
       }
     };
@@ -344,7 +344,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
         const int pos = (pc0 + t * SP) * kPage + (lane & 15);
         const bool valid = ok && pos >= sigma && pos < N - w;
         sSample[t * kPage + (lane & 15)] =
-            valid ? (uint32_t)(__mul24((int)r8, mx) + (int)kScoreBias) : 0u;
+            valid ? biased_score(__mul24(radius_weight(r8, lin), mx)) : 0u;
         nvalid += valid;
       }
     }
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u)
-        keep(wave + kWv * (i0 + u), score_page<KS, G>(op, cw[u], r8[u], ok[u]));
+        keep(wave + kWv * (i0 + u), score_page<KS, G>(op, cw[u], r8[u], ok[u], lin));
     }
     for (int off = 32; off > 0; off >>= 1) nvalid += __shfl_xor(nvalid, off);
     if (lane == 0) sCount[wave] = nvalid;
@@ -420,7 +420,7 @@ hipError_t launch_prep(const DecodeDims &d, const uint16_t *q,
                        k_pool, codes_w, radii_w,                               \
                        d.num_blocks, code_bytes, radius_bytes, block_table,    \
                        d.max_blocks, seq_lens, d.n_max, q8, qop, qneg, lthr,   \
-                       d.Hq, d.Hkv, d.b, d.W, d.k, d.w, d.sigma);              \
+                       d.Hq, d.Hkv, d.b, d.W, d.k, d.w, d.sigma, d.lin);       \
     return hipGetLastError();                                                  \
   }
   DKV_PREP_CASE(1, 1)

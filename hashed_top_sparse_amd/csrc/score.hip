@@ -88,8 +88,9 @@ __device__ __forceinline__ void transpose_rows(uint32_t (&x)[4]) {
 }
 
 // W: code words per key (2, 4 or 8); KS: 128-bit matrix-core K-steps;
-// DBG: also write every score to scores_out (inspection builds only).
-template <int W, int G, bool DBG, int KS = (W > 4 ? W / 4 : 1)>
+// DBG: also write every score to scores_out (inspection builds only); LIN:
+// linear radius weight (looked up in a per-workgroup LDS table).
+template <int W, int G, bool DBG, bool LIN, int KS = (W > 4 ? W / 4 : 1)>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void filter_kernel(
     const uint32_t *__restrict__ codes, const uint8_t *__restrict__ radii,
     int64_t num_blocks, uint32_t code_bytes, uint32_t radius_bytes,
@@ -103,6 +104,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int stride = gridDim.x * kWaves;
+  // linear radius weights of the 256 codes (before any wave can leave)
+  __shared__ uint16_t wlut[LIN ? 256 : 1];
+  if constexpr (LIN) {
+    for (int i = threadIdx.x; i < 256; i += kThreads)
+      wlut[i] = (uint16_t)radius_weight_linear((uint32_t)i);
+    __syncthreads();
+  }
   const int Hq = Hkv * G;
   const __amdgpu_buffer_rsrc_t code_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint32_t *>(codes), 0, code_bytes, kBufferWord3);
@@ -300,6 +308,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
       // radius byte of key lane&15 of page 4q + lane>>4, and the page id
       // of the refill below, both read from LDS one quad ahead
       const uint32_t r8 = r8c;
+      // its weight (LIN: an LDS read issued before the next quad's reads)
+      const int wgt = LIN ? (int)wlut[r8] : (int)r8;
       // ---- refill the slot: the quad kDepth further on (C's, or T1's
       // first ones)
       load_quad(refc, buf[slot]);
@@ -318,7 +328,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
         for (int j = 0; j < 4; ++j) cw[j][ks] = x[ks][j];
       }
       const int mx = score_quad_max_seq<KS, G>(opC, cw);
-      const uint32_t u = (uint32_t)(__mul24((int)r8, mx) + (int)kScoreBias);
+      const uint32_t u = biased_score(__mul24(wgt, mx));
       const int qpos = C.key0 + 64 * q; // first position of the quad
       const int pos = qpos + lane;
       if constexpr (DBG) {
@@ -409,11 +419,11 @@ hipError_t launch_score(const DecodeDims &d, const uint32_t *codes,
   if (ntasks > 0x7FFFFFFF - 65536) return hipErrorInvalidValue;
   const uint32_t code_bytes = (uint32_t)((uint64_t)d.num_blocks * d.Hkv * d.W * kPage * 4);
   const uint32_t radius_bytes = (uint32_t)((uint64_t)d.num_blocks * d.Hkv * kPage);
-#define DKV_SCORE_LAUNCH(WV, GV, DV)                                           \
+#define DKV_SCORE_LAUNCH(WV, GV, DV, LV)                                       \
   {                                                                            \
     const int64_t nwg = std::min<int64_t>((ntasks + kWaves - 1) / kWaves,       \
                                           (int64_t)kWgPerCu * device_cu_count()); \
-    hipLaunchKernelGGL((filter_kernel<WV, GV, DV>), dim3((unsigned)nwg),       \
+    hipLaunchKernelGGL((filter_kernel<WV, GV, DV, LV>), dim3((unsigned)nwg),   \
                        dim3(kThreads), 0, stream, codes, radii, d.num_blocks,  \
                        code_bytes, radius_bytes, block_table, d.max_blocks,    \
                        seq_lens, d.n_max, qop, qneg, lthr, d.B, d.Hkv,         \
@@ -423,8 +433,12 @@ hipError_t launch_score(const DecodeDims &d, const uint32_t *codes,
   }
 #define DKV_SCORE_CASE(WV, GV)                                                 \
   if (d.W == WV && d.G == GV) {                                                \
-    if (scores_out != nullptr) DKV_SCORE_LAUNCH(WV, GV, true)                  \
-    DKV_SCORE_LAUNCH(WV, GV, false)                                            \
+    if (d.lin) {                                                               \
+      if (scores_out != nullptr) DKV_SCORE_LAUNCH(WV, GV, true, true)          \
+      DKV_SCORE_LAUNCH(WV, GV, false, true)                                    \
+    }                                                                          \
+    if (scores_out != nullptr) DKV_SCORE_LAUNCH(WV, GV, true, false)           \
+    DKV_SCORE_LAUNCH(WV, GV, false, false)                                     \
   }
   DKV_SCORE_CASE(2, 1)
   DKV_SCORE_CASE(2, 2)

@@ -4,7 +4,9 @@
 // [SPHERICAL KV, §2.1]: the logit is approximated straight from the stored
 // radius and the packed angle code, without rebuilding the dense key.
 //   s_h = sum_j q8_hj * (bit_j ? +1 : -1)   for the G heads of a KV group
-//   S   = r8 * max_h s_h                     (exact integer, |S| < 2^23)
+//   S   = w * max_h s_h                      (exact integer, |S| < 2^31)
+// with the key's radius weight w: its code r8 (log weight), or
+// rne(2^(r8/16)), linear in the radius the code stands for.
 //
 // The per-page work is one 16x16x128 fp8 x fp4 matrix-core op per 128 code
 // bits (operand layout: see qprep.hip):
@@ -16,7 +18,8 @@
 //     lo), and the accumulator starts at -Q in the low rows, so row 2h gives
 //     2*D_hi and row 2h+1 gives 2*D_lo - Q exactly (D = sum_j q8_j*bit_j);
 //   - s_h = 16*row(2h) + row(2h+1); the max over the group's heads uses the
-//     gfx950 16/32-lane row swaps; S = r8 * max in fp32 (exact below 2^24).
+//     gfx950 16/32-lane row swaps; S = w * max with a 24-bit integer multiply
+//     (|w| < 2^16, |max| < 2^15).
 // After scoring, lanes 0..15 hold S of the keys in slots 0..15.
 #pragma once
 
@@ -27,7 +30,24 @@ namespace dkv {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr uint32_t kScoreBias = 1u << 23; // u = S + 2^23 is positive
+// u = S + 2^31 (mod 2^32) orders like S; u = 0 is below every score
+constexpr uint32_t kScoreBias = 1u << 31;
+
+__device__ __forceinline__ uint32_t biased_score(int S) {
+  return (uint32_t)S + kScoreBias; // unsigned: wraps by definition
+}
+
+// Linear radius weight rne(2^(r8/16)) of code r8 (0..255).  2^(r8/16) lies
+// at least 1.8e-7 (relative) from the nearest half-integer, so the double
+// exp2 (error below 1e-15) rounds to the right integer.
+__device__ __forceinline__ int radius_weight_linear(uint32_t r8) {
+  return (int)__builtin_rint(exp2((double)r8 * 0.0625));
+}
+
+// Radius weight of code r8: the code itself, or linear when lin.
+__device__ __forceinline__ int radius_weight(uint32_t r8, bool lin) {
+  return lin ? radius_weight_linear(r8) : (int)r8;
+}
 constexpr uint32_t kBufferWord3 = 0x00020000u; // raw buffer, gfx9 family
 
 template <int KS>
@@ -152,11 +172,12 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
 }
 
 // S of the page whose code words (this lane's KS dwords) and radius byte
-// are given; valid in lanes 0..15 (slot = lane).  Every lane must call it.
+// are given; valid in lanes 0..15 (slot = lane).  lin selects the linear
+// radius weight.  Every lane must call it.
 template <int KS, int G>
 __device__ __forceinline__ int score_page(const QueryOperand<KS> &op,
                                           uint32_t (&cw_in)[KS], uint32_t r8,
-                                          bool ok) {
+                                          bool ok, bool lin) {
   // The loaded words are first read here: without this the compiler may
   // move their first use (the radius conversion) up to the loads and wait
   // for each load as it is issued.
@@ -176,7 +197,7 @@ __device__ __forceinline__ int score_page(const QueryOperand<KS> &op,
   if (G >= 2) m = fmaxf(m, 16.f * acc[2] + acc[3]);
   if (G >= 4) m = max_rows16(m);
   if (G >= 8) m = max_rows32(m);
-  int S = ok ? (int)((float)r8 * m) : 0;
+  int S = ok ? __mul24(radius_weight(r8, lin), (int)m) : 0;
   // computed in every lane so the radius load is not sunk into a store
   // branch (where it would wait for every outstanding load)
   asm volatile("" : "+v"(S));

@@ -29,7 +29,12 @@
  *               (|k|^2 summed in double precision in index order).
  *   query code  q8 = round_half_even(p*127/M), p = q.P in double precision,
  *               M = max |p| over the KV group's G query heads and b columns.
- *   score       S = r8 * max_{h in group} sum_j q8_hj * (bit_j ? +1 : -1).
+ *   score       S = w(r8) * max_{h in group} sum_j q8_hj * (bit_j ? +1 : -1)
+ *               with the radius weight w chosen per config: the code itself
+ *               (w = r8), or linear in the radius the code stands for
+ *               (w = round_half_even(2^(r8/16)), 1..62757; [SKV §2.1]: the
+ *               approximate logit scales the code similarity by the
+ *               decoded radius).  |S| < 2^31 in both.
  *   selection   per (sequence, KV head): sinks [0, sigma), window
  *               [N-w, N), plus the top k of [sigma, N-w) by (S descending,
  *               position ascending).
@@ -100,7 +105,14 @@ typedef struct {
   int32_t top_k;        /* k >= 0                                         */
   int32_t window;       /* w >= 0: most recent tokens always kept         */
   int32_t sinks;        /* sigma >= 0: first tokens always kept           */
+  int32_t radius_weight; /* score weight of a key's radius code r8:
+                            DKV_RADIUS_LOG (0): w = r8;
+                            DKV_RADIUS_LINEAR (1): w = rne(2^(r8/16));
+                            other values: DKV_ERR_UNSUPPORTED            */
 } dkv_config;
+
+#define DKV_RADIUS_LOG 0
+#define DKV_RADIUS_LINEAR 1
 
 /* Limits checked by every entry point (DKV_ERR_UNSUPPORTED beyond them). */
 #define DKV_MAX_SEQ_LEN (1 << 24)
@@ -258,7 +270,7 @@ const char *dkv_decode_stage_name(int32_t stage);
 const char *dkv_status_string(dkv_status status);
 
 /* ABI version of this header (bumped on any signature or layout change). */
-#define DKV_ABI_VERSION 2
+#define DKV_ABI_VERSION 3
 int32_t dkv_abi_version(void);
 
 #ifdef __cplusplus

@@ -100,8 +100,9 @@ def gpu_decode_append(cfg: dkv.Config, inp: dict):
 
 
 def check_unit(cfg: dkv.Config, inp: dict, gpu: dict, codes, radii, s: int, g: int,
-               check_codes: bool = True, needles=None) -> dict:
-    """Compares one (sequence s, KV head g) unit with the oracle."""
+               check_codes: bool = True, needles=None, code_pool=None) -> dict:
+    """Compares one (sequence s, KV head g) unit with the oracle.  code_pool:
+    the key pool the codes were built from, when it is not the attended one."""
     bt = inp["block_table"].cpu().numpy()
     N = int(inp["seq_lens"][s].item())
     G = cfg.group
@@ -109,7 +110,8 @@ def check_unit(cfg: dkv.Config, inp: dict, gpu: dict, codes, radii, s: int, g: i
     q = tensor_bits(inp["q"][s, g * G:(g + 1) * G])
     K = logical_rows(inp["k_pool"], bt, s, N, g)
     V = logical_rows(inp["v_pool"], bt, s, N, g)
-    o_codes, o_radii = oracle.encode_keys(K, P)
+    Kc = K if code_pool is None else logical_rows(code_pool, bt, s, N, g)
+    o_codes, o_radii = oracle.encode_keys(Kc, P)
     if check_codes:
         g_codes = logical_codes(codes, bt, s, N, g)
         g_radii = logical_radii(radii, bt, s, N, g)
@@ -117,7 +119,7 @@ def check_unit(cfg: dkv.Config, inp: dict, gpu: dict, codes, radii, s: int, g: i
         assert len(bad) == 0, f"codes differ at {len(bad)} keys, first {bad[:5]}"
         assert np.array_equal(g_radii, o_radii), "radii differ"
     r = oracle.decode_unit(q, P, o_codes, o_radii, K, V, cfg.top_k, cfg.window,
-                           cfg.sinks)
+                           cfg.sinks, radius_mode=cfg.radius_weight)
     if "q8" in gpu:
         g_q8 = gpu["q8"][s, g * G:(g + 1) * G].cpu().numpy()
         assert np.array_equal(g_q8, r["q8"]), "query codes differ"

@@ -38,7 +38,7 @@ def test_status_strings():
 
 def _cfg(**over):
     kw = dict(head_dim=128, num_q_heads=32, num_kv_heads=8, code_bits=128,
-              page_size=16, top_k=64, window=16, sinks=4)
+              page_size=16, top_k=64, window=16, sinks=4, radius_weight=0)
     kw.update(over)
     return dkv._CConfig(*[kw[f] for f, _ in dkv._CConfig._fields_])
 
@@ -57,7 +57,7 @@ def _decode(cfg, ws_bytes=1 << 30, workspace=FAKE, q=FAKE, batch=2, max_seq_len=
     (dict(page_size=32), 2), (dict(num_q_heads=24, num_kv_heads=8), 2),  # G = 3
     (dict(num_q_heads=30, num_kv_heads=8), 1), (dict(top_k=-1), 1),
     (dict(window=-5), 1), (dict(sinks=-1), 1), (dict(num_kv_heads=0), 1),
-    (dict(top_k=1 << 20), 2),
+    (dict(top_k=1 << 20), 2), (dict(radius_weight=2), 2), (dict(radius_weight=-1), 2),
 ])
 def test_decode_rejects_bad_config(over, status):
     assert _decode(_cfg(**over)) == status

@@ -293,3 +293,70 @@ def test_threshold_fallback_stays_exact(factor):
     gpu = gpu_decode(cfg, inp, codes, radii, debug=True)
     for g in range(wl.num_kv_heads):
         check_unit(cfg, inp, gpu, codes, radii, 0, g)
+
+
+# ---------------------------------------------------- linear radius weight
+LIN = dict(radius_weight=dkv.RADIUS_LINEAR)
+
+
+@pytest.mark.parametrize("name", sorted(workloads.SMALL))
+def test_linear_radius_weight_small_every_unit(name):
+    """Scores w(r8) * max_h s_h with w = rne(2^(r8/16)): bit-exact scores,
+    selection and counts, outputs within tolerance, on every unit."""
+    stats = _run(workloads.get(name), **LIN)
+    rec = [st["recall"] for st in stats if st["recall"] is not None]
+    print(name, "needle recall (linear weight)", np.mean(rec) if rec else None)
+
+
+@pytest.mark.parametrize("name,units", [
+    ("gqa32x8_bs16_n128k_b128", [(0, 0), (15, 7)]),
+    ("gqa32x8_bs4_n256k_b256_lognormal", [(1, 2)]),
+])
+def test_full_size_linear_radius_weight(name, units):
+    _run(workloads.get(name), units, **LIN)
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("factor", [4.0, 0.125])
+def test_linear_weight_threshold_fallback_stays_exact(factor):
+    """The adversarial sample of the fallback test under the linear weight
+    (the merge's rescan scores with the same weight)."""
+    import dataclasses
+    base = workloads.get("small_gqa_b128")
+    wl = dataclasses.replace(base, name="adversarial", batch=1, seq_len=40000,
+                             needles=0)
+    print(f"[case] adversarial linear factor={factor}", flush=True)
+    cfg = config_of(wl, **LIN)
+    inp = workloads.make_inputs(wl, DEV)
+    keff = min(wl.top_k, wl.seq_len - wl.window - wl.sinks)
+    sp = _sample_stride(keff)
+    _scale_pages(inp, wl, lambda p: p % sp == 0, factor)
+    codes, radii = gpu_encode_all(cfg, inp)
+    gpu = gpu_decode(cfg, inp, codes, radii, debug=True)
+    for g in range(wl.num_kv_heads):
+        check_unit(cfg, inp, gpu, codes, radii, 0, g)
+
+
+def test_linear_weight_largest_radii():
+    """Codes built from keys scaled so most radius codes clamp at 255
+    (weight 62757, the largest) at b = 256: scores far beyond the exact
+    range of a float product stay exact and ordered.  (Attention runs over
+    the unscaled pool, so the outputs keep ordinary logits.)"""
+    import dataclasses
+    wl = dataclasses.replace(workloads.get("small_gqa_b256_lognormal"), name="big_radii",
+                             needles=0)
+    print("[case] big radii linear", flush=True)
+    cfg = config_of(wl, **LIN)
+    inp = workloads.make_inputs(wl, DEV)
+    k_big = (inp["k_pool"].float() * 512.0).to(torch.bfloat16)
+    codes, radii = gpu_encode_all(cfg, dict(inp, k_pool=k_big))
+    assert (radii == 255).float().mean().item() > 0.5
+    gpu = gpu_decode(cfg, inp, codes, radii, debug=True)
+    big = 0
+    for s in range(wl.batch):
+        for g in range(wl.num_kv_heads):
+            check_unit(cfg, inp, gpu, codes, radii, s, g, code_pool=k_big)
+            n = int(inp["seq_lens"][s].item())
+            big = max(big, int(gpu["scores"][s, g, :n].abs().max().item()))
+    # far past 2^24, where a float product would no longer be exact
+    assert big > 2 ** 26, big
