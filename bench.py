@@ -112,7 +112,7 @@ def counter_traffic(kernel_src_digest: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(wl, inp, units: int, seconds: float) -> dict:
+def cpu_baseline(wl, inp, units: int, seconds: float, radius_mode: int = 0) -> dict:
     """The CPU oracle (as it stands) on a bounded sample of the workload."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import numpy as np
@@ -146,7 +146,7 @@ def cpu_baseline(wl, inp, units: int, seconds: float) -> dict:
     t0 = time.perf_counter()
     while True:
         oracle.decode_units(q, P, codes, radii, K, V, N, wl.top_k, wl.window,
-                            wl.sinks, want_scores=False)
+                            wl.sinks, want_scores=False, radius_mode=radius_mode)
         reps += 1
         dt = time.perf_counter() - t0
         if dt >= seconds or reps >= 100000:
@@ -171,6 +171,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--cold-steps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--radius-weight", choices=("log", "linear"), default="log",
+                    help="score weight of the radius code: the code r8 itself "
+                         "(log) or rne(2^(r8/16)) (linear)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (for "
                          "scaling PMC byte counters)")
@@ -191,7 +194,9 @@ def main():
     wl = workloads.get(args.workload)
     cfg = dkv.Config(num_q_heads=wl.num_q_heads, num_kv_heads=wl.num_kv_heads,
                      code_bits=wl.code_bits, top_k=wl.top_k, window=wl.window,
-                     sinks=wl.sinks)
+                     sinks=wl.sinks,
+                     radius_weight=(dkv.RADIUS_LINEAR if args.radius_weight == "linear"
+                                    else dkv.RADIUS_LOG))
     print(f"[bench] drawing {wl.name}", file=sys.stderr, flush=True)
     inp = workloads.make_inputs(wl, "cuda")
     B, Hkv = wl.batch, wl.num_kv_heads
@@ -317,7 +322,8 @@ def main():
         "config": {"workload": wl.name, "batch": B, "seq_len": max_len,
                    "q_heads": wl.num_q_heads, "kv_heads": Hkv, "head_dim": wl.head_dim,
                    "code_bits": wl.code_bits, "top_k": wl.top_k, "window": wl.window,
-                   "sinks": wl.sinks, "page": PAGE, "parallelism": "single GPU"},
+                   "sinks": wl.sinks, "page": PAGE, "radius_weight": args.radius_weight,
+                   "parallelism": "single GPU"},
         "latency_us": ms_per_step * 1e3,
         "gpu_step_us": gpu_ms * 1e3,
         "step_algorithmic_bytes": ab["total"],
@@ -330,7 +336,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_units, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_units, args.cpu_seconds,
+                                              cfg.radius_weight)
     print(json.dumps(result), flush=True)
 
 
