@@ -299,7 +299,9 @@ def main():
     score_s = stage_ms["score"] * 1e-3
     score_src = [os.path.join(ROOT, "hashed_top_sparse_amd", "csrc", f)
                  for f in ("score.hip", "score_common.h", "internal.h")]
-    traffic = counter_traffic(source_digest(score_src), wl.name)
+    # the counters were taken for the log radius weight's kernel
+    traffic = (counter_traffic(source_digest(score_src), wl.name)
+               if args.radius_weight == "log" else None)
     roofline = {"bound": "hbm", "kernel": "score",
                 "achieved": ab["score"] / score_s / 1e9, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": ab["score"] / score_s / 1e9 / HBM_PEAK_GBS,
