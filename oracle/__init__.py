@@ -19,6 +19,8 @@ Parity status of each function (what pins it is listed in the tests):
                            exact powers of two at r = 16m, monotone)
   score                    pinned (Python-integer brute force, identities)
   select                   pinned (brute-force sort, special cases)
+  select_pages             pinned (brute-force page sort, equals select when
+                           scores are constant on aligned pages, limits)
   attend                   pinned (dense softmax attention special case,
                            single-key and identical-key closed forms)
   decode_unit(s)           composition of the above; whole-pipeline values
@@ -65,11 +67,13 @@ def _load():
     lib.orc_score.restype = ctypes.c_int32
     lib.orc_select.argtypes = [P, i32, i32, i32, i32, P]
     lib.orc_select.restype = i32
+    lib.orc_select_pages.argtypes = [P, i32, i32, i32, i32, P]
+    lib.orc_select_pages.restype = i32
     lib.orc_attend.argtypes = [P, i32, P, P, i32, P, i32, P]
     lib.orc_attend.restype = None
-    lib.orc_decode_unit.argtypes = [i32] * 7 + [P] * 6 + [i32] + [P] * 4
+    lib.orc_decode_unit.argtypes = [i32] * 8 + [P] * 6 + [i32] + [P] * 4
     lib.orc_decode_unit.restype = i32
-    lib.orc_decode_units.argtypes = [i32] * 8 + [P] * 7 + [i32, P, P, P, i32, P, P]
+    lib.orc_decode_units.argtypes = [i32] * 9 + [P] * 7 + [i32, P, P, P, i32, P, P]
     lib.orc_decode_units.restype = None
     lib.orc_num_threads.argtypes = []
     lib.orc_num_threads.restype = i32
@@ -172,6 +176,16 @@ def select(S: np.ndarray, k: int, w: int, sigma: int) -> np.ndarray:
     return sel[:n].copy()
 
 
+def select_pages(S: np.ndarray, k: int, w: int, sigma: int) -> np.ndarray:
+    """T2 over scores S [N] -> int32 positions (sinks, window, top pages)."""
+    S = _c(S, np.int32)
+    N = S.shape[0]
+    cap = max(1, min(N, sigma + w + k))
+    sel = np.full(cap, -1, np.int32)
+    n = _load().orc_select_pages(_p(S), N, k, w, sigma, _p(sel))
+    return sel[:n].copy()
+
+
 def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, sel: np.ndarray) -> np.ndarray:
     """A1: q [G][d], K/V [N][d] (bf16 bits), sel positions -> fp64 [G][d]."""
     q = _c(q, np.uint16)
@@ -185,7 +199,7 @@ def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, sel: np.ndarray) -> np.n
 
 
 def decode_unit(q, P, codes, radii, K, V, k: int, w: int, sigma: int,
-                radius_mode: int = 0):
+                radius_mode: int = 0, pages: bool = False):
     """One (sequence, KV head) decode step.
 
     q [G][d]; P [d][b]; codes [N][b/32]; radii [N]; K, V [N][d] (logical
@@ -204,14 +218,15 @@ def decode_unit(q, P, codes, radii, K, V, k: int, w: int, sigma: int,
     cap = max(1, min(N, sigma + w + k))
     sel = np.full(cap, -1, np.int32)
     out = np.zeros((G, d), np.float64)
-    n = _load().orc_decode_unit(G, d, b, k, w, sigma, radius_mode, _p(q), _p(P), _p(codes),
+    n = _load().orc_decode_unit(G, d, b, k, w, sigma, radius_mode, int(pages), _p(q), _p(P),
+                                _p(codes),
                                 _p(radii), _p(K), _p(V), N, _p(q8), _p(S),
                                 _p(sel), _p(out))
     return {"q8": q8, "scores": S[:N].copy(), "sel": sel[:n].copy(), "out": out}
 
 
 def decode_units(q, P, codes, radii, K, V, N, k: int, w: int, sigma: int,
-                 want_scores: bool = True, radius_mode: int = 0):
+                 want_scores: bool = True, radius_mode: int = 0, pages: bool = False):
     """Many units at once (OpenMP over units).
 
     q [U][G][d]; codes [U][Nmax][b/32]; radii [U][Nmax]; K, V [U][Nmax][d];
@@ -233,7 +248,8 @@ def decode_units(q, P, codes, radii, K, V, N, k: int, w: int, sigma: int,
     sel = np.full((U, cap), -1, np.int32)
     cnt = np.zeros(U, np.int32)
     out = np.zeros((U, G, d), np.float64)
-    _load().orc_decode_units(U, G, d, b, k, w, sigma, radius_mode, _p(q), _p(P), _p(codes),
+    _load().orc_decode_units(U, G, d, b, k, w, sigma, radius_mode, int(pages), _p(q), _p(P),
+                             _p(codes),
                              _p(radii), _p(K), _p(V), _p(N), Nmax, _p(q8),
                              _p(S) if S is not None else None, _p(sel), cap,
                              _p(cnt), _p(out))

@@ -247,6 +247,53 @@ ORC_EXPORT int orc_select(const int32_t *S, int N, int k, int w, int sigma,
 }
 
 /* ---------------------------------------------------------------------- */
+/* T2 -- page-granular selection.  [DSA, CSA section]: several history
+ * tokens are first condensed into one entry and the top-k is taken over
+ * those entries, not over single tokens; [SKV §2.2]: states grouped into
+ * pages are read as one stream instead of scattered rows.  Reading: the
+ * entry is the 16-token page.  A page's score is the largest key score S_i
+ * over its keys inside the candidate range C = [sigma, N-w); the best
+ * min(k/16, pages meeting C) pages by (page score descending, page index
+ * ascending) are selected, and every key of theirs inside C joins the sinks
+ * and the window (so the list never exceeds sigma + w + k).  Returns the
+ * count; sel gets sinks, window, then the selected pages' keys, page by
+ * page in rank order, ascending inside a page. */
+ORC_EXPORT int orc_select_pages(const int32_t *S, int N, int k, int w,
+                                int sigma, int32_t *sel) {
+  const int page = 16;
+  int n = 0;
+  int ns = sigma < N ? sigma : N;
+  for (int i = 0; i < ns; ++i) sel[n++] = i;
+  int ws = (N - w > ns) ? N - w : ns;
+  for (int i = ws; i < N; ++i) sel[n++] = i;
+  int c0 = sigma, c1 = N - w;
+  if (c1 <= c0) return n;
+  int p0 = c0 / page, p1 = (c1 + page - 1) / page; /* pages meeting C */
+  int np = p1 - p0;
+  orc_cand *c = (orc_cand *)malloc(sizeof(orc_cand) * (size_t)np);
+  for (int p = p0; p < p1; ++p) {
+    int lo = p * page > c0 ? p * page : c0;
+    int hi = (p + 1) * page < c1 ? (p + 1) * page : c1;
+    int32_t best = S[lo];
+    for (int i = lo + 1; i < hi; ++i)
+      if (S[i] > best) best = S[i];
+    c[p - p0].score = best;
+    c[p - p0].pos = p;
+  }
+  qsort(c, (size_t)np, sizeof(orc_cand), orc_cand_cmp); /* pos = page */
+  int kp = k / page;
+  int keff = kp < np ? kp : np;
+  for (int r = 0; r < keff; ++r) {
+    int p = c[r].pos;
+    int lo = p * page > c0 ? p * page : c0;
+    int hi = (p + 1) * page < c1 ? (p + 1) * page : c1;
+    for (int i = lo; i < hi; ++i) sel[n++] = i;
+  }
+  free(c);
+  return n;
+}
+
+/* ---------------------------------------------------------------------- */
 /* A1 -- exact attention over the selected keys.  [DYS, item 1]:
  * softmax(QK^T / sqrt(d)); [DSA]: the real attention runs only over the
  * selected history.  In double precision: l_t = (q.k_t)/sqrt(d),
@@ -283,12 +330,13 @@ ORC_EXPORT void orc_attend(const uint16_t *q, int G, const uint16_t *K,
 
 /* ---------------------------------------------------------------------- */
 /* One decode step for one (sequence, KV head) unit: Q1, S1 (with the W1
- * weight of radius_mode) for every cached key, T1, A1.  q: [G][d] (the
+ * weight of radius_mode) for every cached key, T1 (or T2 when select_pages
+ * is non-zero), A1.  q: [G][d] (the
  * group's query heads); codes [N][b/32]; radii [N]; K, V: [N][d] in logical
  * token order.  scores (length N) may be NULL.  sel must hold
  * min(N, sigma+w+k) entries.  Returns the count. */
 ORC_EXPORT int orc_decode_unit(int G, int d, int b, int k, int w, int sigma,
-                               int radius_mode,
+                               int radius_mode, int select_pages,
                                const uint16_t *q, const uint16_t *P,
                                const uint32_t *codes, const uint8_t *radii,
                                const uint16_t *K, const uint16_t *V, int N,
@@ -300,7 +348,8 @@ ORC_EXPORT int orc_decode_unit(int G, int d, int b, int k, int w, int sigma,
   for (int i = 0; i < N; ++i)
     S[i] = orc_score(q8, G, b, codes + (size_t)i * (b / 32),
                      orc_radius_weight(radii[i], radius_mode));
-  int n = orc_select(S, N, k, w, sigma, sel);
+  int n = select_pages ? orc_select_pages(S, N, k, w, sigma, sel)
+                       : orc_select(S, N, k, w, sigma, sel);
   orc_attend(q, G, K, V, d, sel, n, out);
   if (!scores) free(S);
   return n;
@@ -312,7 +361,8 @@ ORC_EXPORT int orc_decode_unit(int G, int d, int b, int k, int w, int sigma,
  *   N [U], q8 [U][G][b], scores [U][Nmax] (or NULL), sel [U][sel_cap],
  *   sel_cnt [U], out [U][G][d]. */
 ORC_EXPORT void orc_decode_units(int U, int G, int d, int b, int k, int w,
-                                 int sigma, int radius_mode, const uint16_t *q,
+                                 int sigma, int radius_mode, int select_pages,
+                                 const uint16_t *q,
                                  const uint16_t *P, const uint32_t *codes,
                                  const uint8_t *radii, const uint16_t *K,
                                  const uint16_t *V, const int32_t *N, int Nmax,
@@ -322,7 +372,7 @@ ORC_EXPORT void orc_decode_units(int U, int G, int d, int b, int k, int w,
   for (int u = 0; u < U; ++u) {
     size_t tok = (size_t)u * (size_t)Nmax;
     sel_cnt[u] = orc_decode_unit(
-        G, d, b, k, w, sigma, radius_mode, q + (size_t)u * G * d, P,
+        G, d, b, k, w, sigma, radius_mode, select_pages, q + (size_t)u * G * d, P,
         codes + tok * (b / 32), radii + tok, K + tok * d, V + tok * d, N[u],
         q8 + (size_t)u * G * b, scores ? scores + tok : NULL,
         sel + (size_t)u * sel_cap, out + (size_t)u * G * d);

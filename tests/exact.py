@@ -95,3 +95,21 @@ def brute_select(S, k, w, sigma):
     cand.sort(key=lambda i: (-int(S[i]), i))
     top = cand[:max(0, min(k, len(cand)))]
     return sinks, window, top
+
+
+def brute_select_pages(S, k, w, sigma, page=16):
+    """Sinks, window and the keys of the top k//page pages: each page of the
+    candidate range scored by a Python max over its candidate keys, pages
+    ranked by a full sort on (-page score, page index)."""
+    N = len(S)
+    sinks = list(range(min(sigma, N)))
+    window = list(range(max(min(sigma, N), N - w), N))
+    cand = range(sigma, N - w)
+    pages = {}
+    for i in cand:
+        pages.setdefault(i // page, []).append(i)
+    ranked = sorted(pages, key=lambda p: (-max(int(S[i]) for i in pages[p]), p))
+    top = []
+    for p in ranked[:max(0, k // page)]:
+        top += pages[p]
+    return sinks, window, top

@@ -14,7 +14,8 @@ import pytest
 import torch
 
 import oracle
-from exact import (bf16_fraction, brute_score, brute_select, exact_projection,
+from exact import (bf16_fraction, brute_score, brute_select, brute_select_pages,
+                   exact_projection,
                    exact_query_int8, exact_radius_code, exact_sign_code)
 from helpers import bf16_bits, bits_to_float
 
@@ -339,6 +340,55 @@ def test_select_picks_largest_scores():
     S[hot] = [5, 9, 7, 9]
     got = oracle.select(S, 4, 10, 4)
     assert list(got[14:]) == [99, 301, 250, 17]   # score desc, then position
+
+
+# ---------------------------------------------------------- T2 select pages
+@pytest.mark.parametrize("N,k,w,sigma", [
+    (500, 48, 16, 4), (1000, 64, 64, 5), (90, 16, 50, 4), (60, 16, 50, 4),
+    (30, 16, 50, 4), (3, 16, 1, 4), (200, 500, 16, 4), (200, 15, 16, 4),
+    (200, 0, 16, 4), (200, 40, 0, 0), (64, 16, 8, 60), (333, 37, 21, 19)])
+def test_select_pages_matches_brute_force(N, k, w, sigma):
+    rng = np.random.default_rng(N + 3 * k)
+    S = rng.integers(-50, 50, size=N).astype(np.int32)   # many page ties
+    got = oracle.select_pages(S, k, w, sigma)
+    sinks, window, top = brute_select_pages(S, k, w, sigma)
+    assert list(got) == sinks + window + top
+    assert len(got) <= min(N, sigma + w + k)
+    assert len(set(got.tolist())) == len(got)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_select_pages_equals_select_on_page_constant_scores(seed):
+    """Scores constant on each page, sigma, N - w and k multiples of 16:
+    the token top-k takes whole pages in (score desc, page asc) order, so
+    both selections are the same set (T1 is pinned independently)."""
+    rng = np.random.default_rng(seed)
+    npg = 64
+    S = np.repeat(rng.integers(-20, 20, size=npg), 16).astype(np.int32)
+    for k, w, sigma in [(160, 32, 16), (16, 0, 0), (480, 64, 48)]:
+        pages = oracle.select_pages(S, k, w, sigma)
+        tokens = oracle.select(S, k, w, sigma)
+        assert sorted(pages.tolist()) == sorted(tokens.tolist())
+
+
+def test_select_pages_limits():
+    S = np.arange(1000, dtype=np.int32)
+    # k below one page: sinks and window only
+    assert list(oracle.select_pages(S, 15, 10, 4)) == list(range(4)) + list(range(990, 1000))
+    # enough pages for the whole candidate range: dense
+    assert sorted(oracle.select_pages(S, 1000, 10, 4).tolist()) == list(range(1000))
+    # partial edge pages: the sinks' page and the window's page give only
+    # their keys inside [sigma, N - w)
+    got = oracle.select_pages(S, 2 * 16, 10, 4)[4 + 10:]
+    assert list(got) == list(range(976, 990)) + list(range(960, 976))
+    # a page's score is its best key: one hot key lifts its whole page
+    S2 = np.zeros(1000, np.int32)
+    S2[517] = 3
+    got = oracle.select_pages(S2, 16, 10, 4)[14:]
+    assert list(got) == list(range(512, 528))
+    # equal page scores: the lowest page wins
+    got = oracle.select_pages(np.zeros(1000, np.int32), 16, 10, 4)[14:]
+    assert list(got) == list(range(4, 16))
 
 
 # ---------------------------------------------------------------- A1 attend

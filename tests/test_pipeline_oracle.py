@@ -61,15 +61,16 @@ def test_pipeline_dense_limit_equals_sdpa():
         break
 
 
-@pytest.mark.parametrize("mode", [0, 1])
-def test_decode_unit_is_the_composition(mode):
+@pytest.mark.parametrize("mode,pages", [(0, False), (1, False), (0, True), (1, True)])
+def test_decode_unit_is_the_composition(mode, pages):
     for wl, s, g, q, P, K, V, _ in _units("small_ragged_b128"):
         codes, radii = oracle.encode_keys(K, P)
         r = oracle.decode_unit(q, P, codes, radii, K, V, wl.top_k, wl.window, wl.sinks,
-                               radius_mode=mode)
+                               radius_mode=mode, pages=pages)
         q8 = oracle.query_int8(q, P)
         S = oracle.scores(q8, codes, radii, radius_mode=mode)
-        sel = oracle.select(S, wl.top_k, wl.window, wl.sinks)
+        pick = oracle.select_pages if pages else oracle.select
+        sel = pick(S, wl.top_k, wl.window, wl.sinks)
         out = oracle.attend(q, K, V, sel)
         assert np.array_equal(r["q8"], q8)
         assert np.array_equal(r["scores"], S)
@@ -79,8 +80,8 @@ def test_decode_unit_is_the_composition(mode):
             break
 
 
-@pytest.mark.parametrize("mode", [0, 1])
-def test_decode_units_batch_equals_single_units(mode):
+@pytest.mark.parametrize("mode,pages", [(0, False), (1, False), (0, True)])
+def test_decode_units_batch_equals_single_units(mode, pages):
     units = list(_units("small_gqa_b128"))[:3]
     wl = units[0][0]
     Nmax = max(u[5].shape[0] for u in units)
@@ -98,11 +99,12 @@ def test_decode_units_batch_equals_single_units(mode):
         K[i, :n], V[i, :n], N[i] = u[5], u[6], n
         codes[i, :n], radii[i, :n] = oracle.encode_keys(u[5], P)
     r = oracle.decode_units(q, P, codes, radii, K, V, N, wl.top_k, wl.window, wl.sinks,
-                            radius_mode=mode)
+                            radius_mode=mode, pages=pages)
     for i, u in enumerate(units):
         n = N[i]
         one = oracle.decode_unit(q[i], P, codes[i, :n], radii[i, :n], K[i, :n], V[i, :n],
-                                 wl.top_k, wl.window, wl.sinks, radius_mode=mode)
+                                 wl.top_k, wl.window, wl.sinks, radius_mode=mode,
+                                 pages=pages)
         assert np.array_equal(r["sel"][i], one["sel"])
         assert np.array_equal(r["out"][i], one["out"])
         assert np.array_equal(r["scores"][i, :n], one["scores"])
