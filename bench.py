@@ -112,7 +112,8 @@ def counter_traffic(kernel_src_digest: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(wl, inp, units: int, seconds: float, radius_mode: int = 0) -> dict:
+def cpu_baseline(wl, inp, units: int, seconds: float, radius_mode: int = 0,
+                 pages: bool = False) -> dict:
     """The CPU oracle (as it stands) on a bounded sample of the workload."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import numpy as np
@@ -146,7 +147,8 @@ def cpu_baseline(wl, inp, units: int, seconds: float, radius_mode: int = 0) -> d
     t0 = time.perf_counter()
     while True:
         oracle.decode_units(q, P, codes, radii, K, V, N, wl.top_k, wl.window,
-                            wl.sinks, want_scores=False, radius_mode=radius_mode)
+                            wl.sinks, want_scores=False, radius_mode=radius_mode,
+                            pages=pages)
         reps += 1
         dt = time.perf_counter() - t0
         if dt >= seconds or reps >= 100000:
@@ -171,6 +173,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--cold-steps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--select", choices=("keys", "pages"), default="keys",
+                    help="select the top_k keys, or the top top_k/16 pages "
+                         "(each scored by its best candidate key)")
     ap.add_argument("--radius-weight", choices=("log", "linear"), default="log",
                     help="score weight of the radius code: the code r8 itself "
                          "(log) or rne(2^(r8/16)) (linear)")
@@ -196,7 +201,8 @@ def main():
                      code_bits=wl.code_bits, top_k=wl.top_k, window=wl.window,
                      sinks=wl.sinks,
                      radius_weight=(dkv.RADIUS_LINEAR if args.radius_weight == "linear"
-                                    else dkv.RADIUS_LOG))
+                                    else dkv.RADIUS_LOG),
+                     select_pages=args.select == "pages")
     print(f"[bench] drawing {wl.name}", file=sys.stderr, flush=True)
     inp = workloads.make_inputs(wl, "cuda")
     B, Hkv = wl.batch, wl.num_kv_heads
@@ -298,10 +304,11 @@ def main():
     ab = algorithmic_bytes(wl, lens, cfg)
     score_s = stage_ms["score"] * 1e-3
     score_src = [os.path.join(ROOT, "hashed_top_sparse_amd", "csrc", f)
-                 for f in ("score.hip", "score_common.h", "internal.h")]
-    # the counters were taken for the log radius weight's kernel
+                 for f in ("score_filter.h", "score_keys_log.hip", "score_common.h",
+                           "internal.h")]
+    # the counters were taken for the key-selecting, log-weight kernel
     traffic = (counter_traffic(source_digest(score_src), wl.name)
-               if args.radius_weight == "log" else None)
+               if args.radius_weight == "log" and args.select == "keys" else None)
     roofline = {"bound": "hbm", "kernel": "score",
                 "achieved": ab["score"] / score_s / 1e9, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": ab["score"] / score_s / 1e9 / HBM_PEAK_GBS,
@@ -325,6 +332,7 @@ def main():
                    "q_heads": wl.num_q_heads, "kv_heads": Hkv, "head_dim": wl.head_dim,
                    "code_bits": wl.code_bits, "top_k": wl.top_k, "window": wl.window,
                    "sinks": wl.sinks, "page": PAGE, "radius_weight": args.radius_weight,
+                   "select": args.select,
                    "parallelism": "single GPU"},
         "latency_us": ms_per_step * 1e3,
         "gpu_step_us": gpu_ms * 1e3,
@@ -339,7 +347,7 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_units, args.cpu_seconds,
-                                              cfg.radius_weight)
+                                              cfg.radius_weight, cfg.select_pages)
     print(json.dumps(result), flush=True)
 
 

@@ -32,7 +32,7 @@ EXPORTED_SYMBOLS = ("dkv_encode", "dkv_decode_workspace_size", "dkv_decode",
                     "dkv_decode_debug", "dkv_decode_profiled", "dkv_decode_append",
                     "dkv_decode_num_stages", "dkv_decode_stage_name",
                     "dkv_status_string", "dkv_abi_version")
-ABI_VERSION = 3
+ABI_VERSION = 4
 RADIUS_LOG = 0
 RADIUS_LINEAR = 1
 
@@ -49,7 +49,7 @@ class DkvError(RuntimeError):
 class _CConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "head_dim", "num_q_heads", "num_kv_heads", "code_bits", "page_size",
-        "top_k", "window", "sinks", "radius_weight")]
+        "top_k", "window", "sinks", "radius_weight", "select_pages")]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -65,11 +65,14 @@ class Config:
     # score weight of the radius code: RADIUS_LOG (w = r8) or RADIUS_LINEAR
     # (w = rne(2^(r8/16)))
     radius_weight: int = 0
+    # select the top top_k/16 pages (scored by their best candidate key)
+    # instead of the top_k keys
+    select_pages: bool = False
 
     def _c(self) -> _CConfig:
         return _CConfig(self.head_dim, self.num_q_heads, self.num_kv_heads,
                         self.code_bits, self.page_size, self.top_k, self.window,
-                        self.sinks, self.radius_weight)
+                        self.sinks, self.radius_weight, int(self.select_pages))
 
     @property
     def group(self) -> int:

@@ -37,7 +37,8 @@ bool valid_config(const dkv_config *cfg, dkv_status *why) {
       !(G == 1 || G == 2 || G == 4 || G == 8) || sel > DKV_MAX_SELECT ||
       cfg->num_kv_heads > 4096 ||
       !(cfg->radius_weight == DKV_RADIUS_LOG ||
-        cfg->radius_weight == DKV_RADIUS_LINEAR)) {
+        cfg->radius_weight == DKV_RADIUS_LINEAR) ||
+      !(cfg->select_pages == 0 || cfg->select_pages == 1)) {
     *why = DKV_ERR_UNSUPPORTED;
     return false;
   }
@@ -68,6 +69,7 @@ bool make_dims(const dkv_config *cfg, int32_t batch, int32_t max_seq_len,
   d->w = cfg->window;
   d->sigma = cfg->sinks;
   d->lin = cfg->radius_weight == DKV_RADIUS_LINEAR;
+  d->pages = cfg->select_pages == 1;
   d->cap = d->k + d->w + d->sigma;
   d->max_seq_len = max_seq_len;
   const int64_t by_blocks = (int64_t)kPage * max_blocks;

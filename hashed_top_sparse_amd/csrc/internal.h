@@ -23,6 +23,7 @@ struct DecodeDims {
   int KS;                    // 128-bit MFMA K-steps per key: max(1, b/128)
   int k, w, sigma, cap;      // cap = k + w + sigma (selection list length)
   bool lin;                  // linear radius weight (DKV_RADIUS_LINEAR)
+  bool pages;                // page-granular selection (select_pages)
   int max_seq_len;           // caller's bound (workspace stride)
   int n_max;                 // min(max_seq_len, 16*max_blocks)
   int max_blocks;
@@ -67,12 +68,30 @@ hipError_t launch_prep(const DecodeDims &d, const uint16_t *q,
 // region of cand [B*Hkv][cand_groups][kGroupKeys] as (u, position) in
 // position order, with their number in tcount [B*Hkv][cand_groups].  Groups
 // at or past a sequence's length are not written.
+// With page-granular selection the candidates are pages instead: (best u
+// of the page's keys in [sinks, N - window), page index), one per page that
+// meets that range.
 hipError_t launch_score(const DecodeDims &d, const uint32_t *codes,
                         const uint8_t *radii, const int32_t *block_table,
                         const int32_t *seq_lens, const uint32_t *qop,
                         const float *qneg, const uint32_t *lthr, uint2 *cand,
                         uint32_t *tcount, int32_t *scores_out,
                         hipStream_t stream);
+
+// The filter of each (selection granularity, radius weight), one per
+// translation unit (score_keys_log.hip, score_keys_linear.hip,
+// score_pages_log.hip, score_pages_linear.hip) so they compile in parallel;
+// launch_score picks one.  Same arguments as launch_score.
+#define DKV_FILTER_DECL(NAME)                                                  \
+  hipError_t NAME(const DecodeDims &d, const uint32_t *codes,                  \
+                  const uint8_t *radii, const int32_t *block_table,            \
+                  const int32_t *seq_lens, const uint32_t *qop,                \
+                  const float *qneg, const uint32_t *lthr, uint2 *cand,        \
+                  uint32_t *tcount, int32_t *scores_out, hipStream_t stream)
+DKV_FILTER_DECL(launch_filter_keys_log);
+DKV_FILTER_DECL(launch_filter_keys_linear);
+DKV_FILTER_DECL(launch_filter_pages_log);
+DKV_FILTER_DECL(launch_filter_pages_linear);
 
 // Final selection (sinks, window, exact top-k in position order): rows
 // (physical row ids blk*16+slot, -1 past the count), cnt, and the optional

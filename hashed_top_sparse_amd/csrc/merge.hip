@@ -59,8 +59,8 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
     int32_t *__restrict__ user_cnt, const uint32_t *__restrict__ codes,
     const uint8_t *__restrict__ radii, uint32_t code_bytes,
     uint32_t radius_bytes, int W, const uint32_t *__restrict__ qop,
-    const float *__restrict__ qneg, bool lin) {
-  __shared__ uint2 st[kStage];
+    const float *__restrict__ qneg, bool lin, bool pages) {
+  __shared__ __align__(16) uint2 st[kStage];
   __shared__ uint32_t gpre[kMaxGroupsLds + 1];
   __shared__ SelectShared<kThreads> sel;
 
@@ -73,9 +73,16 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
   const int ws = (N - w > ns) ? N - w : ns;
   const int nwin = N - ws;
   const int nc = max(0, N - w - sigma);
-  const int keff = min(k, nc);
-  const int total = ns + nwin + keff;
+  const int c0 = sigma, c1 = N - w; // candidate positions [c0, c1)
+  // pages: the items ranked are the pages meeting [c0, c1); the number of
+  // rows they bring is known only after the selection (edge pages are
+  // partial) unless none or all of them are taken
+  const int npc = nc > 0 ? (c1 + kPage - 1) / kPage - c0 / kPage : 0;
+  const int nitems = pages ? npc : nc;
+  const int keff = pages ? min(k / kPage, npc) : min(k, nc);
+  const bool rows_known = !pages || keff == 0 || keff == npc;
   const int base = ns + nwin;
+  int total = base + (keff == nitems ? nc : (pages ? 0 : keff));
   const int32_t *bt = block_table + (int64_t)s * max_blocks;
   int32_t *R = rows + (int64_t)unit * cap;
   int32_t *U = user_sel ? user_sel + (int64_t)unit * cap : nullptr;
@@ -85,19 +92,26 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
     R[i] = row_of(bt, pos, num_blocks);
     if (U) U[i] = pos;
   }
-  for (int i = total + tid; i < cap; i += kThreads) {
-    R[i] = -1;
-    if (U) U[i] = -1;
+  if (rows_known) {
+    for (int i = total + tid; i < cap; i += kThreads) {
+      R[i] = -1;
+      if (U) U[i] = -1;
+    }
   }
 
   if (keff > 0) {
     uint32_t *bm = bitmap + (int64_t)unit * bm_stride;
     const int nwords = (N + 31) / 32;
-    const int c0 = sigma, c1 = N - w; // candidate positions [c0, c1)
     bool use_bitmap = true;
-    if (keff == nc) {
+    // marks the candidate positions of page p
+    auto mark_page = [&](int p) {
+      const int lo = max(c0, p * kPage), hi = min(c1, (p + 1) * kPage);
+      if (hi > lo) // a page's bits never span two words
+        atomicOr(&bm[lo >> 5], ((1u << (hi - lo)) - 1u) << (lo & 31));
+    };
+    if (keff == nitems) {
       // every candidate is selected, in position order
-      for (int i = tid; i < keff; i += kThreads) {
+      for (int i = tid; i < nc; i += kThreads) {
         const int pos = c0 + i;
         R[base + i] = row_of(bt, pos, num_blocks);
         if (U) U[base + i] = pos;
@@ -208,7 +222,8 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
         int rowv[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          rowv[k] = (staged && i0 + k < i1) ? row_of(bt, (int)st[i0 + k].y, num_blocks) : -1;
+          rowv[k] = (staged && !pages && i0 + k < i1)
+                        ? row_of(bt, (int)st[i0 + k].y, num_blocks) : -1;
         // the cut: survivors are u > Tu, or u == Tu and pos <= Tpos
         uint32_t Tu = 0, Tpos = 0;
         bool cut = false;
@@ -232,7 +247,84 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
           return cut ? (u > Tu || (u == Tu && (uint32_t)pos <= Tpos))
                      : (u > T || (u == T && kPosMax - (uint32_t)pos >= Pt));
         };
-        if (staged) {
+        if (pages && staged) {
+          // stable compaction of the selected pages' candidate keys: thread
+          // t takes the run [i0, i1) of the staged (page-ordered) list and
+          // writes all rows of its kept pages after a prefix sum of their
+          // row counts
+          auto rows_of_page = [&](int p) {
+            return max(0, min(c1, (p + 1) * kPage) - max(c0, p * kPage));
+          };
+          // The block ids of all kept pages are requested together; after
+          // two prefix sums (rows, pages) every kept page goes to an LDS list
+          // (block id, page, first row) that reuses the staging buffer, and
+          // 16 lanes write each page's rows side by side.
+          constexpr int kPer = kStage / kThreads; // >= i1 - i0
+          uint32_t c = 0, kept = 0;
+          int blk[kPer], pg[kPer];
+#pragma unroll
+          for (int j = 0; j < kPer; ++j) {
+            const uint32_t i = i0 + j;
+            blk[j] = -1;
+            pg[j] = 0;
+            if (i < i1 && keep(st[i].x, (int)st[i].y)) {
+              pg[j] = (int)st[i].y;
+              c += (uint32_t)rows_of_page(pg[j]);
+              kept |= 1u << j;
+              blk[j] = bt[pg[j]];
+            }
+          }
+          uint32_t tot, npk;
+          uint32_t o = wg_exclusive_scan<kThreads>(c, &sel.red[3][0], &tot);
+          uint32_t e = wg_exclusive_scan<kThreads>((uint32_t)__popc(kept), &sel.red[3][0], &npk);
+          // (the scans' barriers: no thread reads the staged list any more)
+          const uint32_t room = (uint32_t)(cap - base);
+          uint4 *lst = reinterpret_cast<uint4 *>(st);
+          const bool listed = npk <= (uint32_t)(kStage / 2); // workgroup-uniform
+#pragma unroll
+          for (int j = 0; j < kPer; ++j) {
+            if ((kept >> j) & 1u) {
+              const int p = pg[j];
+              if (listed) {
+                lst[e++] = make_uint4((uint32_t)blk[j], (uint32_t)p, o, 0u);
+                o += (uint32_t)rows_of_page(p);
+              } else {
+                const bool okb = blk[j] >= 0 && blk[j] < num_blocks;
+                for (int pos = max(c0, p * kPage); pos < min(c1, (p + 1) * kPage) && o < room;
+                     ++pos) {
+                  R[base + o] = okb ? blk[j] * kPage + pos % kPage : -1;
+                  if (U) U[base + o] = pos;
+                  ++o;
+                }
+              }
+            }
+          }
+          if (listed) {
+            __syncthreads();
+            const int l = tid & (kPage - 1);
+            for (uint32_t x = (uint32_t)(tid / kPage); x < npk; x += kThreads / kPage) {
+              const uint4 ent = lst[x];
+              const int b = (int)ent.x, p = (int)ent.y;
+              const int pos = max(c0, p * kPage) + l;
+              const uint32_t r = ent.z + (uint32_t)l;
+              if (pos < min(c1, (p + 1) * kPage) && r < room) {
+                R[base + r] = (b >= 0 && b < num_blocks) ? b * kPage + pos % kPage : -1;
+                if (U) U[base + r] = pos;
+              }
+            }
+          }
+          total = base + (int)min(tot, room);
+          for (int i = total + tid; i < cap; i += kThreads) {
+            R[i] = -1;
+            if (U) U[i] = -1;
+          }
+          use_bitmap = false;
+        } else if (pages) {
+          // the selected pages' candidate keys go to the bitmap
+          for_each([&](uint32_t u, int p) {
+            if (keep(u, p)) mark_page(p);
+          });
+        } else if (staged) {
           // stable compaction of the survivors: thread t takes the run
           // [i0, i1) of the staged list
           uint32_t c = 0;
@@ -269,12 +361,14 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
         for (int i = tid; i < nwords; i += kThreads) bm[i] = 0u;
         __syncthreads();
         // ---- exact fallback: rescore every candidate key of the unit
+        // (pages: every page, scored by its best candidate key)
         const QueryOperand<KS> op = load_query_operand<KS, G>(
             qop, qneg, unit, s, g, Hkv * G, lane);
         const PoolView view = make_pool_view(codes, radii, code_bytes,
                                              radius_bytes, W, Hkv, g, lane);
         const int pc0 = c0 / kPage, pc1 = (c1 + kPage - 1) / kPage;
-        // fn(u, pos) for every candidate, lanes 0..15 of each wave
+        // fn(u, pos) for every candidate, lanes 0..15 of each wave (pages:
+        // fn(u, page) in lane 0)
         auto rescan = [&](auto fn) {
           for (int p0 = pc0 + wave * 8; p0 < pc1; p0 += kWaves * 8) {
             uint32_t cw[8][KS], r8[8];
@@ -290,8 +384,13 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
             for (int u = 0; u < 8; ++u) {
               const int S = score_page<KS, G>(op, cw[u], r8[u], ok[u], lin);
               const int pos = (p0 + u) * kPage + lane;
-              if (lane < kPage && pos >= c0 && pos < c1)
+              const bool in_c = lane < kPage && pos >= c0 && pos < c1;
+              if (pages) { // workgroup-uniform; the row max needs every lane
+                const uint32_t up = row_max16(in_c ? biased_score(S) : 0u);
+                if (lane == 0 && up != 0u) fn(up, p0 + u);
+              } else if (in_c) {
                 fn(biased_score(S), pos);
+              }
             }
           }
         };
@@ -308,15 +407,27 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
           }, take_eq, Pt, t2, n2);
         }
         rescan([&](uint32_t u, int pos) {
-          if (u > T || (u == T && kPosMax - (uint32_t)pos >= Pt))
-            atomicOr(&bm[pos >> 5], 1u << (pos & 31));
+          if (u > T || (u == T && kPosMax - (uint32_t)pos >= Pt)) {
+            if (pages)
+              mark_page(pos);
+            else
+              atomicOr(&bm[pos >> 5], 1u << (pos & 31));
+          }
         });
       }
     }
     if (use_bitmap) { // workgroup-uniform
       __syncthreads();
-      emit_bitmap<kThreads>(bm, nwords, bt, num_blocks, R + base,
-                            U ? U + base : nullptr, &sel.red[3][0]);
+      const uint32_t nsel = emit_bitmap<kThreads>(bm, nwords, bt, num_blocks, R + base,
+                                                  U ? U + base : nullptr, &sel.red[3][0],
+                                                  (uint32_t)(cap - base));
+      if (!rows_known) {
+        total = base + (int)nsel;
+        for (int i = total + tid; i < cap; i += kThreads) {
+          R[i] = -1;
+          if (U) U[i] = -1;
+        }
+      }
     }
   }
   if (tid == 0) {
@@ -345,7 +456,7 @@ hipError_t launch_merge(const DecodeDims &d, const uint2 *cand,
                        d.max_blocks, d.num_blocks, d.Hkv, d.k, d.w, d.sigma,   \
                        d.cap, bitmap, d.bm_words, rows, cnt, user_sel,         \
                        user_cnt, codes, radii, code_bytes, radius_bytes, d.W,  \
-                       qop, qneg, d.lin);                                      \
+                       qop, qneg, d.lin, d.pages);                             \
     return hipGetLastError();                                                  \
   }
   DKV_MERGE_CASE(1, 1)

@@ -74,7 +74,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     const int32_t *__restrict__ seq_lens, int n_max, int8_t *__restrict__ q8,
     uint32_t *__restrict__ qop, float *__restrict__ qneg,
     uint32_t *__restrict__ lthr, int Hq,
-    int Hkv, int b, int W, int k, int w, int sigma, bool lin) {
+    int Hkv, int b, int W, int k, int w, int sigma, bool lin, bool pages) {
   const int unit = blockIdx.x;
   const int s = unit / Hkv;
   const int g = unit % Hkv;
@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     P.pc0 = 0;
     P.SP = 1;
     P.nsp = 0;
-    if (P.keff > 0 && P.keff < P.nc) {
+    if (!pages && P.keff > 0 && P.keff < P.nc) {
       P.pc0 = sigma / kPage;
       const int ncp = (n - w + kPage - 1) / kPage - P.pc0;
       while (P.SP < 32 && 2 * P.SP <= P.keff / 32) P.SP *= 2;
@@ -381,6 +381,14 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
       }, ks_take);
     }
   }
+  if (pages) {
+    // page-granular selection: every page meeting [sigma, N - w) is a
+    // candidate (L = 0) unless none or all of them are selected
+    const int c0 = sigma, c1 = N - w;
+    const int npc = c1 > c0 ? (c1 + kPage - 1) / kPage - c0 / kPage : 0;
+    const int kp = min(k / kPage, npc);
+    L = (kp > 0 && kp < npc) ? 0u : 0xFFFFFFFFu;
+  }
   if (threadIdx.x == 0) lthr[unit] = L;
   int8_t *qo = q8 + ((int64_t)s * Hq + (int64_t)g * G) * b;
 #pragma unroll
@@ -420,7 +428,8 @@ hipError_t launch_prep(const DecodeDims &d, const uint16_t *q,
                        k_pool, codes_w, radii_w,                               \
                        d.num_blocks, code_bytes, radius_bytes, block_table,    \
                        d.max_blocks, seq_lens, d.n_max, q8, qop, qneg, lthr,   \
-                       d.Hq, d.Hkv, d.b, d.W, d.k, d.w, d.sigma, d.lin);       \
+                       d.Hq, d.Hkv, d.b, d.W, d.k, d.w, d.sigma, d.lin,         \
+                       d.pages);                                               \
     return hipGetLastError();                                                  \
   }
   DKV_PREP_CASE(1, 1)

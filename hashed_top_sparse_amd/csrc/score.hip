@@ -1,410 +1,8 @@
-// score.hip -- code-domain score of every cached key in one streaming pass;
-// keys reaching the (sequence, KV head)'s candidate threshold L leave the
-// chip as (biased score, position) candidates.
-//
-// [SPHERICAL KV, §2.1]: the logit comes straight from the stored radius and
-// the packed angle code, no dense key rebuilt; [DeepSeek, "starting from
-// DSA"]: a light indexer scores every cached key.  The per-page scoring is
-// in score_common.h (one fp8 x fp4 matrix-core op per 128 code bits).
-//
-// Work: persistent waves (4 per workgroup), each streaming a static stride
-// of 64-page tasks (sequence, page group, KV head); task ids run KV head
-// fastest, then sequence, then page group, so the heads of one page block
-// are read together.  Codes are key-major, so one 16-byte load per lane
-// brings a page quad: lanes 16j..16j+15 read page j's 16 keys (each lane a
-// whole 128-bit key; 64-bit keys use 8-byte loads, 256-bit keys two loads).
-// Four gfx950 row swaps (v_permlane32_swap, v_permlane16_swap) transpose
-// that into the matrix-core operand of each page (lane L: word L/16 of key
-// L%16).  Each lane also loads one radius byte per quad.  A wave keeps
-// kDepth quads of loads in flight in registers (the compiler's own wait
-// counts order them), continuing into the next task; the block ids of the
-// task after next are loaded one task ahead.  Candidates (positions in
-// [sinks, N - window) with u >= L) are compacted per quad by ballots, in
-// position order, into the task's own region of the candidate buffer (room
-// for every key of the group, so no atomics and no overflow), and the
-// task's count is written beside it.
-#include <algorithm>
-#include <type_traits>
-
-#include "score_common.h"
+// score.hip -- picks the streaming filter (score_filter.h) for the call's
+// selection granularity and radius weight.
+#include "internal.h"
 
 namespace dkv {
-namespace {
-
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
-constexpr int kTaskQuads = kGroupPages / 4; // page quads per task
-constexpr int kDepth = 4;                   // quads of loads in flight per wave
-static_assert(kTaskQuads % kDepth == 0 && kTaskQuads >= 2 * kDepth, "prefetch rounds");
-// quad of a task at which the task after next and the next task's operand
-// are loaded: kDepth quads before the next task's first prefetch
-constexpr int kLookahead = kTaskQuads - 2 * kDepth;
-// Workgroups per CU: one wave per SIMD each, four waves per SIMD in all.
-// More resident waves do not help (the kernel is bound by instruction
-// issue), and four per SIMD keeps each wave's task count equal when the
-// task count is a multiple of 4 x 4 x CUs.
-constexpr int kWgPerCu = 4;
-// per-wave candidate list: kCandList entries, then one spare entry per lane
-// (8 KB of LDS in all)
-constexpr int kCandList = kGroupKeys - 64;
-constexpr int kTaskTable = 16;        // tasks recorded before a forced write
-
-// Compile-time loop: f(std::integral_constant<int, I>) for I in [I0, N).
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for(F &&f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<I + 1, N>(f);
-  }
-}
-
-// One task of the stream (all fields wave-uniform); unit < 0: none.
-struct Task {
-  int s, g, grp, unit, N, key0, npg, lo, hi;
-};
-
-// Loaded code words of one page quad: lane 16j+c holds the KS*4 words of
-// key c of page j (words 4ks..4ks+3 in d[ks]).
-template <int KS>
-struct QuadLoad {
-  uint32_t d[KS][4];
-};
-
-// An empty use of a register value: the compiler waits for its load here
-// (32-bit operands only, which the host pass of the compiler also accepts).
-__device__ __forceinline__ void mark_loaded(uint32_t x) { asm volatile("" ::"v"(x)); }
-
-// 4x4 transpose across the four 16-lane rows: afterwards x[j] in row a holds
-// what x[a] held in row j (for every lane position in the row).
-__device__ __forceinline__ void transpose_rows(uint32_t (&x)[4]) {
-  auto a = __builtin_amdgcn_permlane32_swap(x[0], x[2], false, false);
-  auto b = __builtin_amdgcn_permlane32_swap(x[1], x[3], false, false);
-  auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
-  auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
-  x[0] = c[0];
-  x[1] = c[1];
-  x[2] = d[0];
-  x[3] = d[1];
-}
-
-// W: code words per key (2, 4 or 8); KS: 128-bit matrix-core K-steps;
-// DBG: also write every score to scores_out (inspection builds only); LIN:
-// linear radius weight (looked up in a per-workgroup LDS table).
-template <int W, int G, bool DBG, bool LIN, int KS = (W > 4 ? W / 4 : 1)>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void filter_kernel(
-    const uint32_t *__restrict__ codes, const uint8_t *__restrict__ radii,
-    int64_t num_blocks, uint32_t code_bytes, uint32_t radius_bytes,
-    const int32_t *__restrict__ block_table, int max_blocks,
-    const int32_t *__restrict__ seq_lens, int n_max,
-    const uint32_t *__restrict__ qop, const float *__restrict__ qneg,
-    const uint32_t *__restrict__ lthr, int B, int Hkv, int ngroups,
-    int ntasks, int w, int sigma, uint2 *__restrict__ cand,
-    uint32_t *__restrict__ tcount, int cand_groups,
-    int32_t *__restrict__ scores_out, int score_stride) {
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int stride = gridDim.x * kWaves;
-  // linear radius weights of the 256 codes (before any wave can leave)
-  __shared__ uint16_t wlut[LIN ? 256 : 1];
-  if constexpr (LIN) {
-    for (int i = threadIdx.x; i < 256; i += kThreads)
-      wlut[i] = (uint16_t)radius_weight_linear((uint32_t)i);
-    __syncthreads();
-  }
-  const int Hq = Hkv * G;
-  const __amdgpu_buffer_rsrc_t code_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint32_t *>(codes), 0, code_bytes, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t rad_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t *>(radii), 0, radius_bytes, kBufferWord3);
-  // Sequence lengths and thresholds are read with vector loads: a scalar
-  // load in the stream would make every wait on the LDS counter a full wait
-  // (scalar loads complete out of order), including the candidate writes.
-  const __amdgpu_buffer_rsrc_t len_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<int32_t *>(seq_lens), 0, (uint32_t)B * 4u, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t thr_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint32_t *>(lthr), 0, (uint32_t)(B * Hkv) * 4u, kBufferWord3);
-  const uint32_t page_bytes = (uint32_t)(kPage * W * 4);
-  // physical page id past the pools: its code and radius loads read 0
-  const uint32_t ph_none = (uint32_t)(num_blocks * Hkv);
-  const uint32_t key_byte = (uint32_t)((lane & 15) * W * 4);
-  const int row = lane >> 4;
-  // per-wave tables of the current and the next task's page ids (lane j
-  // writes page j), read back per page quad by row: one LDS read per quad
-  __shared__ uint32_t ptab[kWaves][2][kGroupPages];
-  uint32_t *tabC = ptab[wave][0], *tab1 = ptab[wave][1];
-  // the current task's radius lines (16 bytes per page, page order), and
-  // its candidates staged before they are written out
-  __shared__ __attribute__((aligned(16))) uint8_t rtab[kWaves][kGroupKeys];
-  // The wave's candidates, (u, index in the task), kept in LDS until the
-  // wave has streamed all its tasks, then written out with the counts: a
-  // global store inside the stream would hold up the completion of every
-  // load issued after it (one in-order counter covers loads and stores).
-  // Per task: (region, first position, entries in the list, count).  A
-  // task that finds the list full writes the rest of its candidates to its
-  // region at once (rare).
-  __shared__ uint2 cstage[kWaves][kCandList + 64];
-  __shared__ uint32_t ttab[kWaves][kTaskTable][4];
-  uint8_t *radC = rtab[wave];
-  uint2 *cst = cstage[wave];
-  uint32_t (*tt)[4] = ttab[wave];
-  uint32_t used = 0;  // list entries in use
-  int ntab = 0;       // tasks recorded
-  // Writes every recorded task's listed candidates and its count.  Lanes
-  // past a task's list length repeat its last entry (same bytes, same slot).
-  auto flush_all = [&]() {
-    uint32_t start = 0;
-    for (int k = 0; k < ntab; ++k) {
-      const uint32_t t_idx = tt[k][0], key0 = tt[k][1], nbuf = tt[k][2], ncount = tt[k][3];
-      uint2 *reg = cand + (int64_t)t_idx * kGroupKeys;
-      for (uint32_t e0 = 0; e0 < nbuf; e0 += 64) {
-        const uint32_t e = min(e0 + (uint32_t)lane, nbuf - 1);
-        const uint2 v = cst[start + e];
-        reg[e] = make_uint2(v.x, key0 + v.y);
-      }
-      if (lane == 0) tcount[t_idx] = ncount;
-      start += nbuf;
-    }
-    used = 0;
-    ntab = 0;
-  };
-
-  // task id -> task, or none if its page group is past the sequence
-  auto decode = [&](int t, Task &T) -> bool {
-    T.g = t % Hkv;
-    const int r = t / Hkv;
-    T.s = r % B;
-    T.grp = r / B;
-    T.N = clamp_int(__builtin_amdgcn_readfirstlane(
-                        __builtin_amdgcn_raw_buffer_load_b32(len_rsrc, T.s * 4, 0, 0)),
-                    0, n_max);
-    T.key0 = T.grp * kGroupKeys;
-    if (T.key0 >= T.N) return false;
-    T.unit = T.s * Hkv + T.g;
-    T.npg = min(kGroupPages, (T.N - T.key0 + kPage - 1) / kPage);
-    T.lo = max(sigma, T.key0);
-    T.hi = max(T.lo, min(T.N - w, T.key0 + T.npg * kPage)); // empty: hi == lo
-    return true;
-  };
-  // the first non-empty task at or after t in this wave's stride
-  auto find = [&](int t, Task &T) {
-    for (; t < ntasks; t += stride)
-      if (decode(t, T)) return t;
-    T.unit = -1;
-    return ntasks;
-  };
-  // Lane j: physical page id (page block index) of the task's page j, or
-  // ph_none past the task or for an invalid block id.
-  auto load_pages = [&](const Task &T) -> int {
-    int blk = -1;
-    if (T.unit >= 0 && lane < T.npg)
-      blk = block_table[(int64_t)T.s * max_blocks + T.key0 / kPage + lane];
-    return blk;
-  };
-  auto page_ids = [&](const Task &T, int blk) -> uint32_t {
-    return (blk >= 0 && blk < num_blocks) ? (uint32_t)blk * (uint32_t)Hkv + (uint32_t)T.g
-                                          : ph_none;
-  };
-  auto load_op = [&](const Task &T, QueryOperandRaw<KS> &op, uint32_t &L) {
-    const int unit = T.unit >= 0 ? T.unit : 0;
-    load_query_operand_raw<KS, G>(qop, qneg, unit, unit / Hkv, unit % Hkv, Hq, lane, op);
-    L = __builtin_amdgcn_raw_buffer_load_b32(thr_rsrc, unit * 4, 0, 0); // uniform
-  };
-  // Loads a page quad; `mine` is the page id of this lane's page (page
-  // lane>>4 of the quad).
-  auto load_quad = [&](uint32_t mine, QuadLoad<KS> &ql) {
-    const int voff = (int)(mine * page_bytes + key_byte);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if constexpr (W == 2) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b64(code_rsrc, voff, 0, 0);
-        ql.d[ks][0] = v[0];
-        ql.d[ks][1] = v[1];
-        ql.d[ks][2] = 0u;
-        ql.d[ks][3] = 0u;
-      } else {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(code_rsrc, voff + 16 * ks, 0, 0);
-        ql.d[ks][0] = v[0];
-        ql.d[ks][1] = v[1];
-        ql.d[ks][2] = v[2];
-        ql.d[ks][3] = v[3];
-      }
-    }
-  };
-
-  // ---- prologue: the first task, its successor, their page ids, operand
-  Task C, T1;
-  const int tC = find(blockIdx.x * kWaves + wave, C);
-  if (C.unit < 0) return;
-  int t1 = find(tC + stride, T1);
-  tabC[lane] = page_ids(C, load_pages(C));
-  tab1[lane] = page_ids(T1, load_pages(T1));
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  QueryOperand<KS> opC;
-  uint32_t LC;
-  {
-    QueryOperandRaw<KS> raw;
-    load_op(C, raw, LC);
-    opC = finish_query_operand<KS, G>(raw, lane);
-  }
-  // The loop below carries opC; uses here make the compiler wait for its
-  // loads now, before the stream starts, instead of (merging this path into
-  // the loop head) in every task.
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) mark_loaded((uint32_t)opC.a[ks][i]);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) mark_loaded(__float_as_uint(opC.cinit[i]));
-  // radius lines: lane j loads page j's 16 bytes (a task ahead of use)
-  auto load_radius = [&](uint32_t ph) -> uint4 {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rad_rsrc, (int)(ph * (uint32_t)kPage), 0, 0);
-    return make_uint4(v[0], v[1], v[2], v[3]);
-  };
-  auto store_radius = [&](const uint4 &v) {
-    *reinterpret_cast<uint4 *>(radC + 16 * lane) = v;
-  };
-  store_radius(load_radius(tabC[lane]));
-  uint4 radN = load_radius(tab1[lane]);
-  QuadLoad<KS> buf[kDepth];
-  static_for<0, kDepth>([&](auto qc) {
-    constexpr int q = decltype(qc)::value;
-    load_quad(tabC[4 * q + row], buf[q]);
-  });
-  // LDS values of the current quad (see run_task)
-  uint32_t r8c = radC[lane];
-  uint32_t refc = tabC[4 * kDepth + row];
-
-  // One task: score C's 16 quads while prefetching, then rotate the stream.
-  // The first call is peeled off the loop so that the loop head is only
-  // entered in the state a task leaves (the compiler's wait counts at the
-  // loop head then match the steady state).
-  auto run_task = [&]() -> bool {
-    Task T2 = {0, 0, 0, -1, 0, 0, 0, 0, 0};
-    int t2 = ntasks;
-    int blk2 = -1; // raw block ids, turned into page ids one task later
-    QueryOperandRaw<KS> op1;
-    uint32_t L1 = 0;
-    const int64_t t_idx = (int64_t)C.unit * cand_groups + C.grp;
-    uint2 *reg = cand + t_idx * kGroupKeys;
-    uint32_t nc = 0; // the task's candidates so far
-    static_for<0, kTaskQuads>([&](auto qc) {
-      constexpr int q = decltype(qc)::value;
-      constexpr int slot = q % kDepth;
-      if constexpr (q == kLookahead) {
-        // the task after next (its page ids, used one task from now) and
-        // the next task's operand (used from the next task's first quad)
-        if (T1.unit >= 0) t2 = find(t1 + stride, T2);
-        blk2 = load_pages(T2);
-        load_op(T1, op1, L1);
-      }
-      // ---- score quad q of C
-      uint32_t x[KS][4];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[ks][i] = buf[slot].d[ks][i];
-      // radius byte of key lane&15 of page 4q + lane>>4, and the page id
-      // of the refill below, both read from LDS one quad ahead
-      const uint32_t r8 = r8c;
-      // its weight (LIN: an LDS read issued before the next quad's reads)
-      const int wgt = LIN ? (int)wlut[r8] : (int)r8;
-      // ---- refill the slot: the quad kDepth further on (C's, or T1's
-      // first ones)
-      load_quad(refc, buf[slot]);
-      // ---- the next quad's LDS reads, before this quad's candidate write
-      // (LDS operations complete in order)
-      if constexpr (q + 1 < kTaskQuads) {
-        r8c = radC[64 * (q + 1) + lane];
-        refc = (q + 1 + kDepth < kTaskQuads) ? tabC[4 * (q + 1 + kDepth) + row]
-                                            : tab1[4 * (q + 1 + kDepth - kTaskQuads) + row];
-      }
-      uint32_t cw[4][KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        transpose_rows(x[ks]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) cw[j][ks] = x[ks][j];
-      }
-      const int mx = score_quad_max_seq<KS, G>(opC, cw);
-      const uint32_t u = biased_score(__mul24(wgt, mx));
-      const int qpos = C.key0 + 64 * q; // first position of the quad
-      const int pos = qpos + lane;
-      if constexpr (DBG) {
-        if (pos < C.N)
-          scores_out[(int64_t)C.unit * score_stride + pos] = (int32_t)(u - kScoreBias);
-      }
-      // A candidate: position in [lo, hi) and u >= L, each test one
-      // compare (the range one on pos - lo, unsigned).  It is appended to
-      // the wave's LDS list without a branch: its slot in the task is the
-      // running count plus the candidates in lower lanes.
-      const bool inr = (uint32_t)(pos - C.lo) < (uint32_t)(C.hi - C.lo);
-      const bool ge = u >= LC;
-      const uint64_t m = __ballot(inr) & __ballot(ge);
-      const uint32_t cslot = __builtin_amdgcn_mbcnt_hi(
-          (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, nc));
-      const uint32_t lslot = used + cslot;
-      // Every lane writes (a branch around the write would leave the
-      // compiler unsure whether it was issued, and every later LDS wait
-      // would then wait for it): lanes without a listed candidate write
-      // their spare entry.  An address-space-qualified pointer keeps this an
-      // LDS store (a flat store would count against the vector-memory wait
-      // counter).
-      const uint32_t wslot = (inr && ge && lslot < (uint32_t)kCandList)
-                                 ? lslot : (uint32_t)(kCandList + lane);
-      ((__attribute__((address_space(3))) uint64_t *)cst)[wslot] =
-          ((uint64_t)(uint32_t)(64 * q + lane) << 32) | u;
-      if (used + nc + (uint32_t)__popcll(m) > (uint32_t)kCandList) { // rare
-        if (inr && ge && lslot >= (uint32_t)kCandList)
-          ((__attribute__((address_space(1))) uint64_t *)reg)[cslot] =
-              ((uint64_t)(uint32_t)pos << 32) | u;
-      }
-      nc += (uint32_t)__popcll(m);
-    });
-    // record the task: its first min(nc, room) candidates are in the list
-    {
-      const uint32_t nbuf = min(nc, (uint32_t)kCandList - used);
-      if (lane == 0) {
-        tt[ntab][0] = (uint32_t)t_idx;
-        tt[ntab][1] = (uint32_t)C.key0;
-        tt[ntab][2] = nbuf;
-        tt[ntab][3] = nc;
-      }
-      used += nbuf;
-      ++ntab;
-      if (ntab == kTaskTable) flush_all(); // many tasks per wave (rare)
-    }
-
-    // rotate the stream
-    if (T1.unit < 0) return false;
-    C = T1;
-    opC = finish_query_operand<KS, G>(op1, lane);
-    LC = L1;
-    T1 = T2;
-    t1 = t2;
-    {
-      uint32_t *t = tabC;
-      tabC = tab1;
-      tab1 = t;
-    }
-    // the old current table is no longer read: T2's page ids go there
-    tab1[lane] = page_ids(T2, blk2);
-    // the new current task's radius lines (loaded a task ago) into LDS, and
-    // the new next task's lines requested
-    store_radius(radN);
-    radN = load_radius(tab1[lane]);
-    r8c = radC[lane];
-    refc = tabC[4 * kDepth + row];
-    return true;
-  };
-  if (run_task())
-    while (run_task()) {
-    }
-  flush_all();
-}
-
-} // namespace
 
 hipError_t launch_score(const DecodeDims &d, const uint32_t *codes,
                         const uint8_t *radii, const int32_t *block_table,
@@ -412,49 +10,10 @@ hipError_t launch_score(const DecodeDims &d, const uint32_t *codes,
                         const float *qneg, const uint32_t *lthr, uint2 *cand,
                         uint32_t *tcount, int32_t *scores_out,
                         hipStream_t stream) {
-  const int pages = (d.n_max + kPage - 1) / kPage;
-  const int64_t ngroups = (pages + kGroupPages - 1) / kGroupPages;
-  if (ngroups == 0) return hipSuccess;
-  const int64_t ntasks = (int64_t)d.B * ngroups * d.Hkv;
-  if (ntasks > 0x7FFFFFFF - 65536) return hipErrorInvalidValue;
-  const uint32_t code_bytes = (uint32_t)((uint64_t)d.num_blocks * d.Hkv * d.W * kPage * 4);
-  const uint32_t radius_bytes = (uint32_t)((uint64_t)d.num_blocks * d.Hkv * kPage);
-#define DKV_SCORE_LAUNCH(WV, GV, DV, LV)                                       \
-  {                                                                            \
-    const int64_t nwg = std::min<int64_t>((ntasks + kWaves - 1) / kWaves,       \
-                                          (int64_t)kWgPerCu * device_cu_count()); \
-    hipLaunchKernelGGL((filter_kernel<WV, GV, DV, LV>), dim3((unsigned)nwg),   \
-                       dim3(kThreads), 0, stream, codes, radii, d.num_blocks,  \
-                       code_bytes, radius_bytes, block_table, d.max_blocks,    \
-                       seq_lens, d.n_max, qop, qneg, lthr, d.B, d.Hkv,         \
-                       (int)ngroups, (int)ntasks, d.w, d.sigma, cand, tcount,  \
-                       d.cand_groups, scores_out, d.max_seq_len);              \
-    return hipGetLastError();                                                  \
-  }
-#define DKV_SCORE_CASE(WV, GV)                                                 \
-  if (d.W == WV && d.G == GV) {                                                \
-    if (d.lin) {                                                               \
-      if (scores_out != nullptr) DKV_SCORE_LAUNCH(WV, GV, true, true)          \
-      DKV_SCORE_LAUNCH(WV, GV, false, true)                                    \
-    }                                                                          \
-    if (scores_out != nullptr) DKV_SCORE_LAUNCH(WV, GV, true, false)           \
-    DKV_SCORE_LAUNCH(WV, GV, false, false)                                     \
-  }
-  DKV_SCORE_CASE(2, 1)
-  DKV_SCORE_CASE(2, 2)
-  DKV_SCORE_CASE(2, 4)
-  DKV_SCORE_CASE(2, 8)
-  DKV_SCORE_CASE(4, 1)
-  DKV_SCORE_CASE(4, 2)
-  DKV_SCORE_CASE(4, 4)
-  DKV_SCORE_CASE(4, 8)
-  DKV_SCORE_CASE(8, 1)
-  DKV_SCORE_CASE(8, 2)
-  DKV_SCORE_CASE(8, 4)
-  DKV_SCORE_CASE(8, 8)
-#undef DKV_SCORE_CASE
-#undef DKV_SCORE_LAUNCH
-  return hipErrorInvalidValue;
+  auto *f = d.pages ? (d.lin ? launch_filter_pages_linear : launch_filter_pages_log)
+                    : (d.lin ? launch_filter_keys_linear : launch_filter_keys_log);
+  return f(d, codes, radii, block_table, seq_lens, qop, qneg, lthr, cand, tcount,
+           scores_out, stream);
 }
 
 } // namespace dkv

@@ -165,6 +165,21 @@ __device__ __forceinline__ float max_rows32(float m) {
   return max_score(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Maximum over each 16-lane row, in every lane of the row: DPP swaps of
+// neighbours (quad_perm 1,0,3,2), of pairs (quad_perm 2,3,0,1), of the two
+// quads of each half-row (row_half_mirror) and of the two half-rows
+// (row_mirror).  Every lane must call it.
+__device__ __forceinline__ uint32_t row_max16(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x140, 0xF, 0xF, false));
+  return x;
+}
+
+// Lanes 0, 16, 32 and 48: the first lane of each 16-lane row.
+constexpr uint64_t kRowHeads = 0x0001000100010001ull;
+
 // Number of set bits of `mask` in lanes below the calling lane.
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),

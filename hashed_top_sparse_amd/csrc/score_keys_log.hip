@@ -1,0 +1,11 @@
+// score_keys_log.hip -- the streaming filter for key candidates, log radius weight.
+#include "score_filter.h"
+
+namespace dkv {
+
+DKV_FILTER_DECL(launch_filter_keys_log) {
+  return launch_filter_impl<false, false>(d, codes, radii, block_table, seq_lens, qop,
+                                       qneg, lthr, cand, tcount, scores_out, stream);
+}
+
+} // namespace dkv

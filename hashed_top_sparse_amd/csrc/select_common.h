@@ -193,12 +193,12 @@ __device__ bool wg_topk_cut(SelectShared<NT> &sh, Visit2 visit2, uint32_t kneed,
 
 // Writes the positions of the set bits of bitmap[0, nwords) (bit p = word
 // p/32, bit p%32) in ascending order to pos_out[0..] / row_out[0..] (row =
-// page*16 + slot through the block table, -1 for an invalid page).  Every
-// thread must call it.
+// page*16 + slot through the block table, -1 for an invalid page), at most
+// max_out of them; returns their number.  Every thread must call it.
 template <int NT>
-__device__ void emit_bitmap(const uint32_t *bitmap, int nwords, const int32_t *bt,
-                            int64_t num_blocks, int32_t *row_out,
-                            int32_t *pos_out, uint32_t *tmp) {
+__device__ uint32_t emit_bitmap(const uint32_t *bitmap, int nwords, const int32_t *bt,
+                                int64_t num_blocks, int32_t *row_out,
+                                int32_t *pos_out, uint32_t *tmp, uint32_t max_out) {
   const int per = (nwords + NT - 1) / NT;
   const int w0 = min(nwords, (int)threadIdx.x * per);
   const int w1 = min(nwords, w0 + per);
@@ -208,7 +208,7 @@ __device__ void emit_bitmap(const uint32_t *bitmap, int nwords, const int32_t *b
   uint32_t o = wg_exclusive_scan<NT>(c, tmp, &total);
   for (int i = w0; i < w1; ++i) {
     uint32_t m = bitmap[i];
-    while (m) {
+    while (m && o < max_out) {
       const int bitp = __ffs(m) - 1;
       m &= m - 1;
       const int pos = i * 32 + bitp;
@@ -218,6 +218,7 @@ __device__ void emit_bitmap(const uint32_t *bitmap, int nwords, const int32_t *b
       ++o;
     }
   }
+  return min(total, max_out);
 }
 
 } // namespace dkv

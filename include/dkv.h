@@ -37,7 +37,13 @@
  *               decoded radius).  |S| < 2^31 in both.
  *   selection   per (sequence, KV head): sinks [0, sigma), window
  *               [N-w, N), plus the top k of [sigma, N-w) by (S descending,
- *               position ascending).
+ *               position ascending); or, with select_pages, the keys in
+ *               [sigma, N-w) of the top k/16 16-token pages by (page score
+ *               descending, page index ascending), a page's score being
+ *               the largest S of its keys in that range ([DeepSeek CSA]:
+ *               several tokens condensed into one entry before the top-k;
+ *               [SKV §2.2]: pages read as one stream instead of scattered
+ *               rows).
  *   attention   exact softmax(q.k/sqrt(d)) . V over the selection, fp32
  *               accumulation, for each query head of the group.
  *
@@ -108,6 +114,10 @@ typedef struct {
   int32_t radius_weight; /* score weight of a key's radius code r8:
                             DKV_RADIUS_LOG (0): w = r8;
                             DKV_RADIUS_LINEAR (1): w = rne(2^(r8/16));
+                            other values: DKV_ERR_UNSUPPORTED            */
+  int32_t select_pages;  /* 0: top_k keys; 1: the top top_k/16 pages, each
+                            scored by its best key in [sigma, N-w), and
+                            their keys in that range (see dkv_decode);
                             other values: DKV_ERR_UNSUPPORTED            */
 } dkv_config;
 
@@ -270,7 +280,7 @@ const char *dkv_decode_stage_name(int32_t stage);
 const char *dkv_status_string(dkv_status status);
 
 /* ABI version of this header (bumped on any signature or layout change). */
-#define DKV_ABI_VERSION 3
+#define DKV_ABI_VERSION 4
 int32_t dkv_abi_version(void);
 
 #ifdef __cplusplus

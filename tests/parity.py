@@ -119,7 +119,8 @@ def check_unit(cfg: dkv.Config, inp: dict, gpu: dict, codes, radii, s: int, g: i
         assert len(bad) == 0, f"codes differ at {len(bad)} keys, first {bad[:5]}"
         assert np.array_equal(g_radii, o_radii), "radii differ"
     r = oracle.decode_unit(q, P, o_codes, o_radii, K, V, cfg.top_k, cfg.window,
-                           cfg.sinks, radius_mode=cfg.radius_weight)
+                           cfg.sinks, radius_mode=cfg.radius_weight,
+                           pages=cfg.select_pages)
     if "q8" in gpu:
         g_q8 = gpu["q8"][s, g * G:(g + 1) * G].cpu().numpy()
         assert np.array_equal(g_q8, r["q8"]), "query codes differ"

@@ -29,6 +29,15 @@ def test_library_exports_every_declared_symbol():
     assert lib.dkv_abi_version() == dkv.ABI_VERSION
 
 
+def test_config_struct_matches_header():
+    """The binding's dkv_config fields are the header's, in order."""
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct \{(.*?)\} dkv_config;", text, re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = re.findall(r"int32_t\s+(\w+)\s*;", body)
+    assert fields == [f for f, _ in dkv._CConfig._fields_]
+
+
 def test_status_strings():
     lib = dkv.load_library()
     for code, name in dkv.STATUS.items():
@@ -38,7 +47,8 @@ def test_status_strings():
 
 def _cfg(**over):
     kw = dict(head_dim=128, num_q_heads=32, num_kv_heads=8, code_bits=128,
-              page_size=16, top_k=64, window=16, sinks=4, radius_weight=0)
+              page_size=16, top_k=64, window=16, sinks=4, radius_weight=0,
+              select_pages=0)
     kw.update(over)
     return dkv._CConfig(*[kw[f] for f, _ in dkv._CConfig._fields_])
 
@@ -58,6 +68,7 @@ def _decode(cfg, ws_bytes=1 << 30, workspace=FAKE, q=FAKE, batch=2, max_seq_len=
     (dict(num_q_heads=30, num_kv_heads=8), 1), (dict(top_k=-1), 1),
     (dict(window=-5), 1), (dict(sinks=-1), 1), (dict(num_kv_heads=0), 1),
     (dict(top_k=1 << 20), 2), (dict(radius_weight=2), 2), (dict(radius_weight=-1), 2),
+    (dict(select_pages=2), 2), (dict(select_pages=-1), 2),
 ])
 def test_decode_rejects_bad_config(over, status):
     assert _decode(_cfg(**over)) == status

@@ -360,3 +360,74 @@ def test_linear_weight_largest_radii():
             big = max(big, int(gpu["scores"][s, g, :n].abs().max().item()))
     # far past 2^24, where a float product would no longer be exact
     assert big > 2 ** 26, big
+
+
+# ------------------------------------------------ page-granular selection
+PAGES = dict(select_pages=True)
+
+
+@pytest.mark.parametrize("name", sorted(workloads.SMALL))
+def test_page_selection_small_every_unit(name):
+    """The top top_k/16 pages, each scored by its best candidate key: bit-exact
+    scores, selected sets and counts, outputs within tolerance."""
+    stats = _run(workloads.get(name), **PAGES)
+    rec = [st["recall"] for st in stats if st["recall"] is not None]
+    print(name, "needle recall (pages)", np.mean(rec) if rec else None)
+
+
+@pytest.mark.parametrize("over", [
+    dict(top_k=5000, window=16, sinks=4),      # every page of the range
+    dict(top_k=15, window=64, sinks=4),        # below one page: window + sinks
+    dict(top_k=64, window=0, sinks=0),
+    dict(top_k=33, window=21, sinks=19),       # partial edge pages
+    dict(top_k=64, window=64, sinks=4, radius_weight=dkv.RADIUS_LINEAR),
+])
+def test_page_selection_edge_configs(over):
+    _run(workloads.get("small_gqa_b128"), **PAGES, **over)
+
+
+def test_page_selection_ties_go_to_lowest_pages():
+    """Identical keys everywhere: every page ties, the lowest pages win."""
+    wl = workloads.get("small_gqa_b128")
+    cfg = config_of(wl, **PAGES)
+    inp = workloads.make_inputs(wl, DEV)
+    inp["k_pool"][:] = inp["k_pool"][0, 0]
+    codes, radii = gpu_encode_all(cfg, inp)
+    gpu = gpu_decode(cfg, inp, codes, radii, debug=True)
+    kp = wl.top_k // PAGE
+    for s in range(wl.batch):
+        for g in range(wl.num_kv_heads):
+            check_unit(cfg, inp, gpu, codes, radii, s, g)
+            sel = np.sort(gpu["sel"][s, g, :int(gpu["cnt"][s, g])].cpu().numpy())
+            top = sel[(sel >= wl.sinks) & (sel < int(inp["seq_lens"][s]) - wl.window)]
+            assert np.array_equal(top, np.arange(wl.sinks, kp * PAGE))
+
+
+def test_page_selection_short_sequences():
+    wl = workloads.get("small_gqa_b128")
+    cfg = config_of(wl, **PAGES)
+    inp = workloads.make_inputs(wl, DEV)
+    codes, radii = gpu_encode_all(cfg, inp)
+    for lens in ([0, 1], [5, 68], [69, 17], [400, 333]):
+        sl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+        sub = dict(inp, seq_lens=sl, max_seq_len=int(max(lens)))
+        print(f"[case] pages lens={lens}", flush=True)
+        gpu = gpu_decode(cfg, sub, codes, radii, debug=True,
+                         seq_lens=sl, max_seq_len=int(max(lens)))
+        for s in range(2):
+            for g in range(wl.num_kv_heads):
+                if lens[s] == 0:
+                    assert int(gpu["cnt"][s, g]) == 0
+                    continue
+                check_unit(cfg, sub, gpu, codes, radii, s, g)
+
+
+@pytest.mark.parametrize("name,units,over", [
+    ("gqa32x8_bs16_n128k_b128", [(0, 0), (15, 7)], {}),
+    ("gqa32x8_ragged64_4k-128k_b128", [(0, 0), (17, 5), (40, 2)], {}),
+    # more pages than the merge stages in LDS (its global-memory path)
+    ("gqa32x8_bs4_n256k_b256_lognormal", [(1, 2)], dict(radius_weight=dkv.RADIUS_LINEAR)),
+])
+def test_full_size_page_selection(name, units, over):
+    _run(workloads.get(name), units, **PAGES, **over)
+    torch.cuda.empty_cache()
