@@ -47,7 +47,8 @@ __device__ __forceinline__ int row_of(const int32_t *bt, int pos,
   return (blk >= 0 && blk < num_blocks) ? blk * kPage + pos % kPage : -1;
 }
 
-template <int KS, int G>
+// PAGES: the candidates are pages (page-granular selection).
+template <int KS, int G, bool PAGES>
 __global__ __launch_bounds__(kThreads) void merge_kernel(
     const uint2 *__restrict__ cand, const uint32_t *__restrict__ tcount,
     int cand_groups,
@@ -59,7 +60,8 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
     int32_t *__restrict__ user_cnt, const uint32_t *__restrict__ codes,
     const uint8_t *__restrict__ radii, uint32_t code_bytes,
     uint32_t radius_bytes, int W, const uint32_t *__restrict__ qop,
-    const float *__restrict__ qneg, bool lin, bool pages) {
+    const float *__restrict__ qneg, bool lin) {
+  constexpr bool pages = PAGES;
   __shared__ __align__(16) uint2 st[kStage];
   __shared__ uint32_t gpre[kMaxGroupsLds + 1];
   __shared__ SelectShared<kThreads> sel;
@@ -448,16 +450,21 @@ hipError_t launch_merge(const DecodeDims &d, const uint2 *cand,
                         hipStream_t stream) {
   const uint32_t code_bytes = (uint32_t)((uint64_t)d.num_blocks * d.Hkv * d.W * kPage * 4);
   const uint32_t radius_bytes = (uint32_t)((uint64_t)d.num_blocks * d.Hkv * kPage);
-#define DKV_MERGE_CASE(KSV, GV)                                                \
-  if (d.KS == KSV && d.G == GV) {                                              \
-    hipLaunchKernelGGL((merge_kernel<KSV, GV>), dim3(d.B * d.Hkv),             \
+#define DKV_MERGE_LAUNCH(KSV, GV, PV)                                          \
+  {                                                                            \
+    hipLaunchKernelGGL((merge_kernel<KSV, GV, PV>), dim3(d.B * d.Hkv),         \
                        dim3(kThreads), 0, stream, cand, tcount,                \
                        d.cand_groups, seq_lens, d.n_max, block_table,          \
                        d.max_blocks, d.num_blocks, d.Hkv, d.k, d.w, d.sigma,   \
                        d.cap, bitmap, d.bm_words, rows, cnt, user_sel,         \
                        user_cnt, codes, radii, code_bytes, radius_bytes, d.W,  \
-                       qop, qneg, d.lin, d.pages);                             \
+                       qop, qneg, d.lin);                                      \
     return hipGetLastError();                                                  \
+  }
+#define DKV_MERGE_CASE(KSV, GV)                                                \
+  if (d.KS == KSV && d.G == GV) {                                              \
+    if (d.pages) DKV_MERGE_LAUNCH(KSV, GV, true)                               \
+    DKV_MERGE_LAUNCH(KSV, GV, false)                                           \
   }
   DKV_MERGE_CASE(1, 1)
   DKV_MERGE_CASE(1, 2)
@@ -468,6 +475,7 @@ hipError_t launch_merge(const DecodeDims &d, const uint2 *cand,
   DKV_MERGE_CASE(2, 4)
   DKV_MERGE_CASE(2, 8)
 #undef DKV_MERGE_CASE
+#undef DKV_MERGE_LAUNCH
   return hipErrorInvalidValue;
 }
 

@@ -4,13 +4,14 @@
 TEST INFRASTRUCTURE: uses the oracle and the seeded workload generator,
 never the GPU library.
 
-For each radius weight (the log code r8, or the linear rne(2^(r8/16))),
+For each selection granularity (keys, or 16-token pages scored by their best
+key), each radius weight (the log code r8, or the linear rne(2^(r8/16))),
 each code width b in {64, 128, 256} and two key distributions (N(0,1) with
 4 outlier channels x8; log-normal radii, sigma = 0.5), on every KV head of
 one sequence of the 32K-token GQA shape (32 query / 8 KV heads, k = 1024,
 window 256, 4 sinks):
 
-  recall@k   |top-k by the score  ∩  top-k by the exact logit| / k, over
+  recall@k   |selected candidates ∩ top-k by the exact logit| / k, over
              the candidates [sinks, N - window); the exact logit of a key
              for a KV group is the largest q_h.k / sqrt(d) over the group's
              query heads (the same max aggregation the score uses);
@@ -59,19 +60,19 @@ def _logical_rows(pool, bt, s, N, g):
     return pool[blk, pos % workloads.PAGE, g]
 
 
-def needle_recall(wl, q, P, K, V, needles, mode):
+def needle_recall(wl, q, P, K, V, needles, mode, pages):
     codes, radii = oracle.encode_keys(K, P)
     r = oracle.decode_unit(q, P, codes, radii, K, V, wl.top_k, wl.window,
-                           wl.sinks, radius_mode=mode)
+                           wl.sinks, radius_mode=mode, pages=pages)
     return float(np.isin(needles, r["sel"]).mean())
 
 
-def study_unit(wl, q, P, K, V, mode):
+def study_unit(wl, q, P, K, V, mode, pages):
     G, d = q.shape
     N = K.shape[0]
     codes, radii = oracle.encode_keys(K, P)
     r = oracle.decode_unit(q, P, codes, radii, K, V, wl.top_k, wl.window,
-                           wl.sinks, radius_mode=mode)
+                           wl.sinks, radius_mode=mode, pages=pages)
     qf, Kf, Vf = _bf16_to_f64(q), _bf16_to_f64(K), _bf16_to_f64(V)
     logits = qf @ Kf.T / np.sqrt(d)                     # [G][N]
     c0, c1 = wl.sinks, N - wl.window
@@ -100,8 +101,8 @@ def main(argv=None):
         "outliers": dict(outliers=True, lognormal_sigma=0.0),
         "lognormal": dict(outliers=False, lognormal_sigma=0.5),
     }
-    print("| keys | b | weight | recall@k | mass | out err | needles |")
-    print("|---|---|---|---|---|---|---|")
+    print("| keys | b | select | weight | recall@k | mass | out err | needles |")
+    print("|---|---|---|---|---|---|---|---|")
     t0 = time.time()
     def units(wl):
         inp = workloads.make_inputs(wl, "cpu")
@@ -119,13 +120,15 @@ def main(argv=None):
             plain = dataclasses.replace(base, code_bits=b, seq_len=args.seq_len,
                                         needles=0, **dkw)
             with_nd = dataclasses.replace(plain, needles=16)
-            for mode, mname in ((0, "log r8"), (1, "linear")):
-                m = np.array([study_unit(plain, q, P, K, V, mode)
-                              for q, P, K, V, _ in units(plain)]).mean(axis=0)
-                nd = np.mean([needle_recall(with_nd, q, P, K, V, n, mode)
-                              for q, P, K, V, n in units(with_nd)])
-                print(f"| {dname} | {b} | {mname} | {m[0]:.3f} | {m[1]:.3f} | "
-                      f"{m[2]:.3f} | {nd:.3f} |", flush=True)
+            for pages in (False, True):
+                for mode, mname in ((0, "log r8"), (1, "linear")):
+                    m = np.array([study_unit(plain, q, P, K, V, mode, pages)
+                                  for q, P, K, V, _ in units(plain)]).mean(axis=0)
+                    nd = np.mean([needle_recall(with_nd, q, P, K, V, n, mode, pages)
+                                  for q, P, K, V, n in units(with_nd)])
+                    sname = "pages" if pages else "keys"
+                    print(f"| {dname} | {b} | {sname} | {mname} | {m[0]:.3f} | "
+                          f"{m[1]:.3f} | {m[2]:.3f} | {nd:.3f} |", flush=True)
     print(f"\n({time.time() - t0:.0f} s; seq_len {args.seq_len}, "
           f"{args.heads} KV heads per row, seed {base.seed})")
 
