@@ -21,6 +21,8 @@ Parity status of each function (what pins it is listed in the tests):
   select                   pinned (brute-force sort, special cases)
   select_pages             pinned (brute-force page sort, equals select when
                            scores are constant on aligned pages, limits)
+  lsh_bucket, select_lsh   pinned (Python bit extraction and brute-force
+                           candidate sort; all-candidate case equals select)
   attend                   pinned (dense softmax attention special case,
                            single-key and identical-key closed forms)
   decode_unit(s)           composition of the above; whole-pipeline values
@@ -69,11 +71,15 @@ def _load():
     lib.orc_select.restype = i32
     lib.orc_select_pages.argtypes = [P, i32, i32, i32, i32, P]
     lib.orc_select_pages.restype = i32
+    lib.orc_lsh_bucket.argtypes = [P, i32, i32]
+    lib.orc_lsh_bucket.restype = i32
+    lib.orc_select_lsh.argtypes = [P, P, i32, P, i32, i32, i32, i32, i32, i32, i32, P]
+    lib.orc_select_lsh.restype = i32
     lib.orc_attend.argtypes = [P, i32, P, P, i32, P, i32, P]
     lib.orc_attend.restype = None
-    lib.orc_decode_unit.argtypes = [i32] * 8 + [P] * 6 + [i32] + [P] * 4
+    lib.orc_decode_unit.argtypes = [i32] * 10 + [P] * 6 + [i32] + [P] * 4
     lib.orc_decode_unit.restype = i32
-    lib.orc_decode_units.argtypes = [i32] * 9 + [P] * 7 + [i32, P, P, P, i32, P, P]
+    lib.orc_decode_units.argtypes = [i32] * 11 + [P] * 7 + [i32, P, P, P, i32, P, P]
     lib.orc_decode_units.restype = None
     lib.orc_num_threads.argtypes = []
     lib.orc_num_threads.restype = i32
@@ -186,6 +192,27 @@ def select_pages(S: np.ndarray, k: int, w: int, sigma: int) -> np.ndarray:
     return sel[:n].copy()
 
 
+def lsh_bucket(code: np.ndarray, t: int, m: int) -> int:
+    """H1: bucket of code (uint32 [W]) in table t of m bits."""
+    code = _c(code, np.uint32)
+    return int(_load().orc_lsh_bucket(_p(code), int(t), int(m)))
+
+
+def select_lsh(S: np.ndarray, codes: np.ndarray, qbits: np.ndarray, T: int, m: int,
+               k: int, w: int, sigma: int) -> np.ndarray:
+    """T3 over scores S [N], codes [N][W], query bits [G][W] -> positions."""
+    S = _c(S, np.int32)
+    codes = _c(codes, np.uint32)
+    qbits = _c(qbits, np.uint32)
+    N, W = codes.shape
+    G = qbits.shape[0]
+    cap = max(1, min(N, sigma + w + k))
+    sel = np.full(cap, -1, np.int32)
+    n = _load().orc_select_lsh(_p(S), _p(codes), W, _p(qbits), G, T, m, N, k, w, sigma,
+                               _p(sel))
+    return sel[:n].copy()
+
+
 def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, sel: np.ndarray) -> np.ndarray:
     """A1: q [G][d], K/V [N][d] (bf16 bits), sel positions -> fp64 [G][d]."""
     q = _c(q, np.uint16)
@@ -199,7 +226,7 @@ def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, sel: np.ndarray) -> np.n
 
 
 def decode_unit(q, P, codes, radii, K, V, k: int, w: int, sigma: int,
-                radius_mode: int = 0, pages: bool = False):
+                radius_mode: int = 0, pages: bool = False, lsh=(0, 0)):
     """One (sequence, KV head) decode step.
 
     q [G][d]; P [d][b]; codes [N][b/32]; radii [N]; K, V [N][d] (logical
@@ -218,7 +245,8 @@ def decode_unit(q, P, codes, radii, K, V, k: int, w: int, sigma: int,
     cap = max(1, min(N, sigma + w + k))
     sel = np.full(cap, -1, np.int32)
     out = np.zeros((G, d), np.float64)
-    n = _load().orc_decode_unit(G, d, b, k, w, sigma, radius_mode, int(pages), _p(q), _p(P),
+    n = _load().orc_decode_unit(G, d, b, k, w, sigma, radius_mode, int(pages),
+                                int(lsh[0]), int(lsh[1]), _p(q), _p(P),
                                 _p(codes),
                                 _p(radii), _p(K), _p(V), N, _p(q8), _p(S),
                                 _p(sel), _p(out))
@@ -226,7 +254,8 @@ def decode_unit(q, P, codes, radii, K, V, k: int, w: int, sigma: int,
 
 
 def decode_units(q, P, codes, radii, K, V, N, k: int, w: int, sigma: int,
-                 want_scores: bool = True, radius_mode: int = 0, pages: bool = False):
+                 want_scores: bool = True, radius_mode: int = 0, pages: bool = False,
+                 lsh=(0, 0)):
     """Many units at once (OpenMP over units).
 
     q [U][G][d]; codes [U][Nmax][b/32]; radii [U][Nmax]; K, V [U][Nmax][d];
@@ -248,7 +277,8 @@ def decode_units(q, P, codes, radii, K, V, N, k: int, w: int, sigma: int,
     sel = np.full((U, cap), -1, np.int32)
     cnt = np.zeros(U, np.int32)
     out = np.zeros((U, G, d), np.float64)
-    _load().orc_decode_units(U, G, d, b, k, w, sigma, radius_mode, int(pages), _p(q), _p(P),
+    _load().orc_decode_units(U, G, d, b, k, w, sigma, radius_mode, int(pages),
+                             int(lsh[0]), int(lsh[1]), _p(q), _p(P),
                              _p(codes),
                              _p(radii), _p(K), _p(V), _p(N), Nmax, _p(q8),
                              _p(S) if S is not None else None, _p(sel), cap,

@@ -294,6 +294,63 @@ ORC_EXPORT int orc_select_pages(const int32_t *S, int N, int k, int w,
 }
 
 /* ---------------------------------------------------------------------- */
+/* H1 -- bucket of a code in LSH table t.  [DASH, "from quadratic to
+ * linear"]: several hash tables split the vector space into regions, so
+ * that similar vectors land in the same bucket.  The code bits are already
+ * signs of random projections (SimHash), so table t takes m of them: code
+ * bits t*m .. t*m+m-1, bit t*m+i giving bit i of the bucket number. */
+ORC_EXPORT int orc_lsh_bucket(const uint32_t *code, int t, int m) {
+  int v = 0;
+  for (int i = 0; i < m; ++i) {
+    int j = t * m + i;
+    v |= (int)((code[j / 32] >> (j % 32)) & 1u) << i;
+  }
+  return v;
+}
+
+/* T3 -- selection over the LSH candidates.  [DASH, "from quadratic to
+ * linear"]: a new query computes its hash, looks only in its buckets for
+ * candidate keys, and the candidates are pruned to the top-k that enter
+ * exact attention.  Reading: the query's hash in table t is built from the
+ * signs of its own projection on the same columns (qbits: the E1 code of
+ * the query row, one per query head of the group); a key in [sigma, N-w)
+ * is a candidate when, for some table and some head, its bucket equals the
+ * head's; the min(k, candidates) best candidates by (S descending,
+ * position ascending) join the sinks and the window.  codes: [N][W];
+ * qbits: [G][W].  Returns the count. */
+ORC_EXPORT int orc_select_lsh(const int32_t *S, const uint32_t *codes, int W,
+                              const uint32_t *qbits, int G, int T, int m,
+                              int N, int k, int w, int sigma, int32_t *sel) {
+  int n = 0;
+  int ns = sigma < N ? sigma : N;
+  for (int i = 0; i < ns; ++i) sel[n++] = i;
+  int ws = (N - w > ns) ? N - w : ns;
+  for (int i = ws; i < N; ++i) sel[n++] = i;
+  int c0 = sigma, c1 = N - w;
+  if (c1 <= c0) return n;
+  orc_cand *c = (orc_cand *)malloc(sizeof(orc_cand) * (size_t)(c1 - c0));
+  int nc = 0;
+  for (int i = c0; i < c1; ++i) {
+    int hit = 0;
+    for (int t = 0; t < T && !hit; ++t) {
+      int kb = orc_lsh_bucket(codes + (size_t)i * W, t, m);
+      for (int h = 0; h < G && !hit; ++h)
+        hit = kb == orc_lsh_bucket(qbits + (size_t)h * W, t, m);
+    }
+    if (hit) {
+      c[nc].score = S[i];
+      c[nc].pos = i;
+      ++nc;
+    }
+  }
+  qsort(c, (size_t)nc, sizeof(orc_cand), orc_cand_cmp);
+  int keff = k < nc ? k : nc;
+  for (int i = 0; i < keff; ++i) sel[n++] = c[i].pos;
+  free(c);
+  return n;
+}
+
+/* ---------------------------------------------------------------------- */
 /* A1 -- exact attention over the selected keys.  [DYS, item 1]:
  * softmax(QK^T / sqrt(d)); [DSA]: the real attention runs only over the
  * selected history.  In double precision: l_t = (q.k_t)/sqrt(d),
@@ -331,12 +388,14 @@ ORC_EXPORT void orc_attend(const uint16_t *q, int G, const uint16_t *K,
 /* ---------------------------------------------------------------------- */
 /* One decode step for one (sequence, KV head) unit: Q1, S1 (with the W1
  * weight of radius_mode) for every cached key, T1 (or T2 when select_pages
- * is non-zero), A1.  q: [G][d] (the
+ * is non-zero, or T3 over lsh_tables tables of lsh_bits bits when
+ * lsh_tables > 0), A1.  q: [G][d] (the
  * group's query heads); codes [N][b/32]; radii [N]; K, V: [N][d] in logical
  * token order.  scores (length N) may be NULL.  sel must hold
  * min(N, sigma+w+k) entries.  Returns the count. */
 ORC_EXPORT int orc_decode_unit(int G, int d, int b, int k, int w, int sigma,
                                int radius_mode, int select_pages,
+                               int lsh_tables, int lsh_bits,
                                const uint16_t *q, const uint16_t *P,
                                const uint32_t *codes, const uint8_t *radii,
                                const uint16_t *K, const uint16_t *V, int N,
@@ -348,8 +407,18 @@ ORC_EXPORT int orc_decode_unit(int G, int d, int b, int k, int w, int sigma,
   for (int i = 0; i < N; ++i)
     S[i] = orc_score(q8, G, b, codes + (size_t)i * (b / 32),
                      orc_radius_weight(radii[i], radius_mode));
-  int n = select_pages ? orc_select_pages(S, N, k, w, sigma, sel)
-                       : orc_select(S, N, k, w, sigma, sel);
+  int n;
+  if (lsh_tables > 0) {
+    uint32_t *qbits = (uint32_t *)malloc(sizeof(uint32_t) * (size_t)G * (b / 32));
+    for (int h = 0; h < G; ++h)
+      orc_key_code(q + (size_t)h * d, P, d, b, qbits + (size_t)h * (b / 32));
+    n = orc_select_lsh(S, codes, b / 32, qbits, G, lsh_tables, lsh_bits, N, k, w,
+                       sigma, sel);
+    free(qbits);
+  } else {
+    n = select_pages ? orc_select_pages(S, N, k, w, sigma, sel)
+                     : orc_select(S, N, k, w, sigma, sel);
+  }
   orc_attend(q, G, K, V, d, sel, n, out);
   if (!scores) free(S);
   return n;
@@ -362,7 +431,7 @@ ORC_EXPORT int orc_decode_unit(int G, int d, int b, int k, int w, int sigma,
  *   sel_cnt [U], out [U][G][d]. */
 ORC_EXPORT void orc_decode_units(int U, int G, int d, int b, int k, int w,
                                  int sigma, int radius_mode, int select_pages,
-                                 const uint16_t *q,
+                                 int lsh_tables, int lsh_bits, const uint16_t *q,
                                  const uint16_t *P, const uint32_t *codes,
                                  const uint8_t *radii, const uint16_t *K,
                                  const uint16_t *V, const int32_t *N, int Nmax,
@@ -372,7 +441,8 @@ ORC_EXPORT void orc_decode_units(int U, int G, int d, int b, int k, int w,
   for (int u = 0; u < U; ++u) {
     size_t tok = (size_t)u * (size_t)Nmax;
     sel_cnt[u] = orc_decode_unit(
-        G, d, b, k, w, sigma, radius_mode, select_pages, q + (size_t)u * G * d, P,
+        G, d, b, k, w, sigma, radius_mode, select_pages, lsh_tables, lsh_bits,
+        q + (size_t)u * G * d, P,
         codes + tok * (b / 32), radii + tok, K + tok * d, V + tok * d, N[u],
         q8 + (size_t)u * G * b, scores ? scores + tok : NULL,
         sel + (size_t)u * sel_cap, out + (size_t)u * G * d);

@@ -113,3 +113,23 @@ def brute_select_pages(S, k, w, sigma, page=16):
     for p in ranked[:max(0, k // page)]:
         top += pages[p]
     return sinks, window, top
+
+
+def brute_lsh_bucket(code, t, m):
+    """Bits t*m .. t*m+m-1 of a code (uint32 words), by Python integers."""
+    big = 0
+    for i, wd in enumerate(code):
+        big |= int(wd) << (32 * i)
+    return (big >> (t * m)) & ((1 << m) - 1)
+
+
+def brute_select_lsh(S, codes, qbits, T, m, k, w, sigma):
+    """Sinks, window and the top-k of the LSH candidates (Python sort)."""
+    N = len(S)
+    sinks = list(range(min(sigma, N)))
+    window = list(range(max(min(sigma, N), N - w), N))
+    cand = [i for i in range(sigma, N - w)
+            if any(brute_lsh_bucket(codes[i], t, m) == brute_lsh_bucket(qb, t, m)
+                   for t in range(T) for qb in qbits)]
+    cand.sort(key=lambda i: (-int(S[i]), i))
+    return sinks, window, cand[:max(0, k)]

@@ -14,8 +14,8 @@ import pytest
 import torch
 
 import oracle
-from exact import (bf16_fraction, brute_score, brute_select, brute_select_pages,
-                   exact_projection,
+from exact import (bf16_fraction, brute_lsh_bucket, brute_score, brute_select,
+                   brute_select_lsh, brute_select_pages, exact_projection,
                    exact_query_int8, exact_radius_code, exact_sign_code)
 from helpers import bf16_bits, bits_to_float
 
@@ -389,6 +389,53 @@ def test_select_pages_limits():
     # equal page scores: the lowest page wins
     got = oracle.select_pages(np.zeros(1000, np.int32), 16, 10, 4)[14:]
     assert list(got) == list(range(4, 16))
+
+
+# ------------------------------------------------------- H1/T3 LSH buckets
+def test_lsh_bucket_matches_bit_extraction():
+    rng = np.random.default_rng(21)
+    for W in (2, 4, 8):
+        for _ in range(20):
+            code = rng.integers(0, 2 ** 32, size=W, dtype=np.uint64).astype(np.uint32)
+            for m in (1, 3, 8, 12):
+                for t in range(min(4, 32 * W // m)):
+                    assert oracle.lsh_bucket(code, t, m) == brute_lsh_bucket(code, t, m)
+
+
+@pytest.mark.parametrize("T,m,G", [(4, 3, 1), (6, 4, 4), (2, 8, 2), (10, 12, 4)])
+def test_select_lsh_matches_brute_force(T, m, G):
+    rng = np.random.default_rng(T * 100 + m)
+    W = 4
+    N, k, w, sigma = 700, 40, 30, 5
+    S = rng.integers(-30, 30, size=N).astype(np.int32)
+    codes = rng.integers(0, 2 ** 32, size=(N, W), dtype=np.uint64).astype(np.uint32)
+    qbits = rng.integers(0, 2 ** 32, size=(G, W), dtype=np.uint64).astype(np.uint32)
+    got = oracle.select_lsh(S, codes, qbits, T, m, k, w, sigma)
+    sinks, window, top = brute_select_lsh(S, codes, qbits, T, m, k, w, sigma)
+    assert list(got) == sinks + window + top
+
+
+def test_select_lsh_all_candidates_equals_select():
+    """Every key shares table 0's bucket with the query: the candidates are
+    the whole range and T3 is T1."""
+    rng = np.random.default_rng(22)
+    N, W = 500, 4
+    S = rng.integers(-20, 20, size=N).astype(np.int32)
+    codes = rng.integers(0, 2 ** 32, size=(N, W), dtype=np.uint64).astype(np.uint32)
+    qbits = rng.integers(0, 2 ** 32, size=(1, W), dtype=np.uint64).astype(np.uint32)
+    codes[:, 0] = (codes[:, 0] & ~np.uint32(0xFF)) | (qbits[0, 0] & np.uint32(0xFF))
+    for k in (0, 17, 300, 1000):
+        assert list(oracle.select_lsh(S, codes, qbits, 3, 8, k, 20, 4)) == \
+            list(oracle.select(S, k, 20, 4))
+
+
+def test_select_lsh_no_candidates():
+    N, W = 300, 4
+    S = np.arange(N, dtype=np.int32)
+    codes = np.zeros((N, W), np.uint32)
+    qbits = np.full((2, W), 0xFFFFFFFF, np.uint32)
+    got = oracle.select_lsh(S, codes, qbits, 5, 6, 64, 10, 4)
+    assert list(got) == list(range(4)) + list(range(290, 300))
 
 
 # ---------------------------------------------------------------- A1 attend

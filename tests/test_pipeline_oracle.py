@@ -61,6 +61,25 @@ def test_pipeline_dense_limit_equals_sdpa():
         break
 
 
+def test_decode_unit_lsh_is_the_composition():
+    """With LSH tables: query bits are the E1 code of each query row, the
+    selection is T3 over the scores."""
+    for wl, s, g, q, P, K, V, _ in _units("small_gqa_b128"):
+        codes, radii = oracle.encode_keys(K, P)
+        for lsh in [(8, 6), (4, 10)]:
+            r = oracle.decode_unit(q, P, codes, radii, K, V, wl.top_k, wl.window, wl.sinks,
+                                   radius_mode=1, lsh=lsh)
+            qbits = np.stack([oracle.key_code(q[h], P) for h in range(q.shape[0])])
+            S = oracle.scores(oracle.query_int8(q, P), codes, radii, radius_mode=1)
+            sel = oracle.select_lsh(S, codes, qbits, lsh[0], lsh[1], wl.top_k, wl.window,
+                                    wl.sinks)
+            assert np.array_equal(r["scores"], S)
+            assert np.array_equal(r["sel"], sel)
+            assert np.array_equal(r["out"], oracle.attend(q, K, V, sel))
+        if s >= 1:
+            break
+
+
 @pytest.mark.parametrize("mode,pages", [(0, False), (1, False), (0, True), (1, True)])
 def test_decode_unit_is_the_composition(mode, pages):
     for wl, s, g, q, P, K, V, _ in _units("small_ragged_b128"):
