@@ -113,7 +113,7 @@ def counter_traffic(kernel_src_digest: str, workload: str):
 
 
 def cpu_baseline(wl, inp, units: int, seconds: float, radius_mode: int = 0,
-                 pages: bool = False) -> dict:
+                 pages: bool = False, lsh=(0, 0)) -> dict:
     """The CPU oracle (as it stands) on a bounded sample of the workload."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import numpy as np
@@ -148,7 +148,7 @@ def cpu_baseline(wl, inp, units: int, seconds: float, radius_mode: int = 0,
     while True:
         oracle.decode_units(q, P, codes, radii, K, V, N, wl.top_k, wl.window,
                             wl.sinks, want_scores=False, radius_mode=radius_mode,
-                            pages=pages)
+                            pages=pages, lsh=lsh)
         reps += 1
         dt = time.perf_counter() - t0
         if dt >= seconds or reps >= 100000:
@@ -176,6 +176,9 @@ def main():
     ap.add_argument("--select", choices=("keys", "pages"), default="keys",
                     help="select the top_k keys, or the top top_k/16 pages "
                          "(each scored by its best candidate key)")
+    ap.add_argument("--lsh", default="",
+                    help="T,m: select among multi-table LSH candidates (T tables "
+                         "of m code bits; the index is built before timing)")
     ap.add_argument("--radius-weight", choices=("log", "linear"), default="log",
                     help="score weight of the radius code: the code r8 itself "
                          "(log) or rne(2^(r8/16)) (linear)")
@@ -202,7 +205,9 @@ def main():
                      sinks=wl.sinks,
                      radius_weight=(dkv.RADIUS_LINEAR if args.radius_weight == "linear"
                                     else dkv.RADIUS_LOG),
-                     select_pages=args.select == "pages")
+                     select_pages=args.select == "pages",
+                     lsh_tables=int(args.lsh.split(",")[0]) if args.lsh else 0,
+                     lsh_bits=int(args.lsh.split(",")[1]) if args.lsh else 0)
     print(f"[bench] drawing {wl.name}", file=sys.stderr, flush=True)
     inp = workloads.make_inputs(wl, "cuda")
     B, Hkv = wl.batch, wl.num_kv_heads
@@ -217,6 +222,15 @@ def main():
     ws = torch.empty(dkv.decode_workspace_size(cfg, B, max_len), dtype=torch.uint8,
                      device=dev)
     out = torch.empty((B, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device=dev)
+    index = None
+    if cfg.lsh_tables > 0:
+        # the bucket index of the cached prefix (untimed, like the encode);
+        # each step's newest key is past it and is tested from its code
+        index = torch.empty(dkv.lsh_index_size(cfg, B, max_len), dtype=torch.uint8,
+                            device=dev)
+        dkv.lsh_build(cfg, codes, inp["block_table"],
+                      torch.clamp(inp["seq_lens"] - 1, min=0).to(torch.int32), max_len,
+                      index)
     torch.cuda.synchronize()
     print("[bench] prefix encoded", file=sys.stderr, flush=True)
 
@@ -230,6 +244,11 @@ def main():
         """One decode step: dkv_decode_append encodes the newest key of every
         sequence and runs the step.  With evs, HIP events bracket every
         stage."""
+        if index is not None:
+            dkv.decode_lsh(cfg, inp["q"], inp["k_pool"], inp["v_pool"], codes, radii,
+                           inp["block_table"], inp["seq_lens"], max_len, inp["proj"],
+                           index, out, ws, events=evs, stream=stream)
+            return
         dkv.decode_append(cfg, inp["q"], inp["k_pool"], inp["v_pool"], codes, radii,
                           inp["block_table"], inp["seq_lens"], max_len, inp["proj"],
                           out, ws, events=evs, stream=stream)
@@ -308,7 +327,8 @@ def main():
                            "internal.h")]
     # the counters were taken for the key-selecting, log-weight kernel
     traffic = (counter_traffic(source_digest(score_src), wl.name)
-               if args.radius_weight == "log" and args.select == "keys" else None)
+               if args.radius_weight == "log" and args.select == "keys" and not args.lsh
+               else None)
     roofline = {"bound": "hbm", "kernel": "score",
                 "achieved": ab["score"] / score_s / 1e9, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": ab["score"] / score_s / 1e9 / HBM_PEAK_GBS,
@@ -332,7 +352,7 @@ def main():
                    "q_heads": wl.num_q_heads, "kv_heads": Hkv, "head_dim": wl.head_dim,
                    "code_bits": wl.code_bits, "top_k": wl.top_k, "window": wl.window,
                    "sinks": wl.sinks, "page": PAGE, "radius_weight": args.radius_weight,
-                   "select": args.select,
+                   "select": args.select, "lsh": args.lsh or None,
                    "parallelism": "single GPU"},
         "latency_us": ms_per_step * 1e3,
         "gpu_step_us": gpu_ms * 1e3,
@@ -347,7 +367,8 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_units, args.cpu_seconds,
-                                              cfg.radius_weight, cfg.select_pages)
+                                              cfg.radius_weight, cfg.select_pages,
+                                              (cfg.lsh_tables, cfg.lsh_bits))
     print(json.dumps(result), flush=True)
 
 

@@ -31,8 +31,9 @@ _lib = None
 EXPORTED_SYMBOLS = ("dkv_encode", "dkv_decode_workspace_size", "dkv_decode",
                     "dkv_decode_debug", "dkv_decode_profiled", "dkv_decode_append",
                     "dkv_decode_num_stages", "dkv_decode_stage_name",
-                    "dkv_status_string", "dkv_abi_version")
-ABI_VERSION = 4
+                    "dkv_status_string", "dkv_abi_version", "dkv_lsh_index_size",
+                    "dkv_lsh_build", "dkv_decode_lsh")
+ABI_VERSION = 5
 RADIUS_LOG = 0
 RADIUS_LINEAR = 1
 
@@ -49,7 +50,8 @@ class DkvError(RuntimeError):
 class _CConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "head_dim", "num_q_heads", "num_kv_heads", "code_bits", "page_size",
-        "top_k", "window", "sinks", "radius_weight", "select_pages")]
+        "top_k", "window", "sinks", "radius_weight", "select_pages", "lsh_tables",
+        "lsh_bits")]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -68,11 +70,16 @@ class Config:
     # select the top top_k/16 pages (scored by their best candidate key)
     # instead of the top_k keys
     select_pages: bool = False
+    # multi-table LSH candidates (decode with decode_lsh): tables and bits
+    # per table (0 tables: none)
+    lsh_tables: int = 0
+    lsh_bits: int = 0
 
     def _c(self) -> _CConfig:
         return _CConfig(self.head_dim, self.num_q_heads, self.num_kv_heads,
                         self.code_bits, self.page_size, self.top_k, self.window,
-                        self.sinks, self.radius_weight, int(self.select_pages))
+                        self.sinks, self.radius_weight, int(self.select_pages),
+                        self.lsh_tables, self.lsh_bits)
 
     @property
     def group(self) -> int:
@@ -112,6 +119,12 @@ def load_library():
     lib.dkv_decode_profiled.restype = ctypes.c_int
     lib.dkv_decode_append.argtypes = dec + [P, P]
     lib.dkv_decode_append.restype = ctypes.c_int
+    lib.dkv_lsh_index_size.argtypes = [cfgp, i32, i32]
+    lib.dkv_lsh_index_size.restype = sz
+    lib.dkv_lsh_build.argtypes = [cfgp, P, i64, P, i32, i32, P, i32, P, sz, P]
+    lib.dkv_lsh_build.restype = ctypes.c_int
+    lib.dkv_decode_lsh.argtypes = dec[:13] + [P, sz] + dec[13:] + [P, P]
+    lib.dkv_decode_lsh.restype = ctypes.c_int
     lib.dkv_decode_num_stages.argtypes = []
     lib.dkv_decode_num_stages.restype = i32
     lib.dkv_decode_stage_name.argtypes = [i32]
@@ -271,6 +284,58 @@ def decode_append(cfg: Config, q, k_pool, v_pool, codes, radii, block_table,
                            seq_lens, max_seq_len, proj, out, workspace, sel_idx,
                            sel_cnt)
     _check(lib.dkv_decode_append(
+        *args, ctypes.cast(arr, ctypes.c_void_p) if arr is not None else None,
+        _stream(stream)))
+
+
+def lsh_index_size(cfg: Config, batch: int, max_seq_len: int) -> int:
+    """Bytes of the LSH index (dkv_lsh_index_size)."""
+    lib = load_library()
+    c = cfg._c()
+    n = lib.dkv_lsh_index_size(ctypes.byref(c), int(batch), int(max_seq_len))
+    if n == 0:
+        raise DkvError(1, "invalid configuration for an LSH index")
+    return int(n)
+
+
+def lsh_build(cfg: Config, codes, block_table, seq_lens, max_seq_len: int, index,
+              stream=None) -> None:
+    """dkv_lsh_build: bucket index of positions [0, seq_lens) of every sequence."""
+    lib = load_library()
+    nb = codes.shape[0]
+    B, max_blocks = block_table.shape
+    _expect(codes, "codes", (nb, cfg.num_kv_heads, cfg.page_size, cfg.code_bits // 32))
+    _expect(seq_lens, "seq_lens", (B,))
+    if index.dtype not in (torch.uint8, torch.int8):
+        raise TypeError("index must be a uint8/int8 tensor")
+    c = cfg._c()
+    _check(lib.dkv_lsh_build(
+        ctypes.byref(c), _ptr(codes, "codes", _U32), nb,
+        _ptr(block_table, "block_table", _I32), max_blocks, B,
+        _ptr(seq_lens, "seq_lens", _I32), int(max_seq_len),
+        _ptr(index, "index", (torch.uint8, torch.int8)), index.numel(), _stream(stream)))
+
+
+def decode_lsh(cfg: Config, q, k_pool, v_pool, codes, radii, block_table, seq_lens,
+               max_seq_len: int, proj, index, out, workspace, sel_idx=None,
+               sel_cnt=None, events=None, stream=None) -> None:
+    """dkv_decode_lsh: one decode step whose top-k runs over the LSH
+    candidates found through ``index`` (built by lsh_build)."""
+    lib = load_library()
+    arr = None
+    if events is not None:
+        n = lib.dkv_decode_num_stages()
+        if len(events) < n + 1:
+            raise ValueError(f"need {n + 1} events, got {len(events)}")
+        arr = (ctypes.c_void_p * len(events))(*events)
+    c, args = _decode_args(cfg, q, k_pool, v_pool, codes, radii, block_table,
+                           seq_lens, max_seq_len, proj, out, workspace, sel_idx,
+                           sel_cnt)
+    if index.dtype not in (torch.uint8, torch.int8):
+        raise TypeError("index must be a uint8/int8 tensor")
+    args = args[:13] + [_ptr(index, "index", (torch.uint8, torch.int8)), index.numel()] + \
+        args[13:]
+    _check(lib.dkv_decode_lsh(
         *args, ctypes.cast(arr, ctypes.c_void_p) if arr is not None else None,
         _stream(stream)))
 

@@ -38,7 +38,10 @@ bool valid_config(const dkv_config *cfg, dkv_status *why) {
       cfg->num_kv_heads > 4096 ||
       !(cfg->radius_weight == DKV_RADIUS_LOG ||
         cfg->radius_weight == DKV_RADIUS_LINEAR) ||
-      !(cfg->select_pages == 0 || cfg->select_pages == 1)) {
+      !(cfg->select_pages == 0 || cfg->select_pages == 1) || cfg->lsh_tables < 0 ||
+      (cfg->lsh_tables > 0 &&
+       (cfg->lsh_bits < 1 || cfg->lsh_bits > 12 || cfg->select_pages != 0 ||
+        (int64_t)cfg->lsh_tables * cfg->lsh_bits > cfg->code_bits))) {
     *why = DKV_ERR_UNSUPPORTED;
     return false;
   }
@@ -70,6 +73,8 @@ bool make_dims(const dkv_config *cfg, int32_t batch, int32_t max_seq_len,
   d->sigma = cfg->sinks;
   d->lin = cfg->radius_weight == DKV_RADIUS_LINEAR;
   d->pages = cfg->select_pages == 1;
+  d->lsh_T = cfg->lsh_tables;
+  d->lsh_m = cfg->lsh_tables > 0 ? cfg->lsh_bits : 0;
   d->cap = d->k + d->w + d->sigma;
   d->max_seq_len = max_seq_len;
   const int64_t by_blocks = (int64_t)kPage * max_blocks;
@@ -106,6 +111,7 @@ dkv_status decode_impl(const dkv_config *cfg, const void *q,
                        float *out, int32_t *sel_idx, int32_t *sel_cnt,
                        void *workspace, size_t workspace_bytes, int8_t *q8_out,
                        int32_t *scores_out, dkv_event_t *events, bool append,
+                       const void *lsh_index, size_t lsh_index_bytes,
                        hipStream_t stream) {
   DecodeDims d;
   dkv_status why = DKV_OK;
@@ -120,6 +126,15 @@ dkv_status decode_impl(const dkv_config *cfg, const void *q,
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) ||
       !aligned16(codes) || !aligned16(radii) || !aligned16(proj))
     return DKV_ERR_INVALID_ARG;
+  // an LSH config decodes through its index, and only then
+  if ((d.lsh_T > 0) != (lsh_index != nullptr)) return DKV_ERR_INVALID_ARG;
+  if (d.lsh_T > 0) {
+    if (max_seq_len > DKV_LSH_MAX_SEQ_LEN) return DKV_ERR_UNSUPPORTED;
+    const size_t need = (size_t)d.B * d.Hkv *
+                        lsh_layout(d.lsh_T, d.lsh_m, d.max_seq_len).unit_bytes;
+    if (lsh_index_bytes < need || ((uintptr_t)lsh_index & 255) != 0)
+      return DKV_ERR_WORKSPACE;
+  }
   const WorkspacePlan plan = plan_workspace(d);
   if (workspace == nullptr || workspace_bytes < plan.total ||
       ((uintptr_t)workspace & 255) != 0)
@@ -136,6 +151,7 @@ dkv_status decode_impl(const dkv_config *cfg, const void *q,
   int32_t *rows = reinterpret_cast<int32_t *>(ws + plan.rows);
   int32_t *cnt = reinterpret_cast<int32_t *>(ws + plan.cnt);
   float *part = reinterpret_cast<float *>(ws + plan.part);
+  uint32_t *qbits = d.lsh_T > 0 ? reinterpret_cast<uint32_t *>(ws + plan.qbits) : nullptr;
   const uint16_t *q16 = static_cast<const uint16_t *>(q);
   const uint16_t *k16 = static_cast<const uint16_t *>(k_pool);
   const uint16_t *v16 = static_cast<const uint16_t *>(v_pool);
@@ -153,13 +169,23 @@ dkv_status decode_impl(const dkv_config *cfg, const void *q,
   uint32_t *codes_w = append ? const_cast<uint32_t *>(codes) : nullptr;
   uint8_t *radii_w = append ? const_cast<uint8_t *>(radii) : nullptr;
   if (!mark() || launch_prep(d, q16, p16, codes, radii, k16, codes_w, radii_w,
-                             block_table, seq_lens, q8, qop, qneg, lthr,
+                             block_table, seq_lens, q8, qop, qneg, lthr, qbits,
                              stream) != hipSuccess)
     return DKV_ERR_LAUNCH;
-  if (!mark() || launch_score(d, codes, radii, block_table, seq_lens, qop, qneg,
-                              lthr, cand, tcount, scores_out, stream) !=
-                     hipSuccess)
+  if (d.lsh_T > 0) {
+    // bucket probe, then scoring of the pages that hold candidates
+    if (!mark() ||
+        launch_lsh_probe(d, codes, block_table, seq_lens,
+                         static_cast<const char *>(lsh_index), qbits, bitmap,
+                         stream) != hipSuccess ||
+        launch_lsh_score(d, codes, radii, block_table, seq_lens, qop, qneg, bitmap,
+                         cand, tcount, stream) != hipSuccess)
+      return DKV_ERR_LAUNCH;
+  } else if (!mark() || launch_score(d, codes, radii, block_table, seq_lens, qop,
+                                     qneg, lthr, cand, tcount, scores_out,
+                                     stream) != hipSuccess) {
     return DKV_ERR_LAUNCH;
+  }
   if (!mark() || launch_merge(d, cand, tcount, seq_lens,
                               block_table, bitmap, rows, cnt, sel_idx, sel_cnt,
                               codes, radii, qop, qneg, stream) != hipSuccess)
@@ -213,6 +239,8 @@ WorkspacePlan plan_workspace(const DecodeDims &d) {
   off += align256(units * 4);
   p.part = off;
   off += align256(units * d.nsplit * d.G * (kHeadDim + 2) * 4);
+  p.qbits = off;
+  off += align256((size_t)d.B * d.Hq * d.W * 4);
   p.total = off;
   return p;
 }
@@ -269,7 +297,7 @@ dkv_decode(const dkv_config *cfg, const void *q, const void *k_pool,
   return decode_impl(cfg, q, k_pool, v_pool, codes, radii, num_blocks,
                      block_table, max_blocks_per_seq, seq_lens, batch,
                      max_seq_len, proj, out, sel_idx, sel_cnt, workspace,
-                     workspace_bytes, nullptr, nullptr, nullptr, false,
+                     workspace_bytes, nullptr, nullptr, nullptr, false, nullptr, 0,
                      reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -284,7 +312,7 @@ __attribute__((visibility("default"))) dkv_status dkv_decode_debug(
   return decode_impl(cfg, q, k_pool, v_pool, codes, radii, num_blocks,
                      block_table, max_blocks_per_seq, seq_lens, batch,
                      max_seq_len, proj, out, sel_idx, sel_cnt, workspace,
-                     workspace_bytes, q8_out, scores_out, nullptr, false,
+                     workspace_bytes, q8_out, scores_out, nullptr, false, nullptr, 0,
                      reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -302,7 +330,7 @@ __attribute__((visibility("default"))) dkv_status dkv_decode_profiled(
   return decode_impl(cfg, q, k_pool, v_pool, codes, radii, num_blocks,
                      block_table, max_blocks_per_seq, seq_lens, batch,
                      max_seq_len, proj, out, sel_idx, sel_cnt, workspace,
-                     workspace_bytes, nullptr, nullptr, stage_events, false,
+                     workspace_bytes, nullptr, nullptr, stage_events, false, nullptr, 0,
                      reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -320,7 +348,60 @@ __attribute__((visibility("default"))) dkv_status dkv_decode_append(
   return decode_impl(cfg, q, k_pool, v_pool, codes, radii, num_blocks,
                      block_table, max_blocks_per_seq, seq_lens, batch,
                      max_seq_len, proj, out, sel_idx, sel_cnt, workspace,
-                     workspace_bytes, nullptr, nullptr, stage_events, true,
+                     workspace_bytes, nullptr, nullptr, stage_events, true, nullptr, 0,
+                     reinterpret_cast<hipStream_t>(stream));
+}
+
+__attribute__((visibility("default"))) size_t
+dkv_lsh_index_size(const dkv_config *cfg, int32_t batch, int32_t max_seq_len) {
+  DecodeDims d;
+  dkv_status why;
+  const int32_t max_blocks = (max_seq_len + kPage - 1) / kPage;
+  if (!make_dims(cfg, batch, max_seq_len, max_blocks, 1, &d, &why) || d.lsh_T == 0 ||
+      max_seq_len > DKV_LSH_MAX_SEQ_LEN)
+    return 0;
+  return (size_t)d.B * d.Hkv * lsh_layout(d.lsh_T, d.lsh_m, max_seq_len).unit_bytes;
+}
+
+__attribute__((visibility("default"))) dkv_status
+dkv_lsh_build(const dkv_config *cfg, const uint32_t *codes, int64_t num_blocks,
+              const int32_t *block_table, int32_t max_blocks_per_seq, int32_t batch,
+              const int32_t *seq_lens, int32_t max_seq_len, void *index,
+              size_t index_bytes, dkv_stream_t stream) {
+  DecodeDims d;
+  dkv_status why = DKV_OK;
+  if (!make_dims(cfg, batch, max_seq_len, max_blocks_per_seq, num_blocks, &d, &why))
+    return why;
+  if (codes == nullptr || block_table == nullptr || seq_lens == nullptr ||
+      max_blocks_per_seq <= 0 || num_blocks <= 0 || d.lsh_T == 0 || !aligned16(codes))
+    return DKV_ERR_INVALID_ARG;
+  if (max_seq_len > DKV_LSH_MAX_SEQ_LEN) return DKV_ERR_UNSUPPORTED;
+  const size_t need = (size_t)d.B * d.Hkv *
+                      lsh_layout(d.lsh_T, d.lsh_m, d.max_seq_len).unit_bytes;
+  if (index == nullptr || index_bytes < need || ((uintptr_t)index & 255) != 0)
+    return DKV_ERR_WORKSPACE;
+  return launch_lsh_build(d, codes, block_table, seq_lens, static_cast<char *>(index),
+                          reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+             ? DKV_OK
+             : DKV_ERR_LAUNCH;
+}
+
+__attribute__((visibility("default"))) dkv_status dkv_decode_lsh(
+    const dkv_config *cfg, const void *q, const void *k_pool, const void *v_pool,
+    const uint32_t *codes, const uint8_t *radii, int64_t num_blocks,
+    const int32_t *block_table, int32_t max_blocks_per_seq, const int32_t *seq_lens,
+    int32_t batch, int32_t max_seq_len, const void *proj, const void *index,
+    size_t index_bytes, float *out, int32_t *sel_idx, int32_t *sel_cnt,
+    void *workspace, size_t workspace_bytes, dkv_event_t *stage_events,
+    dkv_stream_t stream) {
+  if (index == nullptr) return DKV_ERR_INVALID_ARG;
+  if (stage_events != nullptr)
+    for (int i = 0; i <= kDecodeStages; ++i)
+      if (stage_events[i] == nullptr) return DKV_ERR_INVALID_ARG;
+  return decode_impl(cfg, q, k_pool, v_pool, codes, radii, num_blocks, block_table,
+                     max_blocks_per_seq, seq_lens, batch, max_seq_len, proj, out,
+                     sel_idx, sel_cnt, workspace, workspace_bytes, nullptr, nullptr,
+                     stage_events, false, index, index_bytes,
                      reinterpret_cast<hipStream_t>(stream));
 }
 

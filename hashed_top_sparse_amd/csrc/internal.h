@@ -24,6 +24,7 @@ struct DecodeDims {
   int k, w, sigma, cap;      // cap = k + w + sigma (selection list length)
   bool lin;                  // linear radius weight (DKV_RADIUS_LINEAR)
   bool pages;                // page-granular selection (select_pages)
+  int lsh_T, lsh_m;          // LSH tables and bits per table (T = 0: none)
   int max_seq_len;           // caller's bound (workspace stride)
   int n_max;                 // min(max_seq_len, 16*max_blocks)
   int max_blocks;
@@ -36,8 +37,20 @@ struct DecodeDims {
 
 // Byte offsets of the decode workspace regions (each 256-byte aligned).
 struct WorkspacePlan {
-  size_t q8, qop, qneg, lthr, cand, tcount, bitmap, rows, cnt, part, total;
+  size_t q8, qop, qneg, lthr, cand, tcount, bitmap, rows, cnt, part, qbits, total;
 };
+
+// Byte layout of the LSH index of one (sequence, KV head) unit: a 64-byte
+// header (int32 indexed length), then per table the bucket offsets
+// [2^m + 1] and the positions [max_seq_len] (int32), the unit padded to 256
+// bytes.
+struct LshLayout {
+  size_t off0, pos0;   // byte offsets of table 0's offsets and positions
+  size_t off_stride;   // bytes between tables' offset arrays
+  size_t pos_stride;   // bytes between tables' position arrays
+  size_t unit_bytes;
+};
+LshLayout lsh_layout(int T, int m, int max_seq_len);
 
 WorkspacePlan plan_workspace(const DecodeDims &d);
 
@@ -55,13 +68,34 @@ hipError_t launch_encode(const uint16_t *k_pool, int64_t num_blocks,
 // Query codes q8 [B][Hq][b], the score matrix-core operand qop
 // [B*Hkv][KS][64 lanes][8 dwords], qneg [B][Hq] = -sum_j q8, and per
 // (sequence, KV head) the candidate threshold lthr (from a page sample).
+// With qbits (LSH decode) it also writes each query head's sign code
+// [B][Hq][b/32] and no threshold sample is taken (lthr = 0).
 hipError_t launch_prep(const DecodeDims &d, const uint16_t *q,
                        const uint16_t *proj, const uint32_t *codes,
                        const uint8_t *radii, const uint16_t *k_pool,
                        uint32_t *codes_w, uint8_t *radii_w,
                        const int32_t *block_table,
                        const int32_t *seq_lens, int8_t *q8, uint32_t *qop,
-                       float *qneg, uint32_t *lthr, hipStream_t stream);
+                       float *qneg, uint32_t *lthr, uint32_t *qbits,
+                       hipStream_t stream);
+
+// LSH (lsh.hip): the bucket index of positions [0, seq_lens[s]); the probe
+// that marks each unit's candidates in its bitmap [B*Hkv][bm_words]; and
+// the scoring of the pages that hold candidates, which leaves them in the
+// candidate regions as the streaming filter would (u, position), with
+// their counts.
+hipError_t launch_lsh_build(const DecodeDims &d, const uint32_t *codes,
+                            const int32_t *block_table, const int32_t *seq_lens,
+                            char *index, hipStream_t stream);
+hipError_t launch_lsh_probe(const DecodeDims &d, const uint32_t *codes,
+                            const int32_t *block_table, const int32_t *seq_lens,
+                            const char *index, const uint32_t *qbits,
+                            uint32_t *bitmap, hipStream_t stream);
+hipError_t launch_lsh_score(const DecodeDims &d, const uint32_t *codes,
+                            const uint8_t *radii, const int32_t *block_table,
+                            const int32_t *seq_lens, const uint32_t *qop,
+                            const float *qneg, const uint32_t *bitmap, uint2 *cand,
+                            uint32_t *tcount, hipStream_t stream);
 
 // Scores every cached key once; the candidates (u >= lthr) of each
 // (sequence, KV head, group of kGroupKeys positions) go to that group's

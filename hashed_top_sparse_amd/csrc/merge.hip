@@ -47,8 +47,10 @@ __device__ __forceinline__ int row_of(const int32_t *bt, int pos,
   return (blk >= 0 && blk < num_blocks) ? blk * kPage + pos % kPage : -1;
 }
 
-// PAGES: the candidates are pages (page-granular selection).
-template <int KS, int G, bool PAGES>
+// SEL: 0 keys; 1 pages (the candidates are pages: page-granular
+// selection); 2 LSH (the candidates are exactly the LSH candidates, all
+// kept when they are k or fewer).
+template <int KS, int G, int SEL>
 __global__ __launch_bounds__(kThreads) void merge_kernel(
     const uint2 *__restrict__ cand, const uint32_t *__restrict__ tcount,
     int cand_groups,
@@ -61,7 +63,8 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
     const uint8_t *__restrict__ radii, uint32_t code_bytes,
     uint32_t radius_bytes, int W, const uint32_t *__restrict__ qop,
     const float *__restrict__ qneg, bool lin) {
-  constexpr bool pages = PAGES;
+  constexpr bool pages = SEL == 1;
+  constexpr bool lsh = SEL == 2;
   __shared__ __align__(16) uint2 st[kStage];
   __shared__ uint32_t gpre[kMaxGroupsLds + 1];
   __shared__ SelectShared<kThreads> sel;
@@ -81,10 +84,11 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
   // partial) unless none or all of them are taken
   const int npc = nc > 0 ? (c1 + kPage - 1) / kPage - c0 / kPage : 0;
   const int nitems = pages ? npc : nc;
-  const int keff = pages ? min(k / kPage, npc) : min(k, nc);
-  const bool rows_known = !pages || keff == 0 || keff == npc;
+  // (LSH: an upper bound until the candidates are counted)
+  int keff = pages ? min(k / kPage, npc) : min(k, nc);
+  const bool rows_known = (!pages && !lsh) || keff == 0 || (pages && keff == npc);
   const int base = ns + nwin;
-  int total = base + (keff == nitems ? nc : (pages ? 0 : keff));
+  int total = base + (keff == nitems && !lsh ? nc : (pages || lsh ? 0 : keff));
   const int32_t *bt = block_table + (int64_t)s * max_blocks;
   int32_t *R = rows + (int64_t)unit * cap;
   int32_t *U = user_sel ? user_sel + (int64_t)unit * cap : nullptr;
@@ -111,7 +115,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
       if (hi > lo) // a page's bits never span two words
         atomicOr(&bm[lo >> 5], ((1u << (hi - lo)) - 1u) << (lo & 31));
     };
-    if (keff == nitems) {
+    if (!lsh && keff == nitems) {
       // every candidate is selected, in position order
       for (int i = tid; i < nc; i += kThreads) {
         const int pos = c0 + i;
@@ -167,7 +171,18 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
         }
       };
       uint32_t T, take_eq, n_eq;
-      if (nlist >= (uint32_t)keff) {
+      if (lsh) {
+        // the selection is the top min(k, candidates) of the candidates
+        keff = min(keff, (int)nlist);
+        total = base + keff;
+        for (int i = total + tid; i < cap; i += kThreads) {
+          R[i] = -1;
+          if (U) U[i] = -1;
+        }
+      }
+      if (keff == 0) { // LSH without candidates (workgroup-uniform)
+        use_bitmap = false;
+      } else if (nlist >= (uint32_t)keff) {
         // ---- normal path: exact top-k of the candidates
         const bool staged = pre_lds && nlist <= (uint32_t)kStage;
         if (!staged) {
@@ -229,8 +244,12 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
         // the cut: survivors are u > Tu, or u == Tu and pos <= Tpos
         uint32_t Tu = 0, Tpos = 0;
         bool cut = false;
-        if (staged)
+        if (lsh && (uint32_t)keff == nlist) { // every candidate is kept
+          cut = true;
+          Tpos = 0xFFFFFFFFu;
+        } else if (staged) {
           cut = wg_topk_cut<kThreads>(sel, for_each, (uint32_t)keff, Tu, Tpos);
+        }
         uint32_t Pt = 0; // otherwise: ties with (kPosMax - pos) >= Pt are kept
         if (!cut) {
           wg_kth_largest<kThreads>(sel, [&](auto fn) {
@@ -463,8 +482,9 @@ hipError_t launch_merge(const DecodeDims &d, const uint2 *cand,
   }
 #define DKV_MERGE_CASE(KSV, GV)                                                \
   if (d.KS == KSV && d.G == GV) {                                              \
-    if (d.pages) DKV_MERGE_LAUNCH(KSV, GV, true)                               \
-    DKV_MERGE_LAUNCH(KSV, GV, false)                                           \
+    if (d.lsh_T > 0) DKV_MERGE_LAUNCH(KSV, GV, 2)                              \
+    if (d.pages) DKV_MERGE_LAUNCH(KSV, GV, 1)                                  \
+    DKV_MERGE_LAUNCH(KSV, GV, 0)                                               \
   }
   DKV_MERGE_CASE(1, 1)
   DKV_MERGE_CASE(1, 2)

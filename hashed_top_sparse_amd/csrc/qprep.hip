@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     const int32_t *__restrict__ block_table, int max_blocks,
     const int32_t *__restrict__ seq_lens, int n_max, int8_t *__restrict__ q8,
     uint32_t *__restrict__ qop, float *__restrict__ qneg,
-    uint32_t *__restrict__ lthr, int Hq,
+    uint32_t *__restrict__ lthr, uint32_t *__restrict__ qbits, int Hq,
     int Hkv, int b, int W, int k, int w, int sigma, bool lin, bool pages) {
   const int unit = blockIdx.x;
   const int s = unit / Hkv;
@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     P.pc0 = 0;
     P.SP = 1;
     P.nsp = 0;
-    if (!pages && P.keff > 0 && P.keff < P.nc) {
+    if (!pages && qbits == nullptr && P.keff > 0 && P.keff < P.nc) {
       P.pc0 = sigma / kPage;
       const int ncp = (n - w + kPage - 1) / kPage - P.pc0;
       while (P.SP < 32 && 2 * P.SP <= P.keff / 32) P.SP *= 2;
@@ -233,6 +233,10 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
   }
   // the newest key's code bits of columns 64*wave .. 64*wave+63
   const uint64_t key_bits = __ballot(pk > 0.0);
+  // the query heads' own sign codes (LSH buckets): pair idx = h*b + j
+  uint64_t qsign[kMaxPairs];
+#pragma unroll
+  for (int r = 0; r < kMaxPairs; ++r) qsign[r] = __ballot(p[r] > 0.0);
   for (int off = 32; off > 0; off >>= 1) mloc = fmax(mloc, __shfl_xor(mloc, off));
   if (lane == 0) sMax[wave] = mloc;
   __syncthreads();
@@ -389,7 +393,18 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     const int kp = min(k / kPage, npc);
     L = (kp > 0 && kp < npc) ? 0u : 0xFFFFFFFFu;
   }
-  if (threadIdx.x == 0) lthr[unit] = L;
+  if (threadIdx.x == 0) lthr[unit] = qbits != nullptr ? 0u : L;
+  if (qbits != nullptr) {
+#pragma unroll
+    for (int r = 0; r < kMaxPairs; ++r) {
+      const int idx0 = wave * 64 + r * kThreads; // this wave's 64 pairs
+      if (idx0 < npairs && lane < 2) {            // npairs, b: multiples of 64
+        const int h = idx0 / b, j0 = idx0 % b;
+        qbits[((int64_t)s * Hq + (int64_t)g * G + h) * (b / 32) + j0 / 32 + lane] =
+            lane ? (uint32_t)(qsign[r] >> 32) : (uint32_t)qsign[r];
+      }
+    }
+  }
   int8_t *qo = q8 + ((int64_t)s * Hq + (int64_t)g * G) * b;
 #pragma unroll
   for (int r = 0; r < kMaxPairs; ++r) {
@@ -418,7 +433,8 @@ hipError_t launch_prep(const DecodeDims &d, const uint16_t *q,
                        uint32_t *codes_w, uint8_t *radii_w,
                        const int32_t *block_table,
                        const int32_t *seq_lens, int8_t *q8, uint32_t *qop,
-                       float *qneg, uint32_t *lthr, hipStream_t stream) {
+                       float *qneg, uint32_t *lthr, uint32_t *qbits,
+                       hipStream_t stream) {
   const uint32_t code_bytes = (uint32_t)((uint64_t)d.num_blocks * d.Hkv * d.W * kPage * 4);
   const uint32_t radius_bytes = (uint32_t)((uint64_t)d.num_blocks * d.Hkv * kPage);
 #define DKV_PREP_CASE(KSV, GV)                                                 \
@@ -428,6 +444,7 @@ hipError_t launch_prep(const DecodeDims &d, const uint16_t *q,
                        k_pool, codes_w, radii_w,                               \
                        d.num_blocks, code_bytes, radius_bytes, block_table,    \
                        d.max_blocks, seq_lens, d.n_max, q8, qop, qneg, lthr,   \
+                       qbits,                                                  \
                        d.Hq, d.Hkv, d.b, d.W, d.k, d.w, d.sigma, d.lin,         \
                        d.pages);                                               \
     return hipGetLastError();                                                  \

@@ -119,6 +119,10 @@ typedef struct {
                             scored by its best key in [sigma, N-w), and
                             their keys in that range (see dkv_decode);
                             other values: DKV_ERR_UNSUPPORTED            */
+  int32_t lsh_tables;    /* T >= 0 LSH tables (0: none; > 0: decode with
+                            dkv_decode_lsh, see there); T*lsh_bits <= b,
+                            and select_pages must be 0                   */
+  int32_t lsh_bits;      /* m: bits per LSH table, 1..12 when T > 0     */
 } dkv_config;
 
 #define DKV_RADIUS_LOG 0
@@ -127,6 +131,7 @@ typedef struct {
 /* Limits checked by every entry point (DKV_ERR_UNSUPPORTED beyond them). */
 #define DKV_MAX_SEQ_LEN (1 << 24)
 #define DKV_MAX_SELECT (1 << 20) /* top_k + window + sinks */
+#define DKV_LSH_MAX_SEQ_LEN (1 << 19) /* dkv_decode_lsh */
 
 /*
  * dkv_encode -- build key codes and radii when keys are written to the
@@ -271,6 +276,73 @@ dkv_status dkv_decode_append(const dkv_config *cfg, const void *q,
                              void *workspace, size_t workspace_bytes,
                              dkv_event_t *stage_events, dkv_stream_t stream);
 
+/*
+ * Multi-table LSH candidate retrieval ([DASH], "from quadratic to linear":
+ * several hash tables split the space into buckets; a query looks only in
+ * its own buckets, and the candidates found there are pruned to the top-k
+ * that enter exact attention).
+ *
+ * Definition (with T = lsh_tables, m = lsh_bits, W = b/32):
+ *   bucket of a key in table t   code bits t*m .. t*m+m-1 (bit t*m+i is
+ *                                bit i of the bucket number)
+ *   bucket of query head h       the same bits of the query's own sign
+ *                                code: bit j = [p_hj > 0], p_h = q_h.P in
+ *                                double precision, index order (the key
+ *                                code's definition applied to q_h)
+ *   candidates                   keys in [sigma, N-w) that share a bucket
+ *                                with some head of the KV group in some
+ *                                table
+ *   selection                    sinks + window + the min(top_k,
+ *                                candidates) best candidates by
+ *                                (S descending, position ascending)
+ *
+ * The index is an acceleration structure only: keys at positions it does
+ * not hold (appended after dkv_lsh_build) are tested directly, so the
+ * result never depends on when the index was built.
+ *
+ * dkv_lsh_index_size -- bytes of the index for `batch` sequences of at most
+ * max_seq_len tokens (0 on invalid arguments or lsh_tables == 0).
+ */
+size_t dkv_lsh_index_size(const dkv_config *cfg, int32_t batch,
+                          int32_t max_seq_len);
+
+/*
+ * dkv_lsh_build -- (re)builds the bucket index of positions
+ * [0, seq_lens[s]) of every sequence s from the codes dkv_encode wrote.
+ *   codes, num_blocks, block_table, max_blocks_per_seq, batch, seq_lens,
+ *   max_seq_len   as for dkv_decode (seq_lens on the device)
+ *   index         device, dkv_lsh_index_size(cfg, batch, max_seq_len)
+ *                 bytes, 256-byte aligned; owned by the caller, read by
+ *                 dkv_decode_lsh with the same cfg, batch and max_seq_len.
+ *                 Layout per (sequence, KV head): the indexed length, then
+ *                 per table bucket offsets [2^m + 1] and positions
+ *                 [max_seq_len] (int32), grouped by bucket.
+ * Errors as dkv_decode (DKV_ERR_WORKSPACE for a short or misaligned index).
+ */
+dkv_status dkv_lsh_build(const dkv_config *cfg, const uint32_t *codes,
+                         int64_t num_blocks, const int32_t *block_table,
+                         int32_t max_blocks_per_seq, int32_t batch,
+                         const int32_t *seq_lens, int32_t max_seq_len,
+                         void *index, size_t index_bytes, dkv_stream_t stream);
+
+/*
+ * dkv_decode_lsh -- dkv_decode with the LSH candidate selection above
+ * (cfg->lsh_tables > 0; max_seq_len <= 2^19).  Arguments as dkv_decode,
+ * plus the index built by dkv_lsh_build and optional stage_events as in
+ * dkv_decode_append (the bucket probe counts to the score stage).
+ * sel_cnt = min(N, sinks + window) + min(top_k, candidates).
+ */
+dkv_status dkv_decode_lsh(const dkv_config *cfg, const void *q,
+                          const void *k_pool, const void *v_pool,
+                          const uint32_t *codes, const uint8_t *radii,
+                          int64_t num_blocks, const int32_t *block_table,
+                          int32_t max_blocks_per_seq, const int32_t *seq_lens,
+                          int32_t batch, int32_t max_seq_len, const void *proj,
+                          const void *index, size_t index_bytes, float *out,
+                          int32_t *sel_idx, int32_t *sel_cnt, void *workspace,
+                          size_t workspace_bytes, dkv_event_t *stage_events,
+                          dkv_stream_t stream);
+
 /* Number of decode stages and the static name of stage i ("" if out of
  * range). */
 int32_t dkv_decode_num_stages(void);
@@ -280,7 +352,7 @@ const char *dkv_decode_stage_name(int32_t stage);
 const char *dkv_status_string(dkv_status status);
 
 /* ABI version of this header (bumped on any signature or layout change). */
-#define DKV_ABI_VERSION 4
+#define DKV_ABI_VERSION 5
 int32_t dkv_abi_version(void);
 
 #ifdef __cplusplus

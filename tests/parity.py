@@ -73,6 +73,27 @@ def gpu_decode(cfg: dkv.Config, inp: dict, codes, radii, debug: bool = True,
     return res
 
 
+def gpu_decode_lsh(cfg: dkv.Config, inp: dict, codes, radii, index_lens=None):
+    """dkv_lsh_build over [0, index_lens) (default: every cached token), then
+    dkv_decode_lsh over the full lengths."""
+    dev = inp["k_pool"].device
+    B = inp["block_table"].shape[0]
+    T = inp["max_seq_len"]
+    index = torch.empty(dkv.lsh_index_size(cfg, B, T), dtype=torch.uint8, device=dev)
+    lens = inp["seq_lens"] if index_lens is None else index_lens
+    dkv.lsh_build(cfg, codes, inp["block_table"], lens, T, index)
+    ws = torch.empty(dkv.decode_workspace_size(cfg, B, T), dtype=torch.uint8, device=dev)
+    out = torch.full((B, cfg.num_q_heads, cfg.head_dim), float("nan"), device=dev)
+    sel = torch.full((B, cfg.num_kv_heads, cfg.select_cap), -7, dtype=torch.int32,
+                     device=dev)
+    cnt = torch.full((B, cfg.num_kv_heads), -7, dtype=torch.int32, device=dev)
+    dkv.decode_lsh(cfg, inp["q"], inp["k_pool"], inp["v_pool"], codes, radii,
+                   inp["block_table"], inp["seq_lens"], T, inp["proj"], index, out, ws,
+                   sel, cnt)
+    torch.cuda.synchronize()
+    return {"out": out, "sel": sel, "cnt": cnt}
+
+
 def gpu_decode_append(cfg: dkv.Config, inp: dict):
     """dkv_encode over [0, N-1) of every sequence into sentinel-filled pools,
     then dkv_decode_append (which must encode position N-1 itself).  Returns
@@ -120,7 +141,7 @@ def check_unit(cfg: dkv.Config, inp: dict, gpu: dict, codes, radii, s: int, g: i
         assert np.array_equal(g_radii, o_radii), "radii differ"
     r = oracle.decode_unit(q, P, o_codes, o_radii, K, V, cfg.top_k, cfg.window,
                            cfg.sinks, radius_mode=cfg.radius_weight,
-                           pages=cfg.select_pages)
+                           pages=cfg.select_pages, lsh=(cfg.lsh_tables, cfg.lsh_bits))
     if "q8" in gpu:
         g_q8 = gpu["q8"][s, g * G:(g + 1) * G].cpu().numpy()
         assert np.array_equal(g_q8, r["q8"]), "query codes differ"

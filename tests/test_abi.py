@@ -48,7 +48,7 @@ def test_status_strings():
 def _cfg(**over):
     kw = dict(head_dim=128, num_q_heads=32, num_kv_heads=8, code_bits=128,
               page_size=16, top_k=64, window=16, sinks=4, radius_weight=0,
-              select_pages=0)
+              select_pages=0, lsh_tables=0, lsh_bits=0)
     kw.update(over)
     return dkv._CConfig(*[kw[f] for f, _ in dkv._CConfig._fields_])
 
@@ -69,6 +69,10 @@ def _decode(cfg, ws_bytes=1 << 30, workspace=FAKE, q=FAKE, batch=2, max_seq_len=
     (dict(window=-5), 1), (dict(sinks=-1), 1), (dict(num_kv_heads=0), 1),
     (dict(top_k=1 << 20), 2), (dict(radius_weight=2), 2), (dict(radius_weight=-1), 2),
     (dict(select_pages=2), 2), (dict(select_pages=-1), 2),
+    (dict(lsh_tables=-1), 2), (dict(lsh_tables=4, lsh_bits=13), 2),
+    (dict(lsh_tables=4, lsh_bits=0), 2), (dict(lsh_tables=17, lsh_bits=8), 2),  # 136 > b
+    (dict(lsh_tables=4, lsh_bits=8, select_pages=1), 2),
+    (dict(lsh_tables=4, lsh_bits=8), 1),   # an LSH config needs dkv_decode_lsh
 ])
 def test_decode_rejects_bad_config(over, status):
     assert _decode(_cfg(**over)) == status
@@ -149,3 +153,29 @@ def test_python_binding_refuses_host_tensors():
                    1, torch.zeros((128, 64), dtype=torch.bfloat16),
                    torch.zeros((2, 1, 2, 16), dtype=torch.int32),
                    torch.zeros((2, 1, 16), dtype=torch.uint8), stream=0)
+
+
+def test_lsh_entry_points_reject_bad_arguments():
+    lib = dkv.load_library()
+    c = _cfg(lsh_tables=4, lsh_bits=8)
+    size = lib.dkv_lsh_index_size(ctypes.byref(c), 2, 1000)
+    assert size > 0
+    assert lib.dkv_lsh_index_size(ctypes.byref(_cfg()), 2, 1000) == 0       # no tables
+    assert lib.dkv_lsh_index_size(ctypes.byref(c), 2, (1 << 19) + 1) == 0   # too long
+    build = lambda cfg, **kw: lib.dkv_lsh_build(
+        ctypes.byref(cfg), kw.get("codes", FAKE), 200, FAKE, 64, 2, FAKE,
+        kw.get("max_seq_len", 1000), kw.get("index", FAKE), kw.get("bytes", size), None)
+    assert build(_cfg()) == 1                                  # config without tables
+    assert build(c, codes=None) == 1
+    assert build(c, bytes=size - 1) == 3
+    assert build(c, index=ctypes.c_void_p(0x10010)) == 3       # misaligned index
+    assert build(c, max_seq_len=(1 << 19) + 1) == 2
+
+    def dec(cfg, index=FAKE, nbytes=size, max_seq_len=1000):
+        return lib.dkv_decode_lsh(ctypes.byref(cfg), FAKE, FAKE, FAKE, FAKE, FAKE, 200, FAKE,
+                                  64, FAKE, 2, max_seq_len, FAKE, index, nbytes, FAKE, None,
+                                  None, FAKE, 1 << 30, None, None)
+    assert dec(c, index=None) == 1
+    assert dec(_cfg()) == 1                                    # index without tables
+    assert dec(c, nbytes=size - 1) == 3
+    assert dec(c, max_seq_len=(1 << 19) + 1) == 2

@@ -16,7 +16,8 @@ import workloads
 import hashed_top_sparse_amd as dkv
 import oracle
 from helpers import PAGE, logical_codes, logical_radii, logical_rows, tensor_bits
-from parity import check_unit, config_of, gpu_decode, gpu_decode_append, gpu_encode_all
+from parity import (check_unit, config_of, gpu_decode, gpu_decode_append, gpu_decode_lsh,
+                    gpu_encode_all)
 
 pytestmark = pytest.mark.gpu
 
@@ -430,4 +431,57 @@ def test_page_selection_short_sequences():
 ])
 def test_full_size_page_selection(name, units, over):
     _run(workloads.get(name), units, **PAGES, **over)
+    torch.cuda.empty_cache()
+
+
+
+# ------------------------------------------------------ LSH candidates
+def _run_lsh(wl, units=None, index_back=0, **cfg_over):
+    """Index over [0, N - index_back) of every sequence, decode over N: the
+    positions past the index are tested from their codes."""
+    print(f"[case] lsh {wl.name} {cfg_over} index_back={index_back}", flush=True)
+    cfg = config_of(wl, **cfg_over)
+    inp = workloads.make_inputs(wl, DEV)
+    codes, radii = gpu_encode_all(cfg, inp)
+    lens = torch.clamp(inp["seq_lens"] - index_back, min=0).to(torch.int32)
+    gpu = gpu_decode_lsh(cfg, inp, codes, radii, index_lens=lens)
+    if units is None:
+        units = [(s, g) for s in range(wl.batch) for g in range(wl.num_kv_heads)]
+    cnts = []
+    for s, g in units:
+        check_unit(cfg, inp, gpu, codes, radii, s, g)
+        cnts.append(int(gpu["cnt"][s, g]))
+    return cnts
+
+
+@pytest.mark.parametrize("name", sorted(workloads.SMALL))
+def test_lsh_small_every_unit(name):
+    _run_lsh(workloads.get(name), lsh_tables=8, lsh_bits=6)
+
+
+@pytest.mark.parametrize("over", [
+    dict(lsh_tables=8, lsh_bits=6, index_back=700),    # a long unindexed tail
+    dict(lsh_tables=1, lsh_bits=12),                   # few candidates: all kept
+    dict(lsh_tables=16, lsh_bits=2),                   # almost every key
+    dict(lsh_tables=12, lsh_bits=10, radius_weight=dkv.RADIUS_LINEAR),
+    dict(lsh_tables=8, lsh_bits=6, top_k=0, window=64, sinks=4),
+])
+def test_lsh_edge_configs(over):
+    over = dict(over)
+    back = over.pop("index_back", 0)
+    _run_lsh(workloads.get("small_gqa_b128"), index_back=back, **over)
+
+
+def test_lsh_index_of_nothing():
+    """An index built over empty prefixes: every key is tested directly."""
+    wl = workloads.get("small_ragged_b128")
+    _run_lsh(wl, index_back=1 << 20, lsh_tables=6, lsh_bits=8)
+
+
+@pytest.mark.parametrize("name,units,over", [
+    ("gqa32x8_bs16_n128k_b128", [(0, 0), (15, 7)], dict(lsh_tables=8, lsh_bits=10)),
+    ("gqa32x8_bs4_n256k_b256_lognormal", [(1, 2)], dict(lsh_tables=16, lsh_bits=12)),
+])
+def test_full_size_lsh(name, units, over):
+    _run_lsh(workloads.get(name), units, index_back=100, **over)
     torch.cuda.empty_cache()
