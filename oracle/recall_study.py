@@ -4,8 +4,10 @@
 TEST INFRASTRUCTURE: uses the oracle and the seeded workload generator,
 never the GPU library.
 
-For each selection granularity (keys, or 16-token pages scored by their best
-key), each radius weight (the log code r8, or the linear rne(2^(r8/16))),
+For each selection (keys; 16-token pages scored by their best key; the
+top-k among multi-table LSH candidates, T tables of m bits), each radius
+weight (the log code r8, or the linear rne(2^(r8/16)); pages and LSH with
+the linear weight only),
 each code width b in {64, 128, 256} and two key distributions (N(0,1) with
 4 outlier channels x8; log-normal radii, sigma = 0.5), on every KV head of
 one sequence of the 32K-token GQA shape (32 query / 8 KV heads, k = 1024,
@@ -60,19 +62,19 @@ def _logical_rows(pool, bt, s, N, g):
     return pool[blk, pos % workloads.PAGE, g]
 
 
-def needle_recall(wl, q, P, K, V, needles, mode, pages):
+def needle_recall(wl, q, P, K, V, needles, mode, sel):
     codes, radii = oracle.encode_keys(K, P)
     r = oracle.decode_unit(q, P, codes, radii, K, V, wl.top_k, wl.window,
-                           wl.sinks, radius_mode=mode, pages=pages)
+                           wl.sinks, radius_mode=mode, **sel)
     return float(np.isin(needles, r["sel"]).mean())
 
 
-def study_unit(wl, q, P, K, V, mode, pages):
+def study_unit(wl, q, P, K, V, mode, sel):
     G, d = q.shape
     N = K.shape[0]
     codes, radii = oracle.encode_keys(K, P)
     r = oracle.decode_unit(q, P, codes, radii, K, V, wl.top_k, wl.window,
-                           wl.sinks, radius_mode=mode, pages=pages)
+                           wl.sinks, radius_mode=mode, **sel)
     qf, Kf, Vf = _bf16_to_f64(q), _bf16_to_f64(K), _bf16_to_f64(V)
     logits = qf @ Kf.T / np.sqrt(d)                     # [G][N]
     c0, c1 = wl.sinks, N - wl.window
@@ -120,15 +122,16 @@ def main(argv=None):
             plain = dataclasses.replace(base, code_bits=b, seq_len=args.seq_len,
                                         needles=0, **dkw)
             with_nd = dataclasses.replace(plain, needles=16)
-            for pages in (False, True):
-                for mode, mname in ((0, "log r8"), (1, "linear")):
-                    m = np.array([study_unit(plain, q, P, K, V, mode, pages)
-                                  for q, P, K, V, _ in units(plain)]).mean(axis=0)
-                    nd = np.mean([needle_recall(with_nd, q, P, K, V, n, mode, pages)
-                                  for q, P, K, V, n in units(with_nd)])
-                    sname = "pages" if pages else "keys"
-                    print(f"| {dname} | {b} | {sname} | {mname} | {m[0]:.3f} | "
-                          f"{m[1]:.3f} | {m[2]:.3f} | {nd:.3f} |", flush=True)
+            variants = [("keys", 0, {}), ("keys", 1, {}), ("pages", 1, dict(pages=True)),
+                        ("lsh 8x8", 1, dict(lsh=(8, 8))), ("lsh 8x10", 1, dict(lsh=(8, 10)))]
+            for sname, mode, sel in variants:
+                mname = "linear" if mode else "log r8"
+                m = np.array([study_unit(plain, q, P, K, V, mode, sel)
+                              for q, P, K, V, _ in units(plain)]).mean(axis=0)
+                nd = np.mean([needle_recall(with_nd, q, P, K, V, n, mode, sel)
+                              for q, P, K, V, n in units(with_nd)])
+                print(f"| {dname} | {b} | {sname} | {mname} | {m[0]:.3f} | "
+                      f"{m[1]:.3f} | {m[2]:.3f} | {nd:.3f} |", flush=True)
     print(f"\n({time.time() - t0:.0f} s; seq_len {args.seq_len}, "
           f"{args.heads} KV heads per row, seed {base.seed})")
 
