@@ -218,6 +218,18 @@ def main():
     zeros = torch.zeros(B, dtype=torch.int32, device=dev)
     dkv.encode(cfg, inp["k_pool"], inp["block_table"], zeros, inp["seq_lens"],
                inp["max_seq_len"], inp["proj"], codes, radii)
+    # the prefix encode once more, timed (A1 + A2 on every cached token)
+    torch.cuda.synchronize()
+    enc_ev = HipEvents()
+    eev = enc_ev.create(2)
+    enc_ev.record(eev[0], torch.cuda.current_stream().cuda_stream)
+    dkv.encode(cfg, inp["k_pool"], inp["block_table"], zeros, inp["seq_lens"],
+               inp["max_seq_len"], inp["proj"], codes, radii)
+    enc_ev.record(eev[1], torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    enc_us = enc_ev.elapsed_ms(eev[0], eev[1]) * 1e3
+    enc_rows = int(inp["seq_lens"].sum().item()) * Hkv
+    enc_bytes = enc_rows * (2 * wl.head_dim + wl.code_bits // 8 + 1)
     max_len = inp["max_seq_len"]
     ws = torch.empty(dkv.decode_workspace_size(cfg, B, max_len), dtype=torch.uint8,
                      device=dev)
@@ -360,6 +372,12 @@ def main():
         "step_hbm_gbs": ab["total"] / (ms_per_step * 1e-3) / 1e9,
         "step_frac_of_peak": ab["total"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "stages_us": {k: v * 1e3 for k, v in stage_ms.items()},
+        # the untimed-in-the-step prefix encode (every cached key of the
+        # batch), timed once with HIP events: algorithmic bytes (2d bf16
+        # read + b/8 + 1 written per key row) over its time
+        "prefix_encode": {"us": enc_us, "key_rows": enc_rows,
+                          "gbs": enc_bytes / (enc_us * 1e-6) / 1e9,
+                          "frac_of_hbm_peak": enc_bytes / (enc_us * 1e-6) / 1e9 / HBM_PEAK_GBS},
         "cold": cold,
         "roofline": roofline,
         "cpu_baseline": None,

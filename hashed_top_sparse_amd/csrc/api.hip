@@ -267,7 +267,9 @@ dkv_encode(const dkv_config *cfg, const void *k_pool, int64_t num_blocks,
   if (!aligned16(k_pool) || !aligned16(codes) || !aligned16(radii) ||
       !aligned16(proj))
     return DKV_ERR_INVALID_ARG;
-  if (max_encode_len > DKV_MAX_SEQ_LEN) return DKV_ERR_UNSUPPORTED;
+  if (max_encode_len > DKV_MAX_SEQ_LEN ||
+      (int64_t)batch * max_blocks_per_seq >= (int64_t)1 << 30)
+    return DKV_ERR_UNSUPPORTED;
   hipError_t e = launch_encode(
       static_cast<const uint16_t *>(k_pool), num_blocks, block_table,
       max_blocks_per_seq, batch, enc_start, enc_end, max_encode_len,

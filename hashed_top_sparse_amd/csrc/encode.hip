@@ -8,115 +8,301 @@
 // Code bit j = [p_j > 0] with p_j = sum_i k_i * P_ij accumulated in double
 // precision in index order (bf16 x bf16 products are exact in double, so a
 // fused multiply-add equals a multiply then an add).  Radius code r8 =
-// largest m in 1..255 with |k|^2 >= 2^((m-64)/8), else 0.
-//
-// Work mapping: one workgroup per (sequence, 16-token tile).  The tile's
-// (token, KV head) pairs are taken in rounds of eight: the round's key rows
-// are staged in LDS as doubles, wave v owns pairs v and v+4, and lane j
-// keeps the projection chains of columns j, j+64, ... of both pairs, so
-// every lane runs 2*b/64 independent index-order chains side by side.  The
-// 64 sign bits of a column chunk are packed with one wave ballot.  Lanes 0
-// and 1 also run the radius chains of the wave's two pairs.  P is staged
-// once per workgroup in LDS.
+// largest m in 1..255 with |k|^2 >= 2^((m-64)/8), else 0.  The kernel below
+// reaches exactly these values through fp32 matrix ops whose signs are
+// certified, with the fp64 chains only where they are not.
+
+#include <algorithm>
+
 #include "encode_common.h"
 
 namespace dkv {
 namespace {
 
-constexpr int kTile = 16;    // tokens per workgroup
-constexpr int kThreads = 256; // four waves
-constexpr int kRound = 8;     // (token, KV head) pairs staged at a time
+// ---------------------------------------------------------------------------
+// Matrix-core encode.  p = k.P runs as bf16 x bf16 matrix ops (16 keys x 16
+// columns x 32 dims each; the products are exact in fp32, the sums are fp32).
+// A sign is certain when |p32| exceeds a bound on the fp32 summation error
+// in any order (Cauchy-Schwarz: sum |k_i P_ij| <= |k| |P_j|):
+//   |p32 - p| <= 2 (d+1) 2^-23 |k| |P_j| + 2^-100,
+// four times the classic (d+1) 2^-24 bound (headroom for the fp32 norms
+// themselves; the 2^-100 term covers products that underflow).  Uncertain
+// bits are recomputed with the index-order fp64 chain of the definition.
+// Likewise |k|^2: an fp32 sum gives the radius code unless it lies within
+// 2^-15 (relative) of a code threshold; then the fp64 chain decides.
+//
+// Work: persistent waves, each keeping its P fragments (64 columns) in
+// registers; a tile is (sequence, page, KV head) and a 64-column part of the
+// code.  Lane L loads 64 contiguous bytes (dims 32q..32q+31,
+// q = L/16) of key row L%16; matrix K-step c pairs dims 32q+8c..32q+8c+7 of
+// the row with the same dims of column L%16 of P, so every dim is used
+// once.  The next tile's rows are loaded while the current one is scored.
+typedef __bf16 v8bf16 __attribute__((ext_vector_type(8)));
+typedef float v4f32 __attribute__((ext_vector_type(4)));
 
-template <int C> // C = b / 64 column chunks
-__global__ __launch_bounds__(kThreads) void encode_kernel(
-    const uint16_t *__restrict__ k_pool, int64_t num_blocks,
-    const int32_t *__restrict__ block_table, int max_blocks,
-    const int32_t *__restrict__ enc_start, const int32_t *__restrict__ enc_end,
-    int max_encode_len, const uint16_t *__restrict__ proj, int Hkv,
-    uint32_t *__restrict__ codes, uint8_t *__restrict__ radii) {
-  constexpr int b = 64 * C, W = b / 32;
-  __shared__ __align__(16) uint16_t sP[kHeadDim * b]; // [i][j]
-  __shared__ double sK[kRound][kHeadDim];
-  __shared__ int sBlk[kRound];
-  const int s = blockIdx.y;
-  const int limit = kPage * max_blocks;
-  const int start = clamp_int(enc_start[s], 0, limit);
-  int end = clamp_int(enc_end[s], 0, limit);
-  if (end - start > max_encode_len) end = start + max_encode_len;
-  const int t0 = start + blockIdx.x * kTile;
-  if (t0 >= end) return; // whole workgroup leaves together
-  const int npairs = min(kTile, end - t0) * Hkv;
+constexpr int kMmThreads = 256; // four waves
+constexpr int kRangeLds = 1024; // sequences whose encode range sits in LDS
 
-  { // proj is 16-byte aligned (checked on the host)
-    const uint4 *src = reinterpret_cast<const uint4 *>(proj);
-    uint4 *dst = reinterpret_cast<uint4 *>(sP);
-    for (int i = threadIdx.x; i < kHeadDim * b / 8; i += kThreads) dst[i] = src[i];
+__device__ __forceinline__ v8bf16 as_v8bf16(const uint4 &u) {
+  return __builtin_bit_cast(v8bf16, u);
+}
+
+// Index-order fp64 projection of a key row (bf16, staged in LDS) on column
+// n of P (LDS, transposed: sPt[n][i]).
+__device__ double project_fp64(const uint16_t *krow, const uint16_t *pcol) {
+  double acc = 0.0;
+#pragma unroll 4
+  for (int i = 0; i < kHeadDim; ++i)
+    acc = fma((double)bf16_to_float(krow[i]), (double)bf16_to_float(pcol[i]), acc);
+  return acc;
+}
+
+__device__ double sq_norm_fp64(const uint16_t *krow) {
+  double acc = 0.0;
+#pragma unroll 4
+  for (int i = 0; i < kHeadDim; ++i) {
+    const double x = (double)bf16_to_float(krow[i]);
+    acc = fma(x, x, acc);
   }
+  return acc;
+}
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int32_t *bt = block_table + (int64_t)s * max_blocks;
-  for (int p0 = 0; p0 < npairs; p0 += kRound) {
-    __syncthreads(); // sP staged / previous round's rows consumed
-    {
-      // thread -> (pair r, 4 consecutive elements)
-      const int r = threadIdx.x >> 5, e = 4 * (threadIdx.x & 31);
-      const int p = p0 + r;
-      int blk = -1, slot = 0, h = 0;
-      if (p < npairs) {
-        const int t = t0 + p / Hkv;
-        h = p % Hkv;
-        slot = t % kPage;
-        blk = bt[t / kPage];
-        if (blk < 0 || blk >= num_blocks) blk = -1;
+// NB: 16-column blocks per wave (64 columns: 64 VGPRs of fragments, three
+// waves per SIMD); HALVES: b/64 column parts, each taken by its own
+// workgroups (the parts of one tile load the same rows, from L2).
+template <int NB, int HALVES>
+__global__ __launch_bounds__(kMmThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void encode_mfma_kernel(const uint16_t *__restrict__ k_pool, int64_t num_blocks,
+                        const int32_t *__restrict__ block_table, int max_blocks,
+                        int batch, const int32_t *__restrict__ enc_start,
+                        const int32_t *__restrict__ enc_end, int max_encode_len,
+                        int pages_max, const uint16_t *__restrict__ proj, int Hkv,
+                        uint32_t *__restrict__ codes, uint8_t *__restrict__ radii) {
+  constexpr int b = 16 * NB * HALVES, W = b / 32;
+  constexpr int NCOL = 16 * NB;    // columns of this workgroup
+  constexpr int WH = NB / 2;       // code words per key in one half
+  __shared__ __align__(16) uint16_t sPt[NCOL][kHeadDim]; // P^T of the half
+  __shared__ uint64_t sBal[kMmThreads / 64][NB][4];
+  __shared__ float sR2[kMmThreads / 64][16];
+  __shared__ int2 sRange[kRangeLds];
+  // a tile's key rows, staged only when an fp64 chain has to run
+  __shared__ __align__(16) uint16_t sRow[kMmThreads / 64][kPage][kHeadDim];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int q = lane >> 4, col = lane & 15;
+  const int half = HALVES > 1 ? (int)(blockIdx.x % HALVES) : 0;
+  const int col0 = half * NCOL;
+  const int limit = kPage * max_blocks;
+  // a sequence's encode range [start, end), clamped
+  auto range_of = [&](int s_) {
+    const int st = clamp_int(enc_start[s_], 0, limit);
+    int en = clamp_int(enc_end[s_], 0, limit);
+    if (en - st > max_encode_len) en = st + max_encode_len;
+    return make_int2(st, en);
+  };
+  // stage the half's columns of P transposed, and the first sequences'
+  // ranges
+  for (int e = threadIdx.x; e < kHeadDim * NCOL; e += kMmThreads) {
+    const int i = e / NCOL, j = e % NCOL;
+    sPt[j][i] = proj[(int64_t)i * b + col0 + j];
+  }
+  for (int i = threadIdx.x; i < batch && i < kRangeLds; i += kMmThreads) sRange[i] = range_of(i);
+  __syncthreads();
+  const __amdgpu_buffer_rsrc_t bt_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int32_t *>(block_table), 0, (uint32_t)(batch * max_blocks) * 4u,
+      0x00020000u);
+  // this lane's B fragments and column norms
+  v8bf16 bfr[NB][4];
+  float cn[NB];
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb) {
+    const uint16_t *pc = sPt[16 * cb + col];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      bfr[cb][c] = as_v8bf16(*reinterpret_cast<const uint4 *>(pc + 32 * q + 8 * c));
+    // |P_col|^2 from the fragments (each dim once across the row's lanes)
+    float n2 = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = (float)bfr[cb][c][e];
+        n2 = fmaf(x, x, n2);
       }
-      uint2 raw = make_uint2(0u, 0u);
-      if (blk >= 0) {
-        const uint16_t *krow =
-            k_pool + (((int64_t)blk * kPage + slot) * Hkv + h) * kHeadDim;
-        raw = *reinterpret_cast<const uint2 *>(krow + e);
-      }
-      sK[r][e + 0] = (double)bf16_to_float(raw.x & 0xFFFFu);
-      sK[r][e + 1] = (double)bf16_to_float(raw.x >> 16);
-      sK[r][e + 2] = (double)bf16_to_float(raw.y & 0xFFFFu);
-      sK[r][e + 3] = (double)bf16_to_float(raw.y >> 16);
-      if ((threadIdx.x & 31) == 0) sBlk[r] = blk;
-    }
-    __syncthreads();
+    n2 += __shfl_xor(n2, 16);
+    n2 += __shfl_xor(n2, 32);
+    cn[cb] = sqrtf(n2) * (1.f + 0x1p-20f);
+  }
+  const int ntiles = batch * pages_max * Hkv;
+  const int wstride = (gridDim.x / HALVES) * (kMmThreads / 64);
 
-    const int r0 = wave, r1 = wave + 4;
-    double acc0[C], acc1[C];
+  struct Tile {
+    int s, h, p, start, end, blk;
+  };
+  // tile id -> tile, block id not yet known
+  auto tile_of = [&](int t, Tile &T) {
+    T.h = t % Hkv;
+    const int r = t / Hkv;
+    T.s = r % batch;
+    const int pi = r / batch;
+    const int2 rg = T.s < kRangeLds ? sRange[T.s] : range_of(T.s);
+    T.start = rg.x;
+    T.end = rg.y;
+    T.p = T.start / kPage + pi;
+    T.blk = -1;
+  };
+  // the tile's block id by a vector load (a scalar load would stall the
+  // wave where it is used; this one is issued a tile ahead), or -1 when the
+  // page is past the range
+  auto blk_load = [&](const Tile &T, bool any) -> int {
+    if (!any || T.p * kPage >= T.end) return -1;
+    return __builtin_amdgcn_raw_buffer_load_b32(
+        bt_rsrc, (T.s * max_blocks + T.p) * 4, 0, 0);
+  };
+  auto set_blk = [&](Tile &T, int v) {
+    const int blk = __builtin_amdgcn_readfirstlane(v);
+    T.blk = (blk >= 0 && blk < num_blocks) ? blk : -1;
+  };
+  auto row_ptr = [&](const Tile &T, int r) {
+    return k_pool + (((int64_t)T.blk * kPage + r) * Hkv + T.h) * kHeadDim;
+  };
+  auto load_rows = [&](const Tile &T, uint4 (&a)[4]) {
+    if (T.blk >= 0) {
+      const uint4 *src = reinterpret_cast<const uint4 *>(row_ptr(T, col) + 32 * q);
 #pragma unroll
-    for (int c = 0; c < C; ++c) acc0[c] = acc1[c] = 0.0;
-    double r2 = 0.0;
-    const int rr = (lane & 1) ? r1 : r0; // radius chain of lane 0 / lane 1
-#pragma unroll 8
-    for (int i = 0; i < kHeadDim; ++i) {
-      const double k0 = sK[r0][i], k1 = sK[r1][i], kr = sK[rr][i];
+      for (int c = 0; c < 4; ++c) a[c] = src[c];
+    } else {
 #pragma unroll
-      for (int c = 0; c < C; ++c) {
-        const double pv = (double)bf16_to_float(sP[i * b + 64 * c + lane]);
-        acc0[c] = fma(k0, pv, acc0[c]);
-        acc1[c] = fma(k1, pv, acc1[c]);
-      }
-      r2 = fma(kr, kr, r2);
+      for (int c = 0; c < 4; ++c) a[c] = make_uint4(0u, 0u, 0u, 0u);
     }
+  };
+
+  // three stages: the block id of tile k+2, the rows of tile k+1 and the
+  // scoring of tile k overlap
+  int t = (int)(blockIdx.x / HALVES) * (kMmThreads / 64) + wave;
+  if (t >= ntiles) return; // no barriers below
+  Tile cur, nxt;
+  tile_of(t, cur);
+  set_blk(cur, blk_load(cur, true));
+  const bool has1 = t + wstride < ntiles;
+  if (has1) tile_of(t + wstride, nxt);
+  int bn = blk_load(nxt, has1);
+  uint4 a[4];
+  load_rows(cur, a);
+  for (; t < ntiles; t += wstride) {
+    Tile nn;
+    const bool has2 = t + 2 * wstride < ntiles;
+    if (has2) tile_of(t + 2 * wstride, nn);
+    const int bnn = blk_load(nn, has2);
+    // the next tile's rows are requested before this one is scored
+    uint4 an[4];
+    set_blk(nxt, bn);
+    load_rows(nxt, an);
+    if (cur.blk >= 0) { // wave-uniform
+      // |k|^2 of row `col` in fp32 (the four lanes of a row combined)
+      float r2 = 0.f;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int r = q ? r1 : r0;
-      const int p = p0 + r;
-      const int blk = sBlk[r];
-      if (blk < 0) continue; // wave-uniform
-      const int t = t0 + p / Hkv, h = p % Hkv, slot = t % kPage;
-      uint32_t *cw = codes + (((int64_t)blk * Hkv + h) * kPage + slot) * W;
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t wv[4] = {a[c].x, a[c].y, a[c].z, a[c].w};
 #pragma unroll
-      for (int c = 0; c < C; ++c) {
-        const uint64_t mask = __ballot((q ? acc1[c] : acc0[c]) > 0.0);
-        if (lane < 2) cw[2 * c + lane] = lane ? (uint32_t)(mask >> 32) : (uint32_t)mask;
+        for (int u = 0; u < 4; ++u) {
+          const float lo = bf16_to_float(wv[u] & 0xFFFFu), hi = bf16_to_float(wv[u] >> 16);
+          r2 = fmaf(lo, lo, r2);
+          r2 = fmaf(hi, hi, r2);
+        }
       }
-      if (lane == q)
-        radii[((int64_t)blk * Hkv + h) * kPage + slot] = (uint8_t)radius_code(r2);
+      r2 += __shfl_xor(r2, 16);
+      r2 += __shfl_xor(r2, 32);
+      if (lane < 16) sR2[wave][lane] = r2;
+      // (read back below by other lanes of the wave)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // the projections
+      v4f32 acc[NB];
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) acc[cb] = v4f32{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb)
+          acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf16(a[c]), bfr[cb][c],
+                                                            acc[cb], 0, 0, 0);
+      // the matrix ops stay in wave-uniform control flow
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) asm volatile("" : "+v"(acc[cb][0]), "+v"(acc[cb][1]), "+v"(acc[cb][2]), "+v"(acc[cb][3]));
+      // result lane L: keys 4q+i, column 16cb + col
+      float kb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        kb[i] = (float)(2 * (kHeadDim + 1)) * 0x1p-23f * sqrtf(sR2[wave][4 * q + i] * (1.f + 0x1p-20f));
+      // sign and certainty of entry (cb, i): bit 4*cb + i
+      uint32_t bits = 0, unc = 0;
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = acc[cb][i];
+          bits |= (uint32_t)(p > 0.f) << (4 * cb + i);
+          unc |= (uint32_t)!(fabsf(p) > fmaf(kb[i], cn[cb], 0x1p-100f)) << (4 * cb + i);
+        }
+      }
+      // radius code of row `lane` from the fp32 sum, unless near a threshold
+      int r8 = 0;
+      bool runc = false;
+      if (lane < kPage) {
+        const float r2f = sR2[wave][lane];
+        r8 = radius_code_f(r2f * (1.f - 0x1p-15f));
+        runc = r8 != radius_code_f(r2f * (1.f + 0x1p-15f));
+      }
+      if (__ballot(unc != 0u || runc)) { // rare: the fp64 chains decide
+        // the rows go to LDS (lane L holds dims 32q.. of row L%16)
+        uint4 *dst = reinterpret_cast<uint4 *>(&sRow[wave][col][32 * q]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) dst[c] = a[c];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        for (uint32_t m = unc; m; m &= m - 1) {
+          const int e = __builtin_ctz(m), cb = e >> 2, i = e & 3;
+          const double v = project_fp64(sRow[wave][4 * q + i], sPt[16 * cb + col]);
+          bits = (bits & ~(1u << e)) | ((uint32_t)(v > 0.0) << e);
+        }
+        if (runc) r8 = radius_code(sq_norm_fp64(sRow[wave][lane]));
+      }
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint64_t m = __ballot((bits >> (4 * cb + i)) & 1u);
+          if (lane == 0) sBal[wave][cb][i] = m;
+        }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // code words of this half: lane = key * WH + word
+      const int base = cur.p * kPage;
+      if (lane < kPage * WH) {
+        const int kk = lane / WH, w = lane % WH;
+        const int pos = base + kk;
+        const int qq = kk >> 2, ii = kk & 3;
+        const uint32_t lo = (uint32_t)(sBal[wave][2 * w][ii] >> (16 * qq)) & 0xFFFFu;
+        const uint32_t hi = (uint32_t)(sBal[wave][2 * w + 1][ii] >> (16 * qq)) & 0xFFFFu;
+        if (pos >= cur.start && pos < cur.end)
+          codes[(((int64_t)cur.blk * Hkv + cur.h) * kPage + kk) * W + half * WH + w] =
+              lo | (hi << 16);
+      }
+      // radius of row `lane` (one part writes it)
+      if (half == 0 && lane < kPage) {
+        const int pos = base + lane;
+        if (pos >= cur.start && pos < cur.end)
+          radii[((int64_t)cur.blk * Hkv + cur.h) * kPage + lane] = (uint8_t)r8;
+      }
     }
+    cur = nxt;
+    nxt = nn;
+    bn = bnn;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) a[c] = an[c];
   }
 }
 
@@ -129,17 +315,27 @@ hipError_t launch_encode(const uint16_t *k_pool, int64_t num_blocks,
                          int b, uint32_t *codes, uint8_t *radii,
                          hipStream_t stream) {
   if (max_encode_len <= 0 || batch <= 0) return hipSuccess;
-  dim3 grid((max_encode_len + kTile - 1) / kTile, batch);
-#define DKV_ENCODE_CASE(CV)                                                    \
-  if (b == 64 * CV) {                                                          \
-    hipLaunchKernelGGL(encode_kernel<CV>, grid, dim3(kThreads), 0, stream,     \
-                       k_pool, num_blocks, block_table, max_blocks, enc_start, \
-                       enc_end, max_encode_len, proj, Hkv, codes, radii);      \
+  // a range of n positions meets at most ceil(n/16) + 1 pages
+  const int pages_max = (max_encode_len + kPage - 1) / kPage + 1;
+  const int64_t ntiles = (int64_t)batch * pages_max * Hkv;
+  if (ntiles > 0x7FFFFFFF - 65536) return hipErrorInvalidValue;
+  if ((int64_t)batch * max_blocks >= (int64_t)1 << 30) return hipErrorInvalidValue;
+  // persistent: three workgroups of four waves per CU, over all parts
+  auto streams = [&](int parts) {
+    return std::min<int64_t>((ntiles + 3) / 4,
+                             std::max<int64_t>(1, 3LL * device_cu_count() / parts));
+  };
+#define DKV_ENCODE_CASE(BV, NBV, HV)                                           \
+  if (b == BV) {                                                               \
+    hipLaunchKernelGGL((encode_mfma_kernel<NBV, HV>), dim3((unsigned)(streams(HV) * HV)), \
+                       dim3(kMmThreads), 0, stream, k_pool, num_blocks,        \
+                       block_table, max_blocks, batch, enc_start, enc_end,     \
+                       max_encode_len, pages_max, proj, Hkv, codes, radii);    \
     return hipGetLastError();                                                  \
   }
-  DKV_ENCODE_CASE(1)
-  DKV_ENCODE_CASE(2)
-  DKV_ENCODE_CASE(4)
+  DKV_ENCODE_CASE(64, 4, 1)
+  DKV_ENCODE_CASE(128, 4, 2)
+  DKV_ENCODE_CASE(256, 4, 4)
 #undef DKV_ENCODE_CASE
   return hipErrorInvalidValue;
 }

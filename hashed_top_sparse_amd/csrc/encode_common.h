@@ -33,4 +33,21 @@ static __device__ int radius_code(double r2) {
   return (int)m;
 }
 
+// The same code from an fp32 |k|^2 with fp32 thresholds (each within 2^-24
+// of its double).  Only used to find codes whose value is certain: a caller
+// compares the codes of r2 (1 - 2^-15) and r2 (1 + 2^-15), which a rounding
+// of 2^-24 here cannot make equal when the exact code differs.
+__device__ __forceinline__ int radius_code_f(float r2) {
+  if (!(r2 > 0.f)) return 0;
+  int e;
+  const float M = 2.f * frexpf(r2, &e); // r2 = M * 2^(e-1), M in [1,2)
+  e -= 1;
+  int f = 0;
+#pragma unroll
+  for (int i = 1; i < 8; ++i)
+    if (M >= (float)kEighthOctave[i]) f = i;
+  const int m = 64 + 8 * e + f;
+  return m < 1 ? 0 : (m > 255 ? 255 : m);
+}
+
 } // namespace dkv

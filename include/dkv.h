@@ -156,7 +156,11 @@ typedef struct {
  * Bits are bit-exact with the definition above: the projection is summed in
  * double precision in index order (a product of two bf16 values is exact in
  * double), and the radius code comes from an exact double-precision
- * threshold table.
+ * threshold table.  (The library computes the projections on the matrix
+ * cores in fp32, keeps each sign whose margin exceeds a bound on the fp32
+ * error, and recomputes the others with the double-precision chain; the
+ * result is the same.)  batch * max_blocks_per_seq must stay below 2^30
+ * (DKV_ERR_UNSUPPORTED otherwise).
  */
 dkv_status dkv_encode(const dkv_config *cfg, const void *k_pool,
                       int64_t num_blocks, const int32_t *block_table,
