@@ -39,9 +39,16 @@ namespace {
 // once.  The next tile's rows are loaded while the current one is scored.
 typedef __bf16 v8bf16 __attribute__((ext_vector_type(8)));
 typedef float v4f32 __attribute__((ext_vector_type(4)));
+typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
 
 constexpr int kMmThreads = 256; // four waves
 constexpr int kRangeLds = 1024; // sequences whose encode range sits in LDS
+constexpr int kQueue = 64;      // uncertain signs queued per wave
+
+__device__ __forceinline__ uint32_t lanes_below_u64(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
 
 __device__ __forceinline__ v8bf16 as_v8bf16(const uint4 &u) {
   return __builtin_bit_cast(v8bf16, u);
@@ -67,11 +74,11 @@ __device__ double sq_norm_fp64(const uint16_t *krow) {
   return acc;
 }
 
-// NB: 16-column blocks per wave (64 columns: 64 VGPRs of fragments, three
+// NB: 16-column blocks per wave (64 columns: 64 VGPRs of fragments, two
 // waves per SIMD); HALVES: b/64 column parts, each taken by its own
 // workgroups (the parts of one tile load the same rows, from L2).
 template <int NB, int HALVES>
-__global__ __launch_bounds__(kMmThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
+__global__ __launch_bounds__(kMmThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void encode_mfma_kernel(const uint16_t *__restrict__ k_pool, int64_t num_blocks,
                         const int32_t *__restrict__ block_table, int max_blocks,
                         int batch, const int32_t *__restrict__ enc_start,
@@ -82,7 +89,9 @@ void encode_mfma_kernel(const uint16_t *__restrict__ k_pool, int64_t num_blocks,
   constexpr int NCOL = 16 * NB;    // columns of this workgroup
   constexpr int WH = NB / 2;       // code words per key in one half
   __shared__ __align__(16) uint16_t sPt[NCOL][kHeadDim]; // P^T of the half
-  __shared__ uint64_t sBal[kMmThreads / 64][NB][4];
+  __shared__ uint64_t sBal[kMmThreads / 64][NB][4]; // sign masks of (cb, i)
+  __shared__ uint64_t sUnc[kMmThreads / 64][NB][4]; // uncertain entries
+  __shared__ uint4 sQ[kMmThreads / 64][kQueue];      // queued fp64 chains
   __shared__ float sR2[kMmThreads / 64][16];
   __shared__ int2 sRange[kRangeLds];
   // a tile's key rows, staged only when an fp64 chain has to run
@@ -132,29 +141,52 @@ void encode_mfma_kernel(const uint16_t *__restrict__ k_pool, int64_t num_blocks,
     n2 += __shfl_xor(n2, 32);
     cn[cb] = sqrtf(n2) * (1.f + 0x1p-20f);
   }
+  // tiles t = ((s * pages_max + pi) * Hkv + h): the heads of a page are
+  // neighbours; each wave walks a contiguous run of them (a carry step per
+  // tile, no divisions) -- the parts of one tile walk the same runs
   const int ntiles = batch * pages_max * Hkv;
-  const int wstride = (gridDim.x / HALVES) * (kMmThreads / 64);
+  const int nstream = (int)(gridDim.x / HALVES) * (kMmThreads / 64);
+  const int chunk = (ntiles + nstream - 1) / nstream;
+  const int wid = (int)(blockIdx.x / HALVES) * (kMmThreads / 64) + wave;
+  const int t_begin = wid * chunk, t_end = min(ntiles, t_begin + chunk);
+  if (t_begin >= t_end) return; // no barriers below
 
   struct Tile {
-    int s, h, p, start, end, blk;
+    int s, pi, h, start, end, p, blk;
+    bool any; // inside the wave's run
   };
-  // tile id -> tile, block id not yet known
-  auto tile_of = [&](int t, Tile &T) {
-    T.h = t % Hkv;
-    const int r = t / Hkv;
-    T.s = r % batch;
-    const int pi = r / batch;
+  auto set_seq = [&](Tile &T) {
     const int2 rg = T.s < kRangeLds ? sRange[T.s] : range_of(T.s);
     T.start = rg.x;
     T.end = rg.y;
-    T.p = T.start / kPage + pi;
+  };
+  auto tile_at = [&](int t, Tile &T) {
+    T.h = t % Hkv;
+    const int r = t / Hkv;
+    T.pi = r % pages_max;
+    T.s = r / pages_max;
+    set_seq(T);
+    T.p = T.start / kPage + T.pi;
+    T.any = t < t_end;
+    T.blk = -1;
+  };
+  auto step = [&](Tile &T, int t_next) { // T becomes tile t_next = its id + 1
+    if (++T.h == Hkv) {
+      T.h = 0;
+      if (++T.pi == pages_max) {
+        T.pi = 0;
+        if (++T.s < batch) set_seq(T);
+      }
+      T.p = T.start / kPage + T.pi;
+    }
+    T.any = t_next < t_end;
     T.blk = -1;
   };
   // the tile's block id by a vector load (a scalar load would stall the
   // wave where it is used; this one is issued a tile ahead), or -1 when the
   // page is past the range
-  auto blk_load = [&](const Tile &T, bool any) -> int {
-    if (!any || T.p * kPage >= T.end) return -1;
+  auto blk_load = [&](const Tile &T) -> int {
+    if (!T.any || T.p * kPage >= T.end) return -1;
     return __builtin_amdgcn_raw_buffer_load_b32(
         bt_rsrc, (T.s * max_blocks + T.p) * 4, 0, 0);
   };
@@ -176,38 +208,64 @@ void encode_mfma_kernel(const uint16_t *__restrict__ k_pool, int64_t num_blocks,
     }
   };
 
+  // the queue of uncertain signs: (key row, code word, column | bit << 8)
+  uint32_t qn = 0;
+  auto flush = [&]() {
+    // the words these entries patch were stored by this wave: let those
+    // stores complete first
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if ((uint32_t)lane < qn) {
+      const uint4 ent = sQ[wave][lane];
+      const uint4 *krow = reinterpret_cast<const uint4 *>(k_pool + (int64_t)ent.x * kHeadDim);
+      const uint16_t *pcol = sPt[ent.z & 0xFFu];
+      double v = 0.0; // the index-order chain
+      for (int c = 0; c < kHeadDim / 8; ++c) {
+        const uint4 k8 = krow[c];
+        const uint32_t kw[4] = {k8.x, k8.y, k8.z, k8.w};
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const uint32_t kb16 = (u & 1) ? (kw[u / 2] >> 16) : (kw[u / 2] & 0xFFFFu);
+          v = fma((double)bf16_to_float(kb16), (double)bf16_to_float(pcol[8 * c + u]), v);
+        }
+      }
+      const uint32_t bit = 1u << (ent.z >> 8);
+      if (v > 0.0)
+        atomicOr(&codes[ent.y], bit);
+      else
+        atomicAnd(&codes[ent.y], ~bit);
+    }
+    qn = 0;
+  };
+
   // three stages: the block id of tile k+2, the rows of tile k+1 and the
   // scoring of tile k overlap
-  int t = (int)(blockIdx.x / HALVES) * (kMmThreads / 64) + wave;
-  if (t >= ntiles) return; // no barriers below
   Tile cur, nxt;
-  tile_of(t, cur);
-  set_blk(cur, blk_load(cur, true));
-  const bool has1 = t + wstride < ntiles;
-  if (has1) tile_of(t + wstride, nxt);
-  int bn = blk_load(nxt, has1);
+  tile_at(t_begin, cur);
+  set_blk(cur, blk_load(cur));
+  nxt = cur;
+  step(nxt, t_begin + 1);
+  int bn = blk_load(nxt);
   uint4 a[4];
   load_rows(cur, a);
-  for (; t < ntiles; t += wstride) {
-    Tile nn;
-    const bool has2 = t + 2 * wstride < ntiles;
-    if (has2) tile_of(t + 2 * wstride, nn);
-    const int bnn = blk_load(nn, has2);
+  for (int t = t_begin; t < t_end; ++t) {
+    Tile nn = nxt;
+    step(nn, t + 2);
+    const int bnn = blk_load(nn);
     // the next tile's rows are requested before this one is scored
     uint4 an[4];
     set_blk(nxt, bn);
     load_rows(nxt, an);
     if (cur.blk >= 0) { // wave-uniform
-      // |k|^2 of row `col` in fp32 (the four lanes of a row combined)
+      // |k|^2 of row `col` in fp32, two bf16 squares per dot2 (the four
+      // lanes of a row combined)
       float r2 = 0.f;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const uint32_t wv[4] = {a[c].x, a[c].y, a[c].z, a[c].w};
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const float lo = bf16_to_float(wv[u] & 0xFFFFu), hi = bf16_to_float(wv[u] >> 16);
-          r2 = fmaf(lo, lo, r2);
-          r2 = fmaf(hi, hi, r2);
+          const v2bf16 x = __builtin_bit_cast(v2bf16, wv[u]);
+          r2 = __builtin_amdgcn_fdot2_f32_bf16(x, x, r2, false);
         }
       }
       r2 += __shfl_xor(r2, 16);
@@ -235,17 +293,30 @@ void encode_mfma_kernel(const uint16_t *__restrict__ k_pool, int64_t num_blocks,
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         kb[i] = (float)(2 * (kHeadDim + 1)) * 0x1p-23f * sqrtf(sR2[wave][4 * q + i] * (1.f + 0x1p-20f));
-      // sign and certainty of entry (cb, i): bit 4*cb + i
-      uint32_t bits = 0, unc = 0;
+      // rows of the tile inside the encode range (result layout: 4q + i)
+      const int base = cur.p * kPage;
+      uint64_t inr[4];
 #pragma unroll
-      for (int cb = 0; cb < NB; ++cb) {
+      for (int i = 0; i < 4; ++i) {
+        const int pos = base + 4 * q + i;
+        inr[i] = __ballot(pos >= cur.start && pos < cur.end);
+      }
+      // signs and uncertain entries of (cb, i) as wave masks, to LDS
+      uint32_t n_unc = 0;
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float p = acc[cb][i];
-          bits |= (uint32_t)(p > 0.f) << (4 * cb + i);
-          unc |= (uint32_t)!(fabsf(p) > fmaf(kb[i], cn[cb], 0x1p-100f)) << (4 * cb + i);
+          const uint64_t pos = __ballot(p > 0.f);
+          const uint64_t unc =
+              __ballot(!(fabsf(p) > fmaf(kb[i], cn[cb], 0x1p-100f))) & inr[i];
+          n_unc += (uint32_t)__popcll(unc);
+          if (lane == 0) {
+            sBal[wave][cb][i] = pos;
+            sUnc[wave][cb][i] = unc;
+          }
         }
-      }
       // radius code of row `lane` from the fp32 sum, unless near a threshold
       int r8 = 0;
       bool runc = false;
@@ -254,7 +325,31 @@ void encode_mfma_kernel(const uint16_t *__restrict__ k_pool, int64_t num_blocks,
         r8 = radius_code_f(r2f * (1.f - 0x1p-15f));
         runc = r8 != radius_code_f(r2f * (1.f + 0x1p-15f));
       }
-      if (__ballot(unc != 0u || runc)) { // rare: the fp64 chains decide
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // Uncertain signs: the fp32 sign is written now and the entry joins
+      // the wave's queue, whose fp64 chains run 64 at a time (one per lane)
+      // and patch the written words; a tile with more entries than the
+      // queue holds runs its chains here.
+      const bool inline_fix = n_unc > (uint32_t)kQueue;
+      if (n_unc != 0 && !inline_fix) {
+        if (qn + n_unc > (uint32_t)kQueue) flush();
+        for (int e = 0; e < NB * 4; ++e) {
+          const int cb = e >> 2, i = e & 3;
+          const uint64_t unc = sUnc[wave][cb][i];
+          if (unc == 0) continue; // wave-uniform
+          if ((unc >> lane) & 1u) {
+            const int kk = 4 * q + i;
+            sQ[wave][qn + lanes_below_u64(unc)] = make_uint4(
+                (uint32_t)(((int64_t)cur.blk * kPage + kk) * Hkv + cur.h),
+                (uint32_t)((((int64_t)cur.blk * Hkv + cur.h) * kPage + kk) * W + half * WH + cb / 2),
+                (uint32_t)(16 * cb + col) | ((uint32_t)(16 * (cb & 1) + col) << 8), 0u);
+          }
+          qn += (uint32_t)__popcll(unc);
+        }
+      }
+      if (inline_fix || __ballot(runc)) { // rare: the fp64 chains decide
         // the rows go to LDS (lane L holds dims 32q.. of row L%16)
         uint4 *dst = reinterpret_cast<uint4 *>(&sRow[wave][col][32 * q]);
 #pragma unroll
@@ -262,25 +357,22 @@ void encode_mfma_kernel(const uint16_t *__restrict__ k_pool, int64_t num_blocks,
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        for (uint32_t m = unc; m; m &= m - 1) {
-          const int e = __builtin_ctz(m), cb = e >> 2, i = e & 3;
-          const double v = project_fp64(sRow[wave][4 * q + i], sPt[16 * cb + col]);
-          bits = (bits & ~(1u << e)) | ((uint32_t)(v > 0.0) << e);
+        for (int e = 0; inline_fix && e < NB * 4; ++e) {
+          const int cb = e >> 2, i = e & 3;
+          const uint64_t unc = sUnc[wave][cb][i];
+          if (unc == 0) continue; // wave-uniform
+          const bool mine = (unc >> lane) & 1u;
+          double v = 0.0;
+          if (mine) v = project_fp64(sRow[wave][4 * q + i], sPt[16 * cb + col]);
+          const uint64_t fixed = __ballot(mine && v > 0.0);
+          if (lane == 0) sBal[wave][cb][i] = (sBal[wave][cb][i] & ~unc) | fixed;
         }
         if (runc) r8 = radius_code(sq_norm_fp64(sRow[wave][lane]));
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       }
-#pragma unroll
-      for (int cb = 0; cb < NB; ++cb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint64_t m = __ballot((bits >> (4 * cb + i)) & 1u);
-          if (lane == 0) sBal[wave][cb][i] = m;
-        }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // code words of this half: lane = key * WH + word
-      const int base = cur.p * kPage;
+      // code words of this part: lane = key * WH + word
       if (lane < kPage * WH) {
         const int kk = lane / WH, w = lane % WH;
         const int pos = base + kk;
@@ -297,6 +389,10 @@ void encode_mfma_kernel(const uint16_t *__restrict__ k_pool, int64_t num_blocks,
         if (pos >= cur.start && pos < cur.end)
           radii[((int64_t)cur.blk * Hkv + cur.h) * kPage + lane] = (uint8_t)r8;
       }
+      // the next tile's LDS writes wait for these reads
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
     cur = nxt;
     nxt = nn;
@@ -304,6 +400,7 @@ void encode_mfma_kernel(const uint16_t *__restrict__ k_pool, int64_t num_blocks,
 #pragma unroll
     for (int c = 0; c < 4; ++c) a[c] = an[c];
   }
+  if (qn != 0) flush();
 }
 
 } // namespace
@@ -320,10 +417,13 @@ hipError_t launch_encode(const uint16_t *k_pool, int64_t num_blocks,
   const int64_t ntiles = (int64_t)batch * pages_max * Hkv;
   if (ntiles > 0x7FFFFFFF - 65536) return hipErrorInvalidValue;
   if ((int64_t)batch * max_blocks >= (int64_t)1 << 30) return hipErrorInvalidValue;
-  // persistent: three workgroups of four waves per CU, over all parts
+  // queued fixes name key rows and code words with 32-bit indices
+  if ((uint64_t)num_blocks * kPage * Hkv * (b / 32) >= (uint64_t)1 << 32)
+    return hipErrorInvalidValue;
+  // persistent: two workgroups of four waves per CU, over all parts
   auto streams = [&](int parts) {
     return std::min<int64_t>((ntiles + 3) / 4,
-                             std::max<int64_t>(1, 3LL * device_cu_count() / parts));
+                             std::max<int64_t>(1, 2LL * device_cu_count() / parts));
   };
 #define DKV_ENCODE_CASE(BV, NBV, HV)                                           \
   if (b == BV) {                                                               \
