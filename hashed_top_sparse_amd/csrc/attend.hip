@@ -23,8 +23,9 @@
 //     rescale factors to the value pass through a per-wave LDS tile;
 //   - values on the vector units: 16-lane row groups, lane l holding dims
 //     8l .. 8l+7 of rows g, g+4, g+8, g+12 of the tile.
-// The next tile's key and value rows are loaded while the current one is
-// used.  The selection list already holds physical row ids (page*16 +
+// A wave requests all its tiles' key and value rows at once, then uses them
+// in order (its 64 row ids come with one load and are handed out by lane
+// shuffles).  The selection list already holds physical row ids (page*16 +
 // slot); all G query heads of the KV group share the rows.
 #include "internal.h"
 
@@ -105,12 +106,9 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(
   const int r0 = split * kAttnRows;
   const int r1 = (r0 + kAttnRows < n) ? r0 + kAttnRows : n;
 
-  // the split's row ids, once, into LDS
-  __shared__ int32_t sid[kAttnRows];
-  for (int i = threadIdx.x; i < kAttnRows; i += kThreads) {
-    const int r = r0 + i;
-    sid[i] = r < r1 ? rows[(int64_t)unit * cap + r] : -1;
-  }
+  // this wave's 64 row ids, one per lane (handed out by lane shuffles)
+  const int row0 = wave * kWaveRows;
+  const int myid = r0 + row0 + lane < r1 ? rows[(int64_t)unit * cap + r0 + row0 + lane] : -1;
 
   // query operand: head lrow (zero past G); K-step c takes dims
   // 32c + 8*lgrp .. +8, the same dims the key rows give this lane
@@ -122,7 +120,6 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(
 #pragma unroll
     for (int c = 0; c < 4; ++c) qb[c] = *reinterpret_cast<const uint4 *>(src + 32 * c);
   }
-  __syncthreads();
 
   // per-wave hand-off tile: p[row][head] and the rescale factors
   __shared__ __attribute__((aligned(16))) float sp[kWaves][kTileRows][kPStride];
@@ -135,10 +132,9 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[h][c] = 0.f;
 
-  const int row0 = wave * kWaveRows;
   auto load_tile = [&](int t, uint4 (&kr)[4], uint4 (&vr)[4], uint32_t &kvalid) {
-    const int base = row0 + t * kTileRows;
-    const int kid = sid[base + lrow];
+    const int base = t * kTileRows;
+    const int kid = __shfl(myid, base + lrow);
     kvalid = kid >= 0;
 #pragma unroll
     for (int c = 0; c < 4; ++c) kr[c] = make_uint4(0u, 0u, 0u, 0u);
@@ -150,7 +146,7 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int vid = sid[base + lgrp + 4 * i];
+      const int vid = __shfl(myid, base + lgrp + 4 * i);
       vr[i] = make_uint4(0u, 0u, 0u, 0u);
       if (vid >= 0)
         vr[i] = *reinterpret_cast<const uint4 *>(
@@ -225,16 +221,13 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(
     __builtin_amdgcn_wave_barrier();
   };
   {
-    uint4 ka[4], va[4], kb[4], vb[4];
-    uint32_t oka, okb;
-    load_tile(0, ka, va, oka);
+    // every tile's rows are requested at once, then used in order
+    uint4 kt[kTiles][4], vt[kTiles][4];
+    uint32_t ok[kTiles];
 #pragma unroll
-    for (int t = 0; t < kTiles; t += 2) {
-      if (t + 1 < kTiles) load_tile(t + 1, kb, vb, okb);
-      use_tile(ka, va, oka);
-      if (t + 2 < kTiles) load_tile(t + 2, ka, va, oka);
-      if (t + 1 < kTiles) use_tile(kb, vb, okb);
-    }
+    for (int t = 0; t < kTiles; ++t) load_tile(t, kt[t], vt[t], ok[t]);
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) use_tile(kt[t], vt[t], ok[t]);
   }
 
   // The wave's state: m, l per head (lane lrow), acc per row group over its
