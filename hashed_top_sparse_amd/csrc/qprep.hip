@@ -109,7 +109,25 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     }
     return P;
   };
-  // The sample pages' loads go first so they are in flight while the query
+  // P and the group's query rows are requested first, into registers: the
+  // staging barrier below then waits only for them and not for the sample
+  // pages requested after them (loads count down in order).
+  constexpr int kPLoads = 4 * KS; // uint4 of P per thread (b <= 128 * KS)
+  uint4 pv[kPLoads];
+  const int pn = kHeadDim * b / 8;
+  {
+    const uint4 *psrc = reinterpret_cast<const uint4 *>(proj); // 16-byte aligned
+#pragma unroll
+    for (int r = 0; r < kPLoads; ++r) {
+      const int i = (int)threadIdx.x + r * kThreads;
+      pv[r] = i < pn ? psrc[i] : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  const uint4 *qsrc = reinterpret_cast<const uint4 *>(
+      q + ((int64_t)s * Hq + (int64_t)g * G) * kHeadDim);
+  const uint4 qv4 = (int)threadIdx.x < G * kHeadDim / 8 ? qsrc[threadIdx.x]
+                                                         : make_uint4(0u, 0u, 0u, 0u);
+  // The sample pages' loads go next so they are in flight while the query
   // is projected.  Their block ids are read with the plan of the longest
   // length (n_max) before the sequence's own length has arrived; when that
   // length gives another stride or start (ragged batches) they are read
@@ -158,13 +176,11 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     reinterpret_cast<uint32_t *>(sK)[threadIdx.x] = krow[threadIdx.x];
   }
 
-  const uint16_t *qg = q + ((int64_t)s * Hq + (int64_t)g * G) * kHeadDim;
-  for (int i = threadIdx.x; i < G * kHeadDim; i += kThreads)
-    sQ[i] = qg[i];
-  { // proj is 16-byte aligned (checked on the host)
-    const uint4 *src = reinterpret_cast<const uint4 *>(proj);
-    uint4 *dst = reinterpret_cast<uint4 *>(sP);
-    for (int i = threadIdx.x; i < kHeadDim * b / 8; i += kThreads) dst[i] = src[i];
+  if ((int)threadIdx.x < G * kHeadDim / 8) reinterpret_cast<uint4 *>(sQ)[threadIdx.x] = qv4;
+#pragma unroll
+  for (int r = 0; r < kPLoads; ++r) {
+    const int i = (int)threadIdx.x + r * kThreads;
+    if (i < pn) reinterpret_cast<uint4 *>(sP)[i] = pv[r];
   }
   if (threadIdx.x < 8) sSum[threadIdx.x] = 0;
   __syncthreads();
