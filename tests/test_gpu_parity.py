@@ -485,3 +485,31 @@ def test_lsh_index_of_nothing():
 def test_full_size_lsh(name, units, over):
     _run_lsh(workloads.get(name), units, index_back=100, **over)
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------- every code width x group size
+@pytest.mark.parametrize("b", [64, 128, 256])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_every_code_width_and_group_size(b, G):
+    """Each (b, G) pair runs its own kernel instantiations: a small batch of
+    two sequences, two KV heads, every unit checked."""
+    import dataclasses
+    wl = dataclasses.replace(workloads.get("small_gqa_b128"), name=f"b{b}_g{G}",
+                             code_bits=b, num_q_heads=2 * G, num_kv_heads=2,
+                             seq_len=2500, needles=4, top_k=160, window=48)
+    stats = _run(wl)
+    rec = [st["recall"] for st in stats if st["recall"] is not None]
+    assert rec and all(r == 1.0 for r in rec)
+
+
+@pytest.mark.parametrize("G", [2, 8])
+@pytest.mark.parametrize("mode", ["pages", "lsh"])
+def test_group_sizes_in_page_and_lsh_modes(G, mode):
+    import dataclasses
+    wl = dataclasses.replace(workloads.get("small_gqa_b128"), name=f"{mode}_g{G}",
+                             num_q_heads=2 * G, num_kv_heads=2, seq_len=3000,
+                             needles=4, top_k=160, window=48)
+    if mode == "pages":
+        _run(wl, **PAGES)
+    else:
+        _run_lsh(wl, index_back=40, lsh_tables=8, lsh_bits=7)
