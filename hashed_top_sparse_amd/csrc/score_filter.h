@@ -357,22 +357,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
       const bool isc = PAGES ? ((lane & 15) == 0 && cu != 0u && cu >= LC) : (inr && cu >= LC);
       const uint64_t m = PAGES ? __ballot(cu != 0u) & __ballot(cu >= LC) & kRowHeads
                                : __ballot(inr) & __ballot(cu >= LC);
-      const uint32_t cslot = __builtin_amdgcn_mbcnt_hi(
-          (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, nc));
-      const uint32_t lslot = used + cslot;
+      const uint32_t lslot = __builtin_amdgcn_mbcnt_hi(
+          (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, used + nc));
       // Every lane writes (a branch around the write would leave the
       // compiler unsure whether it was issued, and every later LDS wait
       // would then wait for it): lanes without a listed candidate write
       // their spare entry.  An address-space-qualified pointer keeps this an
       // LDS store (a flat store would count against the vector-memory wait
-      // counter).
-      const uint32_t wslot = (isc && lslot < (uint32_t)kCandList)
-                                 ? lslot : (uint32_t)(kCandList + lane);
-      ((__attribute__((address_space(3))) uint64_t *)cst)[wslot] =
-          ((uint64_t)cidx << 32) | cu;
-      if (used + nc + (uint32_t)__popcll(m) > (uint32_t)kCandList) { // rare
-        if (isc && lslot >= (uint32_t)kCandList)
-          ((__attribute__((address_space(1))) uint64_t *)reg)[cslot] =
+      // counter).  While the list has room for a whole quad (wave-uniform),
+      // a candidate's slot needs no range test.
+      if (used + nc + 64u <= (uint32_t)kCandList) {
+        const uint32_t wslot = isc ? lslot : (uint32_t)(kCandList + lane);
+        ((__attribute__((address_space(3))) uint64_t *)cst)[wslot] =
+            ((uint64_t)cidx << 32) | cu;
+      } else { // the list is nearly full (rare): the rest go to the region
+        const bool listed = isc && lslot < (uint32_t)kCandList;
+        const uint32_t wslot = listed ? lslot : (uint32_t)(kCandList + lane);
+        ((__attribute__((address_space(3))) uint64_t *)cst)[wslot] =
+            ((uint64_t)cidx << 32) | cu;
+        if (isc && !listed)
+          ((__attribute__((address_space(1))) uint64_t *)reg)[lslot - used] =
               ((uint64_t)(cbase + cidx) << 32) | cu;
       }
       nc += (uint32_t)__popcll(m);
