@@ -166,7 +166,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
       for (uint32_t e0 = 0; e0 < nbuf; e0 += 64) {
         const uint32_t e = min(e0 + (uint32_t)lane, nbuf - 1);
         const uint2 v = cst[start + e];
-        reg[e] = make_uint2(v.x, key0 + v.y);
+        // key lists hold raw scores: biased here, once per candidate
+        reg[e] = make_uint2(PAGES ? v.x : v.x + kScoreBias, key0 + v.y);
       }
       if (lane == 0) tcount[t_idx] = ncount;
       start += nbuf;
@@ -250,6 +251,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   QueryOperand<KS> opC;
   uint32_t LC;
+  int LCs; // LC as a signed score: S >= LCs iff S + 2^31 >= LC
   {
     QueryOperandRaw<KS> raw;
     load_op(C, raw, LC);
@@ -264,6 +266,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     for (int i = 0; i < 8; ++i) mark_loaded((uint32_t)opC.a[ks][i]);
 #pragma unroll
   for (int i = 0; i < 4; ++i) mark_loaded(__float_as_uint(opC.cinit[i]));
+  LCs = (int)(LC ^ kScoreBias);
   // radius lines: lane j loads page j's 16 bytes (a task ahead of use)
   auto load_radius = [&](uint32_t ph) -> uint4 {
     const auto v = __builtin_amdgcn_raw_buffer_load_b128(rad_rsrc, (int)(ph * (uint32_t)kPage), 0, 0);
@@ -297,6 +300,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     // first position (page, for PAGES) of the task: list entries hold
     // their index relative to it
     const uint32_t cbase = PAGES ? (uint32_t)(C.key0 / kPage) : (uint32_t)C.key0;
+    // pos - lo of this lane's key in quad q is lrel + 64 q (one add a quad)
+    const uint32_t lrel = (uint32_t)(lane + C.key0 - C.lo);
+    const uint32_t nrange = (uint32_t)(C.hi - C.lo);
     uint2 *reg = cand + t_idx * kGroupKeys;
     uint32_t nc = 0; // the task's candidates so far
     static_for<0, kTaskQuads>([&](auto qc) {
@@ -338,7 +344,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
         for (int j = 0; j < 4; ++j) cw[j][ks] = x[ks][j];
       }
       const int mx = score_quad_max_seq<KS, G>(opC, cw);
-      const uint32_t u = biased_score(__mul24(wgt, mx));
+      const int Sv = __mul24(wgt, mx);
+      const uint32_t u = biased_score(Sv);
       const int qpos = C.key0 + 64 * q; // first position of the quad
       const int pos = qpos + lane;
       if constexpr (DBG) {
@@ -346,17 +353,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
           scores_out[(int64_t)C.unit * score_stride + pos] = (int32_t)(u - kScoreBias);
       }
       // A candidate: position in [lo, hi) and u >= L, each test one
-      // compare (the range one on pos - lo, unsigned).  It is appended to
+      // compare (the range one on pos - lo, unsigned, as lrel + 64 q).  It is appended to
       // the wave's LDS list without a branch: its slot in the task is the
       // running count plus the candidates in lower lanes.
-      const bool inr = (uint32_t)(pos - C.lo) < (uint32_t)(C.hi - C.lo);
+      const bool inr = lrel + (uint32_t)(64 * q) < nrange;
       // PAGES: the first lane of each 16-lane row stands for its page, with
       // the best u of the page's keys in [lo, hi) (0: none there)
-      const uint32_t cu = PAGES ? row_max16(inr ? u : 0u) : u;
+      // (keys: the raw score, compared signed with the threshold and biased
+      // when the list is written out)
+      const uint32_t cu = PAGES ? row_max16(inr ? u : 0u) : (uint32_t)Sv;
+      const bool pass = PAGES ? cu >= LC : Sv >= LCs;
       const uint32_t cidx = PAGES ? (uint32_t)(4 * q + (lane >> 4)) : (uint32_t)(64 * q + lane);
-      const bool isc = PAGES ? ((lane & 15) == 0 && cu != 0u && cu >= LC) : (inr && cu >= LC);
-      const uint64_t m = PAGES ? __ballot(cu != 0u) & __ballot(cu >= LC) & kRowHeads
-                               : __ballot(inr) & __ballot(cu >= LC);
+      const bool isc = PAGES ? ((lane & 15) == 0 && cu != 0u && pass) : (inr && pass);
+      const uint64_t m = PAGES ? __ballot(cu != 0u) & __ballot(pass) & kRowHeads
+                               : __ballot(inr) & __ballot(pass);
       const uint32_t lslot = __builtin_amdgcn_mbcnt_hi(
           (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, used + nc));
       // Every lane writes (a branch around the write would leave the
@@ -377,7 +387,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
             ((uint64_t)cidx << 32) | cu;
         if (isc && !listed)
           ((__attribute__((address_space(1))) uint64_t *)reg)[lslot - used] =
-              ((uint64_t)(cbase + cidx) << 32) | cu;
+              ((uint64_t)(cbase + cidx) << 32) | (PAGES ? cu : cu + kScoreBias);
       }
       nc += (uint32_t)__popcll(m);
     });
@@ -400,6 +410,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     C = T1;
     opC = finish_query_operand<KS, G>(op1, lane);
     LC = L1;
+    LCs = (int)(LC ^ kScoreBias);
     T1 = T2;
     t1 = t2;
     {
