@@ -237,24 +237,28 @@ void encode_mfma_kernel(const uint16_t *__restrict__ k_pool, int64_t num_blocks,
     qn = 0;
   };
 
-  // three stages: the block id of tile k+2, the rows of tile k+1 and the
-  // scoring of tile k overlap
-  Tile cur, nxt;
+  // four stages: the block id of tile k+3, the rows of tiles k+2 and k+1
+  // (two tiles of rows in flight) and the scoring of tile k overlap
+  Tile cur, nxt, nx2;
   tile_at(t_begin, cur);
   set_blk(cur, blk_load(cur));
   nxt = cur;
   step(nxt, t_begin + 1);
-  int bn = blk_load(nxt);
-  uint4 a[4];
+  set_blk(nxt, blk_load(nxt));
+  nx2 = nxt;
+  step(nx2, t_begin + 2);
+  int bn2 = blk_load(nx2);
+  uint4 a[4], an[4];
   load_rows(cur, a);
+  load_rows(nxt, an);
   for (int t = t_begin; t < t_end; ++t) {
-    Tile nn = nxt;
-    step(nn, t + 2);
+    Tile nn = nx2;
+    step(nn, t + 3);
     const int bnn = blk_load(nn);
-    // the next tile's rows are requested before this one is scored
-    uint4 an[4];
-    set_blk(nxt, bn);
-    load_rows(nxt, an);
+    // the rows two tiles ahead are requested before this one is scored
+    uint4 an2[4];
+    set_blk(nx2, bn2);
+    load_rows(nx2, an2);
     if (cur.blk >= 0) { // wave-uniform
       // |k|^2 of row `col` in fp32, two bf16 squares per dot2 (the four
       // lanes of a row combined)
@@ -395,10 +399,14 @@ void encode_mfma_kernel(const uint16_t *__restrict__ k_pool, int64_t num_blocks,
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
     cur = nxt;
-    nxt = nn;
-    bn = bnn;
+    nxt = nx2;
+    nx2 = nn;
+    bn2 = bnn;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) a[c] = an[c];
+    for (int c = 0; c < 4; ++c) {
+      a[c] = an[c];
+      an[c] = an2[c];
+    }
   }
   if (qn != 0) flush();
 }
