@@ -244,7 +244,7 @@ __device__ __forceinline__ int score_quad_max(const QueryOperand<KS> &op,
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     float m = 16.f * acc[j][0] + acc[j][1];
-    if (G >= 2) m = fmaxf(m, 16.f * acc[j][2] + acc[j][3]);
+    if (G >= 2) m = max_score(m, 16.f * acc[j][2] + acc[j][3]);
     // all 64 lanes take part: keep the ops in wave-uniform control flow
     asm volatile("" : "+v"(m));
     if (G >= 8) m = max_rows32(m);

@@ -40,11 +40,14 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kTaskQuads = kGroupPages / 4; // page quads per task
-constexpr int kDepth = 4;                   // quads of loads in flight per wave
-static_assert(kTaskQuads % kDepth == 0 && kTaskQuads >= 2 * kDepth, "prefetch rounds");
+// quads of loads in flight per wave: 4 KB per wave for every code width
+// (256-bit codes hold two quads; four would spill registers)
+template <int W>
+constexpr int kDepthFor = W > 4 ? 2 : 4;
 // quad of a task at which the task after next and the next task's operand
 // are loaded: kDepth quads before the next task's first prefetch
-constexpr int kLookahead = kTaskQuads - 2 * kDepth;
+template <int W>
+constexpr int kLookaheadFor = kTaskQuads - 2 * kDepthFor<W>;
 // Workgroups per CU: one wave per SIMD each, four waves per SIMD in all.
 // More resident waves do not help (the kernel is bound by instruction
 // issue), and four per SIMD keeps each wave's task count equal when the
@@ -108,6 +111,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     int ntasks, int w, int sigma, uint2 *__restrict__ cand,
     uint32_t *__restrict__ tcount, int cand_groups,
     int32_t *__restrict__ scores_out, int score_stride) {
+  constexpr int kDepth = kDepthFor<W>;
+  constexpr int kLookahead = kLookaheadFor<W>;
+  static_assert(kTaskQuads % kDepth == 0 && kTaskQuads >= 2 * kDepth, "prefetch rounds");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int stride = gridDim.x * kWaves;
@@ -305,6 +311,48 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     const uint32_t nrange = (uint32_t)(C.hi - C.lo);
     uint2 *reg = cand + t_idx * kGroupKeys;
     uint32_t nc = 0; // the task's candidates so far
+    // Scores quad q of C from its loaded words x (transposed here) and the
+    // radius weights, and returns its candidates: the entry (cu, cidx) of
+    // this lane, whether it is one (isc), and the wave's mask of them.
+    struct QuadCand {
+      uint32_t cu, cidx;
+      bool isc;
+      uint64_t m;
+    };
+    auto quad_cands = [&](int q, uint32_t (&x)[KS][4], int wgt) -> QuadCand {
+      uint32_t cw[4][KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        transpose_rows(x[ks]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cw[j][ks] = x[ks][j];
+      }
+      // (256-bit codes: the pages one after another, which needs fewer
+      // registers)
+      const int mx = KS > 1 ? score_quad_max_seq<KS, G>(opC, cw) : score_quad_max<KS, G>(opC, cw);
+      const int Sv = __mul24(wgt, mx);
+      const uint32_t u = biased_score(Sv);
+      const int pos = C.key0 + 64 * q + lane;
+      if constexpr (DBG) {
+        if (pos < C.N)
+          scores_out[(int64_t)C.unit * score_stride + pos] = (int32_t)(u - kScoreBias);
+      }
+      // A candidate: position in [lo, hi) and u >= L, each test one compare
+      // (the range one on pos - lo, unsigned, as lrel + 64 q).
+      const bool inr = lrel + (uint32_t)(64 * q) < nrange;
+      QuadCand c;
+      // PAGES: the first lane of each 16-lane row stands for its page, with
+      // the best u of the page's keys in [lo, hi) (0: none there).  Keys:
+      // the raw score, compared signed with the threshold and biased when
+      // the list is written out.
+      c.cu = PAGES ? row_max16(inr ? u : 0u) : (uint32_t)Sv;
+      const bool pass = PAGES ? c.cu >= LC : Sv >= LCs;
+      c.cidx = PAGES ? (uint32_t)(4 * q + (lane >> 4)) : (uint32_t)(64 * q + lane);
+      c.isc = PAGES ? ((lane & 15) == 0 && c.cu != 0u && pass) : (inr && pass);
+      c.m = PAGES ? __ballot(c.cu != 0u) & __ballot(pass) & kRowHeads
+                  : __ballot(inr) & __ballot(pass);
+      return c;
+    };
     static_for<0, kTaskQuads>([&](auto qc) {
       constexpr int q = decltype(qc)::value;
       constexpr int slot = q % kDepth;
@@ -336,61 +384,48 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
         refc = (q + 1 + kDepth < kTaskQuads) ? tabC[4 * (q + 1 + kDepth) + row]
                                             : tab1[4 * (q + 1 + kDepth - kTaskQuads) + row];
       }
-      uint32_t cw[4][KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        transpose_rows(x[ks]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) cw[j][ks] = x[ks][j];
-      }
-      const int mx = score_quad_max_seq<KS, G>(opC, cw);
-      const int Sv = __mul24(wgt, mx);
-      const uint32_t u = biased_score(Sv);
-      const int qpos = C.key0 + 64 * q; // first position of the quad
-      const int pos = qpos + lane;
-      if constexpr (DBG) {
-        if (pos < C.N)
-          scores_out[(int64_t)C.unit * score_stride + pos] = (int32_t)(u - kScoreBias);
-      }
-      // A candidate: position in [lo, hi) and u >= L, each test one
-      // compare (the range one on pos - lo, unsigned, as lrel + 64 q).  It is appended to
-      // the wave's LDS list without a branch: its slot in the task is the
-      // running count plus the candidates in lower lanes.
-      const bool inr = lrel + (uint32_t)(64 * q) < nrange;
-      // PAGES: the first lane of each 16-lane row stands for its page, with
-      // the best u of the page's keys in [lo, hi) (0: none there)
-      // (keys: the raw score, compared signed with the threshold and biased
-      // when the list is written out)
-      const uint32_t cu = PAGES ? row_max16(inr ? u : 0u) : (uint32_t)Sv;
-      const bool pass = PAGES ? cu >= LC : Sv >= LCs;
-      const uint32_t cidx = PAGES ? (uint32_t)(4 * q + (lane >> 4)) : (uint32_t)(64 * q + lane);
-      const bool isc = PAGES ? ((lane & 15) == 0 && cu != 0u && pass) : (inr && pass);
-      const uint64_t m = PAGES ? __ballot(cu != 0u) & __ballot(pass) & kRowHeads
-                               : __ballot(inr) & __ballot(pass);
+      const QuadCand c = quad_cands(q, x, wgt);
       const uint32_t lslot = __builtin_amdgcn_mbcnt_hi(
-          (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, used + nc));
+          (uint32_t)(c.m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)c.m, used + nc));
       // Every lane writes (a branch around the write would leave the
       // compiler unsure whether it was issued, and every later LDS wait
       // would then wait for it): lanes without a listed candidate write
       // their spare entry.  An address-space-qualified pointer keeps this an
       // LDS store (a flat store would count against the vector-memory wait
-      // counter).  While the list has room for a whole quad (wave-uniform),
-      // a candidate's slot needs no range test.
-      if (used + nc + 64u <= (uint32_t)kCandList) {
-        const uint32_t wslot = isc ? lslot : (uint32_t)(kCandList + lane);
-        ((__attribute__((address_space(3))) uint64_t *)cst)[wslot] =
-            ((uint64_t)cidx << 32) | cu;
-      } else { // the list is nearly full (rare): the rest go to the region
-        const bool listed = isc && lslot < (uint32_t)kCandList;
-        const uint32_t wslot = listed ? lslot : (uint32_t)(kCandList + lane);
-        ((__attribute__((address_space(3))) uint64_t *)cst)[wslot] =
-            ((uint64_t)cidx << 32) | cu;
-        if (isc && !listed)
-          ((__attribute__((address_space(1))) uint64_t *)reg)[lslot - used] =
-              ((uint64_t)(cbase + cidx) << 32) | (PAGES ? cu : cu + kScoreBias);
-      }
-      nc += (uint32_t)__popcll(m);
+      // counter).  A candidate past the list's end is left out here and
+      // written by the rescoring below, so the quads of a task form one
+      // branch-free block that the compiler can interleave.
+      const uint32_t wslot =
+          (c.isc && lslot < (uint32_t)kCandList) ? lslot : (uint32_t)(kCandList + lane);
+      ((__attribute__((address_space(3))) uint64_t *)cst)[wslot] =
+          ((uint64_t)c.cidx << 32) | c.cu;
+      nc += (uint32_t)__popcll(c.m);
     });
+    // A task with more candidates than the list had room for (rare): its
+    // quads are scored again, from the same page ids, radius lines and
+    // operand, and the candidates past the room go straight to the task's
+    // region, at their rank in position order.
+    const uint32_t room = (uint32_t)kCandList - used;
+    if (nc > room) {
+      uint32_t nc2 = 0;
+      for (int q = 0; q < kTaskQuads; ++q) {
+        QuadLoad<KS> ql;
+        load_quad(tabC[4 * q + row], ql);
+        const uint32_t r8 = radC[64 * q + lane];
+        const int wgt = LIN ? (int)wlut[r8] : (int)r8;
+        uint32_t x[KS][4];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[ks][i] = ql.d[ks][i];
+        const QuadCand c = quad_cands(q, x, wgt);
+        const uint32_t rank = __builtin_amdgcn_mbcnt_hi(
+            (uint32_t)(c.m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)c.m, nc2));
+        if (c.isc && rank >= room)
+          reg[rank] = make_uint2(PAGES ? c.cu : c.cu + kScoreBias, cbase + c.cidx);
+        nc2 += (uint32_t)__popcll(c.m);
+      }
+    }
     // record the task: its first min(nc, room) candidates are in the list
     {
       const uint32_t nbuf = min(nc, (uint32_t)kCandList - used);
