@@ -152,6 +152,7 @@ dkv_status decode_impl(const dkv_config *cfg, const void *q,
   int32_t *cnt = reinterpret_cast<int32_t *>(ws + plan.cnt);
   float *part = reinterpret_cast<float *>(ws + plan.part);
   uint32_t *qbits = d.lsh_T > 0 ? reinterpret_cast<uint32_t *>(ws + plan.qbits) : nullptr;
+  uint32_t *tasks = reinterpret_cast<uint32_t *>(ws + plan.tasks);
   const uint16_t *q16 = static_cast<const uint16_t *>(q);
   const uint16_t *k16 = static_cast<const uint16_t *>(k_pool);
   const uint16_t *v16 = static_cast<const uint16_t *>(v_pool);
@@ -170,7 +171,7 @@ dkv_status decode_impl(const dkv_config *cfg, const void *q,
   uint8_t *radii_w = append ? const_cast<uint8_t *>(radii) : nullptr;
   if (!mark() || launch_prep(d, q16, p16, codes, radii, k16, codes_w, radii_w,
                              block_table, seq_lens, q8, qop, qneg, lthr, qbits,
-                             stream) != hipSuccess)
+                             tasks, stream) != hipSuccess)
     return DKV_ERR_LAUNCH;
   if (d.lsh_T > 0) {
     // bucket probe, then scoring of the pages that hold candidates
@@ -181,7 +182,7 @@ dkv_status decode_impl(const dkv_config *cfg, const void *q,
         launch_lsh_score(d, codes, radii, block_table, seq_lens, qop, qneg, bitmap,
                          cand, tcount, stream) != hipSuccess)
       return DKV_ERR_LAUNCH;
-  } else if (!mark() || launch_score(d, codes, radii, block_table, seq_lens, qop,
+  } else if (!mark() || launch_score(d, codes, radii, block_table, tasks, qop,
                                      qneg, lthr, cand, tcount, scores_out,
                                      stream) != hipSuccess) {
     return DKV_ERR_LAUNCH;
@@ -241,6 +242,8 @@ WorkspacePlan plan_workspace(const DecodeDims &d) {
   off += align256(units * d.nsplit * d.G * (kHeadDim + 2) * 4);
   p.qbits = off;
   off += align256((size_t)d.B * d.Hq * d.W * 4);
+  p.tasks = off; // count word (padded to 16 bytes), then 16 bytes per group
+  off += align256(16 + (size_t)d.B * d.cand_groups * 16);
   p.total = off;
   return p;
 }

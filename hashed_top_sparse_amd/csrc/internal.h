@@ -37,7 +37,7 @@ struct DecodeDims {
 
 // Byte offsets of the decode workspace regions (each 256-byte aligned).
 struct WorkspacePlan {
-  size_t q8, qop, qneg, lthr, cand, tcount, bitmap, rows, cnt, part, qbits, total;
+  size_t q8, qop, qneg, lthr, cand, tcount, bitmap, rows, cnt, part, qbits, tasks, total;
 };
 
 // Byte layout of the LSH index of one (sequence, KV head) unit: a 64-byte
@@ -69,7 +69,8 @@ hipError_t launch_encode(const uint16_t *k_pool, int64_t num_blocks,
 // [B*Hkv][KS][64 lanes][8 dwords], qneg [B][Hq] = -sum_j q8, and per
 // (sequence, KV head) the candidate threshold lthr (from a page sample).
 // With qbits (LSH decode) it also writes each query head's sign code
-// [B][Hq][b/32] and no threshold sample is taken (lthr = 0).
+// [B][Hq][b/32] and no threshold sample is taken (lthr = 0).  tasks: the
+// score filter's task list (see launch_score).
 hipError_t launch_prep(const DecodeDims &d, const uint16_t *q,
                        const uint16_t *proj, const uint32_t *codes,
                        const uint8_t *radii, const uint16_t *k_pool,
@@ -77,7 +78,7 @@ hipError_t launch_prep(const DecodeDims &d, const uint16_t *q,
                        const int32_t *block_table,
                        const int32_t *seq_lens, int8_t *q8, uint32_t *qop,
                        float *qneg, uint32_t *lthr, uint32_t *qbits,
-                       hipStream_t stream);
+                       uint32_t *tasks, hipStream_t stream);
 
 // LSH (lsh.hip): the bucket index of positions [0, seq_lens[s]); the probe
 // that marks each unit's candidates in its bitmap [B*Hkv][bm_words]; and
@@ -105,9 +106,11 @@ hipError_t launch_lsh_score(const DecodeDims &d, const uint32_t *codes,
 // With page-granular selection the candidates are pages instead: (best u
 // of the page's keys in [sinks, N - window), page index), one per page that
 // meets that range.
+// tasks: the list prep writes (a count word, then per page group of a
+// sequence that holds keys, (sequence, group, length) as 16 bytes).
 hipError_t launch_score(const DecodeDims &d, const uint32_t *codes,
                         const uint8_t *radii, const int32_t *block_table,
-                        const int32_t *seq_lens, const uint32_t *qop,
+                        const uint32_t *tasks, const uint32_t *qop,
                         const float *qneg, const uint32_t *lthr, uint2 *cand,
                         uint32_t *tcount, int32_t *scores_out,
                         hipStream_t stream);
@@ -119,7 +122,7 @@ hipError_t launch_score(const DecodeDims &d, const uint32_t *codes,
 #define DKV_FILTER_DECL(NAME)                                                  \
   hipError_t NAME(const DecodeDims &d, const uint32_t *codes,                  \
                   const uint8_t *radii, const int32_t *block_table,            \
-                  const int32_t *seq_lens, const uint32_t *qop,                \
+                  const uint32_t *tasks, const uint32_t *qop,                  \
                   const float *qneg, const uint32_t *lthr, uint2 *cand,        \
                   uint32_t *tcount, int32_t *scores_out, hipStream_t stream)
 DKV_FILTER_DECL(launch_filter_keys_log);

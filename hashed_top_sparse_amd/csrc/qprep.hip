@@ -73,8 +73,9 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     const int32_t *__restrict__ block_table, int max_blocks,
     const int32_t *__restrict__ seq_lens, int n_max, int8_t *__restrict__ q8,
     uint32_t *__restrict__ qop, float *__restrict__ qneg,
-    uint32_t *__restrict__ lthr, uint32_t *__restrict__ qbits, int Hq,
-    int Hkv, int b, int W, int k, int w, int sigma, bool lin, bool pages) {
+    uint32_t *__restrict__ lthr, uint32_t *__restrict__ qbits,
+    uint32_t *__restrict__ tasks, int Hq, int Hkv, int b, int W, int k, int w,
+    int sigma, bool lin, bool pages) {
   const int unit = blockIdx.x;
   const int s = unit / Hkv;
   const int g = unit % Hkv;
@@ -127,6 +128,10 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
       q + ((int64_t)s * Hq + (int64_t)g * G) * kHeadDim);
   const uint4 qv4 = (int)threadIdx.x < G * kHeadDim / 8 ? qsrc[threadIdx.x]
                                                          : make_uint4(0u, 0u, 0u, 0u);
+  // The streaming filter's task list is written by the workgroups of KV
+  // head 0: the lengths of the sequences before s (the first kThreads of
+  // them, one per thread) are requested now and summed at the end.
+  const int len_before = (g == 0 && (int)threadIdx.x < s) ? seq_lens[threadIdx.x] : 0;
   // The sample pages' loads go next so they are in flight while the query
   // is projected.  Their block ids are read with the plan of the longest
   // length (n_max) before the sequence's own length has arrived; when that
@@ -439,6 +444,24 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     if (threadIdx.x == 0)
       radii_w[((int64_t)a_blk * Hkv + g) * kPage + a_slot] = (uint8_t)radius_code(r2);
   }
+  // ---- the filter's task list: one entry (sequence, page group, length)
+  // per group of kGroupKeys keys, sequence by sequence, after a count word
+  // (padded to 16 bytes).  Only groups that hold keys are listed, so the
+  // filter's waves share the real work evenly in ragged batches.
+  if (g == 0) { // workgroup-uniform
+    auto groups_of = [](int n) { return (uint32_t)((n + kGroupKeys - 1) / kGroupKeys); };
+    uint32_t local = groups_of(clamp_int(len_before, 0, n_max));
+    for (int i = (int)threadIdx.x + kThreads; i < s; i += kThreads)
+      local += groups_of(seq_len_clamped(seq_lens, i, n_max));
+    __shared__ uint32_t sTaskTmp[kThreads / 64];
+    uint32_t before;
+    (void)wg_exclusive_scan<kThreads>(local, sTaskTmp, &before);
+    const uint32_t ng = groups_of(N);
+    uint4 *entries = reinterpret_cast<uint4 *>(tasks + 4);
+    for (uint32_t j = threadIdx.x; j < ng; j += kThreads)
+      entries[before + j] = make_uint4((uint32_t)s, j, (uint32_t)N, 0u);
+    if (s == (int)(gridDim.x / Hkv) - 1 && threadIdx.x == 0) tasks[0] = before + ng;
+  }
 }
 
 } // namespace
@@ -450,7 +473,7 @@ hipError_t launch_prep(const DecodeDims &d, const uint16_t *q,
                        const int32_t *block_table,
                        const int32_t *seq_lens, int8_t *q8, uint32_t *qop,
                        float *qneg, uint32_t *lthr, uint32_t *qbits,
-                       hipStream_t stream) {
+                       uint32_t *tasks, hipStream_t stream) {
   const uint32_t code_bytes = (uint32_t)((uint64_t)d.num_blocks * d.Hkv * d.W * kPage * 4);
   const uint32_t radius_bytes = (uint32_t)((uint64_t)d.num_blocks * d.Hkv * kPage);
 #define DKV_PREP_CASE(KSV, GV)                                                 \
@@ -460,7 +483,7 @@ hipError_t launch_prep(const DecodeDims &d, const uint16_t *q,
                        k_pool, codes_w, radii_w,                               \
                        d.num_blocks, code_bytes, radius_bytes, block_table,    \
                        d.max_blocks, seq_lens, d.n_max, q8, qop, qneg, lthr,   \
-                       qbits,                                                  \
+                       qbits, tasks,                                           \
                        d.Hq, d.Hkv, d.b, d.W, d.k, d.w, d.sigma, d.lin,         \
                        d.pages);                                               \
     return hipGetLastError();                                                  \

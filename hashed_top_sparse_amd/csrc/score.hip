@@ -6,13 +6,13 @@ namespace dkv {
 
 hipError_t launch_score(const DecodeDims &d, const uint32_t *codes,
                         const uint8_t *radii, const int32_t *block_table,
-                        const int32_t *seq_lens, const uint32_t *qop,
+                        const uint32_t *tasks, const uint32_t *qop,
                         const float *qneg, const uint32_t *lthr, uint2 *cand,
                         uint32_t *tcount, int32_t *scores_out,
                         hipStream_t stream) {
   auto *f = d.pages ? (d.lin ? launch_filter_pages_linear : launch_filter_pages_log)
                     : (d.lin ? launch_filter_keys_linear : launch_filter_keys_log);
-  return f(d, codes, radii, block_table, seq_lens, qop, qneg, lthr, cand, tcount,
+  return f(d, codes, radii, block_table, tasks, qop, qneg, lthr, cand, tcount,
            scores_out, stream);
 }
 

@@ -12,9 +12,10 @@
 // in score_common.h (one fp8 x fp4 matrix-core op per 128 code bits).
 //
 // Work: persistent waves (4 per workgroup), each streaming a static stride
-// of 64-page tasks (sequence, page group, KV head); task ids run KV head
-// fastest, then sequence, then page group, so the heads of one page block
-// are read together.  Codes are key-major, so one 16-byte load per lane
+// of 64-page tasks (sequence, page group, KV head).  The (sequence, page
+// group) pairs that hold keys come from a list the prep kernel writes, so
+// ragged batches spread evenly; task ids run KV head fastest over that
+// list, so the heads of one page block are read together.  Codes are key-major, so one 16-byte load per lane
 // brings a page quad: lanes 16j..16j+15 read page j's 16 keys (each lane a
 // whole 128-bit key; 64-bit keys use 8-byte loads, 256-bit keys two loads).
 // Four gfx950 row swaps (v_permlane32_swap, v_permlane16_swap) transpose
@@ -105,10 +106,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     const uint32_t *__restrict__ codes, const uint8_t *__restrict__ radii,
     int64_t num_blocks, uint32_t code_bytes, uint32_t radius_bytes,
     const int32_t *__restrict__ block_table, int max_blocks,
-    const int32_t *__restrict__ seq_lens, int n_max,
+    const uint32_t *__restrict__ tasks, int n_max,
     const uint32_t *__restrict__ qop, const float *__restrict__ qneg,
-    const uint32_t *__restrict__ lthr, int B, int Hkv, int ngroups,
-    int ntasks, int w, int sigma, uint2 *__restrict__ cand,
+    const uint32_t *__restrict__ lthr, int B, int Hkv, int max_entries,
+    int w, int sigma, uint2 *__restrict__ cand,
     uint32_t *__restrict__ tcount, int cand_groups,
     int32_t *__restrict__ scores_out, int score_stride) {
   constexpr int kDepth = kDepthFor<W>;
@@ -132,8 +133,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
   // Sequence lengths and thresholds are read with vector loads: a scalar
   // load in the stream would make every wait on the LDS counter a full wait
   // (scalar loads complete out of order), including the candidate writes.
-  const __amdgpu_buffer_rsrc_t len_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<int32_t *>(seq_lens), 0, (uint32_t)B * 4u, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t task_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t *>(tasks), 0, 16u + 16u * (uint32_t)max_entries, kBufferWord3);
   const __amdgpu_buffer_rsrc_t thr_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint32_t *>(lthr), 0, (uint32_t)(B * Hkv) * 4u, kBufferWord3);
   const uint32_t page_bytes = (uint32_t)(kPage * W * 4);
@@ -182,17 +183,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
     ntab = 0;
   };
 
-  // task id -> task, or none if its page group is past the sequence
+  // The task list: tasks[0] entries, entry e (16 bytes at byte 16 + 16 e)
+  // one page group that holds keys, (sequence, group, length); task id
+  // t = e * Hkv + KV head.  Every entry is real work, so the static stride
+  // below gives each wave the same number of tasks (up to one) whatever the
+  // sequence lengths.
+  const int ntasks = min(__builtin_amdgcn_readfirstlane(
+                             __builtin_amdgcn_raw_buffer_load_b32(task_rsrc, 0, 0, 0)),
+                         (uint32_t)max_entries) * Hkv;
+  // task id -> task, or none if it holds no keys
   auto decode = [&](int t, Task &T) -> bool {
     T.g = t % Hkv;
-    const int r = t / Hkv;
-    T.s = r % B;
-    T.grp = r / B;
-    T.N = clamp_int(__builtin_amdgcn_readfirstlane(
-                        __builtin_amdgcn_raw_buffer_load_b32(len_rsrc, T.s * 4, 0, 0)),
-                    0, n_max);
+    const auto e = __builtin_amdgcn_raw_buffer_load_b128(task_rsrc, 16 + 16 * (t / Hkv), 0, 0);
+    T.s = (int)__builtin_amdgcn_readfirstlane(e[0]);
+    T.grp = (int)__builtin_amdgcn_readfirstlane(e[1]);
+    T.N = clamp_int((int)__builtin_amdgcn_readfirstlane(e[2]), 0, n_max);
     T.key0 = T.grp * kGroupKeys;
-    if (T.key0 >= T.N) return false;
+    if (T.key0 >= T.N || T.s >= B) return false;
     T.unit = T.s * Hkv + T.g;
     T.npg = min(kGroupPages, (T.N - T.key0 + kPage - 1) / kPage);
     T.lo = max(sigma, T.key0);
@@ -472,15 +479,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))
 template <bool LIN, bool PAGES>
 hipError_t launch_filter_impl(const DecodeDims &d, const uint32_t *codes,
                          const uint8_t *radii, const int32_t *block_table,
-                         const int32_t *seq_lens, const uint32_t *qop,
+                         const uint32_t *tasks, const uint32_t *qop,
                          const float *qneg, const uint32_t *lthr, uint2 *cand,
                          uint32_t *tcount, int32_t *scores_out,
                          hipStream_t stream) {
   const int pages = (d.n_max + kPage - 1) / kPage;
   const int64_t ngroups = (pages + kGroupPages - 1) / kGroupPages;
   if (ngroups == 0) return hipSuccess;
-  const int64_t ntasks = (int64_t)d.B * ngroups * d.Hkv;
-  if (ntasks > 0x7FFFFFFF - 65536) return hipErrorInvalidValue;
+  // at most one task list entry per (sequence, page group)
+  const int64_t max_entries = (int64_t)d.B * ngroups;
+  const int64_t ntasks = max_entries * d.Hkv;
+  if (ntasks > 0x7FFFFFFF - 65536 || max_entries >= ((int64_t)1 << 27))
+    return hipErrorInvalidValue;
   const uint32_t code_bytes = (uint32_t)((uint64_t)d.num_blocks * d.Hkv * d.W * kPage * 4);
   const uint32_t radius_bytes = (uint32_t)((uint64_t)d.num_blocks * d.Hkv * kPage);
 #define DKV_SCORE_LAUNCH(WV, GV, DV)                                           \
@@ -490,8 +500,8 @@ hipError_t launch_filter_impl(const DecodeDims &d, const uint32_t *codes,
     hipLaunchKernelGGL((filter_kernel<WV, GV, DV, LIN, PAGES>),                \
                        dim3((unsigned)nwg), dim3(kThreads), 0, stream, codes,  \
                        radii, d.num_blocks, code_bytes, radius_bytes,          \
-                       block_table, d.max_blocks, seq_lens, d.n_max, qop,      \
-                       qneg, lthr, d.B, d.Hkv, (int)ngroups, (int)ntasks, d.w, \
+                       block_table, d.max_blocks, tasks, d.n_max, qop,         \
+                       qneg, lthr, d.B, d.Hkv, (int)max_entries, d.w,          \
                        d.sigma, cand, tcount, d.cand_groups, scores_out,       \
                        d.max_seq_len);                                         \
     return hipGetLastError();                                                  \

@@ -4,7 +4,7 @@
 namespace dkv {
 
 DKV_FILTER_DECL(launch_filter_keys_linear) {
-  return launch_filter_impl<true, false>(d, codes, radii, block_table, seq_lens, qop,
+  return launch_filter_impl<true, false>(d, codes, radii, block_table, tasks, qop,
                                        qneg, lthr, cand, tcount, scores_out, stream);
 }
 

@@ -4,7 +4,7 @@
 namespace dkv {
 
 DKV_FILTER_DECL(launch_filter_keys_log) {
-  return launch_filter_impl<false, false>(d, codes, radii, block_table, seq_lens, qop,
+  return launch_filter_impl<false, false>(d, codes, radii, block_table, tasks, qop,
                                        qneg, lthr, cand, tcount, scores_out, stream);
 }
 

@@ -4,7 +4,7 @@
 namespace dkv {
 
 DKV_FILTER_DECL(launch_filter_pages_linear) {
-  return launch_filter_impl<true, true>(d, codes, radii, block_table, seq_lens, qop,
+  return launch_filter_impl<true, true>(d, codes, radii, block_table, tasks, qop,
                                        qneg, lthr, cand, tcount, scores_out, stream);
 }
 
