@@ -94,6 +94,10 @@ void encode_mfma_kernel(const uint16_t *__restrict__ k_pool, int64_t num_blocks,
   __shared__ uint4 sQ[kMmThreads / 64][kQueue];      // queued fp64 chains
   __shared__ float sR2[kMmThreads / 64][16];
   __shared__ int2 sRange[kRangeLds];
+  // tiles before each sequence's first (balanced mode): sPre[s] =
+  // Hkv-free count of the pages the ranges of sequences 0..s-1 meet
+  __shared__ int sPre[kRangeLds + 1];
+  __shared__ uint32_t sScan[kMmThreads / 64];
   // a tile's key rows, staged only when an fp64 chain has to run
   __shared__ __align__(16) uint16_t sRow[kMmThreads / 64][kPage][kHeadDim];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -116,6 +120,30 @@ void encode_mfma_kernel(const uint16_t *__restrict__ k_pool, int64_t num_blocks,
   }
   for (int i = threadIdx.x; i < batch && i < kRangeLds; i += kMmThreads) sRange[i] = range_of(i);
   __syncthreads();
+  // Balanced mode (every sequence's range in LDS): only the pages the
+  // ranges meet are tiles, numbered sequence by sequence, so the waves'
+  // runs hold equal work in ragged batches.  Otherwise every sequence has
+  // pages_max tile slots, the ones past its range empty.
+  const bool bal = batch <= kRangeLds; // workgroup-uniform
+  auto pages_met = [](int2 rg) { return rg.y > rg.x ? (rg.y - 1) / kPage - rg.x / kPage + 1 : 0; };
+  if (bal) {
+    constexpr int kPer = kRangeLds / kMmThreads; // sequences per thread
+    const int i0 = (int)threadIdx.x * kPer;
+    uint32_t local = 0;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+      if (i0 + u < batch) local += (uint32_t)pages_met(sRange[i0 + u]);
+    uint32_t total;
+    uint32_t run = wg_exclusive_scan<kMmThreads>(local, sScan, &total);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+      if (i0 + u < batch) {
+        sPre[i0 + u] = (int)run;
+        run += (uint32_t)pages_met(sRange[i0 + u]);
+      }
+    if (threadIdx.x == 0) sPre[batch] = (int)total;
+    __syncthreads();
+  }
   const __amdgpu_buffer_rsrc_t bt_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int32_t *>(block_table), 0, (uint32_t)(batch * max_blocks) * 4u,
       0x00020000u);
@@ -144,7 +172,7 @@ void encode_mfma_kernel(const uint16_t *__restrict__ k_pool, int64_t num_blocks,
   // tiles t = ((s * pages_max + pi) * Hkv + h): the heads of a page are
   // neighbours; each wave walks a contiguous run of them (a carry step per
   // tile, no divisions) -- the parts of one tile walk the same runs
-  const int ntiles = batch * pages_max * Hkv;
+  const int ntiles = bal ? sPre[batch] * Hkv : batch * pages_max * Hkv;
   const int nstream = (int)(gridDim.x / HALVES) * (kMmThreads / 64);
   const int chunk = (ntiles + nstream - 1) / nstream;
   const int wid = (int)(blockIdx.x / HALVES) * (kMmThreads / 64) + wave;
@@ -163,8 +191,19 @@ void encode_mfma_kernel(const uint16_t *__restrict__ k_pool, int64_t num_blocks,
   auto tile_at = [&](int t, Tile &T) {
     T.h = t % Hkv;
     const int r = t / Hkv;
-    T.pi = r % pages_max;
-    T.s = r / pages_max;
+    if (bal) { // the last sequence whose first page slot is at or before r
+      int lo = 0, hi = batch; // sPre[lo] <= r < sPre[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (sPre[mid] <= r) lo = mid;
+        else hi = mid;
+      }
+      T.s = lo;
+      T.pi = r - sPre[lo];
+    } else {
+      T.pi = r % pages_max;
+      T.s = r / pages_max;
+    }
     set_seq(T);
     T.p = T.start / kPage + T.pi;
     T.any = t < t_end;
@@ -173,7 +212,15 @@ void encode_mfma_kernel(const uint16_t *__restrict__ k_pool, int64_t num_blocks,
   auto step = [&](Tile &T, int t_next) { // T becomes tile t_next = its id + 1
     if (++T.h == Hkv) {
       T.h = 0;
-      if (++T.pi == pages_max) {
+      if (bal) {
+        if (++T.pi == sPre[T.s + 1] - sPre[T.s]) { // next sequence with pages
+          T.pi = 0;
+          do
+            ++T.s;
+          while (T.s < batch && sPre[T.s + 1] == sPre[T.s]);
+          if (T.s < batch) set_seq(T);
+        }
+      } else if (++T.pi == pages_max) {
         T.pi = 0;
         if (++T.s < batch) set_seq(T);
       }
