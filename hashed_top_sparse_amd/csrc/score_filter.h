@@ -41,19 +41,20 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kTaskQuads = kGroupPages / 4; // page quads per task
-// quads of loads in flight per wave: 4 KB per wave for every code width
-// (256-bit codes hold two quads; four would spill registers)
+// quads of loads in flight per wave: 8 KB per wave for 128- and 256-bit
+// codes (a 256-bit quad is 2 KB), 4 KB for 64-bit codes (at most half a
+// task ahead)
 template <int W>
-constexpr int kDepthFor = W > 4 ? 2 : 4;
+constexpr int kDepthFor = W > 4 ? 4 : 8;
 // quad of a task at which the task after next and the next task's operand
 // are loaded: kDepth quads before the next task's first prefetch
 template <int W>
 constexpr int kLookaheadFor = kTaskQuads - 2 * kDepthFor<W>;
-// Workgroups per CU: one wave per SIMD each, four waves per SIMD in all.
-// More resident waves do not help (the kernel is bound by instruction
-// issue), and four per SIMD keeps each wave's task count equal when the
-// task count is a multiple of 4 x 4 x CUs.
-constexpr int kWgPerCu = 4;
+// Workgroups per CU: one wave per SIMD each, three waves per SIMD in all
+// (up to 168 registers a lane).  Three waves with 8 KB in flight each beat
+// four with 4 KB (the register budget of four per SIMD): 62.4 vs 63.7 us on
+// 16 x 128K keys, although the task count then divides less evenly.
+constexpr int kWgPerCu = 3;
 // per-wave candidate list: kCandList entries, then one spare entry per lane
 // (8 KB of LDS in all)
 constexpr int kCandList = kGroupKeys - 64;
@@ -102,7 +103,7 @@ __device__ __forceinline__ void transpose_rows(uint32_t (&x)[4]) {
 // linear radius weight (looked up in a per-workgroup LDS table); PAGES:
 // candidates are pages (the best score of their keys in [lo, hi)).
 template <int W, int G, bool DBG, bool LIN, bool PAGES, int KS = (W > 4 ? W / 4 : 1)>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void filter_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))) void filter_kernel(
     const uint32_t *__restrict__ codes, const uint8_t *__restrict__ radii,
     int64_t num_blocks, uint32_t code_bytes, uint32_t radius_bytes,
     const int32_t *__restrict__ block_table, int max_blocks,
