@@ -24,7 +24,7 @@
 //   - values on the vector units: 16-lane row groups, lane l holding dims
 //     8l .. 8l+7 of rows g, g+4, g+8, g+12 of the tile.
 // A wave requests all its tiles' key and value rows at once, then uses them
-// in order (its 64 row ids come with one load and are handed out by lane
+// in order (its row ids come with one load and are handed out by lane
 // shuffles).  The selection list already holds physical row ids (page*16 +
 // slot); all G query heads of the KV group share the rows.
 #include "internal.h"
@@ -88,6 +88,7 @@ constexpr int kTileRows = 16;
 constexpr int kWaveRows = kAttnRows / kWaves;
 constexpr int kTiles = kWaveRows / kTileRows;
 static_assert(kTiles * kTileRows * kWaves == kAttnRows, "whole tiles");
+static_assert(kWaveRows <= 64, "one row id per lane");
 constexpr int kPStride = 8; // floats per row of the p tile (G <= 8)
 
 template <int G>
@@ -106,9 +107,10 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(
   const int r0 = split * kAttnRows;
   const int r1 = (r0 + kAttnRows < n) ? r0 + kAttnRows : n;
 
-  // this wave's 64 row ids, one per lane (handed out by lane shuffles)
+  // this wave's row ids, one per lane (handed out by lane shuffles)
   const int row0 = wave * kWaveRows;
-  const int myid = r0 + row0 + lane < r1 ? rows[(int64_t)unit * cap + r0 + row0 + lane] : -1;
+  const int myid = lane < kWaveRows && r0 + row0 + lane < r1
+                       ? rows[(int64_t)unit * cap + r0 + row0 + lane] : -1;
 
   // query operand: head lrow (zero past G); K-step c takes dims
   // 32c + 8*lgrp .. +8, the same dims the key rows give this lane
@@ -264,9 +266,9 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(
 }
 
 // Merge of the split states: one workgroup of 128 threads (one per dim)
-// per (sequence, query head).  Splits are taken 16 at a time, all 16
+// per (sequence, query head).  Splits are taken 32 at a time, all 32
 // states loaded before any is used so the loads overlap.
-constexpr int kCombineChunk = 16;
+constexpr int kCombineChunk = 32;
 
 __global__ __launch_bounds__(kHeadDim) void attend_combine_kernel(
     const float *__restrict__ part, float *__restrict__ out, int Hq, int Hkv,

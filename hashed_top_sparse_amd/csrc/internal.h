@@ -12,7 +12,7 @@ namespace dkv {
 
 constexpr int kPage = 16;       // tokens per page
 constexpr int kHeadDim = 128;   // d
-constexpr int kAttnRows = 256;  // selected rows per attention split
+constexpr int kAttnRows = 128;  // selected rows per attention split
 constexpr int kGroupPages = 64; // pages per candidate group (one scoring task)
 constexpr int kGroupKeys = kGroupPages * kPage;
 constexpr int kLdsPerCu = 160 * 1024; // gfx950 LDS per compute unit
