@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "internal.h"
 
@@ -203,16 +204,21 @@ dkv_status decode_impl(const dkv_config *cfg, const void *q,
 } // namespace
 
 int device_cu_count() {
-  static int cached[64] = {0}; // per device id; a racing first call stores the same value
+  // Per device id; relaxed atomics, so threads that race on a first call
+  // each store the same value and no thread reads a torn one.
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  if (dev < 64) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
           hipSuccess ||
       n <= 0)
     n = 256;
-  if (dev < 64) cached[dev] = n;
+  if (dev < 64) cached[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
@@ -271,6 +277,7 @@ dkv_encode(const dkv_config *cfg, const void *k_pool, int64_t num_blocks,
       !aligned16(proj))
     return DKV_ERR_INVALID_ARG;
   if (max_encode_len > DKV_MAX_SEQ_LEN ||
+      max_blocks_per_seq > DKV_MAX_SEQ_LEN / kPage ||
       (int64_t)batch * max_blocks_per_seq >= (int64_t)1 << 30)
     return DKV_ERR_UNSUPPORTED;
   hipError_t e = launch_encode(

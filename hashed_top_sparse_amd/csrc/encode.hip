@@ -104,7 +104,9 @@ void encode_mfma_kernel(const uint16_t *__restrict__ k_pool, int64_t num_blocks,
   const int q = lane >> 4, col = lane & 15;
   const int half = HALVES > 1 ? (int)(blockIdx.x % HALVES) : 0;
   const int col0 = half * NCOL;
-  const int limit = kPage * max_blocks;
+  // positions a block table row reaches (the host keeps max_blocks at or
+  // below DKV_MAX_SEQ_LEN / 16, so this fits an int)
+  const int limit = (int)min((int64_t)kPage * max_blocks, (int64_t)DKV_MAX_SEQ_LEN);
   // a sequence's encode range [start, end), clamped
   auto range_of = [&](int s_) {
     const int st = clamp_int(enc_start[s_], 0, limit);

@@ -2,11 +2,14 @@
 // position-ordered list built from a selection bitmap.
 //
 // Selection order ([DASH-KV Top-K pruning]; ties to the lowest position):
-// values are biased scores u = S + 2^23 (or, for tie-breaking, inverted
-// positions); the k-th largest value T and the number of elements equal to
-// T to take are found with two histogram passes over 4096 bins: the first
-// over (u - min) >> shift, with the shift chosen so the elements' range
-// fits the bins, the second over the low bits inside the threshold bin.
+// values are biased scores u = S + 2^31 (or, for tie-breaking, inverted
+// positions), so the range of a set of values can span all 32 bits.  The
+// k-th largest value T and the number of elements equal to T to take are
+// found with histogram passes over 4096 bins: the first over
+// (u - min) >> shift, with the shift chosen so the elements' range fits the
+// bins, then one pass per further 12 bits (or fewer) inside the bin found so
+// far, until the bins are single values: at most three passes for a 32-bit
+// range.
 #pragma once
 
 #include "internal.h"
@@ -119,22 +122,34 @@ __device__ void wg_kth_largest(SelectShared<NT> &sh, Visit visit, uint32_t kneed
   int shift;
   wg_histogram<NT>(sh, visit, vmin, shift);
   find_threshold_bin<NT>(sh, kneed);
-  const uint32_t b1 = (uint32_t)sh.bin;
-  const uint32_t kneed2 = kneed - sh.above;
-  __syncthreads();
-  for (int i = threadIdx.x; i < kHistBins; i += NT) sh.hist[i] = 0;
-  __syncthreads();
-  const uint32_t low_mask = (1u << shift) - 1u;
-  visit([&](uint32_t v) {
-    const uint32_t d = v - vmin;
-    if ((d >> shift) == b1) atomicAdd(&sh.hist[d & low_mask], 1u);
-  });
-  __syncthreads();
-  find_threshold_bin<NT>(sh, kneed2);
-  T = vmin + (b1 << shift) + (uint32_t)sh.bin;
-  take_eq = kneed2 - sh.above;
+  // prefix: the bits of (T - vmin) above `shift` found so far
+  uint32_t prefix = (uint32_t)sh.bin;
+  uint32_t kleft = kneed - sh.above; // >= 1: elements still to take at or below the prefix
   n_eq = sh.hist[sh.bin];
   __syncthreads();
+  while (shift > 0) { // workgroup-uniform
+    // the next (at most) kHistBits bits below the prefix
+    const int next = shift > kHistBits ? shift - kHistBits : 0;
+    const int width = shift - next;
+    const uint32_t mask = (1u << width) - 1u;
+    for (int i = threadIdx.x; i < kHistBins; i += NT) sh.hist[i] = 0;
+    __syncthreads();
+    const int sh_ = shift;
+    visit([&](uint32_t v) {
+      const uint32_t d = v - vmin;
+      if ((d >> sh_) == prefix) atomicAdd(&sh.hist[(d >> next) & mask], 1u);
+    });
+    __syncthreads();
+    find_threshold_bin<NT>(sh, kleft);
+    prefix = (prefix << width) | (uint32_t)sh.bin;
+    kleft -= sh.above;
+    n_eq = sh.hist[sh.bin];
+    shift = next;
+    __syncthreads();
+  }
+  // the bins of the last pass were single values
+  T = vmin + prefix;
+  take_eq = kleft;
 }
 
 // The top kneed (1 <= kneed <= element count) of (u, pos) pairs under the

@@ -160,7 +160,8 @@ typedef struct {
  * cores in fp32, keeps each sign whose margin exceeds a bound on the fp32
  * error, and recomputes the others with the double-precision chain; the
  * result is the same.)  batch * max_blocks_per_seq must stay below 2^30
- * (DKV_ERR_UNSUPPORTED otherwise).
+ * and max_blocks_per_seq at or below DKV_MAX_SEQ_LEN/16 (positions are
+ * below DKV_MAX_SEQ_LEN); DKV_ERR_UNSUPPORTED otherwise.
  */
 dkv_status dkv_encode(const dkv_config *cfg, const void *k_pool,
                       int64_t num_blocks, const int32_t *block_table,

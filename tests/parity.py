@@ -165,3 +165,83 @@ def check_unit(cfg: dkv.Config, inp: dict, gpu: dict, codes, radii, s: int, g: i
     return {"max_abs": float(err.max()) if err.size else 0.0,
             "max_rel": float((err[big] / np.abs(r["out"][big])).max()) if big.any() else 0.0,
             "recall": rec}
+
+
+def oracle_check_units(cfg: dkv.Config, inp: dict, gpu: dict, codes, radii, units,
+                       debug: dict = None, chunk: int = 16, log=None) -> dict:
+    """Compares many (sequence, KV head) units with the oracle at once.
+
+    The oracle encodes every unit's keys itself (one call over all rows of a
+    chunk of units) and decodes the chunk with OpenMP over units.  Checked
+    per unit: codes and radii of all N keys (bit-exact), the selection as a
+    set and its count (bit-exact), entries past the count (-1), and the
+    outputs (within the tolerance) of ``gpu``; with ``debug`` (a
+    dkv_decode_debug result) also its query codes and every key's score.
+    Returns the largest absolute output error and the needle recalls."""
+    bt = inp["block_table"].cpu().numpy()
+    lens = inp["seq_lens"].cpu().numpy()
+    G, b, d = cfg.group, cfg.code_bits, cfg.head_dim
+    P = tensor_bits(inp["proj"])
+    qall = tensor_bits(inp["q"])
+    g_cnt = gpu["cnt"].cpu().numpy()
+    g_sel = gpu["sel"].cpu().numpy()
+    g_out = gpu["out"].double().cpu().numpy()
+    d_q8 = debug["q8"].cpu().numpy() if debug is not None else None
+    max_abs, recalls, checked = 0.0, [], 0
+    for c0 in range(0, len(units), chunk):
+        part = units[c0:c0 + chunk]
+        U = len(part)
+        Ns = np.array([int(lens[s]) for s, _ in part], np.int32)
+        Nmax = max(1, int(Ns.max()))
+        K = np.zeros((U, Nmax, d), np.uint16)
+        V = np.zeros((U, Nmax, d), np.uint16)
+        q = np.zeros((U, G, d), np.uint16)
+        for i, (s, g) in enumerate(part):
+            n = int(Ns[i])
+            K[i, :n] = logical_rows(inp["k_pool"], bt, s, n, g)
+            V[i, :n] = logical_rows(inp["v_pool"], bt, s, n, g)
+            q[i] = qall[s, g * G:(g + 1) * G]
+        rows = np.concatenate([K[i, :int(Ns[i])] for i in range(U)], axis=0)
+        oc, orad = oracle.encode_keys(rows, P)
+        o_codes = np.zeros((U, Nmax, b // 32), np.uint32)
+        o_radii = np.zeros((U, Nmax), np.uint8)
+        off = 0
+        for i, (s, g) in enumerate(part):
+            n = int(Ns[i])
+            o_codes[i, :n], o_radii[i, :n] = oc[off:off + n], orad[off:off + n]
+            off += n
+            gc = logical_codes(codes, bt, s, n, g)
+            bad = np.nonzero((gc != o_codes[i, :n]).any(axis=1))[0]
+            assert len(bad) == 0, f"unit {(s, g)}: codes differ at {len(bad)} keys, first {bad[:5]}"
+            assert np.array_equal(logical_radii(radii, bt, s, n, g), o_radii[i, :n]), \
+                f"unit {(s, g)}: radii differ"
+        r = oracle.decode_units(q, P, o_codes, o_radii, K, V, Ns, cfg.top_k, cfg.window,
+                                cfg.sinks, want_scores=debug is not None,
+                                radius_mode=cfg.radius_weight, pages=cfg.select_pages,
+                                lsh=(cfg.lsh_tables, cfg.lsh_bits))
+        for i, (s, g) in enumerate(part):
+            n = int(Ns[i])
+            if debug is not None:
+                assert np.array_equal(d_q8[s, g * G:(g + 1) * G], r["q8"][i]), \
+                    f"unit {(s, g)}: query codes differ"
+                ds = debug["scores"][s, g, :n].cpu().numpy()
+                bad = np.nonzero(ds != r["scores"][i, :n])[0]
+                assert len(bad) == 0, f"unit {(s, g)}: scores differ at {len(bad)} keys"
+            sel = r["sel"][i]
+            cnt = int(g_cnt[s, g])
+            assert cnt == len(sel), (s, g, cnt, len(sel))
+            assert np.array_equal(np.sort(g_sel[s, g, :cnt]), np.sort(sel)), \
+                f"unit {(s, g)}: selection differs"
+            assert (g_sel[s, g, cnt:] == -1).all(), f"unit {(s, g)}: list not -1 past count"
+            ref = r["out"][i]
+            err = np.abs(g_out[s, g * G:(g + 1) * G] - ref)
+            ok = err <= ATOL + RTOL * np.abs(ref)
+            assert ok.all(), f"unit {(s, g)}: out max abs err {err.max():.3g}"
+            max_abs = max(max_abs, float(err.max()) if err.size else 0.0)
+            nd = inp["needles"][s][g]
+            if len(nd):
+                recalls.append(float(np.isin(nd, g_sel[s, g, :cnt]).mean()))
+            checked += 1
+        if log is not None:
+            log(f"  oracle checked {checked}/{len(units)} units")
+    return {"max_abs": max_abs, "recalls": recalls, "units": checked}

@@ -136,6 +136,12 @@ def test_encode_rejects_bad_arguments():
     a4 = list(args)
     a4[0] = None       # k_pool
     assert lib.dkv_encode(ctypes.byref(c), *a4) == 1
+    a6 = list(args)
+    a6[3] = (1 << 20) + 1   # max_blocks_per_seq: positions past DKV_MAX_SEQ_LEN
+    assert lib.dkv_encode(ctypes.byref(c), *a6) == 2
+    a6[3] = 1 << 20         # the largest accepted; still fails later (null range ptr)
+    a6[5] = None
+    assert lib.dkv_encode(ctypes.byref(c), *a6) == 1
     for i in (0, 8, 9, 10):  # k_pool, proj, codes, radii not 16-byte aligned
         a5 = list(args)
         a5[i] = ctypes.c_void_p(0x10002)

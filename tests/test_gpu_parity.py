@@ -4,9 +4,10 @@ Bit-exact: key codes, radii, query codes, scores, selected index sets and
 counts.  Within |err| <= 2e-3 + 1e-2*|ref|: attention outputs (fp32
 accumulation on the GPU, fp64 in the oracle).
 
-Small workloads compare every (sequence, KV head) unit; the five full-size
-workloads run at their real shapes in the same launch configuration the
-benchmark times and compare sampled units.
+Small workloads compare every (sequence, KV head) unit; so do the five
+full-size workloads, which run at their real shapes through the entry points
+the benchmark times.  Option paths (linear weight, pages, LSH) compare
+sampled units at full size.
 """
 import numpy as np
 import pytest
@@ -17,7 +18,7 @@ import hashed_top_sparse_amd as dkv
 import oracle
 from helpers import PAGE, logical_codes, logical_radii, logical_rows, tensor_bits
 from parity import (check_unit, config_of, gpu_decode, gpu_decode_append, gpu_decode_lsh,
-                    gpu_encode_all)
+                    gpu_encode_all, oracle_check_units)
 
 pytestmark = pytest.mark.gpu
 
@@ -229,29 +230,44 @@ def test_decode_is_deterministic():
 
 
 # ---------------------------------------------------------------- full size
-FULL_UNITS = {
-    "mha1_n4k_b64": None,                                   # every unit
-    "gqa32x8_bs1_n32k_b128": None,
-    "gqa32x8_bs16_n128k_b128": [(0, 0), (7, 3), (15, 7)],
-    "gqa32x8_ragged64_4k-128k_b128": [(0, 0), (17, 5), (40, 2), (63, 7)],
-    "gqa32x8_bs4_n256k_b256_lognormal": [(0, 0), (3, 7)],
-}
+def _same_result(a, b, what):
+    assert torch.equal(a["out"], b["out"]), f"{what}: outputs differ"
+    assert torch.equal(a["cnt"], b["cnt"]), f"{what}: counts differ"
+    assert torch.equal(torch.sort(a["sel"], dim=-1).values,
+                       torch.sort(b["sel"], dim=-1).values), f"{what}: selections differ"
 
 
-@pytest.mark.parametrize("name", list(FULL_UNITS))
-def test_full_size_workloads(name):
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_full_size_every_unit(name):
+    """The five workloads at their real shapes, in the benchmark's launch
+    configuration, every (sequence, KV head) unit compared with the oracle.
+
+    The prefix [0, N-1) of every sequence is encoded with dkv_encode into
+    sentinel-filled pools, then dkv_decode_append (the benchmarked step)
+    encodes each sequence's newest key itself and decodes.  dkv_decode over
+    the same codes and dkv_decode_debug (which also returns the query codes
+    and every key's score) must agree with it bit for bit.  Against the
+    oracle: codes and radii of every key, query codes, every score, the
+    selected sets and counts (bit-exact), outputs within tolerance, and
+    needle recall 1.0 where needles are planted."""
     wl = workloads.get(name)
-    stats = _run(wl, FULL_UNITS[name])
-    recalls = [st["recall"] for st in stats if st["recall"] is not None]
+    print(f"[case] full size every unit {name}", flush=True)
+    cfg = config_of(wl)
+    inp = workloads.make_inputs(wl, DEV)
+    app, codes, radii = gpu_decode_append(cfg, inp)
+    plain = gpu_decode(cfg, inp, codes, radii, debug=False)
+    dbg = gpu_decode(cfg, inp, codes, radii, debug=True)
+    _same_result(plain, app, "dkv_decode vs dkv_decode_append")
+    _same_result(dbg, app, "dkv_decode_debug vs dkv_decode_append")
+    units = [(s, g) for s in range(wl.batch) for g in range(wl.num_kv_heads)]
+    st = oracle_check_units(cfg, inp, app, codes, radii, units, debug=dbg,
+                            log=lambda m: print(m, flush=True))
+    assert st["units"] == len(units)
     if wl.needles:
-        assert recalls and all(r == 1.0 for r in recalls)
-    print(name, "max abs err", max(st["max_abs"] for st in stats))
-    torch.cuda.empty_cache()
-
-
-def test_full_size_decode_append():
-    """The benchmarked step: dkv_decode_append at 16 x 128K."""
-    _run_append(workloads.get("gqa32x8_bs16_n128k_b128"), [(0, 0), (9, 5), (15, 7)])
+        assert st["recalls"] and all(r == 1.0 for r in st["recalls"])
+    print(name, "units", st["units"], "max abs err", st["max_abs"], flush=True)
+    del app, plain, dbg, codes, radii, inp
     torch.cuda.empty_cache()
 
 
@@ -336,6 +352,39 @@ def test_linear_weight_threshold_fallback_stays_exact(factor):
     gpu = gpu_decode(cfg, inp, codes, radii, debug=True)
     for g in range(wl.num_kv_heads):
         check_unit(cfg, inp, gpu, codes, radii, 0, g)
+
+
+@pytest.mark.parametrize("mode", ["rescan", "unstaged"])
+def test_linear_weight_wide_score_range_stays_exact(mode):
+    """Scores spanning far more than 2^24 reach the merge's exact k-th
+    largest search.  Codes come from keys scaled x64 (radius codes near the
+    top, linear weights in the tens of thousands); then either the sampled
+    pages are scaled x4 more, so too few keys pass the sampled threshold and
+    the merge rescans every key (a score range near 2^28), or the top-k is
+    so large that the candidates do not fit the merge's LDS staging and the
+    search runs over the lists in global memory.  Attention runs over the
+    unscaled pool."""
+    import dataclasses
+    base = workloads.get("small_gqa_b128")
+    over = dict(top_k=7000) if mode == "unstaged" else {}
+    wl = dataclasses.replace(base, name=f"wide_{mode}", batch=1, seq_len=40000,
+                             needles=0, **over)
+    print(f"[case] wide score range, linear weight, {mode}", flush=True)
+    cfg = config_of(wl, **LIN)
+    inp = workloads.make_inputs(wl, DEV)
+    k_big = dict(inp, k_pool=(inp["k_pool"].float() * 64.0).to(torch.bfloat16))
+    if mode == "rescan":
+        keff = min(wl.top_k, wl.seq_len - wl.window - wl.sinks)
+        sp = _sample_stride(keff)
+        _scale_pages(k_big, wl, lambda p: p % sp == 0, 4.0)
+    codes, radii = gpu_encode_all(cfg, k_big)
+    gpu = gpu_decode(cfg, inp, codes, radii, debug=True)
+    n = int(inp["seq_lens"][0].item())
+    for g in range(wl.num_kv_heads):
+        check_unit(cfg, inp, gpu, codes, radii, 0, g, code_pool=k_big["k_pool"])
+        sc = gpu["scores"][0, g, wl.sinks:n - wl.window].long()
+        assert int(sc.max() - sc.min()) > 2 ** 26   # far past a 24-bit search
+    torch.cuda.empty_cache()
 
 
 def test_linear_weight_largest_radii():

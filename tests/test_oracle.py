@@ -88,6 +88,30 @@ def test_code_matches_exact_rational_sign():
         assert np.array_equal(oracle.key_code(k, P), exact_sign_code(k, P))
 
 
+@pytest.mark.parametrize("b", [64, 128, 256])
+def test_encode_keys_equals_each_row_and_exact_values(b):
+    """The batched encoder (every parity test and the CPU baseline use it)
+    returns, row by row, the single-key code and radius, at an odd row
+    count; spot rows also match the exact-rational sign code and exact
+    radius threshold, so a row or word stride mistake cannot pass."""
+    rng = np.random.default_rng(40 + b)
+    n = 37
+    P = rand_bits(rng, (D, b))
+    scales = np.array([[1.0], [8.0], [0.01], [300.0]], np.float32)
+    K = bf16_bits(rng.standard_normal((n, D)).astype(np.float32) * scales[np.arange(n) % 4])
+    K[5] = 0                                       # a zero row: code 0, radius 0
+    codes, radii = oracle.encode_keys(K, P)
+    assert codes.shape == (n, b // 32) and radii.shape == (n,)
+    for t in range(n):
+        assert np.array_equal(codes[t], oracle.key_code(K[t], P)), t
+        assert radii[t] == oracle.radius_code(oracle.sq_norm(K[t])), t
+    assert not codes[5].any() and radii[5] == 0
+    for t in (0, 1, 18, n - 2, n - 1):
+        assert np.array_equal(codes[t], exact_sign_code(K[t], P)), t
+        r2 = sum((bf16_fraction(x) ** 2 for x in K[t]), Fraction(0))
+        assert int(radii[t]) == exact_radius_code(r2), t
+
+
 def test_code_zero_projection_is_clear_bit():
     b = 32 * 2
     P = np.zeros((D, b), np.float32)
