@@ -19,7 +19,8 @@ from typing import Optional
 import torch
 
 __all__ = ["Config", "DkvError", "encode", "decode", "decode_debug",
-           "decode_profiled", "decode_append", "decode_stage_names",
+           "decode_profiled", "decode_append", "decode_append_noalloc",
+           "decode_stage_names",
            "decode_workspace_size",
            "library_path", "load_library", "EXPORTED_SYMBOLS"]
 
@@ -32,8 +33,10 @@ EXPORTED_SYMBOLS = ("dkv_encode", "dkv_decode_workspace_size", "dkv_decode",
                     "dkv_decode_debug", "dkv_decode_profiled", "dkv_decode_append",
                     "dkv_decode_num_stages", "dkv_decode_stage_name",
                     "dkv_status_string", "dkv_abi_version", "dkv_lsh_index_size",
-                    "dkv_lsh_build", "dkv_decode_lsh")
-ABI_VERSION = 5
+                    "dkv_lsh_build", "dkv_decode_lsh", "dkv_decode_append_noalloc")
+# bytes of the static scratch array dkv_decode_append_noalloc uses
+NOALLOC_SCRATCH_BYTES = 64 << 20
+ABI_VERSION = 6
 RADIUS_LOG = 0
 RADIUS_LINEAR = 1
 
@@ -119,6 +122,8 @@ def load_library():
     lib.dkv_decode_profiled.restype = ctypes.c_int
     lib.dkv_decode_append.argtypes = dec + [P, P]
     lib.dkv_decode_append.restype = ctypes.c_int
+    lib.dkv_decode_append_noalloc.argtypes = dec[:16] + [P]
+    lib.dkv_decode_append_noalloc.restype = ctypes.c_int
     lib.dkv_lsh_index_size.argtypes = [cfgp, i32, i32]
     lib.dkv_lsh_index_size.restype = sz
     lib.dkv_lsh_build.argtypes = [cfgp, P, i64, P, i32, i32, P, i32, P, sz, P]
@@ -224,18 +229,20 @@ def _decode_args(cfg, q, k_pool, v_pool, codes, radii, block_table, seq_lens,
         _expect(sel_idx, "sel_idx", (B, Hkv, cfg.select_cap))
     if sel_cnt is not None:
         _expect(sel_cnt, "sel_cnt", (B, Hkv))
-    if workspace.dtype not in (torch.uint8, torch.int8):
-        raise TypeError("workspace must be a uint8/int8 tensor")
     c = cfg._c()
-    return c, [
+    args = [
         ctypes.byref(c), _ptr(q, "q", _BF16), _ptr(k_pool, "k_pool", _BF16),
         _ptr(v_pool, "v_pool", _BF16), _ptr(codes, "codes", _U32),
         _ptr(radii, "radii", _U8), nb, _ptr(block_table, "block_table", _I32),
         max_blocks, _ptr(seq_lens, "seq_lens", _I32), B, int(max_seq_len),
         _ptr(proj, "proj", _BF16), _ptr(out, "out", (torch.float32,)),
-        _ptr(sel_idx, "sel_idx", _I32), _ptr(sel_cnt, "sel_cnt", _I32),
-        _ptr(workspace, "workspace", (torch.uint8, torch.int8)),
-        workspace.numel() * workspace.element_size()]
+        _ptr(sel_idx, "sel_idx", _I32), _ptr(sel_cnt, "sel_cnt", _I32)]
+    if workspace is None:     # dkv_decode_append_noalloc: no workspace arguments
+        return c, args
+    if workspace.dtype not in (torch.uint8, torch.int8):
+        raise TypeError("workspace must be a uint8/int8 tensor")
+    return c, args + [_ptr(workspace, "workspace", (torch.uint8, torch.int8)),
+                      workspace.numel() * workspace.element_size()]
 
 
 def decode(cfg: Config, q, k_pool, v_pool, codes, radii, block_table, seq_lens,
@@ -286,6 +293,18 @@ def decode_append(cfg: Config, q, k_pool, v_pool, codes, radii, block_table,
     _check(lib.dkv_decode_append(
         *args, ctypes.cast(arr, ctypes.c_void_p) if arr is not None else None,
         _stream(stream)))
+
+
+def decode_append_noalloc(cfg: Config, q, k_pool, v_pool, codes, radii, block_table,
+                          seq_lens, max_seq_len: int, proj, out, sel_idx=None,
+                          sel_cnt=None, stream=None) -> None:
+    """dkv_decode_append_noalloc: decode_append whose workspace is the
+    library's static per-GPU scratch array (no allocation in the call;
+    calls that overlap on one GPU race)."""
+    lib = load_library()
+    c, args = _decode_args(cfg, q, k_pool, v_pool, codes, radii, block_table,
+                           seq_lens, max_seq_len, proj, out, None, sel_idx, sel_cnt)
+    _check(lib.dkv_decode_append_noalloc(*args, _stream(stream)))
 
 
 def lsh_index_size(cfg: Config, batch: int, max_seq_len: int) -> int:

@@ -256,6 +256,35 @@ WorkspacePlan plan_workspace(const DecodeDims &d) {
 
 } // namespace dkv
 
+// The workspace of dkv_decode_append_noalloc: one copy per GPU, held until
+// the process ends.  In host code this name is only a stand-in: kernels get
+// the device address that hipGetSymbolAddress returns for the current
+// device (noalloc_scratch below), never the name itself.
+static __device__ __align__(256) unsigned char scratch[DKV_NOALLOC_SCRATCH_BYTES];
+
+namespace dkv {
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// Device address of the current device's copy of `scratch`, looked up on
+// the first call on that device (with it current) and kept; nullptr when
+// the lookup fails.  Threads racing on a first call store the same address.
+void *noalloc_scratch() {
+  static std::atomic<void *> addr[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void *p = addr[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+    return nullptr;
+  addr[dev].store(p, std::memory_order_release);
+  return p;
+}
+
+} // namespace
+} // namespace dkv
+
 using namespace dkv;
 
 extern "C" {
@@ -364,6 +393,31 @@ __attribute__((visibility("default"))) dkv_status dkv_decode_append(
                      reinterpret_cast<hipStream_t>(stream));
 }
 
+__attribute__((visibility("default"))) dkv_status dkv_decode_append_noalloc(
+    const dkv_config *cfg, const void *q, const void *k_pool, const void *v_pool,
+    uint32_t *codes, uint8_t *radii, int64_t num_blocks, const int32_t *block_table,
+    int32_t max_blocks_per_seq, const int32_t *seq_lens, int32_t batch,
+    int32_t max_seq_len, const void *proj, float *out, int32_t *sel_idx,
+    int32_t *sel_cnt, dkv_stream_t stream) {
+  DecodeDims d;
+  dkv_status why = DKV_OK;
+  if (!make_dims(cfg, batch, max_seq_len, max_blocks_per_seq, num_blocks, &d, &why))
+    return why;
+  if (d.lsh_T > 0) return DKV_ERR_INVALID_ARG; // LSH decodes through dkv_decode_lsh
+  // the size check comes before the device lookup
+  if (plan_workspace(d).total > DKV_NOALLOC_SCRATCH_BYTES) return DKV_ERR_WORKSPACE;
+  if (q == nullptr || k_pool == nullptr || v_pool == nullptr || codes == nullptr ||
+      radii == nullptr || block_table == nullptr || seq_lens == nullptr ||
+      proj == nullptr || out == nullptr)
+    return DKV_ERR_INVALID_ARG;
+  void *ws = noalloc_scratch();
+  if (ws == nullptr) return DKV_ERR_LAUNCH;
+  return decode_impl(cfg, q, k_pool, v_pool, codes, radii, num_blocks, block_table,
+                     max_blocks_per_seq, seq_lens, batch, max_seq_len, proj, out,
+                     sel_idx, sel_cnt, ws, DKV_NOALLOC_SCRATCH_BYTES, nullptr, nullptr,
+                     nullptr, true, nullptr, 0, reinterpret_cast<hipStream_t>(stream));
+}
+
 __attribute__((visibility("default"))) size_t
 dkv_lsh_index_size(const dkv_config *cfg, int32_t batch, int32_t max_seq_len) {
   DecodeDims d;
@@ -440,7 +494,9 @@ dkv_status_string(dkv_status status) {
     return "DKV_ERR_UNSUPPORTED: head_dim, code_bits, page_size, group size "
            "or a size limit is not supported";
   case DKV_ERR_WORKSPACE:
-    return "DKV_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    return "DKV_ERR_WORKSPACE: workspace missing, misaligned or too small "
+           "(dkv_decode_append_noalloc: the step needs more than "
+           "DKV_NOALLOC_SCRATCH_BYTES of workspace)";
   case DKV_ERR_LAUNCH:
     return "DKV_ERR_LAUNCH: a kernel launch failed";
   }

@@ -65,8 +65,10 @@
  *   HIP or torch allocators always are.
  *
  * Ownership and execution: the caller owns every buffer; the library
- * allocates no device or host memory and keeps no mutable global state, so
- * calls on different streams may run concurrently when their output and
+ * allocates no device or host memory and keeps no mutable global state
+ * (apart from a per-device cache of the compute-unit count, and the static
+ * scratch array of dkv_decode_append_noalloc with its per-device address),
+ * so calls on different streams may run concurrently when their output and
  * workspace buffers differ.  Every call only validates its arguments on the
  * host and enqueues kernels on `stream` (a hipStream_t; NULL means the null
  * stream); it returns before the GPU work finishes.  Device-side values
@@ -282,6 +284,37 @@ dkv_status dkv_decode_append(const dkv_config *cfg, const void *q,
                              dkv_event_t *stage_events, dkv_stream_t stream);
 
 /*
+ * dkv_decode_append_noalloc -- dkv_decode_append for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the workspace is the library's
+ * own static device array of DKV_NOALLOC_SCRATCH_BYTES bytes (one per GPU,
+ * held until the process ends) instead of a caller buffer.
+ *   Arguments and outputs as for dkv_decode_append, without workspace and
+ *   stage events; call it with the stream's device current.
+ *   The call allocates nothing (no hipMalloc, hipFree or allocating library
+ *   routine).  Its first call on a device looks up that device's copy of
+ *   the array (hipGetSymbolAddress); DKV_ERR_LAUNCH if that fails.
+ *   DKV_ERR_WORKSPACE when dkv_decode_workspace_size(cfg, batch,
+ *   max_seq_len) exceeds DKV_NOALLOC_SCRATCH_BYTES (for example 16 x 128K
+ *   tokens of 8 KV heads; about 64 (sequence, KV head) pairs of 128K tokens
+ *   fit).  The array needs no initialisation.
+ *   Every call on one GPU uses that GPU's single array: calls that overlap
+ *   on one GPU (concurrent streams, or threads) race and give undefined
+ *   results; serialise them on one stream.
+ */
+#define DKV_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+dkv_status dkv_decode_append_noalloc(const dkv_config *cfg, const void *q,
+                                     const void *k_pool, const void *v_pool,
+                                     uint32_t *codes, uint8_t *radii,
+                                     int64_t num_blocks,
+                                     const int32_t *block_table,
+                                     int32_t max_blocks_per_seq,
+                                     const int32_t *seq_lens, int32_t batch,
+                                     int32_t max_seq_len, const void *proj,
+                                     float *out, int32_t *sel_idx,
+                                     int32_t *sel_cnt, dkv_stream_t stream);
+
+/*
  * Multi-table LSH candidate retrieval ([DASH], "from quadratic to linear":
  * several hash tables split the space into buckets; a query looks only in
  * its own buckets, and the candidates found there are pruned to the top-k
@@ -357,7 +390,7 @@ const char *dkv_decode_stage_name(int32_t stage);
 const char *dkv_status_string(dkv_status status);
 
 /* ABI version of this header (bumped on any signature or layout change). */
-#define DKV_ABI_VERSION 5
+#define DKV_ABI_VERSION 6
 int32_t dkv_abi_version(void);
 
 #ifdef __cplusplus

@@ -185,3 +185,30 @@ def test_lsh_entry_points_reject_bad_arguments():
     assert dec(_cfg()) == 1                                    # index without tables
     assert dec(c, nbytes=size - 1) == 3
     assert dec(c, max_seq_len=(1 << 19) + 1) == 2
+
+
+def test_noalloc_entry_point_rejects_before_any_launch():
+    """dkv_decode_append_noalloc checks the step's workspace need against its
+    static scratch before it touches the device, and validates pointers."""
+    lib = dkv.load_library()
+    c = _cfg()
+
+    def call(cfg, batch, max_seq_len, q=FAKE, num_blocks=200, max_blocks=64):
+        return lib.dkv_decode_append_noalloc(
+            ctypes.byref(cfg) if cfg is not None else None, q, FAKE, FAKE, FAKE, FAKE,
+            num_blocks, FAKE, max_blocks, FAKE, batch, max_seq_len, FAKE, FAKE, None,
+            None, None)
+    need = lib.dkv_decode_workspace_size(ctypes.byref(c), 16, 131072)
+    assert need > dkv.NOALLOC_SCRATCH_BYTES
+    assert call(c, 16, 131072, num_blocks=16 * 8192, max_blocks=8192) == 3
+    assert lib.dkv_decode_workspace_size(ctypes.byref(c), 2, 1000) <= dkv.NOALLOC_SCRATCH_BYTES
+    assert call(c, 2, 1000, q=None) == 1
+    assert call(None, 2, 1000) == 1
+    assert call(_cfg(lsh_tables=4, lsh_bits=8), 2, 1000) == 1
+    assert call(_cfg(code_bits=96), 2, 1000) == 2
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define DKV_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == dkv.NOALLOC_SCRATCH_BYTES
