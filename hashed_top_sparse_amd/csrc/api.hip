@@ -91,8 +91,9 @@ bool make_dims(const dkv_config *cfg, int32_t batch, int32_t max_seq_len,
     *why = DKV_ERR_UNSUPPORTED;
     return false;
   }
-  // buffer views of the code and radius pools use 32-bit byte offsets
-  if ((uint64_t)num_blocks * d->Hkv * d->W * kPage * 4 > 0xFFFFFFFFull) {
+  // buffer views of the code and radius pools use 32-bit byte offsets; a
+  // load of an invalid page starts at the pool's end, and stays below 2^32
+  if ((uint64_t)num_blocks * d->Hkv * d->W * kPage * 4 > 0xFFFFF000ull) {
     *why = DKV_ERR_UNSUPPORTED;
     return false;
   }

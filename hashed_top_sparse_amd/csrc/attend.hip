@@ -92,7 +92,7 @@ static_assert(kWaveRows <= 64, "one row id per lane");
 constexpr int kPStride = 8; // floats per row of the p tile (G <= 8)
 
 template <int G>
-__global__ __launch_bounds__(kThreads) void attend_split_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2, 8))) void attend_split_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_pool,
     const uint16_t *__restrict__ v_pool, const int32_t *__restrict__ rows,
     const int32_t *__restrict__ cnt, int cap, float *__restrict__ part, int Hq,
@@ -107,18 +107,23 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(
   const int r0 = split * kAttnRows;
   const int r1 = (r0 + kAttnRows < n) ? r0 + kAttnRows : n;
 
-  // this wave's row ids, one per lane (handed out by lane shuffles)
+  // Every load below is issued by every lane, at a clamped in-bounds
+  // address, and values that are not needed are dropped where they are
+  // used: a load inside a lane-dependent branch makes the compiler wait for
+  // it (and for every load issued before it) at the end of the branch.
+  //
+  // this wave's row ids, one per lane (handed out by lane shuffles); the
+  // list is filled up to cap (-1 past the count)
   const int row0 = wave * kWaveRows;
-  const int myid = lane < kWaveRows && r0 + row0 + lane < r1
-                       ? rows[(int64_t)unit * cap + r0 + row0 + lane] : -1;
+  const int myid_raw = rows[(int64_t)unit * cap + min(r0 + row0 + lane, cap - 1)];
+  const int myid = lane < kWaveRows && r0 + row0 + lane < r1 ? myid_raw : -1;
 
   // query operand: head lrow (zero past G); K-step c takes dims
   // 32c + 8*lgrp .. +8, the same dims the key rows give this lane
   uint4 qb[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) qb[c] = make_uint4(0u, 0u, 0u, 0u);
-  if (lrow < G) {
-    const uint16_t *src = q + ((int64_t)s * Hq + (int64_t)g * G + lrow) * kHeadDim + 8 * lgrp;
+  {
+    const uint16_t *src = q + ((int64_t)s * Hq + (int64_t)g * G + min(lrow, G - 1)) * kHeadDim +
+                          8 * lgrp;
 #pragma unroll
     for (int c = 0; c < 4; ++c) qb[c] = *reinterpret_cast<const uint4 *>(src + 32 * c);
   }
@@ -134,28 +139,35 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[h][c] = 0.f;
 
-  auto load_tile = [&](int t, uint4 (&kr)[4], uint4 (&vr)[4], uint32_t &kvalid) {
+  // A tile's key and value rows; a row past the list reads pool row 0 (in
+  // bounds) and is dropped in use_tile.  vok bit i: value row lgrp + 4i is
+  // a listed row.
+  auto load_tile = [&](int t, uint4 (&kr)[4], uint4 (&vr)[4], uint32_t &kvalid,
+                       uint32_t &vok) {
     const int base = t * kTileRows;
     const int kid = __shfl(myid, base + lrow);
     kvalid = kid >= 0;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) kr[c] = make_uint4(0u, 0u, 0u, 0u);
-    if (kid >= 0) {
+    {
       // load c: the row's bytes 64c .. 64c+63, 16 per lane row group
-      const uint16_t *src = k_pool + ((int64_t)kid * Hkv + g) * kHeadDim + 8 * lgrp;
+      const uint16_t *src = k_pool + ((int64_t)max(kid, 0) * Hkv + g) * kHeadDim + 8 * lgrp;
 #pragma unroll
       for (int c = 0; c < 4; ++c) kr[c] = *reinterpret_cast<const uint4 *>(src + 32 * c);
     }
+    vok = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int vid = __shfl(myid, base + lgrp + 4 * i);
-      vr[i] = make_uint4(0u, 0u, 0u, 0u);
-      if (vid >= 0)
-        vr[i] = *reinterpret_cast<const uint4 *>(
-            v_pool + ((int64_t)vid * Hkv + g) * kHeadDim + 8 * lrow);
+      vok |= (uint32_t)(vid >= 0) << i;
+      vr[i] = *reinterpret_cast<const uint4 *>(
+          v_pool + ((int64_t)max(vid, 0) * Hkv + g) * kHeadDim + 8 * lrow);
     }
   };
-  auto use_tile = [&](const uint4 (&kr)[4], const uint4 (&vr)[4], uint32_t kvalid) {
+  auto use_tile = [&](const uint4 (&kr)[4], const uint4 (&vr)[4], uint32_t kvalid,
+                      uint32_t vok) {
+    if (lrow >= G) { // the operand's padding heads are zero
+#pragma unroll
+      for (int c = 0; c < 4; ++c) qb[c] = make_uint4(0u, 0u, 0u, 0u);
+    }
     // ---- logits of the tile's 16 rows for every head
     v4f32 S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -208,8 +220,13 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(
       for (int c = 0; c < 8; ++c) acc[h][c] *= cr[h];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      // a value row past the list counts as zeros (its p is 0 too; zeros
+      // keep the stand-in row's values, whatever they are, out of the sums)
       float vf[8];
       unpack8(vr[i], vf);
+      const bool vin = (vok >> i) & 1u;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) vf[c] = vin ? vf[c] : 0.f;
       const int r = lgrp + 4 * i;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
@@ -225,11 +242,11 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(
   {
     // every tile's rows are requested at once, then used in order
     uint4 kt[kTiles][4], vt[kTiles][4];
-    uint32_t ok[kTiles];
+    uint32_t ok[kTiles], vok[kTiles];
 #pragma unroll
-    for (int t = 0; t < kTiles; ++t) load_tile(t, kt[t], vt[t], ok[t]);
+    for (int t = 0; t < kTiles; ++t) load_tile(t, kt[t], vt[t], ok[t], vok[t]);
 #pragma unroll
-    for (int t = 0; t < kTiles; ++t) use_tile(kt[t], vt[t], ok[t]);
+    for (int t = 0; t < kTiles; ++t) use_tile(kt[t], vt[t], ok[t], vok[t]);
   }
 
   // The wave's state: m, l per head (lane lrow), acc per row group over its
@@ -266,8 +283,9 @@ __global__ __launch_bounds__(kThreads) void attend_split_kernel(
 }
 
 // Merge of the split states: one workgroup of 128 threads (one per dim)
-// per (sequence, query head).  Splits are taken 32 at a time, all 32
-// states loaded before any is used so the loads overlap.
+// per (sequence, query head).  Splits are taken 32 at a time: threads 0..31
+// load the splits' (m, l) into LDS while every thread loads its dim of the
+// splits' accumulators, all before any is used, so the loads overlap.
 constexpr int kCombineChunk = 32;
 
 __global__ __launch_bounds__(kHeadDim) void attend_combine_kernel(
@@ -280,29 +298,35 @@ __global__ __launch_bounds__(kHeadDim) void attend_combine_kernel(
   const int dim = threadIdx.x;
   const float *src0 = part + ((int64_t)unit * nsplit * G + h) * kPartStride;
   const int64_t stride = (int64_t)G * kPartStride;
+  __shared__ float sml[2][kCombineChunk];
   float mm = -INFINITY, ll = 0.f, aa = 0.f;
   for (int p0 = 0; p0 < nsplit; p0 += kCombineChunk) {
-    float mp[kCombineChunk], lp[kCombineChunk], ap[kCombineChunk];
-#pragma unroll
-    for (int i = 0; i < kCombineChunk; ++i) {
-      const int p = p0 + i < nsplit ? p0 + i : p0;
-      const float *src = src0 + p * stride;
-      mp[i] = p0 + i < nsplit ? src[0] : -INFINITY;
-      lp[i] = src[1];
-      ap[i] = src[2 + dim];
+    const int n = min(kCombineChunk, nsplit - p0);
+    if (dim < kCombineChunk) {
+      const float *src = src0 + (int64_t)(p0 + dim) * stride;
+      sml[0][dim] = dim < n ? src[0] : -INFINITY;
+      sml[1][dim] = dim < n ? src[1] : 0.f;
     }
+    float ap[kCombineChunk];
+#pragma unroll
+    for (int i = 0; i < kCombineChunk; ++i)
+      ap[i] = i < n ? src0[(int64_t)(p0 + i) * stride + 2 + dim] : 0.f;
+    __syncthreads();
     float mc = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < kCombineChunk; ++i) mc = fmaxf(mc, mp[i]);
-    if (mc == -INFINITY) continue;
-    float lc = 0.f, ac = 0.f;
+    for (int i = 0; i < kCombineChunk; ++i) mc = fmaxf(mc, sml[0][i]);
+    if (mc != -INFINITY) { // workgroup-uniform
+      float lc = 0.f, ac = 0.f;
 #pragma unroll
-    for (int i = 0; i < kCombineChunk; ++i) {
-      const float c = (mp[i] == -INFINITY) ? 0.f : exp2f(mp[i] - mc);
-      lc = fmaf(lp[i], c, lc);
-      ac = fmaf(ap[i], c, ac);
+      for (int i = 0; i < kCombineChunk; ++i) {
+        const float mp = sml[0][i];
+        const float c = (mp == -INFINITY) ? 0.f : exp2f(mp - mc);
+        lc = fmaf(sml[1][i], c, lc);
+        ac = fmaf(ap[i], c, ac);
+      }
+      merge_state(mm, ll, &aa, mc, lc, &ac, 1);
     }
-    merge_state(mm, ll, &aa, mc, lc, &ac, 1);
+    __syncthreads(); // sml is rewritten by the next chunk
   }
   out[(int64_t)sh * kHeadDim + dim] = (ll > 0.f) ? aa / ll : 0.f;
 }

@@ -38,6 +38,8 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kStage = 12288;        // candidates staged in LDS as (u, pos)
+constexpr int kRowAhead = 8;         // staged entries per thread whose rows are looked up early
+constexpr int kStageRound = 8;       // groups per wave whose loads are in flight together
 constexpr int kMaxGroupsLds = 4096;  // groups whose count prefix fits in LDS
 constexpr uint32_t kPosMax = 0x00FFFFFFu; // positions < 2^24
 
@@ -93,17 +95,33 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
   int32_t *R = rows + (int64_t)unit * cap;
   int32_t *U = user_sel ? user_sel + (int64_t)unit * cap : nullptr;
 
-  for (int i = tid; i < base; i += kThreads) {
-    const int pos = i < ns ? i : ws + (i - ns);
-    R[i] = row_of(bt, pos, num_blocks);
-    if (U) U[i] = pos;
-  }
-  if (rows_known) {
-    for (int i = total + tid; i < cap; i += kThreads) {
-      R[i] = -1;
-      if (U) U[i] = -1;
+  // Loads are issued by every thread at clamped in-bounds addresses and
+  // their values dropped where they are used: a load in a lane-dependent
+  // branch, or a select on its value, makes the compiler wait for it (and
+  // for every load issued before it) right there.
+  //
+  // The block id of this thread's first sink or window row is requested
+  // first; the row is written once the group counts are requested too.
+  const int sw_pos = tid < ns ? tid : ws + (tid - ns); // row tid of the list
+  const int sw_blk = bt[clamp_int(sw_pos, 0, max(N - 1, 0)) / kPage];
+  auto write_sinks_window = [&]() {
+    if (tid < base) {
+      R[tid] = (sw_blk >= 0 && sw_blk < num_blocks) ? sw_blk * kPage + sw_pos % kPage : -1;
+      if (U) U[tid] = sw_pos;
     }
-  }
+    for (int i = tid + kThreads; i < base; i += kThreads) { // (a window past kThreads)
+      const int pos = i < ns ? i : ws + (i - ns);
+      R[i] = row_of(bt, pos, num_blocks);
+      if (U) U[i] = pos;
+    }
+    if (rows_known) {
+      for (int i = total + tid; i < cap; i += kThreads) {
+        R[i] = -1;
+        if (U) U[i] = -1;
+      }
+    }
+  };
+  bool sw_done = false;
 
   if (keff > 0) {
     uint32_t *bm = bitmap + (int64_t)unit * bm_stride;
@@ -116,6 +134,8 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
         atomicOr(&bm[lo >> 5], ((1u << (hi - lo)) - 1u) << (lo & 31));
     };
     if (!lsh && keff == nitems) {
+      write_sinks_window();
+      sw_done = true;
       // every candidate is selected, in position order
       for (int i = tid; i < nc; i += kThreads) {
         const int pos = c0 + i;
@@ -136,14 +156,21 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
       {
         constexpr int kPer = kMaxGroupsLds / kThreads;
         uint32_t c[kPer], part = 0;
-        if (pre_lds) {
+        if (pre_lds) { // workgroup-uniform; ngs >= 1 here (N > w + sigma)
+          uint32_t raw[kPer];
+#pragma unroll
+          for (int i = 0; i < kPer; ++i) raw[i] = tc[min(tid * kPer + i, ngs - 1)];
+          write_sinks_window();
+          sw_done = true;
 #pragma unroll
           for (int i = 0; i < kPer; ++i) {
             const int gi = tid * kPer + i;
-            c[i] = gi < ngs ? min(tc[gi], (uint32_t)kGroupKeys) : 0u;
+            c[i] = gi < ngs ? min(raw[i], (uint32_t)kGroupKeys) : 0u;
             part += c[i];
           }
         } else {
+          write_sinks_window();
+          sw_done = true;
           for (int gi = tid; gi < ngs; gi += kThreads)
             part += min(tc[gi], (uint32_t)kGroupKeys);
         }
@@ -191,29 +218,27 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
         __syncthreads();
         if (staged) {
           // group g's candidates go to st[gpre[g] ..): wave v copies groups
-          // v, v+16, ..., four groups' first 64 entries in flight at once
-          for (int g0 = wave; g0 < ngs; g0 += 4 * kWaves) {
-            uint2 e[4];
-            uint32_t dst[4];
+          // v, v+16, ..., kStageRound groups' first 64 entries in flight at
+          // once (every lane loads; entries past a group's count, and
+          // groups past the unit's, are not stored)
+          for (int g0 = wave; g0 < ngs; g0 += kStageRound * kWaves) {
+            uint2 e[kStageRound];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int gi = g0 + r * kWaves;
-              e[r] = make_uint2(0u, 0u);
-              dst[r] = 0xFFFFFFFFu;
-              if (gi < ngs) {
-                const uint32_t b = gpre[gi], n = gpre[gi + 1] - b;
-                if ((uint32_t)lane < n) {
-                  e[r] = cb[(int64_t)gi * kGroupKeys + lane];
-                  dst[r] = b + (uint32_t)lane;
-                }
-              }
+            for (int r = 0; r < kStageRound; ++r) {
+              const int gi = min(g0 + r * kWaves, ngs - 1);
+              e[r] = cb[(int64_t)gi * kGroupKeys + lane];
             }
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (dst[r] != 0xFFFFFFFFu) st[dst[r]] = e[r];
+            for (int r = 0; r < kStageRound; ++r) {
+              const int gi = g0 + r * kWaves;
+              if (gi < ngs) { // wave-uniform
+                const uint32_t b = gpre[gi], n = gpre[gi + 1] - b;
+                if ((uint32_t)lane < n) st[b + (uint32_t)lane] = e[r];
+              }
+            }
             // entries past the first 64 of a group (rare)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
+            for (int r = 0; r < kStageRound; ++r) {
               const int gi = g0 + r * kWaves;
               if (gi < ngs) {
                 const uint32_t b = gpre[gi], n = gpre[gi + 1] - b;
@@ -232,15 +257,22 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
           }
         };
         // the compaction below gives thread t the run [i0, i1) of the staged
-        // list; the physical rows of its first four entries are looked up
-        // now, so the block-table loads overlap the cut
+        // list; the block ids of its first kRowAhead entries are requested
+        // now (positions clamped into the sequence), so the block-table
+        // loads overlap the cut
         const uint32_t per = (nlist + kThreads - 1) / kThreads;
         const uint32_t i0 = min(nlist, tid * per), i1 = min(nlist, i0 + per);
-        int rowv[4];
+        int rblk[kRowAhead];
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-          rowv[k] = (staged && !pages && i0 + k < i1)
-                        ? row_of(bt, (int)st[i0 + k].y, num_blocks) : -1;
+        for (int k = 0; k < kRowAhead; ++k) {
+          const uint32_t i = min(i0 + (uint32_t)k, (uint32_t)kStage - 1u);
+          const int pos = (staged && !pages) ? clamp_int((int)st[i].y, 0, N - 1) : 0;
+          rblk[k] = bt[pos / kPage];
+        }
+        // the row of staged entry i0 + k at position pos
+        auto row_ahead = [&](int k, int pos) {
+          return (rblk[k] >= 0 && rblk[k] < num_blocks) ? rblk[k] * kPage + pos % kPage : -1;
+        };
         // the cut: survivors are u > Tu, or u == Tu and pos <= Tpos
         uint32_t Tu = 0, Tpos = 0;
         bool cut = false;
@@ -353,18 +385,18 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
           uint32_t tot;
           uint32_t o = wg_exclusive_scan<kThreads>(c, &sel.red[3][0], &tot);
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
+          for (int k = 0; k < kRowAhead; ++k) {
             const uint32_t i = i0 + k;
             if (i < i1) {
               const int pos = (int)st[i].y;
               if (keep(st[i].x, pos)) {
-                R[base + o] = rowv[k];
+                R[base + o] = row_ahead(k, pos);
                 if (U) U[base + o] = pos;
                 ++o;
               }
             }
           }
-          for (uint32_t i = i0 + 4; i < i1; ++i) {
+          for (uint32_t i = i0 + kRowAhead; i < i1; ++i) {
             const int pos = (int)st[i].y;
             if (keep(st[i].x, pos)) {
               R[base + o] = row_of(bt, pos, num_blocks);
@@ -451,6 +483,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
       }
     }
   }
+  if (!sw_done) write_sinks_window(); // keff == 0 (workgroup-uniform)
   if (tid == 0) {
     cnt[unit] = total;
     if (user_cnt) user_cnt[unit] = total;

@@ -29,10 +29,11 @@
 //
 // Candidate threshold.  The same workgroup then scores a deterministic
 // sample of the (sequence, KV head)'s candidate pages -- every SP-th page
-// from the first candidate page, SP a power of two <= 32 chosen so the
-// sample holds at most 512 pages -- and sets L = the k_s-th largest sampled
-// biased score, k_s = ceil(2 * k_eff * n_sample / n_candidates), so about
-// 2*k_eff keys are expected to reach L.  The streaming pass keeps every key
+// from the first candidate page, SP the largest power of two <= 64 with
+// 2*SP <= k_eff/16 (about 64 sampled keys at the cut), doubled while the
+// sample would hold more than 512 pages -- and sets L from the k_s-th
+// largest sampled biased score, k_s = ceil(2 * k_eff * n_sample /
+// n_candidates), so about 2*k_eff keys are expected to reach L.  The streaming pass keeps every key
 // with u >= L; the merge checks that at least k_eff did (then the exact
 // top-k is among them) and otherwise rescans exactly.  L = 0 keeps every
 // candidate (used when k_eff covers all of them or the sample is too small
@@ -49,9 +50,10 @@ namespace {
 constexpr int kThreads = 512;
 constexpr int kMaxPairs = 4;      // G*b <= 8*256 = 4*512
 constexpr int kSamplePages = 512; // sample pages per (sequence, KV head)
-constexpr int kSampleKeys = kSamplePages * kPage;
 constexpr int kWv = kThreads / 64;
-constexpr int kPre = 32; // sample pages per wave whose loads start first
+constexpr int kWavePages = kSamplePages / kWv; // sample pages per wave (<= 64)
+constexpr int kWaveQuads = kWavePages / 4;     // their page quads
+static_assert(kWavePages <= 64, "one page per lane");
 
 // e4m3 (bias 7) byte of a small integer v, |v| <= 60 with at most four
 // significant bits (exactly representable).
@@ -64,7 +66,9 @@ __device__ __forceinline__ uint32_t e4m3_of_int(int v) {
   return sign | ((uint32_t)(e + 7) << 3) | mant;
 }
 
-template <int KS, int G>
+// WC: code words per key (b/32: 2, 4 or 8), fixed at compile time so the
+// sample loads need no branch on it; KS: 128-bit matrix-core K-steps.
+template <int WC, int G, int KS = (WC > 4 ? WC / 4 : 1)>
 __global__ __launch_bounds__(kThreads) void prep_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ proj,
     const uint32_t *codes, const uint8_t *radii, const uint16_t *__restrict__ k_pool,
@@ -74,20 +78,25 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     const int32_t *__restrict__ seq_lens, int n_max, int8_t *__restrict__ q8,
     uint32_t *__restrict__ qop, float *__restrict__ qneg,
     uint32_t *__restrict__ lthr, uint32_t *__restrict__ qbits,
-    uint32_t *__restrict__ tasks, int Hq, int Hkv, int b, int W, int k, int w,
+    uint32_t *__restrict__ tasks, int Hq, int Hkv, int k, int w,
     int sigma, bool lin, bool pages) {
+  constexpr int W = WC, b = 32 * WC;
   const int unit = blockIdx.x;
   const int s = unit / Hkv;
   const int g = unit % Hkv;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __shared__ __align__(16) uint16_t sQ[8 * kHeadDim];
-  __shared__ __align__(16) uint16_t sP[kHeadDim * 256];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); // uniform
+  // the group's query rows as doubles, and P: fp32 for b <= 128, bf16 for
+  // b = 256 (64 KB either way); each holds the exact bf16 values
+  __shared__ __align__(16) double sQd[8 * kHeadDim];
+  __shared__ __align__(16) uint32_t sP[kHeadDim * 128];
   __shared__ int sq8[8 * 256];
   __shared__ uint32_t sOp[2 * 512];
-  __shared__ uint32_t sSample[kSampleKeys];
+  // each wave's sample radius lines: 16 bytes per page, page order
+  __shared__ __align__(16) uint8_t sRad[kWv][kWavePages * kPage];
   __shared__ double sMax[kThreads / 64];
   __shared__ int sSum[8];
-  __shared__ uint32_t sCount[kThreads / 64];
+  __shared__ uint32_t sCount[3][kThreads / 64];
   __shared__ SelectShared<kThreads> sel;
 
   // ---- sample plan: every SP-th candidate page from page pc0, nsp pages
@@ -104,156 +113,206 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     if (!pages && qbits == nullptr && P.keff > 0 && P.keff < P.nc) {
       P.pc0 = sigma / kPage;
       const int ncp = (n - w + kPage - 1) / kPage - P.pc0;
-      while (P.SP < 32 && 2 * P.SP <= P.keff / 32) P.SP *= 2;
+      while (P.SP < 64 && 2 * P.SP <= P.keff / 16) P.SP *= 2;
       while ((ncp + P.SP - 1) / P.SP > kSamplePages) P.SP *= 2;
       P.nsp = (ncp + P.SP - 1) / P.SP;
     }
     return P;
   };
-  // P and the group's query rows are requested first, into registers: the
-  // staging barrier below then waits only for them and not for the sample
-  // pages requested after them (loads count down in order).
-  constexpr int kPLoads = 4 * KS; // uint4 of P per thread (b <= 128 * KS)
-  uint4 pv[kPLoads];
-  const int pn = kHeadDim * b / 8;
-  {
-    const uint4 *psrc = reinterpret_cast<const uint4 *>(proj); // 16-byte aligned
-#pragma unroll
-    for (int r = 0; r < kPLoads; ++r) {
-      const int i = (int)threadIdx.x + r * kThreads;
-      pv[r] = i < pn ? psrc[i] : make_uint4(0u, 0u, 0u, 0u);
-    }
-  }
-  const uint4 *qsrc = reinterpret_cast<const uint4 *>(
-      q + ((int64_t)s * Hq + (int64_t)g * G) * kHeadDim);
-  const uint4 qv4 = (int)threadIdx.x < G * kHeadDim / 8 ? qsrc[threadIdx.x]
-                                                         : make_uint4(0u, 0u, 0u, 0u);
-  // The streaming filter's task list is written by the workgroups of KV
-  // head 0: the lengths of the sequences before s (the first kThreads of
-  // them, one per thread) are requested now and summed at the end.
-  const int len_before = (g == 0 && (int)threadIdx.x < s) ? seq_lens[threadIdx.x] : 0;
-  // The sample pages' loads go next so they are in flight while the query
-  // is projected.  Their block ids are read with the plan of the longest
-  // length (n_max) before the sequence's own length has arrived; when that
-  // length gives another stride or start (ragged batches) they are read
-  // again.  Wave v samples pages t = v + 8*i; lane i holds the block id of
-  // its i-th page.
+  // The loads of this prologue are issued by every thread, at clamped
+  // in-bounds addresses, and unused values are dropped only where they are
+  // used: a load inside a lane-dependent branch, or a select on a loaded
+  // value, makes the compiler wait for it -- and for every load issued
+  // before it -- right there.
+  //
+  // First the sample pages' block ids (the sample loads need them soonest):
+  // read with the plan of the longest length (n_max) before the sequence's
+  // own length has arrived, and read again only when the sequence's plan
+  // differs (ragged batches).  Wave v samples pages t = v + 8*i; lane i
+  // holds the block id of its i-th page.
   const int32_t *bt = block_table + (int64_t)s * max_blocks;
   const int tl = wave + kWv * lane;
   const Plan spec = plan_for(n_max);
-  int blk_l = tl < spec.nsp ? bt[spec.pc0 + tl * spec.SP] : -1;
+  // (page pc0 + t*SP < max_blocks for every t < nsp)
+  int blk_raw = bt[spec.nsp > 0 ? spec.pc0 + min(tl, spec.nsp - 1) * spec.SP : 0];
+  // then P and the group's query rows, into registers
+  constexpr int kPLoads = 4 * KS; // uint4 of P per thread (b <= 128 * KS)
+  uint4 pv[kPLoads];
+  constexpr int pn = kHeadDim * b / 8;
+  {
+    const uint4 *psrc = reinterpret_cast<const uint4 *>(proj); // 16-byte aligned
+#pragma unroll
+    for (int r = 0; r < kPLoads; ++r)
+      pv[r] = psrc[min((int)threadIdx.x + r * kThreads, pn - 1)];
+  }
+  const uint4 *qsrc = reinterpret_cast<const uint4 *>(
+      q + ((int64_t)s * Hq + (int64_t)g * G) * kHeadDim);
+  const uint4 qv4 = qsrc[min((int)threadIdx.x, G * kHeadDim / 8 - 1)];
+  // The streaming filter's task list is written by the workgroups of KV
+  // head 0: the lengths of the sequences before s (the first kThreads of
+  // them, one per thread) are requested now and summed at the end.
+  const int len_before_raw = seq_lens[min((int)threadIdx.x, s)];
   const int N = seq_len_clamped(seq_lens, s, n_max);
   const Plan pl = plan_for(N);
   const int nc = pl.nc, keff = pl.keff, pc0 = pl.pc0, SP = pl.SP, nsp = pl.nsp;
   const bool sample = nsp > 0;
   if (SP != spec.SP || pc0 != spec.pc0 || nsp > spec.nsp) // workgroup-uniform
-    blk_l = tl < nsp ? bt[pc0 + tl * SP] : -1;
-  else if (tl >= nsp)
-    blk_l = -1;
-  const PoolView view = make_pool_view(codes, radii, code_bytes, radius_bytes,
-                                       W, Hkv, g, lane);
-  uint32_t pcw[kPre][KS], pr8[kPre];
-  uint32_t pokm = 0; // bit u: preloaded page u is a valid sample page
-  static_assert(kPre <= 32, "page mask");
-  if (nsp > 0) {
-#pragma unroll
-    for (int u = 0; u < kPre; ++u) {
-      const int blk = __builtin_amdgcn_readlane(blk_l, u);
-      const bool ok = wave + kWv * u < nsp && blk >= 0 && blk < num_blocks;
-      pokm |= (uint32_t)ok << u;
-      load_page<KS>(view, blk, ok, pcw[u], pr8[u]);
-    }
-  }
+    blk_raw = bt[nsp > 0 ? pc0 + min(tl, nsp - 1) * SP : 0]; // (ragged lengths)
 
   // ---- append: the workgroup also encodes position N-1 of sequence s for
   // KV head g (the key the caller has just written), as the encode kernel
-  // would: its projection chains run beside the query's below
-  __shared__ __align__(16) uint16_t sK[kHeadDim];
+  // would.  Its row is requested now (three dependent loads: the length,
+  // the block id, the row) and used only after the threshold: the newest
+  // key lies in the window, and with no window the filter reads its code
+  // after this kernel anyway.
+  __shared__ __align__(16) double sKd[kHeadDim];
   int a_blk = -1;
-  if (codes_w != nullptr && N > 0) {
+  if (codes_w != nullptr && N > 0) { // workgroup-uniform
     const int blk = bt[(N - 1) / kPage];
     if (blk >= 0 && blk < num_blocks) a_blk = blk;
   }
   const int a_slot = (N - 1) % kPage;
-  if (a_blk >= 0 && threadIdx.x < kHeadDim / 2) {
-    const uint32_t *krow = reinterpret_cast<const uint32_t *>(
-        k_pool + (((int64_t)a_blk * kPage + a_slot) * Hkv + g) * kHeadDim);
-    reinterpret_cast<uint32_t *>(sK)[threadIdx.x] = krow[threadIdx.x];
-  }
+  // (block 0 stands in when there is no key to encode; threads past the
+  // row's 64 dwords re-read them)
+  const uint32_t *krow = reinterpret_cast<const uint32_t *>(
+      k_pool + (((int64_t)max(a_blk, 0) * kPage + max(a_slot, 0)) * Hkv + g) * kHeadDim);
+  const uint32_t krow_w = krow[threadIdx.x & (kHeadDim / 2 - 1)];
 
-  if ((int)threadIdx.x < G * kHeadDim / 8) reinterpret_cast<uint4 *>(sQ)[threadIdx.x] = qv4;
+  // the threshold histogram is cleared now (its first use is after the
+  // staging barrier)
+  for (int i = threadIdx.x; i < kHistBins; i += kThreads) sel.hist[i] = 0;
+
+  if ((int)threadIdx.x < G * kHeadDim / 8) {
+    const uint32_t w4[4] = {qv4.x, qv4.y, qv4.z, qv4.w};
+    double2 *dst = reinterpret_cast<double2 *>(sQd + 8 * threadIdx.x);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      dst[u] = make_double2((double)bf16_to_float(w4[u] & 0xFFFFu),
+                            (double)bf16_to_float(w4[u] >> 16));
+  }
 #pragma unroll
   for (int r = 0; r < kPLoads; ++r) {
     const int i = (int)threadIdx.x + r * kThreads;
-    if (i < pn) reinterpret_cast<uint4 *>(sP)[i] = pv[r];
+    if (i < pn) {
+      if (KS == 1) { // 8 columns as fp32
+        const uint32_t w4[4] = {pv[r].x, pv[r].y, pv[r].z, pv[r].w};
+        uint4 *dst = reinterpret_cast<uint4 *>(sP + 8 * i);
+        dst[0] = make_uint4(w4[0] << 16, w4[0] & 0xFFFF0000u, w4[1] << 16, w4[1] & 0xFFFF0000u);
+        dst[1] = make_uint4(w4[2] << 16, w4[2] & 0xFFFF0000u, w4[3] << 16, w4[3] & 0xFFFF0000u);
+      } else {
+        reinterpret_cast<uint4 *>(sP)[i] = pv[r];
+      }
+    }
   }
   if (threadIdx.x < 8) sSum[threadIdx.x] = 0;
   __syncthreads();
 
-  // p_hj in double precision, index order (one chain per (h, j) pair).
-  // Batches of 8 terms: the next batch's LDS reads are issued before the
-  // current batch's multiply-adds, which stay in index order.  With KEY,
-  // the thread also runs the newest key's chain for the same column j and
-  // the key's |k|^2 chain.
-  const int npairs = G * b;
-  double p[kMaxPairs];
-  double mloc = 0.0;
-  double pk = 0.0, r2 = 0.0;
-  auto project = [&](auto key_tag, int h, int j) {
-    constexpr bool KEY = decltype(key_tag)::value;
-    const uint4 *qrow = reinterpret_cast<const uint4 *>(sQ + h * kHeadDim);
-    const uint4 *krow = reinterpret_cast<const uint4 *>(sK);
-    const uint16_t *pcol = sP + j;
-    uint4 qa = qrow[0], ka = KEY ? krow[0] : make_uint4(0, 0, 0, 0);
-    uint32_t pa[8];
+  // ---- the sample pages' loads, in flight while the query is projected
+  // (issued after the staging barrier: their addresses need the block ids,
+  // which have arrived by now, while waiting for those ids earlier would
+  // also have waited for every load issued before them).
+  // Page quads as in the streaming filter: lane 16j+c loads the code words
+  // of key c of page 4a+j of the wave; lane i loads the radius line of page
+  // i.  Pages past the wave's share or with an invalid block id read past
+  // the pools (zeros) and count as no sample.
+  const int npw = sample ? (nsp - wave + kWv - 1) / kWv : 0; // wave-uniform
+  const uint32_t ph_none = (uint32_t)(num_blocks * Hkv);
+  const uint32_t ph_l = (lane < npw && blk_raw >= 0 && blk_raw < num_blocks)
+                            ? (uint32_t)blk_raw * (uint32_t)Hkv + (uint32_t)g : ph_none;
+  const uint32_t page_bytes = (uint32_t)(kPage * W * 4);
+  const uint32_t key_byte = (uint32_t)((lane & 15) * W * 4);
+  const __amdgpu_buffer_rsrc_t code_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t *>(codes), 0, code_bytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rad_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(radii), 0, radius_bytes, kBufferWord3);
+  uint32_t qx[kWaveQuads][KS][4];
+  uint4 rline = make_uint4(0u, 0u, 0u, 0u);
+  if (sample) { // workgroup-uniform
+    const auto rv = __builtin_amdgcn_raw_buffer_load_b128(rad_rsrc, (int)(ph_l * (uint32_t)kPage), 0, 0);
+    rline = make_uint4(rv[0], rv[1], rv[2], rv[3]);
+    // The first half of the quads are loaded unconditionally (pages past the
+    // wave's share read zeros), the second half only when the sample needs
+    // them: a branch around each load would make the compiler copy the
+    // loaded words inside it, which waits for the load there.
 #pragma unroll
-    for (int u = 0; u < 8; ++u) pa[u] = pcol[u * b];
+    for (int a = 0; a < kWaveQuads; ++a) {
+      if (a < kWaveQuads / 2 || npw > 2 * kWaveQuads) { // wave-uniform
+        const uint32_t mine = (uint32_t)__shfl((int)ph_l, 4 * a + (lane >> 4));
+        const int voff = (int)(mine * page_bytes + key_byte);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          if constexpr (W == 2) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b64(code_rsrc, voff, 0, 0);
+            qx[a][ks][0] = v[0];
+            qx[a][ks][1] = v[1];
+            qx[a][ks][2] = 0u;
+            qx[a][ks][3] = 0u;
+          } else {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(code_rsrc, voff + 16 * ks, 0, 0);
+            qx[a][ks][0] = v[0];
+            qx[a][ks][1] = v[1];
+            qx[a][ks][2] = v[2];
+            qx[a][ks][3] = v[3];
+          }
+        }
+      }
+    }
+  }
+
+  // p_hj in double precision, index order (one chain per (h, j) pair).
+  // P_ij (exact in fp32 or as bf16) and q_hi (a double in LDS, the same for
+  // the whole wave) go into one fused multiply-add per term: the product of
+  // two bf16 values is exact in double, so this is the definition's chain.
+  // Batches of 8 terms: the next batch's LDS reads are issued before the
+  // current batch's multiply-adds, which stay in index order.
+  const int npairs = G * b;
+  // P_ij as a double
+  auto p_at = [&](int i, int j) -> double {
+    if (KS == 1) return (double)__uint_as_float(sP[i * b + j]);
+    const uint16_t *ph = reinterpret_cast<const uint16_t *>(sP);
+    return (double)bf16_to_float(ph[i * b + j]);
+  };
+  // sum_i x_i P_ij in index order, x a row of doubles in LDS
+  auto chain = [&](const double *x, int j) -> double {
+    double pa[8], xa[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      pa[u] = p_at(u, j);
+      xa[u] = x[u];
+    }
     double acc = 0.0;
 #pragma unroll 2
     for (int i0 = 0; i0 < kHeadDim; i0 += 8) {
-      uint32_t pn[8];
+      double pn[8], xn[8];
       const int i1 = i0 + 8 < kHeadDim ? i0 + 8 : i0; // last batch reloads itself
-      const uint4 qn = qrow[i1 / 8];
-      const uint4 kn = KEY ? krow[i1 / 8] : ka;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) pn[u] = pcol[(i1 + u) * b];
-      const uint32_t qw[4] = {qa.x, qa.y, qa.z, qa.w};
-      const uint32_t kw[4] = {ka.x, ka.y, ka.z, ka.w};
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const uint32_t qb = (u & 1) ? (qw[u / 2] >> 16) : (qw[u / 2] & 0xFFFFu);
-        const double pd = (double)bf16_to_float(pa[u]);
-        acc = fma((double)bf16_to_float(qb), pd, acc);
-        if (KEY) {
-          const uint32_t kb = (u & 1) ? (kw[u / 2] >> 16) : (kw[u / 2] & 0xFFFFu);
-          const double kd = (double)bf16_to_float(kb);
-          pk = fma(kd, pd, pk);
-          r2 = fma(kd, kd, r2);
-        }
+        pn[u] = p_at(i1 + u, j);
+        xn[u] = x[i1 + u];
       }
-      qa = qn;
-      ka = kn;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) pa[u] = pn[u];
+      for (int u = 0; u < 8; ++u) acc = fma(xa[u], pa[u], acc);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        pa[u] = pn[u];
+        xa[u] = xn[u];
+      }
     }
     return acc;
   };
-  // threads 0..b-1 hold (h = 0, j = thread) at r = 0: the key's columns
-  const bool key_wave = a_blk >= 0 && (int)threadIdx.x < b; // wave-uniform
+  double p[kMaxPairs];
+  double mloc = 0.0;
 #pragma unroll
   for (int r = 0; r < kMaxPairs; ++r) {
     const int idx = threadIdx.x + r * kThreads;
     p[r] = 0.0;
     if (idx < npairs) {
       const int h = idx / b, j = idx % b;
-      const double acc = (r == 0 && key_wave) ? project(std::true_type{}, h, j)
-                                             : project(std::false_type{}, h, j);
+      const double acc = chain(sQd + h * kHeadDim, j);
       p[r] = acc;
       mloc = fmax(mloc, fabs(acc));
     }
   }
-  // the newest key's code bits of columns 64*wave .. 64*wave+63
-  const uint64_t key_bits = __ballot(pk > 0.0);
   // the query heads' own sign codes (LSH buckets): pair idx = h*b + j
   uint64_t qsign[kMaxPairs];
 #pragma unroll
@@ -322,7 +381,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
   // L = ~0 asks for no candidates (k_eff = 0, or every candidate is
   // selected and the merge marks them directly)
   uint32_t L = 0xFFFFFFFFu;
-  if (sample) {
+  if (sample) { // workgroup-uniform
     L = 0;
     QueryOperand<KS> op;
 #pragma unroll
@@ -335,75 +394,78 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
                      h1 < G ? -(float)sSum[h1 < G ? h1 : 0] : 0.f};
       op.scale = unit_scale();
     }
-    uint32_t nvalid = 0;
-    auto keep = [&](int t, int S) {
-      if (lane < kPage && t < nsp) {
-        const int pos = (pc0 + t * SP) * kPage + lane;
-        const bool valid = pos >= sigma && pos < N - w;
-        sSample[t * kPage + lane] = valid ? biased_score(S) : 0u;
-        nvalid += valid;
-      }
-    };
-    // the preloaded pages four at a time: after the quad step, lane L holds
-    // key L%16 of page 4a + L/16
-    const int lq = lane >> 4;
+    // the wave's radius lines, page order, read back one byte per lane
+    *reinterpret_cast<uint4 *>(&sRad[wave][16 * lane]) = rline;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // Score the wave's quads: after the transpose, lane L holds key L%16 of
+    // page 4a + L/16.  us[a]: its biased score, 0 when it is no valid sample
+    // key (a biased score is never 0).
+    uint32_t us[kWaveQuads];
+    uint32_t nvalid = 0, vlo = 0xFFFFFFFFu, vhi = 0u;
 #pragma unroll
-    for (int a = 0; a < kPre / 4; ++a) {
-      uint32_t cw[4][KS], r8s[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        // first use of the loaded words is here (see score_page)
+    for (int a = 0; a < kWaveQuads; ++a) {
+      us[a] = 0u;
+      if (4 * a < npw) { // wave-uniform
+        uint32_t cw[4][KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          cw[j][ks] = pcw[4 * a + j][ks];
-          asm volatile("" : "+v"(cw[j][ks]));
+          uint32_t x[4] = {qx[a][ks][0], qx[a][ks][1], qx[a][ks][2], qx[a][ks][3]};
+          transpose_rows(x);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) cw[j][ks] = x[j];
         }
-        r8s[j] = pr8[4 * a + j];
-        asm volatile("" : "+v"(r8s[j]));
-      }
-      const int mx = score_quad_max_seq<KS, G>(op, cw);
-      const uint32_t r8 = lq == 0 ? r8s[0] : lq == 1 ? r8s[1] : lq == 2 ? r8s[2] : r8s[3];
-      const bool ok = (pokm >> (4 * a + lq)) & 1u;
-      const int t = wave + kWv * (4 * a + lq);
-      if (t < nsp) {
-        const int pos = (pc0 + t * SP) * kPage + (lane & 15);
-        const bool valid = ok && pos >= sigma && pos < N - w;
-        sSample[t * kPage + (lane & 15)] =
-            valid ? biased_score(__mul24(radius_weight(r8, lin), mx)) : 0u;
-        nvalid += valid;
+        const int mx = score_quad_max_seq<KS, G>(op, cw);
+        const uint32_t r8 = sRad[wave][64 * a + lane];
+        const int i = 4 * a + (lane >> 4);        // the wave's page index
+        const int pos = (pc0 + (wave + kWv * i) * SP) * kPage + (lane & 15);
+        const uint32_t ph_i = (uint32_t)__shfl((int)ph_l, i);
+        const bool valid = i < npw && ph_i != ph_none && pos >= sigma && pos < N - w;
+        const uint32_t u = biased_score(__mul24(radius_weight(r8, lin), mx));
+        if (valid) {
+          us[a] = u;
+          nvalid += 1;
+          vlo = min(vlo, u);
+          vhi = max(vhi, u);
+        }
       }
     }
-    // pages past the first kPre of each wave (long sequences with a small
-    // stride): 8 loads in flight per step
-    for (int i0 = kPre; wave + kWv * i0 < nsp; i0 += 8) {
-      uint32_t cw[8][KS], r8[8];
-      bool ok[8];
+    // the count and range of the valid sample keys over the workgroup
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = i0 + u;
-        const int blk = __builtin_amdgcn_readlane(blk_l, i & 63);
-        ok[u] = wave + kWv * i < nsp && blk >= 0 && blk < num_blocks;
-        load_page<KS>(view, blk, ok[u], cw[u], r8[u]);
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        keep(wave + kWv * (i0 + u), score_page<KS, G>(op, cw[u], r8[u], ok[u], lin));
+    for (int off = 32; off > 0; off >>= 1) {
+      nvalid += __shfl_xor(nvalid, off);
+      vlo = min(vlo, (uint32_t)__shfl_xor((int)vlo, off));
+      vhi = max(vhi, (uint32_t)__shfl_xor((int)vhi, off));
     }
-    for (int off = 32; off > 0; off >>= 1) nvalid += __shfl_xor(nvalid, off);
-    if (lane == 0) sCount[wave] = nvalid;
+    if (lane == 0) {
+      sCount[0][wave] = nvalid;
+      sCount[1][wave] = vlo;
+      sCount[2][wave] = vhi;
+    }
     __syncthreads();
-    uint32_t ns = 0;
-    for (int i = 0; i < kWv; ++i) ns += sCount[i];
+    uint32_t ns = 0, lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+    for (int i = 0; i < kWv; ++i) {
+      ns += sCount[0][i];
+      lo = min(lo, sCount[1][i]);
+      hi = max(hi, sCount[2][i]);
+    }
     const uint32_t ks_take = (uint32_t)min((int64_t)ns,
         ((int64_t)2 * keff * ns + nc - 1) / nc);
-    if (ks_take > 0 && ks_take < ns) {
-      const int nkeys = nsp * kPage;
-      L = wg_kth_largest_floor<kThreads>(sel, [&](auto fn) {
-        for (int i = threadIdx.x; i < nkeys; i += kThreads) {
-          const uint32_t v = sSample[i];
-          if (v != 0u) fn(v);
-        }
-      }, ks_take);
+    if (ks_take > 0 && ks_take < ns) { // workgroup-uniform
+      // L = the lower edge of the histogram bin (over (u - lo) >> shift,
+      // 4096 bins spanning the sample's range) that holds the ks_take-th
+      // largest sample key, so at least ks_take of them reach L
+      const uint32_t range = hi - lo;
+      const int bits = range == 0 ? 0 : 32 - __clz(range);
+      const int shift = bits > kHistBits ? bits - kHistBits : 0;
+#pragma unroll
+      for (int a = 0; a < kWaveQuads; ++a)
+        if (us[a] != 0u) atomicAdd(&sel.hist[(us[a] - lo) >> shift], 1u);
+      __syncthreads();
+      find_threshold_bin<kThreads>(sel, ks_take);
+      L = lo + ((uint32_t)sel.bin << shift);
     }
   }
   if (pages) {
@@ -413,6 +475,24 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     const int npc = c1 > c0 ? (c1 + kPage - 1) / kPage - c0 / kPage : 0;
     const int kp = min(k / kPage, npc);
     L = (kp > 0 && kp < npc) ? 0u : 0xFFFFFFFFu;
+  }
+  // ---- the newest key's code: threads 0..b-1 run the chain of column j =
+  // thread, and each |k|^2 (squares summed in index order)
+  const bool key_wave = a_blk >= 0 && (int)threadIdx.x < b; // wave-uniform
+  uint64_t key_bits = 0;
+  double r2 = 0.0;
+  if (a_blk >= 0) { // workgroup-uniform
+    if (threadIdx.x < kHeadDim / 2) {
+      sKd[2 * threadIdx.x] = (double)bf16_to_float(krow_w & 0xFFFFu);
+      sKd[2 * threadIdx.x + 1] = (double)bf16_to_float(krow_w >> 16);
+    }
+    __syncthreads();
+    if (key_wave) {
+      const double pk = chain(sKd, (int)threadIdx.x);
+      key_bits = __ballot(pk > 0.0); // columns 64*wave .. 64*wave+63
+    } else if ((int)threadIdx.x == b) { // the first thread past them: |k|^2
+      for (int i = 0; i < kHeadDim; ++i) r2 = fma(sKd[i], sKd[i], r2);
+    }
   }
   if (threadIdx.x == 0) lthr[unit] = qbits != nullptr ? 0u : L;
   if (qbits != nullptr) {
@@ -441,15 +521,16 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     const int W32 = b / 32;
     uint32_t *cw = codes_w + (((int64_t)a_blk * Hkv + g) * kPage + a_slot) * W32;
     if (lane < 2) cw[2 * wave + lane] = lane ? (uint32_t)(key_bits >> 32) : (uint32_t)key_bits;
-    if (threadIdx.x == 0)
-      radii_w[((int64_t)a_blk * Hkv + g) * kPage + a_slot] = (uint8_t)radius_code(r2);
   }
+  if (a_blk >= 0 && (int)threadIdx.x == b)
+    radii_w[((int64_t)a_blk * Hkv + g) * kPage + a_slot] = (uint8_t)radius_code(r2);
   // ---- the filter's task list: one entry (sequence, page group, length)
   // per group of kGroupKeys keys, sequence by sequence, after a count word
   // (padded to 16 bytes).  Only groups that hold keys are listed, so the
   // filter's waves share the real work evenly in ragged batches.
   if (g == 0) { // workgroup-uniform
     auto groups_of = [](int n) { return (uint32_t)((n + kGroupKeys - 1) / kGroupKeys); };
+    const int len_before = (int)threadIdx.x < s ? len_before_raw : 0;
     uint32_t local = groups_of(clamp_int(len_before, 0, n_max));
     for (int i = (int)threadIdx.x + kThreads; i < s; i += kThreads)
       local += groups_of(seq_len_clamped(seq_lens, i, n_max));
@@ -476,26 +557,29 @@ hipError_t launch_prep(const DecodeDims &d, const uint16_t *q,
                        uint32_t *tasks, hipStream_t stream) {
   const uint32_t code_bytes = (uint32_t)((uint64_t)d.num_blocks * d.Hkv * d.W * kPage * 4);
   const uint32_t radius_bytes = (uint32_t)((uint64_t)d.num_blocks * d.Hkv * kPage);
-#define DKV_PREP_CASE(KSV, GV)                                                 \
-  if (d.KS == KSV && d.G == GV) {                                              \
-    hipLaunchKernelGGL((prep_kernel<KSV, GV>), dim3(d.B * d.Hkv),              \
+#define DKV_PREP_CASE(WV, GV)                                                  \
+  if (d.W == WV && d.G == GV) {                                                \
+    hipLaunchKernelGGL((prep_kernel<WV, GV>), dim3(d.B * d.Hkv),               \
                        dim3(kThreads), 0, stream, q, proj, codes, radii,       \
                        k_pool, codes_w, radii_w,                               \
                        d.num_blocks, code_bytes, radius_bytes, block_table,    \
                        d.max_blocks, seq_lens, d.n_max, q8, qop, qneg, lthr,   \
-                       qbits, tasks,                                           \
-                       d.Hq, d.Hkv, d.b, d.W, d.k, d.w, d.sigma, d.lin,         \
+                       qbits, tasks, d.Hq, d.Hkv, d.k, d.w, d.sigma, d.lin,    \
                        d.pages);                                               \
     return hipGetLastError();                                                  \
   }
-  DKV_PREP_CASE(1, 1)
-  DKV_PREP_CASE(1, 2)
-  DKV_PREP_CASE(1, 4)
-  DKV_PREP_CASE(1, 8)
   DKV_PREP_CASE(2, 1)
   DKV_PREP_CASE(2, 2)
   DKV_PREP_CASE(2, 4)
   DKV_PREP_CASE(2, 8)
+  DKV_PREP_CASE(4, 1)
+  DKV_PREP_CASE(4, 2)
+  DKV_PREP_CASE(4, 4)
+  DKV_PREP_CASE(4, 8)
+  DKV_PREP_CASE(8, 1)
+  DKV_PREP_CASE(8, 2)
+  DKV_PREP_CASE(8, 4)
+  DKV_PREP_CASE(8, 8)
 #undef DKV_PREP_CASE
   return hipErrorInvalidValue;
 }

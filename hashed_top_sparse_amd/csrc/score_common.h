@@ -302,6 +302,22 @@ __device__ __forceinline__ int score_quad_max_seq(const QueryOperand<KS> &op,
   return (int)__uint_as_float(c[0]);
 }
 
+// 4x4 transpose across the four 16-lane rows: afterwards x[j] in row a holds
+// what x[a] held in row j (for every lane position in the row).  A page
+// quad loaded with lane 16j+c holding the code words of key c of page j
+// becomes, in x[j], page j's matrix-core operand (lane L: word L/16 of key
+// L%16).
+__device__ __forceinline__ void transpose_rows(uint32_t (&x)[4]) {
+  auto a = __builtin_amdgcn_permlane32_swap(x[0], x[2], false, false);
+  auto b = __builtin_amdgcn_permlane32_swap(x[1], x[3], false, false);
+  auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+  auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  x[0] = c[0];
+  x[1] = c[1];
+  x[2] = d[0];
+  x[3] = d[1];
+}
+
 // Raw buffer views of the code and radius pools (byte sizes < 2^32).
 struct PoolView {
   __amdgpu_buffer_rsrc_t code, radius;

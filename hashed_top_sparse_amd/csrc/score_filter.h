@@ -85,19 +85,6 @@ struct QuadLoad {
 // (32-bit operands only, which the host pass of the compiler also accepts).
 __device__ __forceinline__ void mark_loaded(uint32_t x) { asm volatile("" ::"v"(x)); }
 
-// 4x4 transpose across the four 16-lane rows: afterwards x[j] in row a holds
-// what x[a] held in row j (for every lane position in the row).
-__device__ __forceinline__ void transpose_rows(uint32_t (&x)[4]) {
-  auto a = __builtin_amdgcn_permlane32_swap(x[0], x[2], false, false);
-  auto b = __builtin_amdgcn_permlane32_swap(x[1], x[3], false, false);
-  auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
-  auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
-  x[0] = c[0];
-  x[1] = c[1];
-  x[2] = d[0];
-  x[3] = d[1];
-}
-
 // W: code words per key (2, 4 or 8); KS: 128-bit matrix-core K-steps;
 // DBG: also write every score to scores_out (inspection builds only); LIN:
 // linear radius weight (looked up in a per-workgroup LDS table); PAGES:
@@ -192,13 +179,37 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
   const int ntasks = min(__builtin_amdgcn_readfirstlane(
                              __builtin_amdgcn_raw_buffer_load_b32(task_rsrc, 0, 0, 0)),
                          (uint32_t)max_entries) * Hkv;
-  // task id -> task, or none if it holds no keys
+  // The wave's task entries, 64 at a time in registers: lane j holds the
+  // entry of the wave's task kbase + j (task id first + (kbase + j) *
+  // stride).  They are loaded before the stream starts, so decoding a task
+  // inside the stream waits for no load (a load used at once would also
+  // wait for every load issued before it: the stream's prefetch).
+  const int first = blockIdx.x * kWaves + wave;
+  int kbase = 0;
+  uint32_t te0 = 0, te1 = 0, te2 = 0;
+  auto load_entries = [&](int kb) {
+    const int t = first + (kb + lane) * stride;
+    const int e = min(t, max(ntasks - 1, 0)) / Hkv; // clamped to a listed entry
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(task_rsrc, 16 + 16 * e, 0, 0);
+    te0 = v[0];
+    te1 = v[1];
+    te2 = v[2];
+    // used here, so no later read waits for this load
+    mark_loaded(te0);
+    mark_loaded(te1);
+    mark_loaded(te2);
+    kbase = kb;
+  };
+  load_entries(0);
+  // task id (first + k * stride) -> task, or none if it holds no keys
   auto decode = [&](int t, Task &T) -> bool {
     T.g = t % Hkv;
-    const auto e = __builtin_amdgcn_raw_buffer_load_b128(task_rsrc, 16 + 16 * (t / Hkv), 0, 0);
-    T.s = (int)__builtin_amdgcn_readfirstlane(e[0]);
-    T.grp = (int)__builtin_amdgcn_readfirstlane(e[1]);
-    T.N = clamp_int((int)__builtin_amdgcn_readfirstlane(e[2]), 0, n_max);
+    const int kk = (t - first) / stride;
+    if (kk - kbase >= 64) load_entries(kk & ~63); // (more than 64 tasks a wave)
+    const int l = kk - kbase;
+    T.s = (int)__builtin_amdgcn_readlane(te0, l);
+    T.grp = (int)__builtin_amdgcn_readlane(te1, l);
+    T.N = clamp_int((int)__builtin_amdgcn_readlane(te2, l), 0, n_max);
     T.key0 = T.grp * kGroupKeys;
     if (T.key0 >= T.N || T.s >= B) return false;
     T.unit = T.s * Hkv + T.g;

@@ -35,7 +35,7 @@ struct SelectShared {
 // kneed: count(bins above) < kneed <= count(bins above) + bin.  Every
 // thread must call it; ends with a barrier.
 template <int NT>
-__device__ void find_threshold_bin(SelectShared<NT> &sh, uint32_t kneed) {
+__device__ __forceinline__ void find_threshold_bin(SelectShared<NT> &sh, uint32_t kneed) {
   constexpr int kPer = kHistBins / NT;
   const int top = kHistBins - 1 - kPer * (int)threadIdx.x;
   uint32_t local = 0;
@@ -62,7 +62,7 @@ __device__ void find_threshold_bin(SelectShared<NT> &sh, uint32_t kneed) {
 // (v - vmin) >> shift with the shift chosen so the range fits the bins.
 // Every thread must call it; ends with a barrier.
 template <int NT, class Visit>
-__device__ void wg_histogram(SelectShared<NT> &sh, Visit visit, uint32_t &vmin,
+__device__ __forceinline__ void wg_histogram(SelectShared<NT> &sh, Visit visit, uint32_t &vmin,
                              int &shift) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t lo = 0xFFFFFFFFu, hi = 0u;
@@ -99,7 +99,7 @@ __device__ void wg_histogram(SelectShared<NT> &sh, Visit visit, uint32_t &vmin,
 // count): the lowest value of the histogram bin that holds it, so at least
 // kneed elements are >= the result.  Every thread must call it.
 template <int NT, class Visit>
-__device__ uint32_t wg_kth_largest_floor(SelectShared<NT> &sh, Visit visit,
+__device__ __forceinline__ uint32_t wg_kth_largest_floor(SelectShared<NT> &sh, Visit visit,
                                          uint32_t kneed) {
   uint32_t vmin;
   int shift;
@@ -116,7 +116,7 @@ __device__ uint32_t wg_kth_largest_floor(SelectShared<NT> &sh, Visit visit,
 // (n_eq) and how many of those complete the top kneed (take_eq, >= 1).
 // Every thread must call it (barriers inside).
 template <int NT, class Visit>
-__device__ void wg_kth_largest(SelectShared<NT> &sh, Visit visit, uint32_t kneed,
+__device__ __forceinline__ void wg_kth_largest(SelectShared<NT> &sh, Visit visit, uint32_t kneed,
                                uint32_t &T, uint32_t &take_eq, uint32_t &n_eq) {
   uint32_t vmin;
   int shift;
@@ -161,7 +161,7 @@ __device__ void wg_kth_largest(SelectShared<NT> &sh, Visit visit, uint32_t kneed
 // them exactly.  Returns false otherwise (the caller then searches with
 // wg_kth_largest).  Every thread must call it.
 template <int NT, class Visit2>
-__device__ bool wg_topk_cut(SelectShared<NT> &sh, Visit2 visit2, uint32_t kneed,
+__device__ __forceinline__ bool wg_topk_cut(SelectShared<NT> &sh, Visit2 visit2, uint32_t kneed,
                             uint32_t &Tu, uint32_t &Tpos) {
   uint32_t vmin;
   int shift;
@@ -211,7 +211,7 @@ __device__ bool wg_topk_cut(SelectShared<NT> &sh, Visit2 visit2, uint32_t kneed,
 // page*16 + slot through the block table, -1 for an invalid page), at most
 // max_out of them; returns their number.  Every thread must call it.
 template <int NT>
-__device__ uint32_t emit_bitmap(const uint32_t *bitmap, int nwords, const int32_t *bt,
+__device__ __forceinline__ uint32_t emit_bitmap(const uint32_t *bitmap, int nwords, const int32_t *bt,
                                 int64_t num_blocks, int32_t *row_out,
                                 int32_t *pos_out, uint32_t *tmp, uint32_t max_out) {
   const int per = (nwords + NT - 1) / NT;

@@ -271,11 +271,16 @@ def test_full_size_every_unit(name):
     torch.cuda.empty_cache()
 
 
-def _sample_stride(keff: int) -> int:
-    """The page-sample stride the threshold pass uses for k_eff (largest
-    power of two <= 32 with 2*SP <= k_eff/32, at least 1)."""
+def _sample_stride(keff: int, n: int, w: int, sigma: int) -> int:
+    """The page-sample stride the threshold pass uses: the largest power of
+    two <= 64 with 2*SP <= k_eff/16 (at least 1), doubled until the sample
+    holds at most 512 of the candidate pages (every SP-th from page
+    sigma/16)."""
     sp = 1
-    while sp < 32 and 2 * sp <= keff // 32:
+    while sp < 64 and 2 * sp <= keff // 16:
+        sp *= 2
+    ncp = (n - w + PAGE - 1) // PAGE - sigma // PAGE
+    while (ncp + sp - 1) // sp > 512:
         sp *= 2
     return sp
 
@@ -304,7 +309,7 @@ def test_threshold_fallback_stays_exact(factor):
     cfg = config_of(wl)
     inp = workloads.make_inputs(wl, DEV)
     keff = min(wl.top_k, wl.seq_len - wl.window - wl.sinks)
-    sp = _sample_stride(keff)
+    sp = _sample_stride(keff, wl.seq_len, wl.window, wl.sinks)
     _scale_pages(inp, wl, lambda p: p % sp == 0, factor)
     codes, radii = gpu_encode_all(cfg, inp)
     gpu = gpu_decode(cfg, inp, codes, radii, debug=True)
@@ -346,7 +351,7 @@ def test_linear_weight_threshold_fallback_stays_exact(factor):
     cfg = config_of(wl, **LIN)
     inp = workloads.make_inputs(wl, DEV)
     keff = min(wl.top_k, wl.seq_len - wl.window - wl.sinks)
-    sp = _sample_stride(keff)
+    sp = _sample_stride(keff, wl.seq_len, wl.window, wl.sinks)
     _scale_pages(inp, wl, lambda p: p % sp == 0, factor)
     codes, radii = gpu_encode_all(cfg, inp)
     gpu = gpu_decode(cfg, inp, codes, radii, debug=True)
@@ -375,7 +380,7 @@ def test_linear_weight_wide_score_range_stays_exact(mode):
     k_big = dict(inp, k_pool=(inp["k_pool"].float() * 64.0).to(torch.bfloat16))
     if mode == "rescan":
         keff = min(wl.top_k, wl.seq_len - wl.window - wl.sinks)
-        sp = _sample_stride(keff)
+        sp = _sample_stride(keff, wl.seq_len, wl.window, wl.sinks)
         _scale_pages(k_big, wl, lambda p: p % sp == 0, 4.0)
     codes, radii = gpu_encode_all(cfg, k_big)
     gpu = gpu_decode(cfg, inp, codes, radii, debug=True)
