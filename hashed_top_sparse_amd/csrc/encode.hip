@@ -13,6 +13,8 @@
 // certified, with the fp64 chains only where they are not.
 
 #include <algorithm>
+#include <type_traits>
+#include <utility>
 
 #include "encode_common.h"
 
@@ -20,30 +22,51 @@ namespace dkv {
 namespace {
 
 // ---------------------------------------------------------------------------
-// Matrix-core encode.  p = k.P runs as bf16 x bf16 matrix ops (16 keys x 16
-// columns x 32 dims each; the products are exact in fp32, the sums are fp32).
+// Matrix-core encode.  p = k.P runs as bf16 x bf16 matrix ops (32 keys x 32
+// columns x 16 dims each; the products are exact in fp32, the sums are fp32).
 // A sign is certain when |p32| exceeds a bound on the fp32 summation error
 // in any order (Cauchy-Schwarz: sum |k_i P_ij| <= |k| |P_j|):
-//   |p32 - p| <= 2 (d+1) 2^-23 |k| |P_j| + 2^-100,
+//   |p32 - p| <= 2 (d+1) 2^-23 |k| max_j |P_j| + 2^-100,
 // four times the classic (d+1) 2^-24 bound (headroom for the fp32 norms
-// themselves; the 2^-100 term covers products that underflow).  Uncertain
-// bits are recomputed with the index-order fp64 chain of the definition.
-// Likewise |k|^2: an fp32 sum gives the radius code unless it lies within
-// 2^-15 (relative) of a code threshold; then the fp64 chain decides.
+// themselves; the 2^-100 term covers products that underflow; the largest
+// column norm of the wave's columns stands in for |P_j|, which only widens
+// the bound).  Uncertain bits are recomputed with the index-order fp64
+// chain of the definition.  Likewise |k|^2: an fp32 sum gives the radius
+// code unless it lies near a code threshold (radius_code_certain); then the
+// fp64 chain decides.
 //
-// Work: persistent waves, each keeping its P fragments (64 columns) in
-// registers; a tile is (sequence, page, KV head) and a 64-column part of the
-// code.  Lane L loads 64 contiguous bytes (dims 32q..32q+31,
-// q = L/16) of key row L%16; matrix K-step c pairs dims 32q+8c..32q+8c+7 of
-// the row with the same dims of column L%16 of P, so every dim is used
-// once.  The next tile's rows are loaded while the current one is scored.
+// Work.  A unit is 16 consecutive key rows of a page (the page's rows are
+// stored position-major, [16][Hkv][d], so a unit is 4 KB of contiguous
+// memory: slice q holds rows 16q..16q+15, row m being position m / Hkv of
+// KV head m % Hkv).  A workgroup of four waves walks a run of units, 2X per
+// step (X = 1 for b >= 128, 2 for b = 64), as 32X rows:
+//  - each wave loads 8X of the rows (whole 256-byte rows, four per load
+//    instruction), three steps ahead, then writes them to the step's LDS
+//    tile, with their |k|^2 (fp32), row bound and radius code;
+//  - after one barrier, each wave takes the 32 rows of its row group in
+//    the matrix layout (lane L: row L%32, dims 64h..64h+63, h = L/32;
+//    matrix K-step c takes dims 64h+8c..64h+8c+7 of each half, so every dim
+//    is used once, and column L%32 of P is arranged the same way) and scores
+//    them against its 32 or 64 columns of P, whose fragments stay in its
+//    registers.
+// In the 32x32 result, lane L holds column L%32 of rows 8(j/4) + 4h + j%4:
+// a ballot of one result register is the 32-bit code word of two rows,
+// moved into the lane that stores it.  The units' block ids, slices and row
+// masks are prepared a window of 256 units at a time into LDS (block ids
+// loaded a window ahead), so the step loop walks nothing itself.
 typedef __bf16 v8bf16 __attribute__((ext_vector_type(8)));
-typedef float v4f32 __attribute__((ext_vector_type(4)));
+typedef float v16f32 __attribute__((ext_vector_type(16)));
 typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
+typedef float v4f32 __attribute__((ext_vector_type(4)));
 
-constexpr int kMmThreads = 256; // four waves
-constexpr int kRangeLds = 1024; // sequences whose encode range sits in LDS
-constexpr int kQueue = 64;      // uncertain signs queued per wave
+constexpr int kEncThreads = 256; // four waves
+constexpr int kEncWaves = kEncThreads / 64;
+constexpr int kRangeLds = 512;   // sequences whose encode range sits in LDS
+constexpr int kQueue = 64;       // uncertain signs queued per wave
+constexpr int kTileRow = 272;    // LDS bytes per tile row (256 + 16: the
+                                 // matrix-layout reads are conflict-free)
+constexpr int kWin = 256;        // units per window of unit info
+constexpr int kAhead = 3;        // steps of rows in flight
 
 __device__ __forceinline__ uint32_t lanes_below_u64(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
@@ -54,89 +77,157 @@ __device__ __forceinline__ v8bf16 as_v8bf16(const uint4 &u) {
   return __builtin_bit_cast(v8bf16, u);
 }
 
-// Index-order fp64 projection of a key row (bf16, staged in LDS) on column
-// n of P (LDS, transposed: sPt[n][i]).
-__device__ double project_fp64(const uint16_t *krow, const uint16_t *pcol) {
-  double acc = 0.0;
-#pragma unroll 4
-  for (int i = 0; i < kHeadDim; ++i)
-    acc = fma((double)bf16_to_float(krow[i]), (double)bf16_to_float(pcol[i]), acc);
-  return acc;
+// The compiler's lane write (v_writelane_b32), which clang exposes under no
+// builtin name; as an intrinsic call the hazard pass sees it and spaces it
+// from the compare that wrote its scalar source.
+extern "C" __device__ int dkv_amdgcn_writelane(int val, int lane, int old) __asm("llvm.amdgcn.writelane.i32");
+
+// Places a wave-uniform value in one lane of a register (lane fixed at
+// compile time).
+template <int LANE>
+__device__ __forceinline__ uint32_t write_lane(uint32_t old, uint32_t val) {
+  return (uint32_t)dkv_amdgcn_writelane((int)val, LANE, (int)old);
 }
 
-__device__ double sq_norm_fp64(const uint16_t *krow) {
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+// f(std::integral_constant<int, i>) for i = 0..N-1
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Sum over each row of 16 lanes, in every lane of the row (DPP: quad
+// swaps, then the mirrors of half rows and rows).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f32<0xB1>(v);  // quad_perm [1,0,3,2]
+  v += dpp_f32<0x4E>(v);  // quad_perm [2,3,0,1]
+  v += dpp_f32<0x141>(v); // row_half_mirror
+  v += dpp_f32<0x140>(v); // row_mirror
+  return v;
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Index-order fp64 sums over one key row in global memory: its projection
+// on column col of P ([d][b] row-major, global), or its squared norm
+// (proj null).
+__device__ double row_chain_fp64(const uint16_t *krow_g, const uint16_t *proj, int b, int col) {
+  const uint4 *krow = reinterpret_cast<const uint4 *>(krow_g);
   double acc = 0.0;
-#pragma unroll 4
-  for (int i = 0; i < kHeadDim; ++i) {
-    const double x = (double)bf16_to_float(krow[i]);
-    acc = fma(x, x, acc);
+#pragma unroll 2
+  for (int c = 0; c < kHeadDim / 8; ++c) {
+    const uint4 k8 = krow[c];
+    const uint32_t kw[4] = {k8.x, k8.y, k8.z, k8.w};
+    uint32_t pw[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) pw[u] = proj ? proj[(int64_t)(8 * c + u) * b + col] : 0u;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const double x = (double)bf16_to_float((u & 1) ? (kw[u / 2] >> 16) : (kw[u / 2] & 0xFFFFu));
+      acc = fma(x, proj ? (double)bf16_to_float(pw[u]) : x, acc);
+    }
   }
   return acc;
 }
 
-// NB: 16-column blocks per wave (64 columns: 64 VGPRs of fragments, two
-// waves per SIMD); HALVES: b/64 column parts, each taken by its own
-// workgroups (the parts of one tile load the same rows, from L2).
-template <int NB, int HALVES>
-__global__ __launch_bounds__(kMmThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// The radius code of an fp32 |k|^2 when it is certain, else -1.  With
+// L = 8 log2 |k|^2 the code is floor(L) + 64 clamped to [0, 255]; it is
+// certain when L lies farther than 2^-11 from an integer (the fp32 sum is
+// within 2^-17 of |k|^2 relatively, 8.8e-5 in L, and the hardware log2
+// within a few ulps), when L < -64 (code 0), and when |k|^2 is 0 or at least
+// 2^24 (code 255).
+__device__ __forceinline__ int radius_code_certain(float r2) {
+  if (!(r2 > 0.f)) return r2 == 0.f ? 0 : -1;
+  if (r2 >= 0x1p24f) return 255;
+  const float L = 8.f * __builtin_amdgcn_logf(r2);
+  if (L < -64.f) return 0;
+  const float fl = floorf(L);
+  const float fr = L - fl;
+  if (!(fr > 0x1p-11f && fr < 1.f - 0x1p-11f)) return -1;
+  return clamp_int((int)fl + 64, 0, 255);
+}
+
+template <int NCB>
+struct EncShape {
+  static constexpr int b = 32 * NCB, W = NCB;
+  static constexpr int X = NCB >= 4 ? 1 : 4 / NCB;   // row groups of 32 per step
+  static constexpr int WPR = kEncWaves / X;          // waves per row group
+  static constexpr int BPW = NCB / WPR;              // column blocks per wave
+  static constexpr int ROWS = 32 * X;                // rows per step
+  static constexpr int UPS = 2 * X;                  // units per step
+  static constexpr int LPW = 2 * X;                  // row loads (4 rows) per wave and step
+  static constexpr int PT_BYTES = (b < 128 ? b : 128) * kHeadDim * 2; // P^T staging
+  static constexpr int TILE_BYTES = 2 * ROWS * kTileRow;
+  static constexpr int BUF_BYTES = PT_BYTES > TILE_BYTES ? PT_BYTES : TILE_BYTES;
+  static constexpr int WAVES_PER_EU = BPW == 1 && X == 1 ? 3 : 2;
+  static constexpr int PT_COLS = b < 128 ? b : 128;  // P^T columns staged at once
+};
+
+template <int NCB>
+__global__ __launch_bounds__(kEncThreads)
+__attribute__((amdgpu_waves_per_eu(EncShape<NCB>::WAVES_PER_EU, EncShape<NCB>::WAVES_PER_EU)))
 void encode_mfma_kernel(const uint16_t *__restrict__ k_pool, int64_t num_blocks,
                         const int32_t *__restrict__ block_table, int max_blocks,
                         int batch, const int32_t *__restrict__ enc_start,
                         const int32_t *__restrict__ enc_end, int max_encode_len,
                         int pages_max, const uint16_t *__restrict__ proj, int Hkv,
                         uint32_t *__restrict__ codes, uint8_t *__restrict__ radii) {
-  constexpr int b = 16 * NB * HALVES, W = b / 32;
-  constexpr int NCOL = 16 * NB;    // columns of this workgroup
-  constexpr int WH = NB / 2;       // code words per key in one half
-  __shared__ __align__(16) uint16_t sPt[NCOL][kHeadDim]; // P^T of the half
-  __shared__ uint64_t sBal[kMmThreads / 64][NB][4]; // sign masks of (cb, i)
-  __shared__ uint64_t sUnc[kMmThreads / 64][NB][4]; // uncertain entries
-  __shared__ uint4 sQ[kMmThreads / 64][kQueue];      // queued fp64 chains
-  __shared__ float sR2[kMmThreads / 64][16];
+  using E = EncShape<NCB>;
+  constexpr int b = E::b, W = E::W, X = E::X, WPR = E::WPR, BPW = E::BPW;
+  constexpr int ROWS = E::ROWS, UPS = E::UPS, LPW = E::LPW;
+  // P^T while the fragments are taken, then the two step tiles
+  __shared__ __align__(16) unsigned char sBuf[E::BUF_BYTES];
+  uint16_t (*sPt)[kHeadDim] = reinterpret_cast<uint16_t (*)[kHeadDim]>(sBuf);
+  __shared__ __align__(16) float sKb[2][ROWS];   // row bounds per step slot
+  __shared__ __align__(16) int2 sUnit[2][kWin];  // (block id or -1, slice | rows << 16)
+  __shared__ uint4 sQ[kEncWaves][kQueue];        // queued fp64 chains
   __shared__ int2 sRange[kRangeLds];
-  // tiles before each sequence's first (balanced mode): sPre[s] =
-  // Hkv-free count of the pages the ranges of sequences 0..s-1 meet
+  // units before each sequence's first (balanced mode): sPre[s] = Hkv-free
+  // count of the pages the ranges of sequences 0..s-1 meet
   __shared__ int sPre[kRangeLds + 1];
-  __shared__ uint32_t sScan[kMmThreads / 64];
-  // a tile's key rows, staged only when an fp64 chain has to run
-  __shared__ __align__(16) uint16_t sRow[kMmThreads / 64][kPage][kHeadDim];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int q = lane >> 4, col = lane & 15;
-  const int half = HALVES > 1 ? (int)(blockIdx.x % HALVES) : 0;
-  const int col0 = half * NCOL;
+  __shared__ uint32_t sScan[kEncWaves];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int rg = X == 1 ? 0 : wave / WPR; // the wave's row group
+  const int cb0 = (wave % WPR) * BPW;   // its first column block
+  const int hf = lane >> 5, row = lane & 31;
   // positions a block table row reaches (the host keeps max_blocks at or
   // below DKV_MAX_SEQ_LEN / 16, so this fits an int)
   const int limit = (int)min((int64_t)kPage * max_blocks, (int64_t)DKV_MAX_SEQ_LEN);
-  // a sequence's encode range [start, end), clamped
-  auto range_of = [&](int s_) {
+  auto range_of = [&](int s_) __attribute__((always_inline)) {
     const int st = clamp_int(enc_start[s_], 0, limit);
     int en = clamp_int(enc_end[s_], 0, limit);
     if (en - st > max_encode_len) en = st + max_encode_len;
     return make_int2(st, en);
   };
-  // stage the half's columns of P transposed, and the first sequences'
-  // ranges
-  for (int e = threadIdx.x; e < kHeadDim * NCOL; e += kMmThreads) {
-    const int i = e / NCOL, j = e % NCOL;
-    sPt[j][i] = proj[(int64_t)i * b + col0 + j];
-  }
-  for (int i = threadIdx.x; i < batch && i < kRangeLds; i += kMmThreads) sRange[i] = range_of(i);
+  for (int i = threadIdx.x; i < batch && i < kRangeLds; i += kEncThreads) sRange[i] = range_of(i);
   __syncthreads();
   // Balanced mode (every sequence's range in LDS): only the pages the
-  // ranges meet are tiles, numbered sequence by sequence, so the waves'
-  // runs hold equal work in ragged batches.  Otherwise every sequence has
-  // pages_max tile slots, the ones past its range empty.
+  // ranges meet hold units, numbered sequence by sequence, so the runs hold
+  // equal work in ragged batches.  Otherwise every sequence has pages_max
+  // page slots, the ones past its range empty.
   const bool bal = batch <= kRangeLds; // workgroup-uniform
-  auto pages_met = [](int2 rg) { return rg.y > rg.x ? (rg.y - 1) / kPage - rg.x / kPage + 1 : 0; };
+  auto pages_met = [](int2 rg_) { return rg_.y > rg_.x ? (rg_.y - 1) / kPage - rg_.x / kPage + 1 : 0; };
   if (bal) {
-    constexpr int kPer = kRangeLds / kMmThreads; // sequences per thread
+    constexpr int kPer = (kRangeLds + kEncThreads - 1) / kEncThreads;
     const int i0 = (int)threadIdx.x * kPer;
     uint32_t local = 0;
 #pragma unroll
     for (int u = 0; u < kPer; ++u)
       if (i0 + u < batch) local += (uint32_t)pages_met(sRange[i0 + u]);
     uint32_t total;
-    uint32_t run = wg_exclusive_scan<kMmThreads>(local, sScan, &total);
+    uint32_t run = wg_exclusive_scan<kEncThreads>(local, sScan, &total);
 #pragma unroll
     for (int u = 0; u < kPer; ++u)
       if (i0 + u < batch) {
@@ -146,53 +237,74 @@ void encode_mfma_kernel(const uint16_t *__restrict__ k_pool, int64_t num_blocks,
     if (threadIdx.x == 0) sPre[batch] = (int)total;
     __syncthreads();
   }
+  // this wave's B fragments (columns 32 (cb0 + i) + L%32) and the largest
+  // of their norms; P^T is staged PT_COLS columns at a time
+  v8bf16 bfr[BPW][8];
+  float n2max = 0.f;
+  constexpr int PTC = E::PT_COLS;
+  for (int c0 = 0; c0 < b; c0 += PTC) {
+    if (c0 > 0) __syncthreads(); // the previous columns are read
+    for (int e = threadIdx.x; e < kHeadDim * PTC; e += kEncThreads) {
+      const int i = e / PTC, j = e % PTC;
+      sPt[j][i] = proj[(int64_t)i * b + c0 + j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      if (32 * (cb0 + i) < c0 || 32 * (cb0 + i) >= c0 + PTC) continue; // wave-uniform
+      const uint16_t *pc = &sPt[32 * (cb0 + i) - c0 + row][64 * hf];
+      float n2 = 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        bfr[i][c] = as_v8bf16(*reinterpret_cast<const uint4 *>(pc + 8 * c));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = (float)bfr[i][c][e];
+          n2 = fmaf(x, x, n2);
+        }
+      }
+      n2 += __shfl_xor(n2, 32);
+      n2max = fmaxf(n2max, n2);
+    }
+  }
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) n2max = fmaxf(n2max, __shfl_xor(n2max, o));
+  // the bound's factor for every row: 2 (d+1) 2^-23 max_j |P_j| of the
+  // workgroup's columns (each wave's own would do; one value keeps the row
+  // bounds shareable)
+  __shared__ float sCn[kEncWaves];
+  if (lane == 0) sCn[wave] = n2max;
+  constexpr float kBoundC = (float)(2 * (kHeadDim + 1)) * 0x1p-23f;
+  // m / Hkv = umulhi(m, ceil(2^32 / Hkv)) for m < 2^16 (Hkv > 1)
+  const uint32_t hkv_magic = Hkv > 1 ? (uint32_t)((0x100000000ull + (uint32_t)Hkv - 1u) / (uint32_t)Hkv) : 0u;
+  __syncthreads(); // P^T read: the buffer becomes the step tiles
+  float cnall = 0.f;
+#pragma unroll
+  for (int i = 0; i < kEncWaves; ++i) cnall = fmaxf(cnall, sCn[i]);
+  const float cnmax = sqrtf(cnall) * (1.f + 0x1p-20f);
+
+  // Units u = ((s * pages_max + pi) * Hkv + q) (balanced: (sPre[s] + pi) *
+  // Hkv + q): the slices of a page are neighbours.  Each workgroup walks a
+  // run of UPS-aligned length.
+  const int nunits = bal ? sPre[batch] * Hkv : batch * pages_max * Hkv;
+  const int chunk = ((nunits + (int)gridDim.x - 1) / (int)gridDim.x + UPS - 1) / UPS * UPS;
+  const int u_begin = (int)blockIdx.x * chunk, u_end = min(nunits, u_begin + chunk);
+  if (u_begin >= u_end) return; // the whole workgroup: no barrier is left waiting
+  const int ntile = (u_end - u_begin + UPS - 1) / UPS;
+
+  // Unit info of unit u (one thread per unit): the block table offset, the
+  // slice and the rows to encode (0 past the run or past the range).
   const __amdgpu_buffer_rsrc_t bt_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int32_t *>(block_table), 0, (uint32_t)(batch * max_blocks) * 4u,
       0x00020000u);
-  // this lane's B fragments and column norms
-  v8bf16 bfr[NB][4];
-  float cn[NB];
-#pragma unroll
-  for (int cb = 0; cb < NB; ++cb) {
-    const uint16_t *pc = sPt[16 * cb + col];
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      bfr[cb][c] = as_v8bf16(*reinterpret_cast<const uint4 *>(pc + 32 * q + 8 * c));
-    // |P_col|^2 from the fragments (each dim once across the row's lanes)
-    float n2 = 0.f;
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = (float)bfr[cb][c][e];
-        n2 = fmaf(x, x, n2);
-      }
-    n2 += __shfl_xor(n2, 16);
-    n2 += __shfl_xor(n2, 32);
-    cn[cb] = sqrtf(n2) * (1.f + 0x1p-20f);
-  }
-  // tiles t = ((s * pages_max + pi) * Hkv + h): the heads of a page are
-  // neighbours; each wave walks a contiguous run of them (a carry step per
-  // tile, no divisions) -- the parts of one tile walk the same runs
-  const int ntiles = bal ? sPre[batch] * Hkv : batch * pages_max * Hkv;
-  const int nstream = (int)(gridDim.x / HALVES) * (kMmThreads / 64);
-  const int chunk = (ntiles + nstream - 1) / nstream;
-  const int wid = (int)(blockIdx.x / HALVES) * (kMmThreads / 64) + wave;
-  const int t_begin = wid * chunk, t_end = min(ntiles, t_begin + chunk);
-  if (t_begin >= t_end) return; // no barriers below
-
-  struct Tile {
-    int s, pi, h, start, end, p, blk;
-    bool any; // inside the wave's run
-  };
-  auto set_seq = [&](Tile &T) {
-    const int2 rg = T.s < kRangeLds ? sRange[T.s] : range_of(T.s);
-    T.start = rg.x;
-    T.end = rg.y;
-  };
-  auto tile_at = [&](int t, Tile &T) {
-    T.h = t % Hkv;
-    const int r = t / Hkv;
+  auto unit_plan = [&](int u, int &bt_off, int &q, uint32_t &rows) __attribute__((always_inline)) {
+    bt_off = 0;
+    q = 0;
+    rows = 0u;
+    if (u >= u_end) return;
+    q = u % Hkv;
+    const int r = u / Hkv;
+    int s_, pi;
     if (bal) { // the last sequence whose first page slot is at or before r
       int lo = 0, hi = batch; // sPre[lo] <= r < sPre[hi]
       while (hi - lo > 1) {
@@ -200,83 +312,115 @@ void encode_mfma_kernel(const uint16_t *__restrict__ k_pool, int64_t num_blocks,
         if (sPre[mid] <= r) lo = mid;
         else hi = mid;
       }
-      T.s = lo;
-      T.pi = r - sPre[lo];
+      s_ = lo;
+      pi = r - sPre[lo];
     } else {
-      T.pi = r % pages_max;
-      T.s = r / pages_max;
+      s_ = r / pages_max;
+      pi = r % pages_max;
     }
-    set_seq(T);
-    T.p = T.start / kPage + T.pi;
-    T.any = t < t_end;
-    T.blk = -1;
+    const int2 rg_ = s_ < kRangeLds ? sRange[s_] : range_of(s_);
+    const int p = rg_.x / kPage + pi;
+    bt_off = (int)(((uint32_t)s_ * (uint32_t)max_blocks + (uint32_t)p) * 4u); // past the table: reads 0
+    // the page's rows of positions [lo, hi) are rows lo*Hkv .. hi*Hkv-1
+    const int lo = max(rg_.x - p * kPage, 0), hi = min(rg_.y - p * kPage, kPage);
+    const int a = max(lo * Hkv - kPage * q, 0), e = min(hi * Hkv - kPage * q, kPage);
+    rows = e > a ? ((1u << e) - 1u) & ~((1u << a) - 1u) : 0u;
   };
-  auto step = [&](Tile &T, int t_next) { // T becomes tile t_next = its id + 1
-    if (++T.h == Hkv) {
-      T.h = 0;
-      if (bal) {
-        if (++T.pi == sPre[T.s + 1] - sPre[T.s]) { // next sequence with pages
-          T.pi = 0;
-          do
-            ++T.s;
-          while (T.s < batch && sPre[T.s + 1] == sPre[T.s]);
-          if (T.s < batch) set_seq(T);
-        }
-      } else if (++T.pi == pages_max) {
-        T.pi = 0;
-        if (++T.s < batch) set_seq(T);
-      }
-      T.p = T.start / kPage + T.pi;
+  // window w's unit info: planned and its block id requested (by thread i
+  // for unit u_begin + w*kWin + i), then written to LDS a window later
+  int win_blk = 0, win_q = 0;
+  uint32_t win_rows = 0u;
+  auto win_request = [&](int w) __attribute__((always_inline)) {
+    int off;
+    unit_plan(u_begin + w * kWin + (int)threadIdx.x, off, win_q, win_rows);
+    win_blk = __builtin_amdgcn_raw_buffer_load_b32(bt_rsrc, off, 0, 0);
+  };
+  auto win_store = [&](int w) __attribute__((always_inline)) {
+    const bool ok = win_rows != 0u && win_blk >= 0 && win_blk < num_blocks;
+    sUnit[w & 1][threadIdx.x] = make_int2(ok ? win_blk : -1, win_q | (int)((ok ? win_rows : 0u) << 16));
+  };
+  static_assert(kWin == kEncThreads, "one thread per unit of a window");
+  static_assert(kWin % UPS == 0, "a step's units lie in one window");
+  win_request(0);
+  win_store(0);
+  win_request(1);
+  win_store(1);
+  win_request(2);
+  __syncthreads();
+  // the step's units (wave-uniform): block id (-1: no rows), slice, rows
+  struct StepUnits {
+    int blk[UPS], q[UPS];
+    uint32_t rows[UPS];
+  };
+  auto step_units = [&](int t, StepUnits &U) __attribute__((always_inline)) {
+    const int i0 = t * UPS;
+    const int2 *su = &sUnit[(i0 / kWin) & 1][i0 % kWin];
+#pragma unroll
+    for (int j = 0; j < UPS; ++j) {
+      const int2 v = su[j];
+      U.blk[j] = __builtin_amdgcn_readfirstlane(v.x);
+      const int y = __builtin_amdgcn_readfirstlane(v.y);
+      U.q[j] = y & 0xFFFF;
+      U.rows[j] = (uint32_t)y >> 16;
     }
-    T.any = t_next < t_end;
-    T.blk = -1;
   };
-  // the tile's block id by a vector load (a scalar load would stall the
-  // wave where it is used; this one is issued a tile ahead), or -1 when the
-  // page is past the range
-  auto blk_load = [&](const Tile &T) -> int {
-    if (!T.any || T.p * kPage >= T.end) return -1;
-    return __builtin_amdgcn_raw_buffer_load_b32(
-        bt_rsrc, (T.s * max_blocks + T.p) * 4, 0, 0);
-  };
-  auto set_blk = [&](Tile &T, int v) {
-    const int blk = __builtin_amdgcn_readfirstlane(v);
-    T.blk = (blk >= 0 && blk < num_blocks) ? blk : -1;
-  };
-  auto row_ptr = [&](const Tile &T, int r) {
-    return k_pool + (((int64_t)T.blk * kPage + r) * Hkv + T.h) * kHeadDim;
-  };
-  auto load_rows = [&](const Tile &T, uint4 (&a)[4]) {
-    if (T.blk >= 0) {
-      const uint4 *src = reinterpret_cast<const uint4 *>(row_ptr(T, col) + 32 * q);
+  // tile row r of a step (unit r / 16) -> (block, key index = the radius
+  // index; its code words start at key index * W): the page's row
+  // m = 16q + r % 16 is position m / Hkv of head m % Hkv
+  auto key_index = [&](const StepUnits &U, int r) __attribute__((always_inline)) -> uint32_t {
+    const int j = r >> 4;
+    int blk = U.blk[0], q = U.q[0];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) a[c] = src[c];
-    } else {
+    for (int jj = 1; jj < UPS; ++jj)
+      if (j == jj) blk = U.blk[jj], q = U.q[jj];
+    const uint32_t m = (uint32_t)(kPage * q + (r & 15));
+    const uint32_t pos = Hkv == 1 ? m : __umulhi(m, hkv_magic);
+    const uint32_t h = m - pos * (uint32_t)Hkv;
+    return ((uint32_t)blk * Hkv + h) * kPage + pos;
+  };
+  auto key_row = [&](const StepUnits &U, int r) __attribute__((always_inline)) -> uint32_t {
+    const int j = r >> 4;
+    int blk = U.blk[0], q = U.q[0];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) a[c] = make_uint4(0u, 0u, 0u, 0u);
+    for (int jj = 1; jj < UPS; ++jj)
+      if (j == jj) blk = U.blk[jj], q = U.q[jj];
+    return ((uint32_t)blk * Hkv + q) * kPage + (r & 15);
+  };
+
+  // This wave's rows of a step: load instruction i covers step rows
+  // 8X*wave + 4i .. +3, lane l the 16 bytes 16(l%16) of row +l/16.  Each
+  // unit is read through a buffer over its 4 KB; a unit without rows has an
+  // empty buffer and reads zeros.
+  constexpr int row_bytes = kHeadDim * 2;
+  auto load_rows = [&](const StepUnits &U, uint4 (&S)[LPW]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int r0 = 8 * X * wave + 4 * i; // wave-uniform
+      const int j = r0 >> 4;
+      int blk = U.blk[0], q = U.q[0];
+#pragma unroll
+      for (int jj = 1; jj < UPS; ++jj)
+        if (j == jj) blk = U.blk[jj], q = U.q[jj];
+      const uint16_t *base = blk >= 0 ? k_pool + ((int64_t)blk * Hkv + q) * kPage * kHeadDim : k_pool;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t *>(base), 0, blk >= 0 ? (uint32_t)(kPage * row_bytes) : 0u, 0x00020000u);
+      S[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           rs, ((r0 & 15) + (lane >> 4)) * row_bytes + 16 * (lane & 15), 0, 0));
     }
   };
 
   // the queue of uncertain signs: (key row, code word, column | bit << 8)
   uint32_t qn = 0;
-  auto flush = [&]() {
+  // The queued chains run one per lane (lanes past the queue do nothing).
+  auto flush = [&]() __attribute__((always_inline)) {
+    if (qn == 0) return; // wave-uniform
     // the words these entries patch were stored by this wave: let those
-    // stores complete first
+    // stores complete first (and the queue's LDS writes)
+    wave_lds_sync();
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if ((uint32_t)lane < qn) {
       const uint4 ent = sQ[wave][lane];
-      const uint4 *krow = reinterpret_cast<const uint4 *>(k_pool + (int64_t)ent.x * kHeadDim);
-      const uint16_t *pcol = sPt[ent.z & 0xFFu];
-      double v = 0.0; // the index-order chain
-      for (int c = 0; c < kHeadDim / 8; ++c) {
-        const uint4 k8 = krow[c];
-        const uint32_t kw[4] = {k8.x, k8.y, k8.z, k8.w};
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const uint32_t kb16 = (u & 1) ? (kw[u / 2] >> 16) : (kw[u / 2] & 0xFFFFu);
-          v = fma((double)bf16_to_float(kb16), (double)bf16_to_float(pcol[8 * c + u]), v);
-        }
-      }
+      const double v = row_chain_fp64(k_pool + (int64_t)ent.x * kHeadDim, proj, b, (int)(ent.z & 0xFFu));
       const uint32_t bit = 1u << (ent.z >> 8);
       if (v > 0.0)
         atomicOr(&codes[ent.y], bit);
@@ -286,178 +430,191 @@ void encode_mfma_kernel(const uint16_t *__restrict__ k_pool, int64_t num_blocks,
     qn = 0;
   };
 
-  // four stages: the block id of tile k+3, the rows of tiles k+2 and k+1
-  // (two tiles of rows in flight) and the scoring of tile k overlap
-  Tile cur, nxt, nx2;
-  tile_at(t_begin, cur);
-  set_blk(cur, blk_load(cur));
-  nxt = cur;
-  step(nxt, t_begin + 1);
-  set_blk(nxt, blk_load(nxt));
-  nx2 = nxt;
-  step(nx2, t_begin + 2);
-  int bn2 = blk_load(nx2);
-  uint4 a[4], an[4];
-  load_rows(cur, a);
-  load_rows(nxt, an);
-  for (int t = t_begin; t < t_end; ++t) {
-    Tile nn = nx2;
-    step(nn, t + 3);
-    const int bnn = blk_load(nn);
-    // the rows two tiles ahead are requested before this one is scored
-    uint4 an2[4];
-    set_blk(nx2, bn2);
-    load_rows(nx2, an2);
-    if (cur.blk >= 0) { // wave-uniform
-      // |k|^2 of row `col` in fp32, two bf16 squares per dot2 (the four
-      // lanes of a row combined)
-      float r2 = 0.f;
+  // Staging of this wave's rows of step t: the LDS tile, |k|^2 (fp32, the
+  // 16 lanes of a row combined), the row bound and the radius code.
+  auto stage = [&](int t, const StepUnits &U, const uint4 (&S)[LPW]) __attribute__((always_inline)) {
+    unsigned char *tile = sBuf + (t & 1) * ROWS * kTileRow;
+    float r2[LPW];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint32_t wv[4] = {a[c].x, a[c].y, a[c].z, a[c].w};
+    for (int i = 0; i < LPW; ++i) {
+      const int r = 8 * X * wave + 4 * i + (lane >> 4);
+      *reinterpret_cast<uint4 *>(tile + r * kTileRow + 16 * (lane & 15)) = S[i];
+      const uint32_t wv[4] = {S[i].x, S[i].y, S[i].z, S[i].w};
+      float a = 0.f;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const v2bf16 x = __builtin_bit_cast(v2bf16, wv[u]);
-          r2 = __builtin_amdgcn_fdot2_f32_bf16(x, x, r2, false);
-        }
+      for (int u = 0; u < 4; ++u) {
+        const v2bf16 x = __builtin_bit_cast(v2bf16, wv[u]);
+        a = __builtin_amdgcn_fdot2_f32_bf16(x, x, a, false);
       }
-      r2 += __shfl_xor(r2, 16);
-      r2 += __shfl_xor(r2, 32);
-      if (lane < 16) sR2[wave][lane] = r2;
-      // (read back below by other lanes of the wave)
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // the projections
-      v4f32 acc[NB];
-#pragma unroll
-      for (int cb = 0; cb < NB; ++cb) acc[cb] = v4f32{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int cb = 0; cb < NB; ++cb)
-          acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf16(a[c]), bfr[cb][c],
-                                                            acc[cb], 0, 0, 0);
-      // the matrix ops stay in wave-uniform control flow
-#pragma unroll
-      for (int cb = 0; cb < NB; ++cb) asm volatile("" : "+v"(acc[cb][0]), "+v"(acc[cb][1]), "+v"(acc[cb][2]), "+v"(acc[cb][3]));
-      // result lane L: keys 4q+i, column 16cb + col
-      float kb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        kb[i] = (float)(2 * (kHeadDim + 1)) * 0x1p-23f * sqrtf(sR2[wave][4 * q + i] * (1.f + 0x1p-20f));
-      // rows of the tile inside the encode range (result layout: 4q + i)
-      const int base = cur.p * kPage;
-      uint64_t inr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int pos = base + 4 * q + i;
-        inr[i] = __ballot(pos >= cur.start && pos < cur.end);
-      }
-      // signs and uncertain entries of (cb, i) as wave masks, to LDS
-      uint32_t n_unc = 0;
-#pragma unroll
-      for (int cb = 0; cb < NB; ++cb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = acc[cb][i];
-          const uint64_t pos = __ballot(p > 0.f);
-          const uint64_t unc =
-              __ballot(!(fabsf(p) > fmaf(kb[i], cn[cb], 0x1p-100f))) & inr[i];
-          n_unc += (uint32_t)__popcll(unc);
-          if (lane == 0) {
-            sBal[wave][cb][i] = pos;
-            sUnc[wave][cb][i] = unc;
-          }
-        }
-      // radius code of row `lane` from the fp32 sum, unless near a threshold
-      int r8 = 0;
-      bool runc = false;
-      if (lane < kPage) {
-        const float r2f = sR2[wave][lane];
-        r8 = radius_code_f(r2f * (1.f - 0x1p-15f));
-        runc = r8 != radius_code_f(r2f * (1.f + 0x1p-15f));
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // Uncertain signs: the fp32 sign is written now and the entry joins
-      // the wave's queue, whose fp64 chains run 64 at a time (one per lane)
-      // and patch the written words; a tile with more entries than the
-      // queue holds runs its chains here.
-      const bool inline_fix = n_unc > (uint32_t)kQueue;
-      if (n_unc != 0 && !inline_fix) {
-        if (qn + n_unc > (uint32_t)kQueue) flush();
-        for (int e = 0; e < NB * 4; ++e) {
-          const int cb = e >> 2, i = e & 3;
-          const uint64_t unc = sUnc[wave][cb][i];
-          if (unc == 0) continue; // wave-uniform
-          if ((unc >> lane) & 1u) {
-            const int kk = 4 * q + i;
-            sQ[wave][qn + lanes_below_u64(unc)] = make_uint4(
-                (uint32_t)(((int64_t)cur.blk * kPage + kk) * Hkv + cur.h),
-                (uint32_t)((((int64_t)cur.blk * Hkv + cur.h) * kPage + kk) * W + half * WH + cb / 2),
-                (uint32_t)(16 * cb + col) | ((uint32_t)(16 * (cb & 1) + col) << 8), 0u);
-          }
-          qn += (uint32_t)__popcll(unc);
-        }
-      }
-      if (inline_fix || __ballot(runc)) { // rare: the fp64 chains decide
-        // the rows go to LDS (lane L holds dims 32q.. of row L%16)
-        uint4 *dst = reinterpret_cast<uint4 *>(&sRow[wave][col][32 * q]);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) dst[c] = a[c];
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        for (int e = 0; inline_fix && e < NB * 4; ++e) {
-          const int cb = e >> 2, i = e & 3;
-          const uint64_t unc = sUnc[wave][cb][i];
-          if (unc == 0) continue; // wave-uniform
-          const bool mine = (unc >> lane) & 1u;
-          double v = 0.0;
-          if (mine) v = project_fp64(sRow[wave][4 * q + i], sPt[16 * cb + col]);
-          const uint64_t fixed = __ballot(mine && v > 0.0);
-          if (lane == 0) sBal[wave][cb][i] = (sBal[wave][cb][i] & ~unc) | fixed;
-        }
-        if (runc) r8 = radius_code(sq_norm_fp64(sRow[wave][lane]));
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      }
-      // code words of this part: lane = key * WH + word
-      if (lane < kPage * WH) {
-        const int kk = lane / WH, w = lane % WH;
-        const int pos = base + kk;
-        const int qq = kk >> 2, ii = kk & 3;
-        const uint32_t lo = (uint32_t)(sBal[wave][2 * w][ii] >> (16 * qq)) & 0xFFFFu;
-        const uint32_t hi = (uint32_t)(sBal[wave][2 * w + 1][ii] >> (16 * qq)) & 0xFFFFu;
-        if (pos >= cur.start && pos < cur.end)
-          codes[(((int64_t)cur.blk * Hkv + cur.h) * kPage + kk) * W + half * WH + w] =
-              lo | (hi << 16);
-      }
-      // radius of row `lane` (one part writes it)
-      if (half == 0 && lane < kPage) {
-        const int pos = base + lane;
-        if (pos >= cur.start && pos < cur.end)
-          radii[((int64_t)cur.blk * Hkv + cur.h) * kPage + lane] = (uint8_t)r8;
-      }
-      // the next tile's LDS writes wait for these reads
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      r2[i] = a;
     }
-    cur = nxt;
-    nxt = nx2;
-    nx2 = nn;
-    bn2 = bnn;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      a[c] = an[c];
-      an[c] = an2[c];
+    for (int i = 0; i < LPW; ++i) r2[i] = row16_sum(r2[i]);
+    // lane l: the row of load (l%16) / (16 / LPW), row 4i + l/16 of it
+    constexpr int kSub = 16 / LPW;
+    float v = r2[0];
+#pragma unroll
+    for (int i = 1; i < LPW; ++i)
+      if ((lane & 15) / kSub == i) v = r2[i];
+    const int r = 8 * X * wave + 4 * ((lane & 15) / kSub) + (lane >> 4);
+    const bool lead = (lane & 15) % kSub == 0; // one lane per row
+    uint32_t urows = U.rows[0]; // (selects: r is per lane)
+#pragma unroll
+    for (int jj = 1; jj < UPS; ++jj)
+      if ((r >> 4) == jj) urows = U.rows[jj];
+    const uint32_t rmask = urows >> (r & 15);
+    const bool rin = (rmask & 1u) != 0u;
+    // the row's bound; rows not encoded get -1, so no sign of theirs is
+    // ever uncertain
+    const float kb = rin ? fmaf(kBoundC * __builtin_amdgcn_sqrtf(v * (1.f + 0x1p-20f)), cnmax, 0x1p-100f) : -1.f;
+    if (lead) sKb[t & 1][r] = kb;
+    // the radius code, from the fp32 sum unless near a threshold
+    int r8 = radius_code_certain(rin ? v : 0.f);
+    const bool runc = r8 < 0;
+    if (__ballot(runc && lead) != 0u) { // rare: the fp64 chain decides
+      if (runc && lead)
+        r8 = radius_code(row_chain_fp64(k_pool + (int64_t)key_row(U, r) * kHeadDim, nullptr, b, 0));
     }
+    if (rin && lead) radii[key_index(U, r)] = (uint8_t)r8;
+  };
+
+  // Scoring of step t: this wave's row group against its columns.
+  auto compute = [&](int t, const StepUnits &U) __attribute__((always_inline)) {
+    uint32_t rmask = U.rows[0] | (U.rows[1] << 16); // (selects, not an indexed array)
+#pragma unroll
+    for (int g = 1; g < X; ++g)
+      if (rg == g) rmask = U.rows[2 * g] | (U.rows[2 * g + 1] << 16);
+    if (rmask == 0u) return; // wave-uniform
+    const unsigned char *tile = sBuf + (t & 1) * ROWS * kTileRow + 32 * rg * kTileRow;
+    uint4 R[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      R[c] = *reinterpret_cast<const uint4 *>(tile + row * kTileRow + 128 * hf + 16 * c);
+    v16f32 acc[BPW];
+#pragma unroll
+    for (int i = 0; i < BPW; ++i)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[i][j] = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int i = 0; i < BPW; ++i)
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_v8bf16(R[c]), bfr[i][c], acc[i], 0, 0, 0);
+    // bounds of result rows 8g + 4h + i (register j = 4g + i)
+    v4f32 bq[4];
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq)
+      bq[gq] = *reinterpret_cast<const v4f32 *>(&sKb[t & 1][32 * rg + 8 * gq + 4 * hf]);
+    // code words: lane l holds word l % BPW of the wave's columns for row
+    // l / BPW of the row group
+    uint32_t out = 0u;
+    uint64_t anyu = 0u;
+    static_for<16 * BPW>([&](auto I) {
+      constexpr int i = decltype(I)::value / 16, j = decltype(I)::value % 16;
+      constexpr int r0 = 8 * (j / 4) + (j % 4); // rows r0 (low half) and r0 + 4
+      const float p = acc[i][j];
+      const uint64_t m = __ballot(p > 0.f);
+      out = write_lane<BPW * r0 + i>(out, (uint32_t)m);
+      out = write_lane<BPW * (r0 + 4) + i>(out, (uint32_t)(m >> 32));
+      anyu |= __ballot(fabsf(p) <= bq[j / 4][j % 4]);
+      asm volatile("" : "+s"(anyu)); // folded in as they come
+    });
+    {
+      const int r32 = lane / BPW;
+      if (lane < 32 * BPW && ((rmask >> r32) & 1u))
+        codes[key_index(U, 32 * rg + r32) * W + cb0 + lane % BPW] = out;
+    }
+    // Uncertain signs: the fp32 sign is stored above and the entry joins
+    // the wave's queue, whose fp64 chains run 64 at a time (one per lane)
+    // and patch the stored words.
+    if (anyu != 0u) {
+      // (the masks are taken again here rather than kept from above, which
+      // would hold many scalar registers through the stores)
+#pragma unroll
+      for (int i = 0; i < BPW; ++i) asm volatile("" : "+v"(acc[i]));
+      auto unc_of = [&](auto I) __attribute__((always_inline)) {
+        constexpr int i = decltype(I)::value / 16, j = decltype(I)::value % 16;
+        return __ballot(fabsf(acc[i][j]) <= bq[j / 4][j % 4]);
+      };
+      // entry of (block i, register j) for this lane: its result row
+      // 8(j/4) + 4h + j%4
+      auto entry = [&](int i, int j) __attribute__((always_inline)) {
+        const int r = 32 * rg + 8 * (j / 4) + 4 * hf + (j % 4);
+        return make_uint4(key_row(U, r), key_index(U, r) * W + cb0 + i,
+                          (uint32_t)(32 * (cb0 + i) + row) | ((uint32_t)row << 8), 0u);
+      };
+      uint32_t total = 0;
+      static_for<16 * BPW>([&](auto I) { total += (uint32_t)__popcll(unc_of(I)); });
+      if (qn + total > (uint32_t)kQueue) flush();
+      if (total <= (uint32_t)kQueue) {
+        static_for<16 * BPW>([&](auto I) {
+          const uint64_t unc = unc_of(I);
+          if (unc != 0u) { // wave-uniform
+            if ((unc >> lane) & 1u)
+              sQ[wave][qn + lanes_below_u64(unc)] = entry(decltype(I)::value / 16, decltype(I)::value % 16);
+            qn += (uint32_t)__popcll(unc);
+          }
+        });
+      } else { // more than the queue holds (degenerate rows such as zero
+               // keys): one (block, register) at a time
+        uint32_t ulo = 0u, uhi = 0u; // lane e: the mask of (e / 16, e % 16)
+        static_for<16 * BPW>([&](auto I) {
+          const uint64_t unc = unc_of(I);
+          ulo = write_lane<decltype(I)::value>(ulo, (uint32_t)unc);
+          uhi = write_lane<decltype(I)::value>(uhi, (uint32_t)(unc >> 32));
+        });
+        for (int e = 0; e < 16 * BPW; ++e) {
+          const uint64_t unc = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)ulo, e) |
+                               ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)uhi, e) << 32);
+          if (unc == 0u) continue; // wave-uniform
+          if ((unc >> lane) & 1u) sQ[wave][lanes_below_u64(unc)] = entry(e / 16, e % 16);
+          qn = (uint32_t)__popcll(unc);
+          flush();
+        }
+      }
+    }
+  };
+
+  // The steps.  Rows of steps t+1..t+3 are in flight while step t is
+  // scored; their register sets rotate through three slots (the loop is
+  // unrolled three times, with one exit, so the load waits at its entry
+  // count for every path).  The unit info of window w+1 is written, and
+  // that of window w+2 requested, at the first step of window w, after the
+  // step's barrier (the other slot's readers are past it).
+  uint4 S[kAhead][LPW];
+  StepUnits U0;
+#pragma unroll
+  for (int a = 0; a < kAhead; ++a) {
+    StepUnits Ua;
+    step_units(a, Ua);
+    load_rows(Ua, S[a]);
+    if (a == 0) U0 = Ua;
   }
-  if (qn != 0) flush();
+  constexpr int kStepsPerWin = kWin / UPS;
+  auto body = [&](auto Xc, int t) __attribute__((always_inline)) {
+    constexpr int A = decltype(Xc)::value;
+    stage(t, U0, S[A]);
+    __syncthreads();
+    if (t % kStepsPerWin == 0 && t > 0) { // first step of window w >= 1
+      const int w = t / kStepsPerWin;
+      win_store(w + 1);
+      win_request(w + 2);
+    }
+    StepUnits Un;
+    step_units(t + kAhead, Un); // (past the run: no rows, empty loads)
+    load_rows(Un, S[A]);
+    compute(t, U0);
+    step_units(t + 1, U0);
+  };
+  int t = 0;
+  for (; t + kAhead - 1 < ntile; t += kAhead) {
+    body(std::integral_constant<int, 0>{}, t);
+    body(std::integral_constant<int, 1>{}, t + 1);
+    body(std::integral_constant<int, 2>{}, t + 2);
+  }
+  if (t < ntile) body(std::integral_constant<int, 0>{}, t);
+  if (t + 1 < ntile) body(std::integral_constant<int, 1>{}, t + 1);
+  flush();
 }
 
 } // namespace
@@ -469,30 +626,34 @@ hipError_t launch_encode(const uint16_t *k_pool, int64_t num_blocks,
                          int b, uint32_t *codes, uint8_t *radii,
                          hipStream_t stream) {
   if (max_encode_len <= 0 || batch <= 0) return hipSuccess;
+  if (Hkv <= 0 || Hkv > 4096) return hipErrorInvalidValue; // rows of a page index in 16 bits
   // a range of n positions meets at most ceil(n/16) + 1 pages
   const int pages_max = (max_encode_len + kPage - 1) / kPage + 1;
-  const int64_t ntiles = (int64_t)batch * pages_max * Hkv;
-  if (ntiles > 0x7FFFFFFF - 65536) return hipErrorInvalidValue;
+  const int64_t nunits = (int64_t)batch * pages_max * Hkv;
+  if (nunits > 0x7FFFFFFF - 65536) return hipErrorInvalidValue;
   if ((int64_t)batch * max_blocks >= (int64_t)1 << 30) return hipErrorInvalidValue;
   // queued fixes name key rows and code words with 32-bit indices
   if ((uint64_t)num_blocks * kPage * Hkv * (b / 32) >= (uint64_t)1 << 32)
     return hipErrorInvalidValue;
-  // persistent: two workgroups of four waves per CU, over all parts
-  auto streams = [&](int parts) {
-    return std::min<int64_t>((ntiles + 3) / 4,
-                             std::max<int64_t>(1, 2LL * device_cu_count() / parts));
+  // persistent workgroups (three per CU, two for b = 256), each walking a
+  // run of units
+  auto groups = [&](int ups, int per_cu) {
+    return std::min<int64_t>((nunits + ups - 1) / ups,
+                             std::max<int64_t>(1, (int64_t)per_cu * device_cu_count()));
   };
-#define DKV_ENCODE_CASE(BV, NBV, HV)                                           \
+#define DKV_ENCODE_CASE(BV, NCBV)                                              \
   if (b == BV) {                                                               \
-    hipLaunchKernelGGL((encode_mfma_kernel<NBV, HV>), dim3((unsigned)(streams(HV) * HV)), \
-                       dim3(kMmThreads), 0, stream, k_pool, num_blocks,        \
+    using E = EncShape<NCBV>;                                                  \
+    hipLaunchKernelGGL((encode_mfma_kernel<NCBV>),                             \
+                       dim3((unsigned)groups(E::UPS, E::WAVES_PER_EU)),        \
+                       dim3(kEncThreads), 0, stream, k_pool, num_blocks,       \
                        block_table, max_blocks, batch, enc_start, enc_end,     \
                        max_encode_len, pages_max, proj, Hkv, codes, radii);    \
     return hipGetLastError();                                                  \
   }
-  DKV_ENCODE_CASE(64, 4, 1)
-  DKV_ENCODE_CASE(128, 4, 2)
-  DKV_ENCODE_CASE(256, 4, 4)
+  DKV_ENCODE_CASE(64, 2)
+  DKV_ENCODE_CASE(128, 4)
+  DKV_ENCODE_CASE(256, 8)
 #undef DKV_ENCODE_CASE
   return hipErrorInvalidValue;
 }
