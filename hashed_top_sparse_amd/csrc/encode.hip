@@ -161,16 +161,18 @@ __device__ __forceinline__ int radius_code_certain(float r2) {
 template <int NCB>
 struct EncShape {
   static constexpr int b = 32 * NCB, W = NCB;
-  static constexpr int X = NCB >= 4 ? 1 : 4 / NCB;   // row groups of 32 per step
-  static constexpr int WPR = kEncWaves / X;          // waves per row group
-  static constexpr int BPW = NCB / WPR;              // column blocks per wave
+  static constexpr int X = NCB >= 4 ? 1 : 2;         // row groups of 32 per step
+  static constexpr int BPW = NCB >= 8 ? 2 : 1;       // column blocks per wave
+  static constexpr int CW = NCB / BPW;               // waves across the columns
+  static constexpr int RGW = X * CW / kEncWaves;     // row groups per wave
   static constexpr int ROWS = 32 * X;                // rows per step
   static constexpr int UPS = 2 * X;                  // units per step
   static constexpr int LPW = 2 * X;                  // row loads (4 rows) per wave and step
   static constexpr int PT_BYTES = (b < 128 ? b : 128) * kHeadDim * 2; // P^T staging
   static constexpr int TILE_BYTES = 2 * ROWS * kTileRow;
   static constexpr int BUF_BYTES = PT_BYTES > TILE_BYTES ? PT_BYTES : TILE_BYTES;
-  static constexpr int WAVES_PER_EU = BPW == 1 && X == 1 ? 3 : 2;
+  static constexpr int WAVES_PER_EU = NCB == 4 ? 3 : 2;
+  static_assert(CW * (X / RGW) == kEncWaves, "the waves tile the step");
   static constexpr int PT_COLS = b < 128 ? b : 128;  // P^T columns staged at once
 };
 
@@ -184,7 +186,7 @@ void encode_mfma_kernel(const uint16_t *__restrict__ k_pool, int64_t num_blocks,
                         int pages_max, const uint16_t *__restrict__ proj, int Hkv,
                         uint32_t *__restrict__ codes, uint8_t *__restrict__ radii) {
   using E = EncShape<NCB>;
-  constexpr int b = E::b, W = E::W, X = E::X, WPR = E::WPR, BPW = E::BPW;
+  constexpr int b = E::b, W = E::W, X = E::X, CW = E::CW, BPW = E::BPW, RGW = E::RGW;
   constexpr int ROWS = E::ROWS, UPS = E::UPS, LPW = E::LPW;
   // P^T while the fragments are taken, then the two step tiles
   __shared__ __align__(16) unsigned char sBuf[E::BUF_BYTES];
@@ -199,8 +201,8 @@ void encode_mfma_kernel(const uint16_t *__restrict__ k_pool, int64_t num_blocks,
   __shared__ uint32_t sScan[kEncWaves];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-  const int rg = X == 1 ? 0 : wave / WPR; // the wave's row group
-  const int cb0 = (wave % WPR) * BPW;   // its first column block
+  const int rg0 = RGW == X ? 0 : (wave / CW) * RGW; // the wave's first row group
+  const int cb0 = (wave % CW) * BPW;                 // its first column block
   const int hf = lane >> 5, row = lane & 31;
   // positions a block table row reaches (the host keeps max_blocks at or
   // below DKV_MAX_SEQ_LEN / 16, so this fits an int)
@@ -347,44 +349,39 @@ void encode_mfma_kernel(const uint16_t *__restrict__ k_pool, int64_t num_blocks,
   win_store(1);
   win_request(2);
   __syncthreads();
-  // the step's units (wave-uniform): block id (-1: no rows), slice, rows
+  // A step's units are read from the window in LDS where needed (index
+  // arrays held in registers would be placed in scratch memory): (block id
+  // or -1, slice | rows << 16).
   struct StepUnits {
-    int blk[UPS], q[UPS];
-    uint32_t rows[UPS];
+    const int2 *su;
   };
   auto step_units = [&](int t, StepUnits &U) __attribute__((always_inline)) {
     const int i0 = t * UPS;
-    const int2 *su = &sUnit[(i0 / kWin) & 1][i0 % kWin];
-#pragma unroll
-    for (int j = 0; j < UPS; ++j) {
-      const int2 v = su[j];
-      U.blk[j] = __builtin_amdgcn_readfirstlane(v.x);
-      const int y = __builtin_amdgcn_readfirstlane(v.y);
-      U.q[j] = y & 0xFFFF;
-      U.rows[j] = (uint32_t)y >> 16;
-    }
+    U.su = &sUnit[(i0 / kWin) & 1][i0 % kWin];
   };
-  // tile row r of a step (unit r / 16) -> (block, key index = the radius
-  // index; its code words start at key index * W): the page's row
-  // m = 16q + r % 16 is position m / Hkv of head m % Hkv
+  // unit j of a step, j the same in every lane
+  auto unit_uniform = [&](const StepUnits &U, int j, int &blk, int &q, uint32_t &rows)
+      __attribute__((always_inline)) {
+    const int2 v = U.su[j];
+    blk = __builtin_amdgcn_readfirstlane(v.x);
+    const int y = __builtin_amdgcn_readfirstlane(v.y);
+    q = y & 0xFFFF;
+    rows = (uint32_t)y >> 16;
+  };
+  // tile row r of a step (unit r / 16; r may differ between lanes) ->
+  // (block, key index = the radius index; its code words start at key
+  // index * W): the page's row m = 16q + r % 16 is position m / Hkv of
+  // head m % Hkv
   auto key_index = [&](const StepUnits &U, int r) __attribute__((always_inline)) -> uint32_t {
-    const int j = r >> 4;
-    int blk = U.blk[0], q = U.q[0];
-#pragma unroll
-    for (int jj = 1; jj < UPS; ++jj)
-      if (j == jj) blk = U.blk[jj], q = U.q[jj];
-    const uint32_t m = (uint32_t)(kPage * q + (r & 15));
+    const int2 v = U.su[r >> 4];
+    const uint32_t m = (uint32_t)(kPage * (v.y & 0xFFFF) + (r & 15));
     const uint32_t pos = Hkv == 1 ? m : __umulhi(m, hkv_magic);
     const uint32_t h = m - pos * (uint32_t)Hkv;
-    return ((uint32_t)blk * Hkv + h) * kPage + pos;
+    return ((uint32_t)v.x * Hkv + h) * kPage + pos;
   };
   auto key_row = [&](const StepUnits &U, int r) __attribute__((always_inline)) -> uint32_t {
-    const int j = r >> 4;
-    int blk = U.blk[0], q = U.q[0];
-#pragma unroll
-    for (int jj = 1; jj < UPS; ++jj)
-      if (j == jj) blk = U.blk[jj], q = U.q[jj];
-    return ((uint32_t)blk * Hkv + q) * kPage + (r & 15);
+    const int2 v = U.su[r >> 4];
+    return ((uint32_t)v.x * Hkv + (v.y & 0xFFFF)) * kPage + (r & 15);
   };
 
   // This wave's rows of a step: load instruction i covers step rows
@@ -393,14 +390,13 @@ void encode_mfma_kernel(const uint16_t *__restrict__ k_pool, int64_t num_blocks,
   // empty buffer and reads zeros.
   constexpr int row_bytes = kHeadDim * 2;
   auto load_rows = [&](const StepUnits &U, uint4 (&S)[LPW]) __attribute__((always_inline)) {
+    // (a wave's rows lie in one unit: rows 8X*wave .. 8X*wave + 8X - 1)
+    int blk, q;
+    uint32_t rows_;
+    unit_uniform(U, (8 * X * wave) >> 4, blk, q, rows_);
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int r0 = 8 * X * wave + 4 * i; // wave-uniform
-      const int j = r0 >> 4;
-      int blk = U.blk[0], q = U.q[0];
-#pragma unroll
-      for (int jj = 1; jj < UPS; ++jj)
-        if (j == jj) blk = U.blk[jj], q = U.q[jj];
       const uint16_t *base = blk >= 0 ? k_pool + ((int64_t)blk * Hkv + q) * kPage * kHeadDim : k_pool;
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<uint16_t *>(base), 0, blk >= 0 ? (uint32_t)(kPage * row_bytes) : 0u, 0x00020000u);
@@ -411,7 +407,9 @@ void encode_mfma_kernel(const uint16_t *__restrict__ k_pool, int64_t num_blocks,
 
   // the queue of uncertain signs: (key row, code word, column | bit << 8)
   uint32_t qn = 0;
-  // The queued chains run one per lane (lanes past the queue do nothing).
+  // The queued chains run one per lane (lanes past the queue do nothing),
+  // reading the key row and P from memory (a form that needs few registers:
+  // it runs inside the scoring).
   auto flush = [&]() __attribute__((always_inline)) {
     if (qn == 0) return; // wave-uniform
     // the words these entries patch were stored by this wave: let those
@@ -458,11 +456,7 @@ void encode_mfma_kernel(const uint16_t *__restrict__ k_pool, int64_t num_blocks,
       if ((lane & 15) / kSub == i) v = r2[i];
     const int r = 8 * X * wave + 4 * ((lane & 15) / kSub) + (lane >> 4);
     const bool lead = (lane & 15) % kSub == 0; // one lane per row
-    uint32_t urows = U.rows[0]; // (selects: r is per lane)
-#pragma unroll
-    for (int jj = 1; jj < UPS; ++jj)
-      if ((r >> 4) == jj) urows = U.rows[jj];
-    const uint32_t rmask = urows >> (r & 15);
+    const uint32_t rmask = ((uint32_t)U.su[r >> 4].y >> 16) >> (r & 15);
     const bool rin = (rmask & 1u) != 0u;
     // the row's bound; rows not encoded get -1, so no sign of theirs is
     // ever uncertain
@@ -478,28 +472,50 @@ void encode_mfma_kernel(const uint16_t *__restrict__ k_pool, int64_t num_blocks,
     if (rin && lead) radii[key_index(U, r)] = (uint8_t)r8;
   };
 
-  // Scoring of step t: this wave's row group against its columns.
+  // Scoring of step t: this wave's row groups against its columns (all
+  // matrix ops first, so that the groups' chains interleave).
   auto compute = [&](int t, const StepUnits &U) __attribute__((always_inline)) {
-    uint32_t rmask = U.rows[0] | (U.rows[1] << 16); // (selects, not an indexed array)
+    uint32_t rm[RGW]; // rows to encode per row group
 #pragma unroll
-    for (int g = 1; g < X; ++g)
-      if (rg == g) rmask = U.rows[2 * g] | (U.rows[2 * g + 1] << 16);
-    if (rmask == 0u) return; // wave-uniform
-    const unsigned char *tile = sBuf + (t & 1) * ROWS * kTileRow + 32 * rg * kTileRow;
-    uint4 R[8];
+    for (int rgl = 0; rgl < RGW; ++rgl) {
+      int blk_, q_;
+      uint32_t lo, hi;
+      unit_uniform(U, 2 * (rg0 + rgl), blk_, q_, lo);
+      unit_uniform(U, 2 * (rg0 + rgl) + 1, blk_, q_, hi);
+      rm[rgl] = lo | (hi << 16);
+    }
+    uint32_t rany = 0u;
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
-      R[c] = *reinterpret_cast<const uint4 *>(tile + row * kTileRow + 128 * hf + 16 * c);
-    v16f32 acc[BPW];
+    for (int rgl = 0; rgl < RGW; ++rgl) rany |= rm[rgl];
+    if (rany == 0u) return; // wave-uniform
+    const unsigned char *tile = sBuf + (t & 1) * ROWS * kTileRow;
+    uint4 R[RGW][8];
 #pragma unroll
-    for (int i = 0; i < BPW; ++i)
+    for (int rgl = 0; rgl < RGW; ++rgl)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) acc[i][j] = 0.f;
+      for (int c = 0; c < 8; ++c)
+        R[rgl][c] = *reinterpret_cast<const uint4 *>(
+            tile + (32 * (rg0 + rgl) + row) * kTileRow + 128 * hf + 16 * c);
+    v16f32 acc[RGW][BPW];
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
+    for (int rgl = 0; rgl < RGW; ++rgl)
 #pragma unroll
       for (int i = 0; i < BPW; ++i)
-        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_v8bf16(R[c]), bfr[i][c], acc[i], 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[rgl][i][j] = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int rgl = 0; rgl < RGW; ++rgl)
+#pragma unroll
+        for (int i = 0; i < BPW; ++i)
+          acc[rgl][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_v8bf16(R[rgl][c]), bfr[i][c],
+                                                                acc[rgl][i], 0, 0, 0);
+    static_for<RGW>([&](auto RG) {
+    constexpr int rgl = decltype(RG)::value;
+    const int rg = rg0 + rgl;
+    const uint32_t rmask = rm[rgl];
+    if (rmask == 0u) return; // wave-uniform
     // bounds of result rows 8g + 4h + i (register j = 4g + i)
     v4f32 bq[4];
 #pragma unroll
@@ -512,7 +528,7 @@ void encode_mfma_kernel(const uint16_t *__restrict__ k_pool, int64_t num_blocks,
     static_for<16 * BPW>([&](auto I) {
       constexpr int i = decltype(I)::value / 16, j = decltype(I)::value % 16;
       constexpr int r0 = 8 * (j / 4) + (j % 4); // rows r0 (low half) and r0 + 4
-      const float p = acc[i][j];
+      const float p = acc[rgl][i][j];
       const uint64_t m = __ballot(p > 0.f);
       out = write_lane<BPW * r0 + i>(out, (uint32_t)m);
       out = write_lane<BPW * (r0 + 4) + i>(out, (uint32_t)(m >> 32));
@@ -531,10 +547,10 @@ void encode_mfma_kernel(const uint16_t *__restrict__ k_pool, int64_t num_blocks,
       // (the masks are taken again here rather than kept from above, which
       // would hold many scalar registers through the stores)
 #pragma unroll
-      for (int i = 0; i < BPW; ++i) asm volatile("" : "+v"(acc[i]));
+      for (int i = 0; i < BPW; ++i) asm volatile("" : "+v"(acc[rgl][i]));
       auto unc_of = [&](auto I) __attribute__((always_inline)) {
         constexpr int i = decltype(I)::value / 16, j = decltype(I)::value % 16;
-        return __ballot(fabsf(acc[i][j]) <= bq[j / 4][j % 4]);
+        return __ballot(fabsf(acc[rgl][i][j]) <= bq[j / 4][j % 4]);
       };
       // entry of (block i, register j) for this lane: its result row
       // 8(j/4) + 4h + j%4
@@ -573,6 +589,7 @@ void encode_mfma_kernel(const uint16_t *__restrict__ k_pool, int64_t num_blocks,
         }
       }
     }
+    });
   };
 
   // The steps.  Rows of steps t+1..t+3 are in flight while step t is
