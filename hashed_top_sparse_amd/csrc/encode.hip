@@ -26,11 +26,14 @@ namespace {
 // columns x 16 dims each; the products are exact in fp32, the sums are fp32).
 // A sign is certain when |p32| exceeds a bound on the fp32 summation error
 // in any order (Cauchy-Schwarz: sum |k_i P_ij| <= |k| |P_j|):
-//   |p32 - p| <= 2 (d+1) 2^-23 |k| max_j |P_j| + 2^-100,
-// four times the classic (d+1) 2^-24 bound (headroom for the fp32 norms
-// themselves; the 2^-100 term covers products that underflow; the largest
-// column norm of the wave's columns stands in for |P_j|, which only widens
-// the bound).  Uncertain bits are recomputed with the index-order fp64
+//   |p32 - p| <= (d+2) 2^-23 |k| max_j |P_j| + 2^-100.
+// A sum of d exact products with at most d roundings, each off by less than
+// 2^-23 of its result (an accumulator that truncates; round-to-nearest
+// halves that), errs by at most d 2^-23 (1 + 2^-15) sum |k_i P_ij|; the
+// factor (d+2)/d covers the fp32 norms (sums of d squares, each within
+// 2^-16 of the exact one) and the bound's own roundings.  The 2^-100 term
+// covers products that underflow; the largest column norm of the
+// workgroup's columns stands in for |P_j|, which only widens the bound.  Uncertain bits are recomputed with the index-order fp64
 // chain of the definition.  Likewise |k|^2: an fp32 sum gives the radius
 // code unless it lies near a code threshold (radius_code_certain); then the
 // fp64 chain decides.
@@ -271,12 +274,12 @@ void encode_mfma_kernel(const uint16_t *__restrict__ k_pool, int64_t num_blocks,
   }
 #pragma unroll
   for (int o = 16; o >= 1; o >>= 1) n2max = fmaxf(n2max, __shfl_xor(n2max, o));
-  // the bound's factor for every row: 2 (d+1) 2^-23 max_j |P_j| of the
+  // the bound's factor for every row: (d+2) 2^-23 max_j |P_j| of the
   // workgroup's columns (each wave's own would do; one value keeps the row
   // bounds shareable)
   __shared__ float sCn[kEncWaves];
   if (lane == 0) sCn[wave] = n2max;
-  constexpr float kBoundC = (float)(2 * (kHeadDim + 1)) * 0x1p-23f;
+  constexpr float kBoundC = (float)(kHeadDim + 2) * 0x1p-23f;
   // m / Hkv = umulhi(m, ceil(2^32 / Hkv)) for m < 2^16 (Hkv > 1)
   const uint32_t hkv_magic = Hkv > 1 ? (uint32_t)((0x100000000ull + (uint32_t)Hkv - 1u) / (uint32_t)Hkv) : 0u;
   __syncthreads(); // P^T read: the buffer becomes the step tiles
