@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
   __shared__ double sMax[kThreads / 64];
   __shared__ int sSum[8];
   __shared__ uint32_t sCount[3][kThreads / 64];
-  __shared__ SelectShared<kThreads> sel;
+  __shared__ __align__(16) SelectShared<kThreads> sel;
 
   // ---- sample plan: every SP-th candidate page from page pc0, nsp pages
   struct Plan {
@@ -177,10 +177,6 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
   const uint32_t *krow = reinterpret_cast<const uint32_t *>(
       k_pool + (((int64_t)max(a_blk, 0) * kPage + max(a_slot, 0)) * Hkv + g) * kHeadDim);
   const uint32_t krow_w = krow[threadIdx.x & (kHeadDim / 2 - 1)];
-
-  // the threshold histogram is cleared now (its first use is after the
-  // staging barrier)
-  for (int i = threadIdx.x; i < kHistBins; i += kThreads) sel.hist[i] = 0;
 
   if ((int)threadIdx.x < G * kHeadDim / 8) {
     const uint32_t w4[4] = {qv4.x, qv4.y, qv4.z, qv4.w};
@@ -300,18 +296,39 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     }
     return acc;
   };
+  // The query chains: thread t < HS*b runs the CPT chains of column
+  // j = t % b for heads (t / b) * CPT ..., each term's P_ij read and
+  // widened once for all of them (same terms, same order, same fused
+  // multiply-add per chain); HS = 2 keeps a wave on every SIMD.  The
+  // results go through LDS (the threshold histogram's space, cleared after)
+  // to the pair layout below: pair idx = h*b + j in thread idx % kThreads.
+  constexpr int HS = (G >= 2 && 2 * b <= kThreads) ? 2 : 1;
+  constexpr int CPT = G / HS;
+  double *hand = reinterpret_cast<double *>(sel.hist); // G*b <= 2048 doubles
+  static_assert(G * b * sizeof(double) <= sizeof(sel.hist), "hand-off space");
+  if ((int)threadIdx.x < HS * b) { // whole waves (b is a multiple of 64)
+    const int j = (int)threadIdx.x % b, h0 = ((int)threadIdx.x / b) * CPT;
+    double acc[CPT];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) acc[c] = 0.0;
+    constexpr int kUnroll = CPT >= 4 ? 4 : 8;
+#pragma unroll kUnroll
+    for (int i = 0; i < kHeadDim; ++i) {
+      const double pij = p_at(i, j);
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) acc[c] = fma(sQd[(h0 + c) * kHeadDim + i], pij, acc[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) hand[(h0 + c) * b + j] = acc[c];
+  }
+  __syncthreads();
   double p[kMaxPairs];
   double mloc = 0.0;
 #pragma unroll
   for (int r = 0; r < kMaxPairs; ++r) {
     const int idx = threadIdx.x + r * kThreads;
-    p[r] = 0.0;
-    if (idx < npairs) {
-      const int h = idx / b, j = idx % b;
-      const double acc = chain(sQd + h * kHeadDim, j);
-      p[r] = acc;
-      mloc = fmax(mloc, fabs(acc));
-    }
+    p[r] = idx < npairs ? hand[idx] : 0.0;
+    mloc = fmax(mloc, fabs(p[r]));
   }
   // the query heads' own sign codes (LSH buckets): pair idx = h*b + j
   uint64_t qsign[kMaxPairs];
@@ -322,6 +339,9 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
   __syncthreads();
   double M = sMax[0];
   for (int i = 1; i < kThreads / 64; ++i) M = fmax(M, sMax[i]);
+  // the threshold histogram, cleared for its first use (the hand-off reads
+  // are behind the barrier above)
+  for (int i = threadIdx.x; i < kHistBins; i += kThreads) sel.hist[i] = 0;
 
   // Global stores wait until the end of the kernel: a barrier would
   // otherwise wait for them to complete.
