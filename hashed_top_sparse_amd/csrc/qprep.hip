@@ -436,7 +436,8 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
 #pragma unroll
           for (int j = 0; j < 4; ++j) cw[j][ks] = x[j];
         }
-        const int mx = score_quad_max_seq<KS, G>(op, cw);
+        // (256-bit codes: the pages one after another, for the registers)
+        const int mx = KS > 1 ? score_quad_max_seq<KS, G>(op, cw) : score_quad_max<KS, G>(op, cw);
         const uint32_t r8 = sRad[wave][64 * a + lane];
         const int i = 4 * a + (lane >> 4);        // the wave's page index
         const int pos = (pc0 + (wave + kWv * i) * SP) * kPage + (lane & 15);
