@@ -221,37 +221,43 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
       const_cast<uint32_t *>(codes), 0, code_bytes, kBufferWord3);
   const __amdgpu_buffer_rsrc_t rad_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t *>(radii), 0, radius_bytes, kBufferWord3);
+  // (Issued by every workgroup: with no sample npw is 0, so every page id
+  // is ph_none and the loads read zeros.  Under a branch, the copies of the
+  // loaded values at its end would wait for the loads right there.)
   uint32_t qx[kWaveQuads][KS][4];
-  uint4 rline = make_uint4(0u, 0u, 0u, 0u);
-  if (sample) { // workgroup-uniform
+  uint4 rline;
+  {
     const auto rv = __builtin_amdgcn_raw_buffer_load_b128(rad_rsrc, (int)(ph_l * (uint32_t)kPage), 0, 0);
     rline = make_uint4(rv[0], rv[1], rv[2], rv[3]);
-    // The first half of the quads are loaded unconditionally (pages past the
-    // wave's share read zeros), the second half only when the sample needs
-    // them: a branch around each load would make the compiler copy the
-    // loaded words inside it, which waits for the load there.
+    auto load_quad = [&](int a) __attribute__((always_inline)) {
+      const uint32_t mine = (uint32_t)__shfl((int)ph_l, 4 * a + (lane >> 4));
+      const int voff = (int)(mine * page_bytes + key_byte);
 #pragma unroll
-    for (int a = 0; a < kWaveQuads; ++a) {
-      if (a < kWaveQuads / 2 || npw > 2 * kWaveQuads) { // wave-uniform
-        const uint32_t mine = (uint32_t)__shfl((int)ph_l, 4 * a + (lane >> 4));
-        const int voff = (int)(mine * page_bytes + key_byte);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          if constexpr (W == 2) {
-            const auto v = __builtin_amdgcn_raw_buffer_load_b64(code_rsrc, voff, 0, 0);
-            qx[a][ks][0] = v[0];
-            qx[a][ks][1] = v[1];
-            qx[a][ks][2] = 0u;
-            qx[a][ks][3] = 0u;
-          } else {
-            const auto v = __builtin_amdgcn_raw_buffer_load_b128(code_rsrc, voff + 16 * ks, 0, 0);
-            qx[a][ks][0] = v[0];
-            qx[a][ks][1] = v[1];
-            qx[a][ks][2] = v[2];
-            qx[a][ks][3] = v[3];
-          }
+      for (int ks = 0; ks < KS; ++ks) {
+        if constexpr (W == 2) {
+          const auto v = __builtin_amdgcn_raw_buffer_load_b64(code_rsrc, voff, 0, 0);
+          qx[a][ks][0] = v[0];
+          qx[a][ks][1] = v[1];
+          qx[a][ks][2] = 0u;
+          qx[a][ks][3] = 0u;
+        } else {
+          const auto v = __builtin_amdgcn_raw_buffer_load_b128(code_rsrc, voff + 16 * ks, 0, 0);
+          qx[a][ks][0] = v[0];
+          qx[a][ks][1] = v[1];
+          qx[a][ks][2] = v[2];
+          qx[a][ks][3] = v[3];
         }
       }
+    };
+    // The first half of the quads are loaded unconditionally (pages past the
+    // wave's share read zeros), the second half, under one branch, only when
+    // the sample needs them (its loaded words are copied, and so waited for,
+    // at the branch's end).
+#pragma unroll
+    for (int a = 0; a < kWaveQuads / 2; ++a) load_quad(a);
+    if (npw > 2 * kWaveQuads) { // wave-uniform
+#pragma unroll
+      for (int a = kWaveQuads / 2; a < kWaveQuads; ++a) load_quad(a);
     }
   }
 
