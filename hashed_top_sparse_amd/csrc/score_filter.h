@@ -99,13 +99,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
     const uint32_t *__restrict__ lthr, int B, int Hkv, int max_entries,
     int w, int sigma, uint2 *__restrict__ cand,
     uint32_t *__restrict__ tcount, int cand_groups,
-    int32_t *__restrict__ scores_out, int score_stride) {
+    int32_t *__restrict__ scores_out, int score_stride, int round_wgs) {
   constexpr int kDepth = kDepthFor<W>;
   constexpr int kLookahead = kLookaheadFor<W>;
   static_assert(kTaskQuads % kDepth == 0 && kTaskQuads >= 2 * kDepth, "prefetch rounds");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int stride = gridDim.x * kWaves;
   // linear radius weights of the 256 codes (before any wave can leave)
   __shared__ uint16_t wlut[LIN ? 256 : 1];
   if constexpr (LIN) {
@@ -184,7 +183,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
   // stride).  They are loaded before the stream starts, so decoding a task
   // inside the stream waits for no load (a load used at once would also
   // wait for every load issued before it: the stream's prefetch).
-  const int first = blockIdx.x * kWaves + wave;
+  //
+  // The wave's tasks are first, first + stride, ... below tend.  With one
+  // round of workgroups per CU (round_wgs each), the waves of a SIMD issue
+  // oldest first: the first workgroup placed on a CU streams fastest and
+  // the last slowest (on 16 x 128K keys with equal shares, 44, 47 and 56 us
+  // to the end on average, the last alone at the end).  So the rounds
+  // share the task list 13 : 10 : 8 per wave, oldest first: round 0 takes
+  // the first n0 * Wr tasks, round 1 the next n1 * Wr, round 2 the rest,
+  // each with the stride Wr (its waves), so the four waves of a workgroup
+  // still read four KV heads of the same page block side by side.
+  static_assert(kWgPerCu == 3, "three dispatch rounds");
+  int first = blockIdx.x * kWaves + wave, stride = gridDim.x * kWaves, tend = ntasks;
+  if (round_wgs > 0) {
+    const int Wr = round_wgs * kWaves;
+    const int64_t den = (int64_t)31 * Wr;
+    const int n0 = (int)(((int64_t)ntasks * 13 + den / 2) / den);
+    const int n1 = (int)(((int64_t)ntasks * 10 + den / 2) / den);
+    if (n0 >= 1) { // (few tasks: one stride over all waves)
+      const int c0 = min(ntasks, n0 * Wr);
+      const int c1 = min(ntasks - c0, n1 * Wr);
+      const int r = min((int)blockIdx.x / round_wgs, 2);
+      first = (r == 0 ? 0 : (r == 1 ? c0 : c0 + c1)) +
+              ((int)blockIdx.x - r * round_wgs) * kWaves + wave;
+      tend = r == 0 ? c0 : (r == 1 ? c0 + c1 : ntasks);
+      stride = Wr;
+    }
+  }
   int kbase = 0;
   uint32_t te0 = 0, te1 = 0, te2 = 0;
   auto load_entries = [&](int kb) {
@@ -220,10 +245,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
   };
   // the first non-empty task at or after t in this wave's stride
   auto find = [&](int t, Task &T) {
-    for (; t < ntasks; t += stride)
+    for (; t < tend; t += stride)
       if (decode(t, T)) return t;
     T.unit = -1;
-    return ntasks;
+    return tend;
   };
   // Lane j: physical page id (page block index) of the task's page j, or
   // ph_none past the task or for an invalid block id.
@@ -266,7 +291,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
 
   // ---- prologue: the first task, its successor, their page ids, operand
   Task C, T1;
-  const int tC = find(blockIdx.x * kWaves + wave, C);
+  const int tC = find(first, C);
   if (C.unit < 0) return;
   int t1 = find(tC + stride, T1);
   tabC[lane] = page_ids(C, load_pages(C));
@@ -317,7 +342,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 8))
   // loop head then match the steady state).
   auto run_task = [&]() -> bool {
     Task T2 = {0, 0, 0, -1, 0, 0, 0, 0, 0};
-    int t2 = ntasks;
+    int t2 = tend;
     int blk2 = -1; // raw block ids, turned into page ids one task later
     QueryOperandRaw<KS> op1;
     uint32_t L1 = 0;
@@ -507,15 +532,17 @@ hipError_t launch_filter_impl(const DecodeDims &d, const uint32_t *codes,
   const uint32_t radius_bytes = (uint32_t)((uint64_t)d.num_blocks * d.Hkv * kPage);
 #define DKV_SCORE_LAUNCH(WV, GV, DV)                                           \
   {                                                                            \
+    const int ncu = device_cu_count();                                         \
     const int64_t nwg = std::min<int64_t>((ntasks + kWaves - 1) / kWaves,       \
-                                          (int64_t)kWgPerCu * device_cu_count()); \
+                                          (int64_t)kWgPerCu * ncu);            \
     hipLaunchKernelGGL((filter_kernel<WV, GV, DV, LIN, PAGES>),                \
                        dim3((unsigned)nwg), dim3(kThreads), 0, stream, codes,  \
                        radii, d.num_blocks, code_bytes, radius_bytes,          \
                        block_table, d.max_blocks, tasks, d.n_max, qop,         \
                        qneg, lthr, d.B, d.Hkv, (int)max_entries, d.w,          \
                        d.sigma, cand, tcount, d.cand_groups, scores_out,       \
-                       d.max_seq_len);                                         \
+                       d.max_seq_len,                                          \
+                       nwg == (int64_t)kWgPerCu * ncu ? ncu : 0);              \
     return hipGetLastError();                                                  \
   }
 #define DKV_SCORE_CASE(WV, GV)                                                 \
