@@ -165,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
   // the block id, the row) and used only after the threshold: the newest
   // key lies in the window, and with no window the filter reads its code
   // after this kernel anyway.
-  __shared__ __align__(16) double sKd[kHeadDim];
+  __shared__ __align__(16) double sKd[3 * kHeadDim]; // a copy per wave that needs it
   int a_blk = -1;
   if (codes_w != nullptr && N > 0) { // workgroup-uniform
     const int blk = bt[(N - 1) / kPage];
@@ -312,6 +312,15 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
   constexpr int CPT = G / HS;
   double *hand = reinterpret_cast<double *>(sel.hist); // G*b <= 2048 doubles
   static_assert(G * b * sizeof(double) <= sizeof(sel.hist), "hand-off space");
+  // The newest key's code (append): its projection chains (one column a
+  // thread) and its |k|^2 chain run on the waves past the query chains when
+  // there are enough of them (b <= 128), each wave with its own copy of the
+  // row in LDS; otherwise on threads 0..b after the threshold.
+  constexpr int kKeyEarly0 = HS * b;
+  constexpr bool kKeyEarly = kKeyEarly0 + b + 64 <= kThreads;
+  constexpr int kKey0 = kKeyEarly ? kKeyEarly0 : 0; // the key's first thread
+  uint64_t key_bits = 0;
+  double r2 = 0.0;
   if ((int)threadIdx.x < HS * b) { // whole waves (b is a multiple of 64)
     const int j = (int)threadIdx.x % b, h0 = ((int)threadIdx.x / b) * CPT;
     double acc[CPT];
@@ -326,6 +335,19 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     }
 #pragma unroll
     for (int c = 0; c < CPT; ++c) hand[(h0 + c) * b + j] = acc[c];
+  } else if (kKeyEarly && a_blk >= 0 && (int)threadIdx.x < kKey0 + b + 64) { // whole waves
+    double *kd = sKd + (((int)threadIdx.x - kKey0) / 64) * kHeadDim;
+    kd[2 * lane] = (double)bf16_to_float(krow_w & 0xFFFFu);
+    kd[2 * lane + 1] = (double)bf16_to_float(krow_w >> 16);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if ((int)threadIdx.x < kKey0 + b) {
+      const double pk = chain(kd, (int)threadIdx.x - kKey0);
+      key_bits = __ballot(pk > 0.0); // columns of this wave's 64 threads
+    } else if ((int)threadIdx.x == kKey0 + b) {
+      for (int i = 0; i < kHeadDim; ++i) r2 = fma(kd[i], kd[i], r2);
+    }
   }
   __syncthreads();
   double p[kMaxPairs];
@@ -503,12 +525,12 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     const int kp = min(k / kPage, npc);
     L = (kp > 0 && kp < npc) ? 0u : 0xFFFFFFFFu;
   }
-  // ---- the newest key's code: threads 0..b-1 run the chain of column j =
-  // thread, and each |k|^2 (squares summed in index order)
-  const bool key_wave = a_blk >= 0 && (int)threadIdx.x < b; // wave-uniform
-  uint64_t key_bits = 0;
-  double r2 = 0.0;
-  if (a_blk >= 0) { // workgroup-uniform
+  // ---- the newest key's code, if not taken above: threads 0..b-1 run the
+  // chain of column j = thread, and thread b |k|^2 (squares summed in index
+  // order)
+  const bool key_wave = a_blk >= 0 && (int)threadIdx.x >= kKey0 &&
+                        (int)threadIdx.x < kKey0 + b; // wave-uniform
+  if (!kKeyEarly && a_blk >= 0) { // workgroup-uniform
     if (threadIdx.x < kHeadDim / 2) {
       sKd[2 * threadIdx.x] = (double)bf16_to_float(krow_w & 0xFFFFu);
       sKd[2 * threadIdx.x + 1] = (double)bf16_to_float(krow_w >> 16);
@@ -547,9 +569,11 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
   if (key_wave) {
     const int W32 = b / 32;
     uint32_t *cw = codes_w + (((int64_t)a_blk * Hkv + g) * kPage + a_slot) * W32;
-    if (lane < 2) cw[2 * wave + lane] = lane ? (uint32_t)(key_bits >> 32) : (uint32_t)key_bits;
+    if (lane < 2)
+      cw[2 * (((int)threadIdx.x - kKey0) / 64) + lane] =
+          lane ? (uint32_t)(key_bits >> 32) : (uint32_t)key_bits;
   }
-  if (a_blk >= 0 && (int)threadIdx.x == b)
+  if (a_blk >= 0 && (int)threadIdx.x == kKey0 + b)
     radii_w[((int64_t)a_blk * Hkv + g) * kPage + a_slot] = (uint8_t)radius_code(r2);
   // ---- the filter's task list: one entry (sequence, page group, length)
   // per group of kGroupKeys keys, sequence by sequence, after a count word
