@@ -562,18 +562,33 @@ void encode_mfma_kernel(const uint16_t *__restrict__ k_pool, int64_t num_blocks,
         return make_uint4(key_row(U, r), key_index(U, r) * W + cb0 + i,
                           (uint32_t)(32 * (cb0 + i) + row) | ((uint32_t)row << 8), 0u);
       };
-      uint32_t total = 0;
-      static_for<16 * BPW>([&](auto I) { total += (uint32_t)__popcll(unc_of(I)); });
+      // This lane's uncertain registers (bit 16 i + j for register j of
+      // block i), their count, and the lane's place in the queue: the
+      // counts of the lanes below, summed bit by bit with ballots (a count
+      // is at most 16 * BPW <= 32, six bits).
+      uint32_t um = 0u;
+      static_for<16 * BPW>([&](auto I) {
+        constexpr int i = decltype(I)::value / 16, j = decltype(I)::value % 16;
+        um |= (fabsf(acc[rgl][i][j]) <= bq[j / 4][j % 4] ? 1u : 0u) << decltype(I)::value;
+      });
+      const uint32_t ucount = (uint32_t)__popc(um);
+      uint32_t below = 0u, total = 0u;
+#pragma unroll
+      for (int bit = 0; bit < 6; ++bit) {
+        const uint64_t m = __ballot((ucount >> bit) & 1u);
+        below += lanes_below_u64(m) << bit;
+        total += (uint32_t)__popcll(m) << bit;
+      }
       if (qn + total > (uint32_t)kQueue) flush();
       if (total <= (uint32_t)kQueue) {
-        static_for<16 * BPW>([&](auto I) {
-          const uint64_t unc = unc_of(I);
-          if (unc != 0u) { // wave-uniform
-            if ((unc >> lane) & 1u)
-              sQ[wave][qn + lanes_below_u64(unc)] = entry(decltype(I)::value / 16, decltype(I)::value % 16);
-            qn += (uint32_t)__popcll(unc);
-          }
-        });
+        // each lane lists its own entries, in register order
+        uint32_t slot = qn + below;
+        while (um != 0u) {
+          const int e = __ffs(um) - 1;
+          um &= um - 1u;
+          sQ[wave][slot++] = entry(e / 16, e % 16);
+        }
+        qn += total;
       } else { // more than the queue holds (degenerate rows such as zero
                // keys): one (block, register) at a time
         uint32_t ulo = 0u, uhi = 0u; // lane e: the mask of (e / 16, e % 16)
