@@ -187,7 +187,8 @@ void encode_mfma_kernel(const uint16_t *__restrict__ k_pool, int64_t num_blocks,
                         int batch, const int32_t *__restrict__ enc_start,
                         const int32_t *__restrict__ enc_end, int max_encode_len,
                         int pages_max, const uint16_t *__restrict__ proj, int Hkv,
-                        uint32_t *__restrict__ codes, uint8_t *__restrict__ radii) {
+                        uint32_t *__restrict__ codes, uint8_t *__restrict__ radii,
+                        int round_wgs) {
   using E = EncShape<NCB>;
   constexpr int b = E::b, W = E::W, X = E::X, CW = E::CW, BPW = E::BPW, RGW = E::RGW;
   constexpr int ROWS = E::ROWS, UPS = E::UPS, LPW = E::LPW;
@@ -292,8 +293,36 @@ void encode_mfma_kernel(const uint16_t *__restrict__ k_pool, int64_t num_blocks,
   // Hkv + q): the slices of a page are neighbours.  Each workgroup walks a
   // run of UPS-aligned length.
   const int nunits = bal ? sPre[batch] * Hkv : batch * pages_max * Hkv;
-  const int chunk = ((nunits + (int)gridDim.x - 1) / (int)gridDim.x + UPS - 1) / UPS * UPS;
-  const int u_begin = (int)blockIdx.x * chunk, u_end = min(nunits, u_begin + chunk);
+  int u_begin, u_end;
+  if (round_wgs > 0) {
+    // One workgroup per CU and wave slot: WAVES_PER_EU rounds of round_wgs.
+    // The waves of a SIMD issue oldest first, so with equal runs the later
+    // rounds ended later (16 x 128K keys: 1236, 1329 and 1447 us on
+    // average).  The runs are weighted 35 : 33 : 30 (two rounds: 21 : 19),
+    // oldest first; the last round takes what is left.
+    constexpr int R = E::WAVES_PER_EU;
+    static_assert(R == 2 || R == 3, "two or three rounds");
+    constexpr int w0 = R == 3 ? 35 : 21, w1 = R == 3 ? 33 : 19, wsum = R == 3 ? 98 : 40;
+    const int r = min((int)blockIdx.x / round_wgs, R - 1);
+    const int v = (int)blockIdx.x - r * round_wgs;
+    auto run_of = [&](int wr) { // UPS-aligned run of a workgroup of weight wr
+      const int64_t per = ((int64_t)nunits * wr + (int64_t)wsum * round_wgs - 1) /
+                          ((int64_t)wsum * round_wgs);
+      return (int)((per + UPS - 1) / UPS * UPS);
+    };
+    const int c0 = run_of(w0), c1 = R == 3 ? run_of(w1) : 0;
+    const int64_t base_last = (int64_t)(c0 + c1) * round_wgs;
+    const int rest = (int)max((int64_t)0, (int64_t)nunits - base_last);
+    const int clast = ((rest + round_wgs - 1) / round_wgs + UPS - 1) / UPS * UPS;
+    const int c = r == 0 ? c0 : (r == R - 1 ? clast : c1);
+    const int64_t base = r == 0 ? 0 : (r == 1 ? (int64_t)c0 * round_wgs : base_last);
+    u_begin = (int)min((int64_t)nunits, base + (int64_t)v * c);
+    u_end = min(nunits, u_begin + c);
+  } else {
+    const int chunk = ((nunits + (int)gridDim.x - 1) / (int)gridDim.x + UPS - 1) / UPS * UPS;
+    u_begin = min(nunits, (int)blockIdx.x * chunk);
+    u_end = min(nunits, u_begin + chunk);
+  }
   if (u_begin >= u_end) return; // the whole workgroup: no barrier is left waiting
   const int ntile = (u_end - u_begin + UPS - 1) / UPS;
 
@@ -672,9 +701,10 @@ hipError_t launch_encode(const uint16_t *k_pool, int64_t num_blocks,
     return hipErrorInvalidValue;
   // persistent workgroups (three per CU, two for b = 256), each walking a
   // run of units
+  const int ncu = device_cu_count();
   auto groups = [&](int ups, int per_cu) {
     return std::min<int64_t>((nunits + ups - 1) / ups,
-                             std::max<int64_t>(1, (int64_t)per_cu * device_cu_count()));
+                             std::max<int64_t>(1, (int64_t)per_cu * ncu));
   };
 #define DKV_ENCODE_CASE(BV, NCBV)                                              \
   if (b == BV) {                                                               \
@@ -683,7 +713,9 @@ hipError_t launch_encode(const uint16_t *k_pool, int64_t num_blocks,
                        dim3((unsigned)groups(E::UPS, E::WAVES_PER_EU)),        \
                        dim3(kEncThreads), 0, stream, k_pool, num_blocks,       \
                        block_table, max_blocks, batch, enc_start, enc_end,     \
-                       max_encode_len, pages_max, proj, Hkv, codes, radii);    \
+                       max_encode_len, pages_max, proj, Hkv, codes, radii,     \
+                       groups(E::UPS, E::WAVES_PER_EU) ==                      \
+                               (int64_t)E::WAVES_PER_EU * ncu ? ncu : 0);      \
     return hipGetLastError();                                                  \
   }
   DKV_ENCODE_CASE(64, 2)
