@@ -82,8 +82,18 @@ bool make_dims(const dkv_config *cfg, int32_t batch, int32_t max_seq_len,
   d->n_max = (int)(by_blocks < max_seq_len ? by_blocks : max_seq_len);
   d->max_blocks = max_blocks;
   d->num_blocks = num_blocks;
-  const int cap = d->cap > 0 ? d->cap : 1;
-  d->nsplit = (cap + kAttnRows - 1) / kAttnRows;
+  // The list holds at most sigma sink rows, w window rows, then at most k
+  // top-k rows.  The prep launch attends over the window rows in one extra
+  // workgroup per unit when those fit beside its own workgroups in one
+  // round (they need a compute unit each); the split kernel then takes the
+  // sinks with the top-k rows.  Otherwise it takes the sinks and window in
+  // splits of their own.
+  const int nsw = (d->sigma + d->w + kAttnRows - 1) / kAttnRows;
+  d->window_in_prep = d->w > 0 && 2 * (int64_t)batch * d->Hkv <= device_cu_count();
+  d->nsplit_w = d->window_in_prep ? 1 : nsw;
+  d->nsplit = d->window_in_prep ? 1 + (d->sigma + d->k + kAttnRows - 1) / kAttnRows
+                                : nsw + (d->k + kAttnRows - 1) / kAttnRows;
+  d->nsplit_max = nsw + (d->sigma + d->k + kAttnRows - 1) / kAttnRows;
   d->cand_groups = (max_seq_len + kGroupKeys - 1) / kGroupKeys;
   d->bm_words = (max_seq_len + 31) / 32;
   // candidate regions are numbered with 32-bit ids
@@ -171,9 +181,9 @@ dkv_status decode_impl(const dkv_config *cfg, const void *q,
   // append: the prep kernel also encodes each sequence's newest key
   uint32_t *codes_w = append ? const_cast<uint32_t *>(codes) : nullptr;
   uint8_t *radii_w = append ? const_cast<uint8_t *>(radii) : nullptr;
-  if (!mark() || launch_prep(d, q16, p16, codes, radii, k16, codes_w, radii_w,
+  if (!mark() || launch_prep(d, q16, p16, codes, radii, k16, v16, codes_w, radii_w,
                              block_table, seq_lens, q8, qop, qneg, lthr, qbits,
-                             tasks, stream) != hipSuccess)
+                             tasks, part, stream) != hipSuccess)
     return DKV_ERR_LAUNCH;
   if (d.lsh_T > 0) {
     // bucket probe, then scoring of the pages that hold candidates
@@ -193,7 +203,8 @@ dkv_status decode_impl(const dkv_config *cfg, const void *q,
                               block_table, bitmap, rows, cnt, sel_idx, sel_cnt,
                               codes, radii, qop, qneg, stream) != hipSuccess)
     return DKV_ERR_LAUNCH;
-  if (!mark() || launch_attend(d, q16, k16, v16, rows, cnt, part, stream) !=
+  if (!mark() || launch_attend(d, q16, k16, v16, rows, cnt, seq_lens, block_table,
+                              part, stream) !=
                      hipSuccess)
     return DKV_ERR_LAUNCH;
   if (!mark() || launch_combine(d, part, out, stream) != hipSuccess)
@@ -246,7 +257,7 @@ WorkspacePlan plan_workspace(const DecodeDims &d) {
   p.cnt = off;
   off += align256(units * 4);
   p.part = off;
-  off += align256(units * d.nsplit * d.G * (kHeadDim + 2) * 4);
+  off += align256(units * d.nsplit_max * d.G * (kHeadDim + 2) * 4);
   p.qbits = off;
   off += align256((size_t)d.B * d.Hq * d.W * 4);
   p.tasks = off; // count word (padded to 16 bytes), then 16 bytes per group

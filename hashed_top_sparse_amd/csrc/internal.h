@@ -32,7 +32,13 @@ struct DecodeDims {
   int cand_groups;           // candidate groups per (sequence, KV head):
                              // ceil(max_seq_len / kGroupKeys)
   int bm_words;              // selection bitmap words per (sequence, KV head)
-  int nsplit;                // attention splits per (sequence, KV head)
+  int nsplit;                // attention split states per (sequence, KV head):
+  int nsplit_w;              // the first nsplit_w over its sink and window
+                             // rows, the rest over its top-k rows
+  bool window_in_prep;       // the window rows are attended by extra
+                             // workgroups of the prep launch (one state,
+                             // split 0), the sinks with the top-k rows
+  int nsplit_max;            // the most splits either way (workspace size)
 };
 
 // Byte offsets of the decode workspace regions (each 256-byte aligned).
@@ -71,14 +77,16 @@ hipError_t launch_encode(const uint16_t *k_pool, int64_t num_blocks,
 // With qbits (LSH decode) it also writes each query head's sign code
 // [B][Hq][b/32] and no threshold sample is taken (lthr = 0).  tasks: the
 // score filter's task list (see launch_score).
+// With d.window_in_prep the same launch also attends over every unit's
+// window rows (v_pool, part: as launch_attend), in workgroups of its own.
 hipError_t launch_prep(const DecodeDims &d, const uint16_t *q,
                        const uint16_t *proj, const uint32_t *codes,
                        const uint8_t *radii, const uint16_t *k_pool,
-                       uint32_t *codes_w, uint8_t *radii_w,
+                       const uint16_t *v_pool, uint32_t *codes_w, uint8_t *radii_w,
                        const int32_t *block_table,
                        const int32_t *seq_lens, int8_t *q8, uint32_t *qop,
                        float *qneg, uint32_t *lthr, uint32_t *qbits,
-                       uint32_t *tasks, hipStream_t stream);
+                       uint32_t *tasks, float *part, hipStream_t stream);
 
 // LSH (lsh.hip): the bucket index of positions [0, seq_lens[s]); the probe
 // that marks each unit's candidates in its bitmap [B*Hkv][bm_words]; and
@@ -142,10 +150,15 @@ hipError_t launch_merge(const DecodeDims &d, const uint2 *cand,
                         const uint32_t *qop, const float *qneg,
                         hipStream_t stream);
 
+// Attention splits over the selection list rows (physical row ids, cnt
+// per unit) into part [B*Hkv][nsplit][G][2 + d]; the sink and window rows
+// are found from the positions and the block table, or the window rows
+// were attended in the prep launch (d.window_in_prep).
 hipError_t launch_attend(const DecodeDims &d, const uint16_t *q,
                          const uint16_t *k_pool, const uint16_t *v_pool,
-                         const int32_t *rows, const int32_t *cnt, float *part,
-                         hipStream_t stream);
+                         const int32_t *rows, const int32_t *cnt,
+                         const int32_t *seq_lens, const int32_t *block_table,
+                         float *part, hipStream_t stream);
 
 hipError_t launch_combine(const DecodeDims &d, const float *part, float *out,
                           hipStream_t stream);

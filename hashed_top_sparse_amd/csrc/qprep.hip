@@ -40,6 +40,14 @@
 // to say more).
 #include <type_traits>
 
+// Window attention.  The window rows of a (sequence, KV head) are part of
+// its list whatever the scores are ([DeepSeek CSA]: the sliding window of
+// recent tokens is kept), so when the units leave compute units free, the
+// launch carries one more workgroup per unit that attends over them,
+// beside the prep workgroups, and leaves its state as the unit's first
+// attention split.  (The few sink rows go with the top-k rows: with them a
+// 512-row window would not split into whole tiles over the eight waves.)
+#include "attend_common.h"
 #include "encode_common.h"
 #include "score_common.h"
 #include "select_common.h"
@@ -66,8 +74,94 @@ __device__ __forceinline__ uint32_t e4m3_of_int(int v) {
   return sign | ((uint32_t)(e + 7) << 3) | mant;
 }
 
+// window tiles of a wave whose rows are in flight together (fewer at G = 8,
+// whose accumulators take 64 registers), and the batches whose row ids are
+// requested at the start
+template <int G> constexpr int kWinBatch = G <= 4 ? 4 : 2;
+constexpr int kWinIdBatches = 2;
+
+// The workgroup of unit `unit` that attends over its window rows (the
+// positions [ws, N)): wave v takes their 16-row tiles v, v + 8, v + 16,
+// ..., kWinBatch<G> tiles' rows requested at once; the eight wave states
+// merge in LDS (scratch, >= 38 KB) into part split 0.
+template <int G>
+__device__ __forceinline__ void window_attend(
+    int unit, const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_pool,
+    const uint16_t *__restrict__ v_pool, const int32_t *__restrict__ block_table,
+    int max_blocks, int64_t num_blocks, const int32_t *__restrict__ seq_lens, int n_max,
+    int Hq, int Hkv, int w, int sigma, float *__restrict__ part, int nsplit,
+    uint32_t *scratch) {
+  constexpr int nb = kWinBatch<G>;
+  const int s = unit / Hkv, g = unit % Hkv;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int N = seq_len_clamped(seq_lens, s, n_max);
+  const SinkWindow sw(N, w, sigma);
+  const int nwin = N - sw.ws;
+  const int nt = (nwin + kAttnTileRows - 1) / kAttnTileRows;
+  const int ntw = nt > wave ? (nt - wave + kWv - 1) / kWv : 0; // this wave's tiles
+  auto sp = reinterpret_cast<float(*)[kAttnTileRows][kAttnPStride]>(scratch);
+  auto sc = reinterpret_cast<float(*)[kAttnPStride]>(scratch + kWv * kAttnTileRows * kAttnPStride);
+  auto sm = reinterpret_cast<float(*)[G][kAttnPartStride]>(
+      scratch + kWv * (kAttnTileRows + 1) * kAttnPStride);
+  const int32_t *bt = block_table + (int64_t)s * max_blocks;
+  // Row ids, one per lane: register q of batch j holds in lane L row L%16
+  // of the wave's tile nb*j + 4q + L/16 (-1 for none).  Loads at clamped
+  // in-bounds addresses; unused values are dropped where used.
+  constexpr int nq = (nb + 3) / 4;
+  auto tile_of = [&](int j, int qq) { return nb * j + 4 * qq + lane / kAttnTileRows; };
+  auto row_of = [&](int jt) { return (wave + kWv * jt) * kAttnTileRows + lane % kAttnTileRows; };
+  auto id_load = [&](int j, int qq) {
+    return bt[clamp_int(sw.ws + row_of(tile_of(j, qq)), 0, max(N - 1, 0)) / kPage];
+  };
+  auto row_id = [&](int j, int qq, int raw) {
+    const int jt = tile_of(j, qq);
+    const int r = row_of(jt);
+    return (4 * qq + lane / kAttnTileRows < nb && jt < ntw && r < nwin && raw >= 0 &&
+            raw < num_blocks)
+               ? raw * kPage + (sw.ws + r) % kPage : -1;
+  };
+  // the first batches' block ids are all requested at once
+  int raw[kWinIdBatches][nq];
+#pragma unroll
+  for (int j = 0; j < kWinIdBatches; ++j)
+#pragma unroll
+    for (int qq = 0; qq < nq; ++qq) raw[j][qq] = id_load(j, qq);
+  AttnWave<G> aw;
+  aw.init(q + ((int64_t)s * Hq + (int64_t)g * G) * kHeadDim, lane, sp[wave], sc[wave]);
+  const int nbw = (ntw + nb - 1) / nb; // this wave's batches (wave-uniform)
+  for (int j = 0; j < nbw; ++j) {
+    int ids[nq];
+#pragma unroll
+    for (int qq = 0; qq < nq; ++qq) {
+      int v;
+      if (j < kWinIdBatches) { // (unrolled selection: no indexed register array)
+        v = raw[0][qq];
+#pragma unroll
+        for (int i = 1; i < kWinIdBatches; ++i) v = j == i ? raw[i][qq] : v;
+      } else {
+        v = id_load(j, qq);
+      }
+      ids[qq] = row_id(j, qq, v);
+    }
+    uint4 kt[nb][4], vt[nb][4];
+    uint32_t ok[nb], vok[nb];
+#pragma unroll
+    for (int t = 0; t < nb; ++t)
+      aw.load_tile(ids[t / 4], (t % 4) * kAttnTileRows, k_pool, v_pool, Hkv, g, kt[t], vt[t],
+                   ok[t], vok[t]);
+#pragma unroll
+    for (int t = 0; t < nb; ++t) aw.use_tile(kt[t], vt[t], ok[t], vok[t]);
+  }
+  aw.store(sm[wave]);
+  __syncthreads();
+  attn_merge_waves<G, kWv, kThreads>(sm, part + (int64_t)unit * nsplit * G * kAttnPartStride);
+}
+
 // WC: code words per key (b/32: 2, 4 or 8), fixed at compile time so the
 // sample loads need no branch on it; KS: 128-bit matrix-core K-steps.
+// Workgroups [0, nseq*Hkv) prepare a unit each; with v_pool, workgroups
+// [nseq*Hkv, 2*nseq*Hkv) attend over a unit's sinks and window each.
 template <int WC, int G, int KS = (WC > 4 ? WC / 4 : 1)>
 __global__ __launch_bounds__(kThreads) void prep_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ proj,
@@ -79,7 +173,8 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     uint32_t *__restrict__ qop, float *__restrict__ qneg,
     uint32_t *__restrict__ lthr, uint32_t *__restrict__ qbits,
     uint32_t *__restrict__ tasks, int Hq, int Hkv, int k, int w,
-    int sigma, bool lin, bool pages) {
+    int sigma, bool lin, bool pages, int nseq, const uint16_t *__restrict__ v_pool,
+    float *__restrict__ part, int nsplit) {
   constexpr int W = WC, b = 32 * WC;
   const int unit = blockIdx.x;
   const int s = unit / Hkv;
@@ -98,6 +193,14 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
   __shared__ int sSum[8];
   __shared__ uint32_t sCount[3][kThreads / 64];
   __shared__ __align__(16) SelectShared<kThreads> sel;
+  static_assert(sizeof(sP) >= 4 * kWv * ((kAttnTileRows + 1) * kAttnPStride +
+                                         8 * kAttnPartStride),
+                "window attention scratch");
+  if (unit >= nseq * Hkv) { // workgroup-uniform
+    window_attend<G>(unit - nseq * Hkv, q, k_pool, v_pool, block_table, max_blocks,
+                     num_blocks, seq_lens, n_max, Hq, Hkv, w, sigma, part, nsplit, sP);
+    return;
+  }
 
   // ---- sample plan: every SP-th candidate page from page pc0, nsp pages
   struct Plan {
@@ -592,7 +695,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     uint4 *entries = reinterpret_cast<uint4 *>(tasks + 4);
     for (uint32_t j = threadIdx.x; j < ng; j += kThreads)
       entries[before + j] = make_uint4((uint32_t)s, j, (uint32_t)N, 0u);
-    if (s == (int)(gridDim.x / Hkv) - 1 && threadIdx.x == 0) tasks[0] = before + ng;
+    if (s == nseq - 1 && threadIdx.x == 0) tasks[0] = before + ng;
   }
 }
 
@@ -601,22 +704,24 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
 hipError_t launch_prep(const DecodeDims &d, const uint16_t *q,
                        const uint16_t *proj, const uint32_t *codes,
                        const uint8_t *radii, const uint16_t *k_pool,
-                       uint32_t *codes_w, uint8_t *radii_w,
+                       const uint16_t *v_pool, uint32_t *codes_w, uint8_t *radii_w,
                        const int32_t *block_table,
                        const int32_t *seq_lens, int8_t *q8, uint32_t *qop,
                        float *qneg, uint32_t *lthr, uint32_t *qbits,
-                       uint32_t *tasks, hipStream_t stream) {
+                       uint32_t *tasks, float *part, hipStream_t stream) {
+  const int units = d.B * d.Hkv;
+  const int nwg = d.window_in_prep ? 2 * units : units;
   const uint32_t code_bytes = (uint32_t)((uint64_t)d.num_blocks * d.Hkv * d.W * kPage * 4);
   const uint32_t radius_bytes = (uint32_t)((uint64_t)d.num_blocks * d.Hkv * kPage);
 #define DKV_PREP_CASE(WV, GV)                                                  \
   if (d.W == WV && d.G == GV) {                                                \
-    hipLaunchKernelGGL((prep_kernel<WV, GV>), dim3(d.B * d.Hkv),               \
+    hipLaunchKernelGGL((prep_kernel<WV, GV>), dim3(nwg),                       \
                        dim3(kThreads), 0, stream, q, proj, codes, radii,       \
                        k_pool, codes_w, radii_w,                               \
                        d.num_blocks, code_bytes, radius_bytes, block_table,    \
                        d.max_blocks, seq_lens, d.n_max, q8, qop, qneg, lthr,   \
                        qbits, tasks, d.Hq, d.Hkv, d.k, d.w, d.sigma, d.lin,    \
-                       d.pages);                                               \
+                       d.pages, d.B, v_pool, part, d.nsplit);                  \
     return hipGetLastError();                                                  \
   }
   DKV_PREP_CASE(2, 1)
