@@ -220,7 +220,10 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
           // group g's candidates go to st[gpre[g] ..): wave v copies groups
           // v, v+16, ..., kStageRound groups' first 64 entries in flight at
           // once (every lane loads; entries past a group's count, and
-          // groups past the unit's, are not stored)
+          // groups past the unit's, are not stored).  The range of u the
+          // cut's histogram needs is taken on the way, and the histogram
+          // cleared, before the staging barrier.
+          uint32_t lo = 0xFFFFFFFFu, hi = 0u;
           for (int g0 = wave; g0 < ngs; g0 += kStageRound * kWaves) {
             uint2 e[kStageRound];
 #pragma unroll
@@ -233,7 +236,11 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
               const int gi = g0 + r * kWaves;
               if (gi < ngs) { // wave-uniform
                 const uint32_t b = gpre[gi], n = gpre[gi + 1] - b;
-                if ((uint32_t)lane < n) st[b + (uint32_t)lane] = e[r];
+                if ((uint32_t)lane < n) {
+                  st[b + (uint32_t)lane] = e[r];
+                  lo = min(lo, e[r].x);
+                  hi = max(hi, e[r].x);
+                }
               }
             }
             // entries past the first 64 of a group (rare)
@@ -242,11 +249,21 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
               const int gi = g0 + r * kWaves;
               if (gi < ngs) {
                 const uint32_t b = gpre[gi], n = gpre[gi + 1] - b;
-                for (uint32_t j = 64u + (uint32_t)lane; j < n; j += 64u)
-                  st[b + j] = cb[(int64_t)gi * kGroupKeys + j];
+                for (uint32_t j = 64u + (uint32_t)lane; j < n; j += 64u) {
+                  const uint2 x = cb[(int64_t)gi * kGroupKeys + j];
+                  st[b + j] = x;
+                  lo = min(lo, x.x);
+                  hi = max(hi, x.x);
+                }
               }
             }
           }
+          wave_min_max(lo, hi);
+          if (lane == 0) {
+            sel.red[0][wave] = lo;
+            sel.red[1][wave] = hi;
+          }
+          for (int i = tid; i < kHistBins; i += kThreads) sel.hist[i] = 0u;
           __syncthreads();
         }
         auto for_each = [&](auto fn) {
@@ -280,7 +297,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
           cut = true;
           Tpos = 0xFFFFFFFFu;
         } else if (staged) {
-          cut = wg_topk_cut<kThreads>(sel, for_each, (uint32_t)keff, Tu, Tpos);
+          cut = wg_topk_cut_ranged<kThreads>(sel, for_each, (uint32_t)keff, Tu, Tpos);
         }
         uint32_t Pt = 0; // otherwise: ties with (kPosMax - pos) >= Pt are kept
         if (!cut) {

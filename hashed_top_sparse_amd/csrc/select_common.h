@@ -58,6 +58,28 @@ __device__ __forceinline__ void find_threshold_bin(SelectShared<NT> &sh, uint32_
   __syncthreads();
 }
 
+// Minimum and maximum over a wave: every lane gets both (DPP steps within
+// each 16-lane row, then swaps across rows; no LDS round trips).
+__device__ __forceinline__ void wave_min_max(uint32_t &lo, uint32_t &hi) {
+  // quad perms [1,0,3,2] and [2,3,0,1], then the half-row and row mirrors
+#define DKV_MINMAX_DPP(C)                                                       \
+  lo = min(lo, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo, C, 0xF, 0xF, false)); \
+  hi = max(hi, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hi, C, 0xF, 0xF, false));
+  DKV_MINMAX_DPP(0xB1)
+  DKV_MINMAX_DPP(0x4E)
+  DKV_MINMAX_DPP(0x141)
+  DKV_MINMAX_DPP(0x140)
+#undef DKV_MINMAX_DPP
+  auto a = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+  lo = min(a[0], a[1]);
+  a = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+  hi = max(a[0], a[1]);
+  a = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+  lo = min(a[0], a[1]);
+  a = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+  hi = max(a[0], a[1]);
+}
+
 // Value range of the elements visit(fn) hands out, and the histogram of
 // (v - vmin) >> shift with the shift chosen so the range fits the bins.
 // Every thread must call it; ends with a barrier.
@@ -161,6 +183,11 @@ __device__ __forceinline__ void wg_kth_largest(SelectShared<NT> &sh, Visit visit
 // them exactly.  Returns false otherwise (the caller then searches with
 // wg_kth_largest).  Every thread must call it.
 template <int NT, class Visit2>
+__device__ __forceinline__ bool wg_topk_cut_tail(SelectShared<NT> &sh, Visit2 visit2,
+                                                 uint32_t kneed, uint32_t vmin, int shift,
+                                                 uint32_t &Tu, uint32_t &Tpos);
+
+template <int NT, class Visit2>
 __device__ __forceinline__ bool wg_topk_cut(SelectShared<NT> &sh, Visit2 visit2, uint32_t kneed,
                             uint32_t &Tu, uint32_t &Tpos) {
   uint32_t vmin;
@@ -168,6 +195,36 @@ __device__ __forceinline__ bool wg_topk_cut(SelectShared<NT> &sh, Visit2 visit2,
   wg_histogram<NT>(sh, [&](auto fn) {
     visit2([&](uint32_t u, int) { fn(u); });
   }, vmin, shift);
+  return wg_topk_cut_tail<NT>(sh, visit2, kneed, vmin, shift, Tu, Tpos);
+}
+
+// wg_topk_cut when the caller already has the range: sh.red[0][w] and
+// sh.red[1][w] hold wave w's minimum and maximum u, and sh.hist is zero,
+// both written before a barrier that every thread has passed.
+template <int NT, class Visit2>
+__device__ __forceinline__ bool wg_topk_cut_ranged(SelectShared<NT> &sh, Visit2 visit2,
+                                                   uint32_t kneed, uint32_t &Tu,
+                                                   uint32_t &Tpos) {
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    lo = min(lo, sh.red[0][i]);
+    hi = max(hi, sh.red[1][i]);
+  }
+  const uint32_t range = hi - lo;
+  const int bits = range == 0 ? 0 : 32 - __clz(range);
+  const int shift = bits > kHistBits ? bits - kHistBits : 0;
+  visit2([&](uint32_t u, int) { atomicAdd(&sh.hist[(u - lo) >> shift], 1u); });
+  __syncthreads();
+  return wg_topk_cut_tail<NT>(sh, visit2, kneed, lo, shift, Tu, Tpos);
+}
+
+// The rest of wg_topk_cut once sh.hist holds the histogram of
+// (u - vmin) >> shift (followed by a barrier).
+template <int NT, class Visit2>
+__device__ __forceinline__ bool wg_topk_cut_tail(SelectShared<NT> &sh, Visit2 visit2,
+                                                 uint32_t kneed, uint32_t vmin, int shift,
+                                                 uint32_t &Tu, uint32_t &Tpos) {
   find_threshold_bin<NT>(sh, kneed);
   const uint32_t b1 = (uint32_t)sh.bin;
   const uint32_t kneed2 = kneed - sh.above; // >= 1
