@@ -178,18 +178,84 @@ __device__ __forceinline__ int seq_len_clamped(const int32_t *seq_lens, int s,
   return clamp_int(seq_lens[s], 0, n_max);
 }
 
+// Wave-wide reductions and scans with every lane active, without LDS
+// round trips: DPP moves inside each 16-lane row (quad perms [1,0,3,2] and
+// [2,3,0,1], the half-row and row mirrors, whose sources are always in the
+// row), then the gfx950 swaps across rows 16 and 32 lanes apart.  Every
+// lane gets the result.
+#define DKV_DPP_ROW_ALL(X, OP, MOV)                                            \
+  X = OP(X, MOV(X, 0xB1));                                                     \
+  X = OP(X, MOV(X, 0x4E));                                                     \
+  X = OP(X, MOV(X, 0x141));                                                    \
+  X = OP(X, MOV(X, 0x140));
+#define DKV_DPP_MOV_U32(X, C)                                                  \
+  ((uint32_t)__builtin_amdgcn_update_dpp(0, (int)(X), C, 0xF, 0xF, false))
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
+#define DKV_ADD(A, B) ((A) + (B))
+  DKV_DPP_ROW_ALL(x, DKV_ADD, DKV_DPP_MOV_U32)
+#undef DKV_ADD
+  auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = a[0] + a[1];
+  a = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return a[0] + a[1];
+}
+__device__ __forceinline__ void wave_min_max(uint32_t &lo, uint32_t &hi) {
+#define DKV_MIN(A, B) min((A), (B))
+#define DKV_MAX(A, B) max((A), (B))
+  DKV_DPP_ROW_ALL(lo, DKV_MIN, DKV_DPP_MOV_U32)
+  DKV_DPP_ROW_ALL(hi, DKV_MAX, DKV_DPP_MOV_U32)
+  auto a = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+  lo = DKV_MIN(a[0], a[1]);
+  a = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+  hi = DKV_MAX(a[0], a[1]);
+  a = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+  lo = DKV_MIN(a[0], a[1]);
+  a = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+  hi = DKV_MAX(a[0], a[1]);
+#undef DKV_MIN
+#undef DKV_MAX
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+#define DKV_MAX(A, B) max((A), (B))
+  DKV_DPP_ROW_ALL(x, DKV_MAX, DKV_DPP_MOV_U32)
+  auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = DKV_MAX(a[0], a[1]);
+  a = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return DKV_MAX(a[0], a[1]);
+#undef DKV_MAX
+}
+// Maximum of non-negative doubles, whose bit patterns order as unsigned
+// 64-bit integers: the largest high word, then the largest low word among
+// the lanes that hold it.
+__device__ __forceinline__ double wave_max_nonneg_f64(double x) {
+  const uint64_t v = (uint64_t)__double_as_longlong(x);
+  const uint32_t hi = wave_max_u32((uint32_t)(v >> 32));
+  const uint32_t lo = wave_max_u32((uint32_t)(v >> 32) == hi ? (uint32_t)v : 0u);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Inclusive prefix sum over a wave in lane order: row_shr steps 1, 2, 4, 8
+// inside each 16-lane row (a lane whose source would lie outside its row
+// adds 0), then the totals of the rows below.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);
+  const uint32_t r0 = __builtin_amdgcn_readlane(x, 15);
+  const uint32_t r1 = __builtin_amdgcn_readlane(x, 31);
+  const uint32_t r2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+}
+
 // Exclusive prefix sum over a workgroup of NT threads (NT/64 waves), in
 // thread order.  tmp needs NT/64 words of LDS.  Every thread must call it.
 template <int NT>
 __device__ __forceinline__ uint32_t wg_exclusive_scan(uint32_t v, uint32_t *tmp,
                                                       uint32_t *total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
+  const uint32_t x = wave_inclusive_scan(v);
   if (lane == 63) tmp[wave] = x;
   __syncthreads();
   uint32_t base = 0, tot = 0;

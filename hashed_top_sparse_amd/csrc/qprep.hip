@@ -465,7 +465,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
   uint64_t qsign[kMaxPairs];
 #pragma unroll
   for (int r = 0; r < kMaxPairs; ++r) qsign[r] = __ballot(p[r] > 0.0);
-  for (int off = 32; off > 0; off >>= 1) mloc = fmax(mloc, __shfl_xor(mloc, off));
+  mloc = wave_max_nonneg_f64(mloc);
   if (lane == 0) sMax[wave] = mloc;
   __syncthreads();
   double M = sMax[0];
@@ -490,8 +490,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
       }
       qv[r] = v;
       sq8[idx] = v;
-      int sum = v; // one head per wave
-      for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+      const int sum = (int)wave_sum_u32((uint32_t)v); // one head per wave
       if (lane == 0) atomicAdd(&sSum[idx / b], sum);
     }
   }
@@ -584,12 +583,8 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
       }
     }
     // the count and range of the valid sample keys over the workgroup
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      nvalid += __shfl_xor(nvalid, off);
-      vlo = min(vlo, (uint32_t)__shfl_xor((int)vlo, off));
-      vhi = max(vhi, (uint32_t)__shfl_xor((int)vhi, off));
-    }
+    nvalid = wave_sum_u32(nvalid);
+    wave_min_max(vlo, vhi);
     if (lane == 0) {
       sCount[0][wave] = nvalid;
       sCount[1][wave] = vlo;

@@ -58,28 +58,6 @@ __device__ __forceinline__ void find_threshold_bin(SelectShared<NT> &sh, uint32_
   __syncthreads();
 }
 
-// Minimum and maximum over a wave: every lane gets both (DPP steps within
-// each 16-lane row, then swaps across rows; no LDS round trips).
-__device__ __forceinline__ void wave_min_max(uint32_t &lo, uint32_t &hi) {
-  // quad perms [1,0,3,2] and [2,3,0,1], then the half-row and row mirrors
-#define DKV_MINMAX_DPP(C)                                                       \
-  lo = min(lo, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo, C, 0xF, 0xF, false)); \
-  hi = max(hi, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hi, C, 0xF, 0xF, false));
-  DKV_MINMAX_DPP(0xB1)
-  DKV_MINMAX_DPP(0x4E)
-  DKV_MINMAX_DPP(0x141)
-  DKV_MINMAX_DPP(0x140)
-#undef DKV_MINMAX_DPP
-  auto a = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
-  lo = min(a[0], a[1]);
-  a = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
-  hi = max(a[0], a[1]);
-  a = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
-  lo = min(a[0], a[1]);
-  a = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
-  hi = max(a[0], a[1]);
-}
-
 // Value range of the elements visit(fn) hands out, and the histogram of
 // (v - vmin) >> shift with the shift chosen so the range fits the bins.
 // Every thread must call it; ends with a barrier.
@@ -92,11 +70,7 @@ __device__ __forceinline__ void wg_histogram(SelectShared<NT> &sh, Visit visit, 
     lo = min(lo, v);
     hi = max(hi, v);
   });
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    lo = min(lo, (uint32_t)__shfl_xor((int)lo, off));
-    hi = max(hi, (uint32_t)__shfl_xor((int)hi, off));
-  }
+  wave_min_max(lo, hi);
   if (lane == 0) {
     sh.red[0][wave] = lo;
     sh.red[1][wave] = hi;
