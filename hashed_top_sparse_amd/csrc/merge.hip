@@ -153,6 +153,11 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
       const uint2 *cb = cand + (int64_t)unit * cand_groups * kGroupKeys;
       const bool pre_lds = ngs <= kMaxGroupsLds;
       uint32_t nlist;
+      // The first staging round's entries (the first 64 of groups wave,
+      // wave + 16, ...) are requested right after the counts: their
+      // addresses do not depend on the counts, so both arrive in one round
+      // trip (entries past a group's count are dropped when staged).
+      uint2 e0[kStageRound];
       {
         constexpr int kPer = kMaxGroupsLds / kThreads;
         uint32_t c[kPer], part = 0;
@@ -160,6 +165,9 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
           uint32_t raw[kPer];
 #pragma unroll
           for (int i = 0; i < kPer; ++i) raw[i] = tc[min(tid * kPer + i, ngs - 1)];
+#pragma unroll
+          for (int r = 0; r < kStageRound; ++r)
+            e0[r] = cb[(int64_t)min(wave + r * kWaves, ngs - 1) * kGroupKeys + lane];
           write_sinks_window();
           sw_done = true;
 #pragma unroll
@@ -224,13 +232,8 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
           // cut's histogram needs is taken on the way, and the histogram
           // cleared, before the staging barrier.
           uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-          for (int g0 = wave; g0 < ngs; g0 += kStageRound * kWaves) {
-            uint2 e[kStageRound];
-#pragma unroll
-            for (int r = 0; r < kStageRound; ++r) {
-              const int gi = min(g0 + r * kWaves, ngs - 1);
-              e[r] = cb[(int64_t)gi * kGroupKeys + lane];
-            }
+          auto stage_round = [&](int g0, const uint2 (&e)[kStageRound])
+                                 __attribute__((always_inline)) {
 #pragma unroll
             for (int r = 0; r < kStageRound; ++r) {
               const int gi = g0 + r * kWaves;
@@ -257,6 +260,14 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
                 }
               }
             }
+          };
+          if (wave < ngs) stage_round(wave, e0); // (its loads were issued with the counts)
+          for (int g0 = wave + kStageRound * kWaves; g0 < ngs; g0 += kStageRound * kWaves) {
+            uint2 e[kStageRound];
+#pragma unroll
+            for (int r = 0; r < kStageRound; ++r)
+              e[r] = cb[(int64_t)min(g0 + r * kWaves, ngs - 1) * kGroupKeys + lane];
+            stage_round(g0, e);
           }
           wave_min_max(lo, hi);
           if (lane == 0) {

@@ -131,6 +131,28 @@ def test_short_and_empty_sequences():
                 check_unit(cfg, sub, gpu, codes, radii, s, g)
 
 
+@pytest.mark.parametrize("append", [False, True])
+def test_many_units_window_in_split_kernel(append):
+    """More (sequence, KV head) units than half the compute units: the window
+    rows are attended by the split kernel's own splits (taken from the
+    positions and the block table) instead of beside the query prep.  Ragged
+    short lengths put sequences below sinks + window too."""
+    import dataclasses
+    wl = dataclasses.replace(workloads.get("small_ragged_b128"), name="many_units_ragged",
+                             batch=160, ragged=(3, 900), seed=21)
+    cfg = config_of(wl)
+    inp = workloads.make_inputs(wl, DEV)
+    print(f"[case] {wl.name} units={wl.batch * wl.num_kv_heads} append={append}", flush=True)
+    if append:
+        gpu, codes, radii = gpu_decode_append(cfg, inp)
+    else:
+        codes, radii = gpu_encode_all(cfg, inp)
+        gpu = gpu_decode(cfg, inp, codes, radii, debug=True)
+    for s in range(wl.batch):
+        for g in range(wl.num_kv_heads):
+            check_unit(cfg, inp, gpu, codes, radii, s, g)
+
+
 def test_forced_ties_go_to_lowest_positions():
     """Identical keys everywhere: every score ties, the lowest positions win."""
     wl = workloads.get("small_gqa_b128")
