@@ -83,7 +83,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G <= 4
   __shared__ __attribute__((aligned(16))) float sc[kWaves][kAttnPStride];
   AttnWave<G> aw;
   aw.init(q + ((int64_t)s * Hq + (int64_t)g * G) * kHeadDim, lane, sp[wave], sc[wave]);
-  {
+  // the wave's rows (wave-uniform): a tile without any adds nothing to the
+  // state (its rows' weights are 0 and the rescale factor 1), so it is
+  // neither loaded nor used
+  const int wrows = r1 - (lo + wave * kWaveRows);
+  static_assert(kTiles == 2, "tile cases below");
+  if (wrows > kAttnTileRows) {
     // every tile's rows are requested at once, then used in order
     uint4 kt[kTiles][4], vt[kTiles][4];
     uint32_t ok[kTiles], vok[kTiles];
@@ -92,6 +97,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G <= 4
       aw.load_tile(myid, t * kAttnTileRows, k_pool, v_pool, Hkv, g, kt[t], vt[t], ok[t], vok[t]);
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) aw.use_tile(kt[t], vt[t], ok[t], vok[t]);
+  } else if (wrows > 0) {
+    uint4 kt[4], vt[4];
+    uint32_t ok, vok;
+    aw.load_tile(myid, 0, k_pool, v_pool, Hkv, g, kt, vt, ok, vok);
+    aw.use_tile(kt, vt, ok, vok);
   }
   __shared__ float sm[kWaves][G][kAttnPartStride];
   aw.store(sm[wave]);
