@@ -206,6 +206,12 @@ __global__ __launch_bounds__(kScoreWaves * 64) void lsh_score_kernel(
     const float *__restrict__ qneg, int B, int Hkv, int W, bool lin,
     const uint32_t *__restrict__ bitmap, int bm_stride, uint2 *__restrict__ cand,
     uint32_t *__restrict__ tcount, int cand_groups, int ntasks) {
+  // linear radius weights of the 256 codes (before any wave can leave)
+  __shared__ uint16_t wlut[256];
+  if (lin) { // workgroup-uniform
+    fill_linear_weights(wlut, kScoreWaves * 64);
+    __syncthreads();
+  }
   const int lane = threadIdx.x & 63;
   const int task = blockIdx.x * kScoreWaves + (threadIdx.x >> 6);
   if (task >= ntasks) return; // no barriers below
@@ -248,7 +254,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void lsh_score_kernel(
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
       if (pj[k] >= 0) { // wave-uniform
-        const int S = score_page<KS, G>(op, cw[k], r8[k], ok[k], lin);
+        const int S = score_page<KS, G>(op, cw[k], r8[k], ok[k], lin, wlut);
         const uint32_t mask = (uint32_t)__builtin_amdgcn_readlane((int)pm, pj[k]);
         const bool isc = lane < kPage && ((mask >> lane) & 1u);
         const uint64_t bal = __ballot(isc);

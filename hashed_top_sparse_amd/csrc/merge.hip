@@ -70,10 +70,12 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
   __shared__ __align__(16) uint2 st[kStage];
   __shared__ uint32_t gpre[kMaxGroupsLds + 1];
   __shared__ SelectShared<kThreads> sel;
+  __shared__ uint16_t wlut[256]; // linear radius weights (the exact rescan)
 
   const int unit = blockIdx.x;
   const int s = unit / Hkv, g = unit % Hkv;
   const int tid = threadIdx.x;
+  if (lin) fill_linear_weights(wlut, kThreads); // (many barriers before the rescan)
   const int lane = tid & 63, wave = tid >> 6;
   const int N = seq_len_clamped(seq_lens, s, n_max);
   const int ns = sigma < N ? sigma : N;
@@ -463,7 +465,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-              const int S = score_page<KS, G>(op, cw[u], r8[u], ok[u], lin);
+              const int S = score_page<KS, G>(op, cw[u], r8[u], ok[u], lin, wlut);
               const int pos = (p0 + u) * kPage + lane;
               const bool in_c = lane < kPage && pos >= c0 && pos < c1;
               if (pages) { // workgroup-uniform; the row max needs every lane

@@ -193,6 +193,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
   __shared__ int sSum[8];
   __shared__ uint32_t sCount[3][kThreads / 64];
   __shared__ __align__(16) SelectShared<kThreads> sel;
+  __shared__ uint16_t sWlin[256]; // linear radius weights (the sample)
   static_assert(sizeof(sP) >= 4 * kWv * ((kAttnTileRows + 1) * kAttnPStride +
                                          8 * kAttnPartStride),
                 "window attention scratch");
@@ -304,6 +305,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
     }
   }
   if (threadIdx.x < 8) sSum[threadIdx.x] = 0;
+  if (lin) fill_linear_weights(sWlin, kThreads); // (workgroup-uniform)
   __syncthreads();
 
   // ---- the sample pages' loads, in flight while the query is projected
@@ -573,7 +575,7 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(
         const int pos = (pc0 + (wave + kWv * i) * SP) * kPage + (lane & 15);
         const uint32_t ph_i = (uint32_t)__shfl((int)ph_l, i);
         const bool valid = i < npw && ph_i != ph_none && pos >= sigma && pos < N - w;
-        const uint32_t u = biased_score(__mul24(radius_weight(r8, lin), mx));
+        const uint32_t u = biased_score(__mul24(radius_weight_lut(r8, lin, sWlin), mx));
         if (valid) {
           us[a] = u;
           nvalid += 1;

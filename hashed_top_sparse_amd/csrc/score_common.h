@@ -48,6 +48,22 @@ __device__ __forceinline__ int radius_weight_linear(uint32_t r8) {
 __device__ __forceinline__ int radius_weight(uint32_t r8, bool lin) {
   return lin ? radius_weight_linear(r8) : (int)r8;
 }
+
+// The same through wlut, the 256 linear weights in LDS (filled by the
+// kernel when lin, before a barrier).  With a runtime `lin`, the compiler
+// turns radius_weight's choice into a select that evaluates the fp64 exp2
+// for every key, whichever weight is in use; a table read is cheap either
+// way.
+__device__ __forceinline__ int radius_weight_lut(uint32_t r8, bool lin,
+                                                 const uint16_t *wlut) {
+  return lin ? (int)wlut[r8 & 255u] : (int)r8;
+}
+
+// Fills wlut (LDS, 256 entries) with the linear weights; every thread of a
+// workgroup of nt threads calls it, and a barrier must follow.
+__device__ __forceinline__ void fill_linear_weights(uint16_t *wlut, int nt) {
+  for (int i = threadIdx.x; i < 256; i += nt) wlut[i] = (uint16_t)radius_weight_linear((uint32_t)i);
+}
 constexpr uint32_t kBufferWord3 = 0x00020000u; // raw buffer, gfx9 family
 
 template <int KS>
@@ -188,11 +204,12 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
 
 // S of the page whose code words (this lane's KS dwords) and radius byte
 // are given; valid in lanes 0..15 (slot = lane).  lin selects the linear
-// radius weight.  Every lane must call it.
+// radius weight, read from wlut (radius_weight_lut).  Every lane must call
+// it.
 template <int KS, int G>
 __device__ __forceinline__ int score_page(const QueryOperand<KS> &op,
                                           uint32_t (&cw_in)[KS], uint32_t r8,
-                                          bool ok, bool lin) {
+                                          bool ok, bool lin, const uint16_t *wlut) {
   // The loaded words are first read here: without this the compiler may
   // move their first use (the radius conversion) up to the loads and wait
   // for each load as it is issued.
@@ -212,7 +229,7 @@ __device__ __forceinline__ int score_page(const QueryOperand<KS> &op,
   if (G >= 2) m = fmaxf(m, 16.f * acc[2] + acc[3]);
   if (G >= 4) m = max_rows16(m);
   if (G >= 8) m = max_rows32(m);
-  int S = ok ? __mul24(radius_weight(r8, lin), (int)m) : 0;
+  int S = ok ? __mul24(radius_weight_lut(r8, lin, wlut), (int)m) : 0;
   // computed in every lane so the radius load is not sunk into a store
   // branch (where it would wait for every outstanding load)
   asm volatile("" : "+v"(S));
