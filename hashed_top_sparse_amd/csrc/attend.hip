@@ -159,6 +159,86 @@ __global__ __launch_bounds__(kHeadDim) void attend_combine_kernel(
   out[(int64_t)sh * kHeadDim + dim] = (ll > 0.f) ? aa / ll : 0.f;
 }
 
+// Float maximum and sum over a wave, every lane active (DPP moves inside
+// rows, then the row swaps; see internal.h).
+__device__ __forceinline__ float wave_max_f32(float x) {
+  uint32_t v = __float_as_uint(x);
+#define DKV_FMAX(A, B) __float_as_uint(fmaxf(__uint_as_float(A), __uint_as_float(B)))
+  DKV_DPP_ROW_ALL(v, DKV_FMAX, DKV_DPP_MOV_U32)
+  auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = DKV_FMAX(r[0], r[1]);
+  r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  v = DKV_FMAX(r[0], r[1]);
+#undef DKV_FMAX
+  return __uint_as_float(v);
+}
+__device__ __forceinline__ float wave_sum_f32(float x) {
+  uint32_t v = __float_as_uint(x);
+#define DKV_FADD(A, B) __float_as_uint(__uint_as_float(A) + __uint_as_float(B))
+  DKV_DPP_ROW_ALL(v, DKV_FADD, DKV_DPP_MOV_U32)
+  auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = DKV_FADD(r[0], r[1]);
+  r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  v = DKV_FADD(r[0], r[1]);
+#undef DKV_FADD
+  return __uint_as_float(v);
+}
+
+// The merge for more than kCombineWide states (the 4 x 256K workload has
+// 34): one workgroup of 128 threads (one per dim) per (sequence, query
+// head).  Splits are taken 64 at a time with all their loads issued before
+// any is used (one round trip for up to 64 states): every thread loads its dim of the splits' accumulators, and the
+// first wave, one split a lane, their (m, l).  That wave takes the chunk's
+// maximum m*, each split's factor 2^(m_p - m*) (once per split, into LDS)
+// and the chunk's l = sum l_p 2^(m_p - m*).
+constexpr int kCombineWide = 64;
+
+__global__ __launch_bounds__(kHeadDim) void attend_combine_wide_kernel(
+    const float *__restrict__ part, float *__restrict__ out, int Hq, int Hkv,
+    int G, int nsplit) {
+  const int sh = blockIdx.x;
+  const int s = sh / Hq, hq = sh % Hq;
+  const int g = hq / G, h = hq % G;
+  const int unit = s * Hkv + g;
+  const int dim = threadIdx.x;
+  const float *src0 = part + ((int64_t)unit * nsplit * G + h) * kAttnPartStride;
+  const int64_t stride = (int64_t)G * kAttnPartStride;
+  __shared__ float sfac[kCombineWide];
+  __shared__ float sml[2];
+  float mm = -INFINITY, ll = 0.f, aa = 0.f;
+  for (int p0 = 0; p0 < nsplit; p0 += kCombineWide) { // workgroup-uniform
+    const int n = min(kCombineWide, nsplit - p0);
+    // loads at clamped in-bounds addresses; values past n are dropped at use
+    float ap[kCombineWide];
+#pragma unroll
+    for (int i = 0; i < kCombineWide; ++i)
+      ap[i] = src0[(int64_t)(p0 + min(i, n - 1)) * stride + 2 + dim];
+    if (dim < 64) { // the whole first wave
+      const float *src = src0 + (int64_t)(p0 + min(dim, n - 1)) * stride;
+      const float m_raw = src[0], l_raw = src[1];
+      const float mp = dim < n ? m_raw : -INFINITY;
+      const float mc = wave_max_f32(mp);
+      const float f = (mp == -INFINITY) ? 0.f : exp2f(mp - mc);
+      const float lc = wave_sum_f32(dim < n ? l_raw * f : 0.f);
+      sfac[dim] = f;
+      if (dim == 0) {
+        sml[0] = mc;
+        sml[1] = lc;
+      }
+    }
+    __syncthreads();
+    const float mc = sml[0];
+    if (mc != -INFINITY) { // workgroup-uniform
+      float ac = 0.f;
+#pragma unroll
+      for (int i = 0; i < kCombineWide; ++i) ac = fmaf(i < n ? ap[i] : 0.f, sfac[i], ac);
+      attn_merge_state(mm, ll, &aa, mc, sml[1], &ac, 1);
+    }
+    __syncthreads(); // sfac and sml are rewritten by the next chunk
+  }
+  out[(int64_t)sh * kHeadDim + dim] = (ll > 0.f) ? aa / ll : 0.f;
+}
+
 } // namespace
 
 hipError_t launch_attend(const DecodeDims &d, const uint16_t *q,
@@ -195,8 +275,14 @@ hipError_t launch_attend(const DecodeDims &d, const uint16_t *q,
 
 hipError_t launch_combine(const DecodeDims &d, const float *part, float *out,
                           hipStream_t stream) {
-  hipLaunchKernelGGL(attend_combine_kernel, dim3(d.B * d.Hq), dim3(kHeadDim),
-                     0, stream, part, out, d.Hq, d.Hkv, d.G, d.nsplit);
+  // up to 32 states: the per-thread merge (its loads match the state
+  // count); more: the wide merge, one round trip for up to 64
+  if (d.nsplit <= kCombineChunk)
+    hipLaunchKernelGGL(attend_combine_kernel, dim3(d.B * d.Hq), dim3(kHeadDim),
+                       0, stream, part, out, d.Hq, d.Hkv, d.G, d.nsplit);
+  else
+    hipLaunchKernelGGL(attend_combine_wide_kernel, dim3(d.B * d.Hq), dim3(kHeadDim),
+                       0, stream, part, out, d.Hq, d.Hkv, d.G, d.nsplit);
   return hipGetLastError();
 }
 
